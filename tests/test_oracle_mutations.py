@@ -1,0 +1,117 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check the pins catch them.
+
+Each mutation replaces one oracle function with a subtly wrong variant; at
+least one pin in ``test_oracle_pins`` must then fail. This guards the pins
+themselves: a pin set that a transposed operand or a wrong index slips
+through is not a pin.
+"""
+
+import inspect
+
+import numpy as np
+import pytest
+
+from oracle import bra_oracle as O
+import tests.test_oracle_pins as pins
+
+_orig_affinity = O.affinity
+_orig_softmax = O.softmax_attention
+_orig_mean = O.region_mean
+_orig_attend = O.attend
+
+
+def _transposed_affinity(Qr, Kr):
+    return _orig_affinity(Kr, Qr)
+
+
+def _ties_higher_index_first(A, k):
+    return np.argsort(A, axis=-1, kind="stable")[..., ::-1][..., : int(k)].astype(np.int32)
+
+
+def _column_major_regions(H, W, S, r):
+    sh, sw = H // S, W // S
+    rj, ri = divmod(int(r), S)
+    ys, xs = np.meshgrid(np.arange(ri * sh, (ri + 1) * sh), np.arange(rj * sw, (rj + 1) * sw), indexing="ij")
+    return ys.reshape(-1), xs.reshape(-1)
+
+
+def _swapped_region_extent(H, W, S, r):
+    sw, sh = H // S, W // S  # rows/cols of a region swapped
+    ri, rj = divmod(int(r), S)
+    ys, xs = np.meshgrid(np.arange(ri * sh, (ri + 1) * sh), np.arange(rj * sw, (rj + 1) * sw), indexing="ij")
+    ys, xs = ys.reshape(-1), xs.reshape(-1)
+    return np.minimum(ys, H - 1), np.minimum(xs, W - 1)
+
+
+def _no_scale(q, kg, vg, scale):
+    return _orig_softmax(q, kg, vg, 1.0)
+
+
+def _softmax_over_queries(q, kg, vg, scale):
+    s = (q @ kg.T) * scale
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=0, keepdims=True)) @ vg
+
+
+def _dropped_max_term_key(q, kg, vg, scale):
+    # drops the last gathered key (an off-by-one in the gather length)
+    return _orig_softmax(q, kg[:-1], vg[:-1], scale)
+
+
+def _sum_not_mean(X, S):
+    B, H, W, C = np.shape(X)
+    return _orig_mean(X, S) * ((H // S) * (W // S))
+
+
+def _interleaved_heads(Q, K, V, routes, heads, S, scale=None):
+    Q = np.asarray(Q)
+    C = Q.shape[-1]
+    d = C // heads
+    perm = np.arange(C).reshape(d, heads).T.reshape(-1)
+    inv = np.argsort(perm)
+    return _orig_attend(Q[..., perm], np.asarray(K)[..., perm], np.asarray(V)[..., perm], routes, heads, S, scale)[..., inv]
+
+
+MUTATIONS = {
+    "transposed_affinity": ("affinity", _transposed_affinity),
+    "ties_higher_index_first": ("topk_route", _ties_higher_index_first),
+    "column_major_regions": ("region_token_coords", _column_major_regions),
+    "swapped_region_extent": ("region_token_coords", _swapped_region_extent),
+    "no_softmax_scale": ("softmax_attention", _no_scale),
+    "softmax_over_queries": ("softmax_attention", _softmax_over_queries),
+    "dropped_gathered_key": ("softmax_attention", _dropped_max_term_key),
+    "pool_sum_not_mean": ("region_mean", _sum_not_mean),
+    "interleaved_head_channels": ("attend", _interleaved_heads),
+}
+
+
+def _pin_cases():
+    """Every pin test with one representative parameter set."""
+    cases = []
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        marks = getattr(fn, "pytestmark", [])
+        params = [m for m in marks if m.name == "parametrize"]
+        if not params:
+            cases.append((fn, {}))
+            continue
+        argnames, values = params[0].args[0], params[0].args[1]
+        names = [a.strip() for a in argnames.split(",")]
+        for v in values:
+            v = v if isinstance(v, tuple) else (v,)
+            cases.append((fn, dict(zip(names, v))))
+    return cases
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(mutation, monkeypatch):
+    attr, fn = MUTATIONS[mutation]
+    monkeypatch.setattr(O, attr, fn)
+    failures = 0
+    for case, kwargs in _pin_cases():
+        try:
+            case(**kwargs)
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures > 0, f"no pin caught mutation {mutation}"

@@ -1,0 +1,249 @@
+"""Pins of the fp64 CPU oracle against facts fixed by the pages and by mathematics.
+
+No test here uses the HIP path. Each pin is chosen so that a plausible slip in
+the oracle (a dropped term, a transposed operand, a wrong region or head
+index, a wrong scale, a wrong tie rule) fails at least one of them.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bra_oracle as O
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# --------------------------------------------------------------------------- #
+# Pool + affinity: region-mean affinity equals the mean token-pair affinity
+# (paper summary, Section 6 "Conclusion", regional representations).
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize(
+    "B,H,W,C,S",
+    [(2, 6, 6, 8, 3), (1, 6, 9, 5, 3), (1, 4, 8, 3, 2), (1, 8, 4, 4, 4), (2, 5, 5, 7, 1)],
+)
+def test_affinity_equals_mean_pairwise_token_affinity(B, H, W, C, S):
+    Q = _rand((B, H, W, C), 1)
+    K = _rand((B, H, W, C), 2)
+    A = O.affinity(O.region_mean(Q, S), O.region_mean(K, S))
+    A_ref = brute.pairwise_region_affinity(Q, K, S)
+    np.testing.assert_allclose(A, A_ref, rtol=1e-12, atol=1e-12)
+    if S > 1:
+        # rows are query regions, columns key regions: not symmetric in general
+        assert not np.allclose(A, np.swapaxes(A, -1, -2))
+
+
+def test_region_mean_hand_example():
+    # 4x4 map, S=2, one channel holding its flat index: region 0 is rows 0-1,
+    # cols 0-1 -> values 0,1,4,5 -> mean 2.5; region 1 -> 2,3,6,7 -> 4.5;
+    # region 2 -> 8,9,12,13 -> 10.5; region 3 -> 12.5.
+    X = np.arange(16, dtype=np.float64).reshape(1, 4, 4, 1)
+    np.testing.assert_array_equal(O.region_mean(X, 2)[0, :, 0], [2.5, 4.5, 10.5, 12.5])
+    # 2x6 map, S=2: regions are 1x3; region 1 = row 0, cols 3-5 -> 3,4,5
+    X = np.arange(12, dtype=np.float64).reshape(1, 2, 6, 1)
+    np.testing.assert_array_equal(O.region_mean(X, 2)[0, :, 0], [1.0, 4.0, 7.0, 10.0])
+
+
+# --------------------------------------------------------------------------- #
+# Top-k routing
+# --------------------------------------------------------------------------- #
+def _brute_topk_row(row, k):
+    order = sorted(range(len(row)), key=lambda j: (-row[j], j))
+    return order[:k]
+
+
+@pytest.mark.parametrize("R,k", [(16, 2), (49, 1), (49, 4), (49, 16), (64, 4), (49, 49), (9, 9), (1, 1)])
+def test_topk_route_matches_full_sort(R, k):
+    rng = np.random.default_rng(R * 100 + k)
+    A = rng.standard_normal((3, R, R))
+    # plant exact ties (rounded values) in one image
+    A[1] = np.round(A[1], 1)
+    I = O.topk_route(A, k)
+    assert I.dtype == np.int32 and I.shape == (3, R, k)
+    for b in range(3):
+        for i in range(R):
+            row = A[b, i]
+            assert list(I[b, i]) == _brute_topk_row(list(row), k)
+            sel = set(I[b, i].tolist())
+            assert len(sel) == k and all(0 <= j < R for j in sel)
+            unsel = [row[j] for j in range(R) if j not in sel]
+            if unsel:
+                assert min(row[list(sel)]) >= max(unsel)
+    if k == R:
+        assert np.array_equal(np.sort(I, axis=-1), np.broadcast_to(np.arange(R), I.shape))
+
+
+def test_topk_ties_lower_index_first():
+    A = np.array([[[1.0, 3.0, 3.0, 2.0, 3.0]]])
+    assert O.topk_route(A, 3).tolist() == [[[1, 2, 4]]]
+    assert O.topk_route(A, 4).tolist() == [[[1, 2, 4, 3]]]
+    A = np.zeros((1, 1, 6))
+    assert O.topk_route(A, 2).tolist() == [[[0, 1]]]
+
+
+# --------------------------------------------------------------------------- #
+# Attention: special cases that reduce to textbook routines
+# --------------------------------------------------------------------------- #
+def _sdpa(Q, K, V, heads, scale=None):
+    B, H, W, C = Q.shape
+    d = C // heads
+
+    def split(X):
+        return torch.from_numpy(X).reshape(B, H * W, heads, d).permute(0, 2, 1, 3).contiguous()
+
+    o = torch.nn.functional.scaled_dot_product_attention(split(Q), split(K), split(V), scale=scale)
+    return o.permute(0, 2, 1, 3).reshape(B, H, W, C).numpy()
+
+
+@pytest.mark.parametrize(
+    "B,H,W,C,heads,S",
+    [(1, 8, 8, 8, 2, 2), (2, 6, 9, 6, 3, 3), (1, 4, 4, 4, 1, 4), (1, 6, 6, 12, 2, 1)],
+)
+def test_full_routing_equals_global_attention(B, H, W, C, heads, S):
+    Q, K, V = (_rand((B, H, W, C), s) for s in (3, 4, 5))
+    out, routes = O.bra(Q, K, V, heads, S, S * S)
+    ref = brute.global_attention(Q, K, V, heads)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(out, _sdpa(Q, K, V, heads), rtol=1e-10, atol=1e-12)
+
+
+def test_one_region_top1_equals_global_attention():
+    Q, K, V = (_rand((2, 5, 7, 8), s) for s in (6, 7, 8))
+    out, routes = O.bra(Q, K, V, heads=2, S=1, topk=1)
+    assert routes.tolist() == [[[0]], [[0]]]
+    np.testing.assert_allclose(out, _sdpa(Q, K, V, 2), rtol=1e-10, atol=1e-12)
+
+
+def test_scale_is_a_parameter_and_defaults_to_inverse_sqrt_d():
+    Q, K, V = (_rand((1, 4, 4, 8), s) for s in (9, 10, 11))
+    out1, _ = O.bra(Q, K, V, heads=2, S=2, topk=4, scale=1.0)
+    np.testing.assert_allclose(out1, _sdpa(Q, K, V, 2, scale=1.0), rtol=1e-10, atol=1e-12)
+    out_d, _ = O.bra(Q, K, V, heads=2, S=2, topk=4)
+    assert not np.allclose(out1, out_d)
+
+
+def _planted(B, H, W, C, S, seed, partner=None, noise=0.05):
+    """Q, K whose region means are scaled basis vectors: K region j has mean
+    4*e_j; Q region i has mean 4*e_i (+ 2*e_partner(i) when given), so the
+    region affinity is diagonally dominant (or has a known second choice)."""
+    R = S * S
+    assert C >= R
+    rng = np.random.default_rng(seed)
+    qm = np.zeros((R, C))
+    km = np.zeros((R, C))
+    for r in range(R):
+        km[r, r] = 4.0
+        qm[r, r] = 4.0
+        if partner is not None:
+            qm[r, partner[r]] += 2.0
+    sh, sw = H // S, W // S
+
+    def expand(m):
+        g = m.reshape(S, S, C).repeat(sh, axis=0).repeat(sw, axis=1)
+        return np.broadcast_to(g, (B, H, W, C))
+
+    Q = expand(qm) + noise * rng.standard_normal((B, H, W, C))
+    K = expand(km) + noise * rng.standard_normal((B, H, W, C))
+    V = rng.standard_normal((B, H, W, C))
+    return Q, K, V
+
+
+@pytest.mark.parametrize("B,H,W,C,heads,S", [(2, 8, 8, 8, 2, 2), (1, 6, 9, 12, 3, 3), (1, 4, 8, 4, 1, 2)])
+def test_planted_top1_routing_is_window_attention(B, H, W, C, heads, S):
+    R = S * S
+    Q, K, V = _planted(B, H, W, C, S, seed=12)
+    out, routes = O.bra(Q, K, V, heads, S, 1)
+    assert routes[..., 0].tolist() == [list(range(R))] * B
+    ref = brute.window_attention_over(Q, K, V, heads, S, routes)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+    # and it is not global attention
+    assert not np.allclose(out, brute.global_attention(Q, K, V, heads))
+
+
+def test_planted_top2_routing_gathers_the_partner_region():
+    B, H, W, C, heads, S = 2, 6, 9, 12, 3, 3
+    R = S * S
+    partner = [(r * 4 + 5) % R for r in range(R)]
+    partner = [p if p != r else (r + 1) % R for r, p in enumerate(partner)]
+    Q, K, V = _planted(B, H, W, C, S, seed=13, partner=partner)
+    out, routes = O.bra(Q, K, V, heads, S, 2)
+    for b in range(B):
+        assert routes[b].tolist() == [[r, partner[r]] for r in range(R)]
+    ref = brute.window_attention_over(Q, K, V, heads, S, routes)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_zero_keys_give_mean_of_first_k_regions():
+    B, H, W, C, heads, S, k = 2, 6, 6, 8, 2, 3, 3
+    Q = _rand((B, H, W, C), 14)
+    K = np.zeros((B, H, W, C))
+    V = _rand((B, H, W, C), 15)
+    out, routes = O.bra(Q, K, V, heads, S, k)
+    assert (routes == np.arange(k)).all()  # all affinities tie -> lowest indices
+    mean = brute.window_mean(V, S, range(k))
+    np.testing.assert_allclose(out, np.broadcast_to(mean[:, None, None, :], out.shape), rtol=1e-12, atol=1e-13)
+
+
+def test_unit_values_give_unit_output_and_convex_hull():
+    B, H, W, C, heads, S, k = 1, 8, 8, 8, 2, 4, 3
+    Q, K, V = (_rand((B, H, W, C), s) for s in (16, 17, 18))
+    out, _ = O.bra(Q, K, np.ones_like(V), heads, S, k)
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-13)
+    out, routes = O.bra(Q, K, V, heads, S, k)
+    for i in range(S * S):
+        gy, gx = O.gather_coords(H, W, S, routes[0, i])
+        qy, qx = O.region_token_coords(H, W, S, i)
+        lo = V[0, gy, gx, :].min(axis=0)
+        hi = V[0, gy, gx, :].max(axis=0)
+        o = out[0, qy, qx, :]
+        assert (o >= lo - 1e-12).all() and (o <= hi + 1e-12).all()
+
+
+def test_route_order_permutation_invariance():
+    B, H, W, C, heads, S, k = 2, 8, 8, 8, 2, 4, 5
+    Q, K, V = (_rand((B, H, W, C), s) for s in (19, 20, 21))
+    routes = O.route(Q, K, S, k)
+    rng = np.random.default_rng(22)
+    shuffled = np.array([[rng.permutation(row) for row in img] for img in routes])
+    a = O.attend(Q, K, V, routes, heads, S)
+    b = O.attend(Q, K, V, shuffled, heads, S)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- #
+# Printed example: attended tokens per stage (explainer, Part 6.3 table)
+# --------------------------------------------------------------------------- #
+def test_attended_tokens_match_the_pages_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "attended_tokens.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append([int(x) for x in line.split()])
+    assert len(rows) == 12
+    for H, W, S, k, expect in rows:
+        assert O.attended_tokens(H, W, S, k) == expect
+        # the gather really concatenates that many tokens
+        gy, gx = O.gather_coords(H, W, S, list(range(k)))
+        assert len(gy) == expect and len(set(zip(gy.tolist(), gx.tolist()))) == expect
+
+
+def test_check_config_rejects_undefined_shapes():
+    O.check_config(1, 56, 56, 64, 2, 7, 1)
+    with pytest.raises(ValueError):
+        O.check_config(1, 56, 56, 64, 2, 5, 1)  # S does not divide H
+    with pytest.raises(ValueError):
+        O.check_config(1, 56, 56, 64, 3, 7, 1)  # heads does not divide C
+    with pytest.raises(ValueError):
+        O.check_config(1, 56, 56, 64, 2, 7, 0)
+    with pytest.raises(ValueError):
+        O.check_config(1, 56, 56, 64, 2, 7, 50)
+    with pytest.raises(ValueError):
+        O.check_config(0, 56, 56, 64, 2, 7, 1)

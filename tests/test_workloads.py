@@ -1,0 +1,38 @@
+"""Seeded input generators: determinism, shapes, dtypes and the clustered recipe."""
+
+import torch
+
+from vision_transformer_dynamic_amd import workloads as wl
+
+
+def test_five_workloads_shapes():
+    assert len(wl.WORKLOADS) == 5
+    kv = [w.kv for w in wl.WORKLOADS]
+    assert kv == [32, 64, 64, 64, 1024]
+    assert all(w.d == 32 for w in wl.WORKLOADS)
+    assert wl.HEADLINE.H == 56 and wl.HEADLINE.S == 7
+
+
+def test_inputs_are_deterministic_and_typed():
+    w = wl.custom(2, 8, 8, 64, 2, 4, 2, dtype="bf16", seed=7)
+    a = wl.make_inputs(w)
+    b = wl.make_inputs(w)
+    for x, y in zip(a, b):
+        assert x.dtype == torch.bfloat16 and x.shape == (2, 8, 8, 64) and x.is_contiguous()
+        assert torch.equal(x, y)
+    c = wl.make_inputs(wl.custom(2, 8, 8, 64, 2, 4, 2, dtype="bf16", seed=8))
+    assert not torch.equal(a[0], c[0])
+
+
+def test_clustered_tokens_share_their_region_mean():
+    w = wl.custom(1, 16, 16, 32, 1, 4, 2, dtype="f32", seed=3, content="clustered")
+    q, k, v = wl.make_inputs(w)
+    # within-region spread ~0.5, between-region spread ~1: region means of the
+    # drawn tokens must be far closer to each other inside a region
+    g = q.reshape(1, 4, 4, 4, 4, 32).permute(0, 1, 3, 2, 4, 5).reshape(1, 16, 16, 32)
+    within = g.std(dim=2).mean().item()
+    between = g.mean(dim=2).std(dim=1).mean().item()
+    assert 0.4 < within < 0.6 and between > 0.7
+    # V is iid, not clustered
+    gv = v.reshape(1, 4, 4, 4, 4, 32).permute(0, 1, 3, 2, 4, 5).reshape(1, 16, 16, 32)
+    assert gv.std(dim=2).mean().item() > 0.85

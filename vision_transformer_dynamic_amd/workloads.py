@@ -1,0 +1,125 @@
+"""Seeded synthetic BRA workloads (shapes and input generators).
+
+This module only draws inputs; it holds none of the attention arithmetic,
+and both the HIP path's tests and the CPU oracle consume what it draws.
+
+The shapes follow the BiFormer pages: stage maps of a 224x224 image at
+S = 7 with top-k [1, 4, 16] (explainer "BiFormer Reshapes Visual Attention
+with 'Bi-Level Routing'", Part 4.3 "Model Scaling Specifications" and Part
+6.3 table; 64 attended tokens per query at every stage), and a dense
+prediction map at S = 8 (Part 4.3: S = 8 for segmentation). Head dim 32.
+No dataset or trained activation is used; the region-clustered workload
+stands in for spatially coherent features.
+
+Draw recipe (reproducibility only; parity never depends on it):
+``torch.Generator('cpu').manual_seed(seed)``, ``torch.randn`` float32 of
+shape [B, H, W, C] for Q, then K, then V. The clustered workload draws, in
+order, region means of Q [B, S*S, C], token noise of Q [B, H, W, C], the same
+two for K, then V; each token of Q (K) is its region's mean plus 0.5 times
+its noise. bf16 workloads are cast (round to nearest even) after composing.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, asdict
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    W: int
+    C: int
+    heads: int
+    S: int
+    topk: int
+    dtype: str  # "f32" or "bf16"
+    seed: int
+    content: str = "iid"  # "iid" or "clustered"
+
+    @property
+    def R(self) -> int:
+        return self.S * self.S
+
+    @property
+    def n(self) -> int:
+        return (self.H // self.S) * (self.W // self.S)
+
+    @property
+    def d(self) -> int:
+        return self.C // self.heads
+
+    @property
+    def kv(self) -> int:
+        return self.topk * self.n
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.H * self.W
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def asdict(self) -> dict:
+        return asdict(self)
+
+
+WORKLOADS = [
+    Workload("tiny-b1-16x16-c32-h1-s4-k2-f32", 1, 16, 16, 32, 1, 4, 2, "f32", 0),
+    Workload("stage1-b64-56x56-c64-h2-s7-k1-bf16", 64, 56, 56, 64, 2, 7, 1, "bf16", 1),
+    Workload("stage2-b64-28x28-c128-h4-s7-k4-bf16", 64, 28, 28, 128, 4, 7, 4, "bf16", 2),
+    Workload("stage3-b64-14x14-c256-h8-s7-k16-bf16", 64, 14, 14, 256, 8, 7, 16, "bf16", 3),
+    Workload("dense-b2-128x128-c64-h2-s8-k4-bf16-clustered", 2, 128, 128, 64, 2, 8, 4, "bf16", 4, "clustered"),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+# The headline workload: stage-1 shape, 56x56 map, S = 7.
+HEADLINE = WORKLOADS[1]
+
+
+def custom(B, H, W, C, heads, S, topk, dtype="bf16", seed=0, content="iid", name=None) -> Workload:
+    """An ad-hoc workload (tests of ragged and edge shapes)."""
+    name = name or f"custom-b{B}-{H}x{W}-c{C}-h{heads}-s{S}-k{topk}-{dtype}-{content}-seed{seed}"
+    return Workload(name, B, H, W, C, heads, S, topk, dtype, seed, content)
+
+
+def _expand_regions(means: torch.Tensor, H: int, W: int, S: int) -> torch.Tensor:
+    """[B, S*S, C] region means -> [B, H, W, C] with each token set to its
+    region's mean (regions row-major over the S x S grid)."""
+    B, R, C = means.shape
+    g = means.reshape(B, S, S, C)
+    g = g.repeat_interleave(H // S, dim=1).repeat_interleave(W // S, dim=2)
+    return g
+
+
+def make_inputs(w: Workload):
+    """Draw (Q, K, V) on the CPU in the workload's dtype, [B, H, W, C]."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(w.seed))
+    shape = (w.B, w.H, w.W, w.C)
+    if w.content == "iid":
+        q = torch.randn(shape, generator=gen, dtype=torch.float32)
+        k = torch.randn(shape, generator=gen, dtype=torch.float32)
+        v = torch.randn(shape, generator=gen, dtype=torch.float32)
+    elif w.content == "clustered":
+        mq = torch.randn((w.B, w.R, w.C), generator=gen, dtype=torch.float32)
+        nq = torch.randn(shape, generator=gen, dtype=torch.float32)
+        mk = torch.randn((w.B, w.R, w.C), generator=gen, dtype=torch.float32)
+        nk = torch.randn(shape, generator=gen, dtype=torch.float32)
+        v = torch.randn(shape, generator=gen, dtype=torch.float32)
+        q = _expand_regions(mq, w.H, w.W, w.S) + 0.5 * nq
+        k = _expand_regions(mk, w.H, w.W, w.S) + 0.5 * nk
+    else:
+        raise ValueError(f"unknown content kind {w.content!r}")
+    dt = w.torch_dtype
+    return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous()
+
+
+def to_f64(t: torch.Tensor):
+    """Exact upcast of a CPU/GPU tensor (fp32 or bf16) to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
