@@ -1,0 +1,125 @@
+/*
+ * bra.h - C ABI of the MI355X (gfx950) Bi-Level Routing Attention forward pass.
+ *
+ * Bi-Level Routing Attention (BRA), from BiFormer (CVPR 2023, arXiv 2303.08810),
+ * as described by the explainer "BiFormer Reshapes Visual Attention with
+ * 'Bi-Level Routing'", Part 2.2 "The Overall BRA Flow" (steps 1-4 and the
+ * PyTorch-style pseudocode), and by the paper summary "BiFormer: Vision
+ * Transformer with Bi-Level Routing Attention", Section 3 "Our Approach".
+ * Q, K, V are taken as already projected (the pseudocode's linear_qkv output);
+ * the local-context term (+ dwconv(V)) is not part of this operator.
+ *
+ * Tensors
+ *   Q, K, V, O : [B, H, W, C] row-major, channels fastest, all of one dtype,
+ *                caller-owned device memory, 16-byte aligned. O must not
+ *                alias Q, K or V.
+ *   idx        : [B, S*S, topk] int32 device memory, 4-byte aligned.
+ * Regions      : S must divide H and W (no padding). Region r covers rows
+ *                [(r/S)*H/S, (r/S+1)*H/S) and columns [(r%S)*W/S, (r%S+1)*W/S);
+ *                n = (H/S)*(W/S) tokens per region.
+ * Heads        : head m owns channels [m*d, (m+1)*d), d = C/heads. Supported:
+ *                d == 32. Routing is shared by all heads and uses all C channels.
+ * Scale        : softmax(q k^T / sqrt(d)).
+ * Limits       : 1 <= S*S <= 256, 1 <= topk <= S*S, B*H*W*C < 2^40.
+ *
+ * Streams and errors
+ *   Every call only enqueues work on `stream` (NULL = the legacy default
+ *   stream) and returns; none synchronises. Arguments are checked on the host
+ *   before anything is enqueued: a null pointer, a non-positive size, S not
+ *   dividing H or W, heads not dividing C, topk outside [1, S*S], a
+ *   misaligned pointer or a too-small workspace give BRA_EINVAL; a head dim,
+ *   region count or dtype this build does not implement gives
+ *   BRA_EUNSUPPORTED. A HIP error reported while enqueueing gives BRA_EHIP;
+ *   a failed workspace allocation gives BRA_ENOMEM. On any error nothing has
+ *   been enqueued, except for BRA_EHIP, where earlier launches of the same
+ *   call may already be queued. The library keeps no global state and is
+ *   thread-safe; calls that share a workspace must be ordered by the caller.
+ *
+ * Workspace
+ *   bra_forward and bra_route need bra_workspace_bytes(...) bytes of device
+ *   scratch (region descriptors and, for bra_forward, the routing table).
+ *   Pass a caller-owned buffer (256-byte aligned), or NULL/0 to let the call
+ *   allocate and free it stream-ordered (hipMallocAsync / hipFreeAsync) on
+ *   `stream`.
+ */
+#ifndef BRA_H_
+#define BRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* HIP's own stream handle type; repeated here so the header needs no HIP headers. */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum bra_dtype {
+  BRA_F32 = 0,  /* IEEE binary32 in, binary32 out */
+  BRA_BF16 = 1  /* bfloat16 in, bfloat16 out (round to nearest even) */
+} bra_dtype;
+
+typedef enum bra_status {
+  BRA_OK = 0,
+  BRA_EINVAL = 1,
+  BRA_EUNSUPPORTED = 2,
+  BRA_EHIP = 3,
+  BRA_ENOMEM = 4
+} bra_status;
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* bra_status_string(bra_status status);
+
+/* Bytes of device workspace that bra_forward and bra_route need for these
+ * sizes (0 if the sizes are invalid). */
+size_t bra_workspace_bytes(int B, int H, int W, int C, int S, int topk);
+
+/*
+ * bra_route - region-level routing (explainer Part 2.2, step 3, pseudocode
+ * steps 3-5; paper summary Section 3 "Region partition and routing").
+ *
+ * Computes the region means Q^r, K^r of Q and K (fp32 accumulation), the
+ * affinity A = Q^r (K^r)^T over all C channels in fp32, and writes to idx the
+ * topk largest entries of each row of A: idx[b][i][0..topk) in descending
+ * affinity, the lower region index first on exact ties. Deterministic: the
+ * same inputs give bit-identical idx, and bra_forward routes with exactly
+ * this table.
+ */
+bra_status bra_route(const void* Q, const void* K, int32_t* idx,
+                     int B, int H, int W, int C, int S, int topk,
+                     bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * bra_attend - token-level attention over routed regions (explainer Part 2.2,
+ * step 4, pseudocode steps 6-7 without the dwconv term; paper summary
+ * Section 3 "Token-to-token attention").
+ *
+ * For every image b, region i and head m, the queries of region i attend with
+ * softmax(q k^T / sqrt(d)) to the keys/values of the tokens of regions
+ * idx[b][i][0..topk), which are read straight from K and V (no gathered copy
+ * is made). fp32 accumulation and softmax; bf16 P for the P.V product on the
+ * bf16 path. idx entries are read from device memory: an entry outside
+ * [0, S*S) is never dereferenced and makes region i's output NaN.
+ */
+bra_status bra_attend(const void* Q, const void* K, const void* V,
+                      const int32_t* idx, void* O,
+                      int B, int H, int W, int C, int heads, int S, int topk,
+                      bra_dtype dtype, hipStream_t stream);
+
+/*
+ * bra_forward - the whole BRA forward: bra_route into the workspace, then
+ * bra_attend with that table (explainer Part 2.2 pseudocode steps 1 and
+ * 3-7 without the dwconv term). O = BRA(Q, K, V).
+ */
+bra_status bra_forward(const void* Q, const void* K, const void* V, void* O,
+                       int B, int H, int W, int C, int heads, int S, int topk,
+                       bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BRA_H_ */

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments on the host before any HIP call.
+
+Only argument combinations that fail validation are passed here; the fake
+device pointers are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import vision_transformer_dynamic_amd as bra
+from vision_transformer_dynamic_amd import build as bra_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bra.h")
+
+EINVAL, EUNSUP = bra.BRA_EINVAL, bra.BRA_EUNSUPPORTED
+P = 0x10000  # aligned fake device pointers (never dereferenced)
+P2, P3, P4, PW = 0x20000, 0x30000, 0x40000, 0x50000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bra.library_path()):
+        bra_build.build()
+    return bra.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bra_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_exactly_the_binding_exports():
+    assert _declared_functions() == sorted(bra.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bra.library_path()],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (bra_[a-z_]+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = lib.bra_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 3
+    assert lib.bra_status_string(0) == b"success"
+    assert lib.bra_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    # [Qr | Kr | idx], each rounded up to 256 bytes
+    B, H, W, C, S, k = 64, 56, 56, 64, 7, 1
+    pooled = 4 * B * 49 * C
+    idx = -(-4 * B * 49 * k // 256) * 256
+    assert lib.bra_workspace_bytes(B, H, W, C, S, k) == 2 * pooled + idx
+    assert lib.bra_workspace_bytes(1, 16, 16, 32, 4, 2) == 2 * 2048 + 256
+    assert lib.bra_workspace_bytes(1, 16, 16, 32, 5, 2) == 0  # S does not divide H
+    assert lib.bra_workspace_bytes(1, 16, 16, 32, 4, 17) == 0  # topk > S*S
+
+
+def _fwd(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4, ws=PW, wsb=1 << 20):
+    return lib.bra_forward(q, kk, v, o, B, H, W, C, heads, S, k, dt, ws, wsb, None)
+
+
+def _route(lib, B=1, H=16, W=16, C=32, S=4, k=2, dt=0, q=P, kk=P2, idx=P3, ws=PW, wsb=1 << 20):
+    return lib.bra_route(q, kk, idx, B, H, W, C, S, k, dt, ws, wsb, None)
+
+
+def _attend(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, idx=P4, o=PW):
+    return lib.bra_attend(q, kk, v, idx, o, B, H, W, C, heads, S, k, dt, None)
+
+
+@pytest.mark.parametrize("call", [_fwd, _route, _attend])
+@pytest.mark.parametrize(
+    "kwargs,status",
+    [
+        (dict(H=18), EINVAL),            # S does not divide H
+        (dict(W=10), EINVAL),            # S does not divide W
+        (dict(k=0), EINVAL),
+        (dict(k=17), EINVAL),            # topk > S*S
+        (dict(B=0), EINVAL),
+        (dict(C=-32), EINVAL),
+        (dict(S=0), EINVAL),
+        (dict(q=0), EINVAL),             # null pointer
+        (dict(q=P + 2), EINVAL),         # misaligned pointer
+        (dict(kk=0), EINVAL),
+        (dict(dt=7), EUNSUP),            # unknown dtype
+        (dict(S=17, H=17, W=17), EUNSUP),  # 289 regions
+        (dict(C=36), EUNSUP),            # C not a multiple of 8 (route) / d != 32
+    ],
+)
+def test_host_validation(lib, call, kwargs, status):
+    assert call(lib, **kwargs) == status
+
+
+@pytest.mark.parametrize("call", [_fwd, _attend])
+@pytest.mark.parametrize(
+    "kwargs,status",
+    [
+        (dict(heads=3), EINVAL),         # heads does not divide C
+        (dict(heads=0), EINVAL),
+        (dict(C=64, heads=1), EUNSUP),   # head dim 64
+        (dict(C=64, heads=4), EUNSUP),   # head dim 16
+        (dict(v=0), EINVAL),
+        (dict(o=P), EINVAL),             # output aliases Q
+    ],
+)
+def test_host_validation_heads_and_outputs(lib, call, kwargs, status):
+    assert call(lib, **kwargs) == status
+
+
+def test_attend_null_index_table(lib):
+    assert _attend(lib, idx=0) == EINVAL
+    assert _attend(lib, idx=P4 + 2) == EINVAL
+
+
+@pytest.mark.parametrize("call", [_fwd, _route])
+def test_workspace_validation(lib, call):
+    assert call(lib, wsb=16) == EINVAL           # too small
+    assert call(lib, ws=PW + 64) == EINVAL       # not 256-byte aligned
+    assert call(lib, ws=0, wsb=16) == EINVAL     # size without a buffer
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bra, "_lib", None)
+    monkeypatch.setenv("BRA_LIBRARY", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        bra.load_library()

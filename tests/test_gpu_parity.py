@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Inputs are the seeded synthetic workloads; the oracle sees the exact values
+the GPU sees (bf16 upcast exactly). Routing is checked with the tie-band rule,
+outputs against ``oracle.attend`` run with the GPU's own routing table (so a
+legitimate tie-band choice cannot show up as an output error). At the full
+workload sizes the GPU runs the whole batch in the launch configuration the
+benchmark uses and the oracle checks a sample of images.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import vision_transformer_dynamic_amd as bra
+from vision_transformer_dynamic_amd import workloads as wl
+from oracle import bra_oracle as O
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _gpu(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def _f64(t):
+    return wl.to_f64(t)
+
+
+def _sample_images(B, max_images=4):
+    if B <= max_images:
+        return list(range(B))
+    return sorted({0, 1, B // 2, B - 1})
+
+
+def _oracle_affinity(q64, k64, S):
+    return O.affinity(O.region_mean(q64, S), O.region_mean(k64, S))
+
+
+def _check_case(w, q, k, v, images=None, check_exact_routes=True):
+    """Route + attend + forward on the GPU for one workload; compare sampled
+    images with the oracle. Returns (route mismatches, max_abs, mean_rel)."""
+    print(f"\n[case] {w.name}", flush=True)
+    qd, kd, vd = _gpu(q, k, v)
+    idx = bra.route(qd, kd, w.S, w.topk)
+    out_attend = bra.attend(qd, kd, vd, idx, w.heads, w.S)
+    out_fwd = bra.forward(qd, kd, vd, w.heads, w.S, w.topk)
+    torch.cuda.synchronize()
+    # forward is exactly route followed by attend
+    assert torch.equal(out_fwd, out_attend)
+
+    images = images if images is not None else _sample_images(w.B)
+    q64, k64, v64 = _f64(q[images]), _f64(k[images]), _f64(v[images])
+    idx_np = idx.cpu().numpy()[images]
+    A = _oracle_affinity(q64, k64, w.S)
+    bad = parity.route_violations(A, idx_np, w.topk)
+    assert not bad, f"{w.name}: routing violations {bad[:5]}"
+    mism = parity.exact_route_mismatches(O.topk_route(A, w.topk), idx_np)
+    ref = O.attend(q64, k64, v64, idx_np, w.heads, w.S)
+    out = _f64(out_fwd.cpu()[images])
+    max_abs, mean_rel = parity.assert_output_close(out, ref, w.dtype, w.name)
+    print(f"[case] {w.name}: route mismatches {mism}, max-abs {max_abs:.3e}, mean-rel {mean_rel:.3e}", flush=True)
+    return mism, max_abs, mean_rel
+
+
+@pytest.mark.parametrize("w", wl.WORKLOADS, ids=[w.name for w in wl.WORKLOADS])
+def test_workload_parity(w):
+    q, k, v = wl.make_inputs(w)
+    mism, _, _ = _check_case(w, q, k, v)
+    # iid / clustered content has no near-ties at these sizes: the canonical
+    # table is reproduced exactly
+    assert mism == 0
+
+
+@pytest.mark.parametrize("w", wl.WORKLOADS[1:4], ids=[w.name for w in wl.WORKLOADS[1:4]])
+def test_full_size_route_all_images(w):
+    """Routing of every image of the full-size workloads against the oracle."""
+    q, k, _ = wl.make_inputs(w)
+    qd, kd = _gpu(q, k)
+    idx = bra.route(qd, kd, w.S, w.topk).cpu().numpy()
+    A = _oracle_affinity(_f64(q), _f64(k), w.S)
+    bad = parity.route_violations(A, idx, w.topk)
+    assert not bad, bad[:5]
+    assert parity.exact_route_mismatches(O.topk_route(A, w.topk), idx) == 0
+
+
+# Ragged and edge shapes: n not a multiple of 16, kv not a multiple of 64,
+# more than 64 queries per region, a partial head group, H != W, many regions,
+# full routing, one region, one token per region.
+EDGE = [
+    wl.custom(2, 6, 6, 32, 1, 2, 3, "bf16", seed=10),      # n=9, kv=27
+    wl.custom(1, 20, 20, 64, 2, 2, 2, "bf16", seed=11),    # n=100: two query blocks, ragged
+    wl.custom(1, 8, 12, 192, 6, 4, 5, "bf16", seed=12),    # H!=W, 6 heads: partial head group
+    wl.custom(1, 16, 16, 32, 1, 16, 7, "bf16", seed=13),   # 256 regions, n=1
+    wl.custom(1, 16, 16, 32, 1, 16, 256, "bf16", seed=14), # full routing over 256 regions
+    wl.custom(2, 12, 12, 64, 2, 3, 9, "bf16", seed=15),    # k = S*S
+    wl.custom(2, 9, 9, 64, 2, 1, 1, "bf16", seed=16),      # one region: global attention
+    wl.custom(1, 14, 14, 256, 8, 7, 16, "f32", seed=17),   # fp32, stage-3 shape
+    wl.custom(2, 24, 24, 64, 2, 3, 2, "f32", seed=18),     # fp32, n=64, two head group of 1
+    wl.custom(1, 32, 32, 64, 2, 2, 2, "f32", seed=19),     # fp32, n=256, 4 query blocks
+    wl.custom(3, 10, 15, 96, 3, 5, 4, "bf16", seed=20, content="clustered"),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=[w.name for w in EDGE])
+def test_edge_shapes(w):
+    q, k, v = wl.make_inputs(w)
+    _check_case(w, q, k, v, images=list(range(w.B)))
+
+
+def test_one_region_equals_global_attention():
+    w = wl.custom(2, 8, 8, 64, 2, 1, 1, "f32", seed=21)
+    q, k, v = wl.make_inputs(w)
+    out = bra.forward(*_gpu(q, k, v), w.heads, w.S, w.topk).cpu()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(t.double().reshape(2, 64, 2, 32).permute(0, 2, 1, 3) for t in (q, k, v)))
+    ref = ref.permute(0, 2, 1, 3).reshape(2, 8, 8, 64).numpy()
+    parity.assert_output_close(_f64(out), ref, "f32", "S=1 global attention")
+
+
+def test_zero_keys_route_to_lowest_indices_and_average_values():
+    w = wl.custom(2, 14, 14, 64, 2, 7, 5, "bf16", seed=22)
+    q, _, v = wl.make_inputs(w)
+    k = torch.zeros_like(q)
+    qd, kd, vd = _gpu(q, k, v)
+    idx = bra.route(qd, kd, w.S, w.topk).cpu()
+    assert torch.equal(idx, torch.arange(5, dtype=torch.int32).expand(2, 49, 5))
+    out = _f64(bra.forward(qd, kd, vd, w.heads, w.S, w.topk).cpu())
+    ref = O.attend(_f64(q), _f64(k), _f64(v), idx.numpy(), w.heads, w.S)
+    parity.assert_output_close(out, ref, "bf16", "K=0")
+
+
+def test_unit_values_give_unit_output():
+    w = wl.custom(2, 28, 28, 128, 4, 7, 4, "bf16", seed=23)
+    q, k, _ = wl.make_inputs(w)
+    v = torch.ones_like(q)
+    out = bra.forward(*_gpu(q, k, v), w.heads, w.S, w.topk).float().cpu()
+    assert torch.all(out == 1.0)
+
+
+def test_planted_diagonal_routing_is_window_attention():
+    B, H, W, C, heads, S = 2, 16, 16, 64, 2, 4
+    R = S * S
+    g = torch.Generator().manual_seed(24)
+    means = torch.zeros(R, C)
+    means[torch.arange(R), torch.arange(R)] = 4.0
+    grid = means.reshape(S, S, C).repeat_interleave(H // S, 0).repeat_interleave(W // S, 1)
+    q = (grid + 0.05 * torch.randn(B, H, W, C, generator=g)).to(torch.bfloat16)
+    k = (grid + 0.05 * torch.randn(B, H, W, C, generator=g)).to(torch.bfloat16)
+    v = torch.randn(B, H, W, C, generator=g).to(torch.bfloat16)
+    qd, kd, vd = _gpu(q, k, v)
+    idx = bra.route(qd, kd, S, 1).cpu()
+    assert torch.equal(idx[..., 0], torch.arange(R, dtype=torch.int32).expand(B, R))
+    out = _f64(bra.forward(qd, kd, vd, heads, S, 1).cpu())
+    ref = O.attend(_f64(q), _f64(k), _f64(v), idx.numpy(), heads, S)
+    parity.assert_output_close(out, ref, "bf16", "planted routing")
+
+
+def test_route_order_does_not_change_output_beyond_rounding():
+    w = wl.custom(2, 28, 28, 128, 4, 7, 4, "f32", seed=25)
+    q, k, v = _gpu(*wl.make_inputs(w))
+    idx = bra.route(q, k, w.S, w.topk)
+    flipped = idx.flip(-1).contiguous()
+    a = bra.attend(q, k, v, idx, w.heads, w.S)
+    b = bra.attend(q, k, v, flipped, w.heads, w.S)
+    assert (a - b).abs().max().item() <= 1e-5
+
+
+def test_out_of_range_route_entries_give_nan_rows_only():
+    w = wl.custom(1, 14, 14, 64, 2, 7, 2, "bf16", seed=26)
+    q, k, v = _gpu(*wl.make_inputs(w))
+    idx = bra.route(q, k, w.S, w.topk)
+    good = bra.attend(q, k, v, idx, w.heads, w.S).float().cpu()
+    bad_idx = idx.clone()
+    bad_idx[0, 3, 1] = 49
+    bad_idx[0, 10, 0] = -1
+    out = bra.attend(q, k, v, bad_idx, w.heads, w.S).float().cpu()
+    o = out.reshape(1, 7, 2, 7, 2, 64).permute(0, 1, 3, 2, 4, 5).reshape(1, 49, 4, 64)
+    gd = good.reshape(1, 7, 2, 7, 2, 64).permute(0, 1, 3, 2, 4, 5).reshape(1, 49, 4, 64)
+    assert torch.isnan(o[0, 3]).all() and torch.isnan(o[0, 10]).all()
+    keep = [r for r in range(49) if r not in (3, 10)]
+    assert torch.equal(o[0, keep], gd[0, keep])
+
+
+def test_deterministic_and_stream_ordered():
+    w = wl.WORKLOADS[2]
+    q, k, v = _gpu(*wl.make_inputs(w))
+    a = bra.forward(q, k, v, w.heads, w.S, w.topk)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        b = bra.forward(q, k, v, w.heads, w.S, w.topk)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -1,0 +1,184 @@
+"""Bi-Level Routing Attention (BRA) forward for MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``libbra.so`` (declared in
+``include/bra.h``). This module only marshals arguments: every step of the
+computation runs in the library's HIP kernels. PyTorch supplies device memory
+and the current stream. If the library has not been built, every call raises
+``RuntimeError``; there is no fallback.
+
+    route(q, k, S, topk)              -> idx [B, S*S, topk] int32
+    attend(q, k, v, idx, heads, S)    -> o   [B, H, W, C]
+    forward(q, k, v, heads, S, topk)  -> o   [B, H, W, C]
+
+q, k, v: contiguous [B, H, W, C] tensors on one GPU, float32 or bfloat16.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BraError",
+    "library_path",
+    "load_library",
+    "workspace_bytes",
+    "route",
+    "attend",
+    "forward",
+    "EXPORTS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_ENV = "BRA_LIBRARY"
+
+BRA_F32 = 0
+BRA_BF16 = 1
+BRA_OK, BRA_EINVAL, BRA_EUNSUPPORTED, BRA_EHIP, BRA_ENOMEM = range(5)
+
+# Every symbol include/bra.h declares.
+EXPORTS = ("bra_status_string", "bra_workspace_bytes", "bra_route", "bra_attend", "bra_forward")
+
+_lib = None
+
+
+class BraError(RuntimeError):
+    """A non-success status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"BRA status {status}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get(_LIB_ENV, os.path.join(_PKG, "libbra.so"))
+
+
+def load_library():
+    """Load libbra.so once; raise RuntimeError if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library not built: {path} is missing "
+            "(run `python -m vision_transformer_dynamic_amd.build`)"
+        )
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.bra_status_string.restype = ctypes.c_char_p
+    lib.bra_status_string.argtypes = [i32]
+    lib.bra_workspace_bytes.restype = sz
+    lib.bra_workspace_bytes.argtypes = [i32] * 6
+    lib.bra_route.restype = i32
+    lib.bra_route.argtypes = [vp, vp, vp] + [i32] * 6 + [i32, vp, sz, vp]
+    lib.bra_attend.restype = i32
+    lib.bra_attend.argtypes = [vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
+    lib.bra_forward.restype = i32
+    lib.bra_forward.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [i32, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status == BRA_OK:
+        return
+    msg = load_library().bra_status_string(status).decode()
+    if status == BRA_EINVAL:
+        raise ValueError(f"BRA status {status}: {msg}")
+    if status == BRA_EUNSUPPORTED:
+        raise NotImplementedError(f"BRA status {status}: {msg}")
+    raise BraError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return BRA_F32
+    if t.dtype == torch.bfloat16:
+        return BRA_BF16
+    raise NotImplementedError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check_maps(*ts: torch.Tensor):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("tensors must be [B, H, W, C]")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on a GPU")
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (and out) must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, W, C]")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_bytes(B: int, H: int, W: int, C: int, S: int, topk: int) -> int:
+    n = load_library().bra_workspace_bytes(B, H, W, C, S, topk)
+    if n == 0:
+        raise ValueError("invalid sizes for BRA")
+    return int(n)
+
+
+def _workspace(q: torch.Tensor, S: int, topk: int, workspace):
+    B, H, W, C = q.shape
+    need = workspace_bytes(B, H, W, C, S, topk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes")
+    return workspace, need
+
+
+def route(q: torch.Tensor, k: torch.Tensor, S: int, topk: int, out=None, workspace=None) -> torch.Tensor:
+    """Routing table [B, S*S, topk] int32 (descending affinity, lower index on ties)."""
+    lib = load_library()
+    _check_maps(q, k)
+    B, H, W, C = q.shape
+    if out is None:
+        out = torch.empty((B, S * S, topk), dtype=torch.int32, device=q.device)
+    if out.dtype != torch.int32 or not out.is_contiguous() or out.shape != (B, S * S, topk):
+        raise ValueError("out must be a contiguous int32 [B, S*S, topk] tensor")
+    ws, nbytes = _workspace(q, S, topk, workspace)
+    _check(lib.bra_route(q.data_ptr(), k.data_ptr(), out.data_ptr(), B, H, W, C, S, topk,
+                         _dtype_code(q), ws.data_ptr(), nbytes, _stream(q.device)))
+    return out
+
+
+def attend(q, k, v, idx: torch.Tensor, heads: int, S: int, out=None) -> torch.Tensor:
+    """Attention of every region's queries over the tokens of its routed regions."""
+    lib = load_library()
+    _check_maps(q, k, v)
+    B, H, W, C = q.shape
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() != 3 or idx.device != q.device:
+        raise ValueError("idx must be a contiguous int32 [B, S*S, topk] tensor on q's device")
+    if tuple(idx.shape[:2]) != (B, S * S):
+        raise ValueError("idx must be [B, S*S, topk]")
+    topk = idx.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    _check_maps(q, out)
+    _check(lib.bra_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), out.data_ptr(),
+                          B, H, W, C, heads, S, topk, _dtype_code(q), _stream(q.device)))
+    return out
+
+
+def forward(q, k, v, heads: int, S: int, topk: int, out=None, workspace=None) -> torch.Tensor:
+    """Full BRA forward (without the local-context dwconv term)."""
+    lib = load_library()
+    _check_maps(q, k, v)
+    B, H, W, C = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_maps(q, out)
+    ws, nbytes = _workspace(q, S, topk, workspace)
+    _check(lib.bra_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           B, H, W, C, heads, S, topk, _dtype_code(q),
+                           ws.data_ptr(), nbytes, _stream(q.device)))
+    return out

@@ -1,0 +1,75 @@
+"""Build ``libbra.so`` (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Usage: ``python -m vision_transformer_dynamic_amd.build`` (or call ``build()``).
+Every call recompiles; the library is written next to this file and replaced
+atomically so a process that has it loaded is never handed a half-written file.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libbra.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = ["pool.hip", "route.hip", "attend.hip", "bra_api.hip"]
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Packed fp32 VALU ops are switched off: the compiler's automatic v_pk_* fp32
+# forms are avoided on this target.
+CFLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-result",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def _run(cmd):
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"command failed ({proc.returncode}): {' '.join(cmd)}\n{proc.stdout}")
+    return proc.stdout
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every HIP source and link the shared library; return its path."""
+    tmp = tempfile.mkdtemp(prefix="bra_build_")
+    try:
+        objs = []
+        cmds = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src.replace(".hip", ".o"))
+            objs.append(obj)
+            cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+            for out in ex.map(_run, cmds):
+                if verbose and out.strip():
+                    print(out, file=sys.stderr)
+        tmp_lib = os.path.join(tmp, LIB_NAME)
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp_lib, *objs])
+        staged = LIB_PATH + ".tmp"
+        shutil.copyfile(tmp_lib, staged)
+        os.replace(staged, LIB_PATH)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

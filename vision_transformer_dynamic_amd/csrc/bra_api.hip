@@ -1,0 +1,157 @@
+// Host side of the C ABI declared in include/bra.h: argument validation,
+// workspace handling and kernel dispatch. No torch types, no global state.
+#include "bra.h"
+#include "bra_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+using bra::Shape;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape checks shared by every entry point. `heads` < 0 means "not an
+// argument of this call" (bra_route: routing is shared by all heads).
+bra_status check_shape(int B, int H, int W, int C, int heads, int S, int topk, int dtype, Shape* out) {
+  if (B <= 0 || H <= 0 || W <= 0 || C <= 0 || S <= 0 || topk <= 0) return BRA_EINVAL;
+  if (heads == 0 || heads < -1) return BRA_EINVAL;
+  if (H % S != 0 || W % S != 0) return BRA_EINVAL;  // regions must tile the map
+  if (heads > 0 && C % heads != 0) return BRA_EINVAL;
+  const int64_t R = (int64_t)S * S;
+  if (topk > R) return BRA_EINVAL;
+  if ((int64_t)B * H * W * C >= (int64_t(1) << 40)) return BRA_EINVAL;
+  if ((int64_t)B * R * topk >= (int64_t(1) << 31)) return BRA_EINVAL;
+  if (dtype != bra::kF32 && dtype != bra::kBF16) return BRA_EUNSUPPORTED;
+  if (R > bra::kMaxRegions) return BRA_EUNSUPPORTED;
+  if (C % 8 != 0) return BRA_EUNSUPPORTED;
+  if (C > (dtype == bra::kBF16 ? bra::kMaxChannelsBf16 : bra::kMaxChannelsF32)) return BRA_EUNSUPPORTED;
+  if (heads > 0 && C / heads != bra::kHeadDim) return BRA_EUNSUPPORTED;
+  Shape s;
+  s.B = B; s.H = H; s.W = W; s.C = C; s.heads = heads > 0 ? heads : 1; s.S = S; s.topk = topk;
+  s.sh = H / S; s.sw = W / S; s.n = s.sh * s.sw; s.R = (int)R;
+  s.d = heads > 0 ? C / heads : C;
+  const int64_t kv = (int64_t)topk * s.n;
+  if (kv >= (int64_t(1) << 30)) return BRA_EINVAL;
+  s.kv = (int)kv;
+  *out = s;
+  return BRA_OK;
+}
+
+size_t pooled_bytes(const Shape& s) { return align_up(sizeof(float) * (size_t)s.B * s.R * s.C); }
+size_t index_bytes(const Shape& s) { return align_up(sizeof(int32_t) * (size_t)s.B * s.R * s.topk); }
+
+// Workspace: [Qr | Kr | idx], each 256-byte aligned.
+size_t workspace_for(const Shape& s) { return 2 * pooled_bytes(s) + index_bytes(s); }
+
+// Holds the workspace for one call: the caller's, or a stream-ordered one.
+struct Workspace {
+  char* ptr = nullptr;
+  bool owned = false;
+  hipStream_t stream = nullptr;
+  bra_status acquire(void* user, size_t user_bytes, size_t need, hipStream_t s) {
+    stream = s;
+    if (user != nullptr) {
+      if (user_bytes < need || !aligned(user, kAlign)) return BRA_EINVAL;
+      ptr = static_cast<char*>(user);
+      return BRA_OK;
+    }
+    if (user_bytes != 0) return BRA_EINVAL;
+    void* p = nullptr;
+    if (hipMallocAsync(&p, need, s) != hipSuccess || p == nullptr) return BRA_ENOMEM;
+    ptr = static_cast<char*>(p);
+    owned = true;
+    return BRA_OK;
+  }
+  ~Workspace() {
+    if (owned) (void)hipFreeAsync(ptr, stream);
+  }
+};
+
+bool bad_tensor(const void* p) { return p == nullptr || !aligned(p, 16); }
+
+bra_status enqueue_route(const void* Q, const void* K, int32_t* idx, const Shape& s, int dtype,
+                         char* ws, hipStream_t stream) {
+  float* Qr = reinterpret_cast<float*>(ws);
+  float* Kr = reinterpret_cast<float*>(ws + pooled_bytes(s));
+  if (bra::launch_pool(Q, K, Qr, Kr, s, dtype, stream) != hipSuccess) return BRA_EHIP;
+  if (bra::launch_route(Qr, Kr, idx, s, stream) != hipSuccess) return BRA_EHIP;
+  return BRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bra_status_string(bra_status status) {
+  switch (status) {
+    case BRA_OK: return "success";
+    case BRA_EINVAL: return "invalid argument (null or misaligned pointer, non-positive size, S not dividing H or W, heads not dividing C, topk outside [1, S*S], or workspace too small)";
+    case BRA_EUNSUPPORTED: return "unsupported configuration (head dim other than 32, more than 256 regions, C not a multiple of 8 or too large, or unknown dtype)";
+    case BRA_EHIP: return "HIP runtime error while enqueueing a kernel";
+    case BRA_ENOMEM: return "device workspace allocation failed";
+  }
+  return "unknown status";
+}
+
+size_t bra_workspace_bytes(int B, int H, int W, int C, int S, int topk) {
+  Shape s;
+  if (check_shape(B, H, W, C, -1, S, topk, bra::kBF16, &s) != BRA_OK) return 0;
+  return workspace_for(s);
+}
+
+bra_status bra_route(const void* Q, const void* K, int32_t* idx,
+                     int B, int H, int W, int C, int S, int topk,
+                     bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, -1, S, topk, (int)dtype, &s);
+  if (st != BRA_OK) return st;
+  if (bad_tensor(Q) || bad_tensor(K)) return BRA_EINVAL;
+  if (idx == nullptr || !aligned(idx, 4)) return BRA_EINVAL;
+  Workspace ws;
+  st = ws.acquire(workspace, workspace_bytes, 2 * pooled_bytes(s), stream);
+  if (st != BRA_OK) return st;
+  return enqueue_route(Q, K, idx, s, (int)dtype, ws.ptr, stream);
+}
+
+bra_status bra_attend(const void* Q, const void* K, const void* V,
+                      const int32_t* idx, void* O,
+                      int B, int H, int W, int C, int heads, int S, int topk,
+                      bra_dtype dtype, hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, heads, S, topk, (int)dtype, &s);
+  if (st != BRA_OK) return st;
+  if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(V) || bad_tensor(O))
+    return BRA_EINVAL;
+  if (idx == nullptr || !aligned(idx, 4)) return BRA_EINVAL;
+  if (O == Q || O == K || O == V) return BRA_EINVAL;
+  if (bra::launch_attend(Q, K, V, idx, O, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
+  return BRA_OK;
+}
+
+bra_status bra_forward(const void* Q, const void* K, const void* V, void* O,
+                       int B, int H, int W, int C, int heads, int S, int topk,
+                       bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, heads, S, topk, (int)dtype, &s);
+  if (st != BRA_OK) return st;
+  if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(V) || bad_tensor(O))
+    return BRA_EINVAL;
+  if (O == Q || O == K || O == V) return BRA_EINVAL;
+  Workspace ws;
+  st = ws.acquire(workspace, workspace_bytes, workspace_for(s), stream);
+  if (st != BRA_OK) return st;
+  int32_t* idx = reinterpret_cast<int32_t*>(ws.ptr + 2 * pooled_bytes(s));
+  st = enqueue_route(Q, K, idx, s, (int)dtype, ws.ptr, stream);
+  if (st != BRA_OK) return st;
+  if (bra::launch_attend(Q, K, V, idx, O, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
+  return BRA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Internal launch interface shared by the host API and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bra {
+
+// Validated problem shape. Region grid S x S; each region is sh x sw tokens.
+struct Shape {
+  int B, H, W, C, heads, S, topk;
+  int sh, sw;  // region rows / columns (H/S, W/S)
+  int n;       // tokens per region
+  int R;       // regions per image (S*S)
+  int d;       // head dim (C/heads)
+  int kv;      // keys per query (topk * n)
+};
+
+constexpr int kHeadDim = 32;       // head dim implemented by the attention kernel
+constexpr int kMaxRegions = 256;   // route kernel: at most 4 candidates per lane
+constexpr int kMaxChannelsBf16 = 2048;
+constexpr int kMaxChannelsF32 = 1024;
+
+// dtype codes match bra_dtype in include/bra.h
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+
+// Region means of Q and K, fp32: Qr, Kr are [B, R, C].
+hipError_t launch_pool(const void* Q, const void* K, float* Qr, float* Kr,
+                       const Shape& s, int dtype, hipStream_t stream);
+
+// Affinity Qr Kr^T per image and top-k per row: idx is [B, R, topk].
+hipError_t launch_route(const float* Qr, const float* Kr, int32_t* idx,
+                        const Shape& s, hipStream_t stream);
+
+// Token attention over routed regions: O = softmax(q k_g^T / sqrt(d)) v_g.
+hipError_t launch_attend(const void* Q, const void* K, const void* V,
+                         const int32_t* idx, void* O, const Shape& s, int dtype,
+                         hipStream_t stream);
+
+}  // namespace bra
