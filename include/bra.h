@@ -20,16 +20,18 @@
  * Heads        : head m owns channels [m*d, (m+1)*d), d = C/heads. Supported:
  *                d == 32. Routing is shared by all heads and uses all C channels.
  * Scale        : softmax(q k^T / sqrt(d)).
- * Limits       : 1 <= S*S <= 256, 1 <= topk <= S*S, B*H*W*C < 2^40.
+ * Limits       : 1 <= S*S <= 256, 1 <= topk <= S*S, C % 8 == 0,
+ *                C <= 2048 (bf16) or 1024 (fp32), H*W*C < 2^31 per image,
+ *                topk*n < 2^22 keys per query, B*H*W*C < 2^40.
  *
  * Streams and errors
  *   Every call only enqueues work on `stream` (NULL = the legacy default
  *   stream) and returns; none synchronises. Arguments are checked on the host
  *   before anything is enqueued: a null pointer, a non-positive size, S not
  *   dividing H or W, heads not dividing C, topk outside [1, S*S], a
- *   misaligned pointer or a too-small workspace give BRA_EINVAL; a head dim,
- *   region count or dtype this build does not implement gives
- *   BRA_EUNSUPPORTED. A HIP error reported while enqueueing gives BRA_EHIP;
+ *   misaligned pointer, a too-small workspace or sizes beyond the size limits
+ *   give BRA_EINVAL; a head dim, region count, channel count or dtype this
+ *   build does not implement gives BRA_EUNSUPPORTED. A HIP error reported while enqueueing gives BRA_EHIP;
  *   a failed workspace allocation gives BRA_ENOMEM. On any error nothing has
  *   been enqueued, except for BRA_EHIP, where earlier launches of the same
  *   call may already be queued. The library keeps no global state and is

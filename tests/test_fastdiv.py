@@ -1,0 +1,33 @@
+"""The float-reciprocal division the kernels use for index arithmetic is exact.
+
+The kernels compute q = trunc(float(a) * fl(1/d)) and repair q with one
+remainder check. For 0 <= a < 2^22 and 1 <= d < 2^22 the float quotient is
+within 0.5 of a/d, so one correction suffices. Emulated here in float32
+(round-to-nearest multiply, truncating conversion), on boundary and random
+numerators.
+"""
+
+import numpy as np
+
+
+def fdiv(a: np.ndarray, d: int):
+    inv = np.float32(1.0) / np.float32(d)
+    q = (a.astype(np.float32) * inv).astype(np.int64)  # truncation toward zero
+    r = a - q * d
+    q = np.where(r < 0, q - 1, np.where(r >= d, q + 1, q))
+    r = a - q * d
+    return q, r
+
+
+def test_fastdiv_exact_on_boundaries_and_random():
+    rng = np.random.default_rng(0)
+    divisors = list(range(1, 300)) + [1023, 1024, 1025, 4095, 4096, 16383, 65535, (1 << 21) + 3, (1 << 22) - 1]
+    amax = 1 << 22
+    for d in divisors:
+        mult = np.arange(0, amax, d, dtype=np.int64)[-2000:]
+        a = np.concatenate([mult, mult + 1, mult - 1, mult + d - 1,
+                            rng.integers(0, amax, 5000), np.array([0, amax - 1])])
+        a = a[(a >= 0) & (a < amax)]
+        q, r = fdiv(a, d)
+        assert np.array_equal(q, a // d), d
+        assert np.array_equal(r, a % d), d

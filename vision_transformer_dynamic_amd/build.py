@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -35,6 +36,8 @@ CFLAGS = [
     "-Wall",
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results go straight to VGPRs (no copies through AGPRs)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
@@ -47,6 +50,20 @@ def _run(cmd):
     return proc.stdout
 
 
+def _check_resources(report: str, src: str):
+    """Reject kernels that spill registers or use scratch: on this path every
+    per-thread array must live in registers."""
+    current = None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            current = m.group(1)
+            continue
+        m = re.search(r"(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill): (\d+)", line)
+        if m and int(m.group(2)) != 0:
+            raise RuntimeError(f"{src}: kernel {current} has {m.group(1)} = {m.group(2)}")
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
     """Compile every HIP source and link the shared library; return its path."""
     tmp = tempfile.mkdtemp(prefix="bra_build_")
@@ -56,11 +73,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage",
+                         "-c", os.path.join(CSRC, src), "-o", obj])
         with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-            for out in ex.map(_run, cmds):
-                if verbose and out.strip():
-                    print(out, file=sys.stderr)
+            for src, out in zip(SOURCES, ex.map(_run, cmds)):
+                _check_resources(out, src)
+                if verbose:
+                    for line in out.splitlines():
+                        if "remark" in line and ("Name" in line or "VGPRs:" in line or "Occupancy" in line):
+                            print(line.split("remark: ")[-1], file=sys.stderr)
         tmp_lib = os.path.join(tmp, LIB_NAME)
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp_lib, *objs])
         staged = LIB_PATH + ".tmp"

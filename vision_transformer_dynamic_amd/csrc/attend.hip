@@ -76,6 +76,12 @@ struct Tr<__bf16> {
     for (int e = 0; e < 8; ++e) r[e] = (__bf16)0.0f;
     return r;
   }
+  __device__ static inline op8 ones() {
+    op8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)1.0f;
+    return r;
+  }
   __device__ static inline void store8(__bf16* p, const float* v) {
     *reinterpret_cast<op8*>(p) = from_f32(v);
   }
@@ -112,6 +118,12 @@ struct Tr<float> {
     for (int e = 0; e < 8; ++e) r[e] = 0.f;
     return r;
   }
+  __device__ static inline op8 ones() {
+    op8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = 1.f;
+    return r;
+  }
   __device__ static inline void store8(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -130,7 +142,9 @@ struct AttnParams {
   int nqb;   // query blocks per region
   int HG;    // heads per workgroup
   int nhg;   // head groups
+  int nbuf;  // LDS chunk buffers (2: double-buffered, when kv spans several chunks)
   float c;   // softmax scale * log2(e)
+  FastDiv div_n, div_sw;
 };
 
 __device__ inline float wave_max_groups(float v) {
@@ -140,20 +154,45 @@ __device__ inline float wave_max_groups(float v) {
   return v;
 }
 
-__device__ inline float wave_sum_groups(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+// Channel-row swizzle of the V^T tile: column blocks of 8 keys are permuted
+// by an XOR that depends on the row's 8-row group, so the transposed writes of
+// one wave spread over the LDS banks. Blocks of 8 keys stay contiguous (and
+// even columns stay even), which is what the P.V operand reads and the packed
+// key-pair writes need.
+__device__ inline int vt_col(int row, int col) { return col ^ (((row >> 3) & 7) << 3); }
+
+// Two keys' 16-byte vectors -> per channel e, the pair (key0, key1) as one
+// 32-bit (bf16) or 64-bit (fp32) LDS word of the V^T tile.
+__device__ inline void store_vt_pair(__bf16* Vt, int ldv, int row0, int col, const uint4& a, const uint4& b) {
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = (wa[e] & 0xffffu) | (wb[e] << 16);          // channel 2e
+    const uint32_t hi = (wa[e] >> 16) | (wb[e] & 0xffff0000u);      // channel 2e+1
+    *reinterpret_cast<uint32_t*>(Vt + (row0 + 2 * e) * ldv + col) = lo;
+    *reinterpret_cast<uint32_t*>(Vt + (row0 + 2 * e + 1) * ldv + col) = hi;
+  }
 }
 
-template <typename T>
+__device__ inline void store_vt_pair(float* Vt, int ldv, int row0, int col, const uint4& a, const uint4& b) {
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    *reinterpret_cast<uint2*>(Vt + (row0 + e) * ldv + col) = make_uint2(wa[e], wb[e]);
+}
+
+// NV: 16-byte vectors per tensor per thread per chunk (2 or 4, even).
+// MULTI: kv spans more than one chunk (prefetch the next chunk during compute).
+template <typename T, int NV, bool MULTI>
 __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
   constexpr int VEC = TT::VEC;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int sidx[kMaxRegions];
+  __shared__ int rbase[kMaxRegions];  // token offset of each routed region's corner
   __shared__ int sbad;
 
   const int tid = threadIdx.x;
@@ -162,7 +201,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
   const int g = lane >> 4;      // lane group: contraction slots 8g..8g+7
   const int col = lane & 15;    // query column of the 16-query tile
 
-  int w = blockIdx.x;
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
+  // each XCD a contiguous range of work items (same image -> same L2).
+  int w;
+  {
+    const int nwg = gridDim.x, bid = blockIdx.x;
+    const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
+    w = x * q8 + min(x, r8) + loc;
+  }
   const int hg = w % p.nhg;  w /= p.nhg;
   const int qb = w % p.nqb;  w /= p.nqb;
   const int i = w % p.R;
@@ -178,53 +224,61 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
   const int U = nh * ntiles;          // units
   const int ldk = p.HG * D + TT::PADK;   // LDS row stride of K (elements)
   const int ldv = KC + TT::PADV;         // LDS row stride of V^T (elements)
-  T* Ks = reinterpret_cast<T*>(smem_raw);
-  T* Vt = Ks + KC * ldk;
+  const int bufsz = KC * ldk + p.HG * D * ldv;
 
-  const T* Qg = static_cast<const T*>(p.Q);
-  const T* Kg = static_cast<const T*>(p.K);
-  const T* Vg = static_cast<const T*>(p.V);
-  T* Og = static_cast<T*>(p.O);
-
-  // routing row of region i
-  if (tid == 0) sbad = 0;
-  __syncthreads();
-  for (int j = tid; j < p.topk; j += blockDim.x) {
-    const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
-    const bool ok = r >= 0 && r < p.R;
-    sidx[j] = ok ? r : 0;
-    if (!ok) sbad = 1;
-  }
-  __syncthreads();
-
+  // per-image bases; offsets inside an image fit in 32 bits (H*W*C < 2^31)
+  const int64_t img = (int64_t)b * p.H * p.W * p.C;
+  const T* Qg = static_cast<const T*>(p.Q) + img;
+  const T* Kg = static_cast<const T*>(p.K) + img;
+  const T* Vg = static_cast<const T*>(p.V) + img;
+  T* Og = static_cast<T*>(p.O) + img;
   const int ri = i / p.S, rj = i - (i / p.S) * p.S;
-  // per-unit state
+  const int qcorner = ri * p.sh * p.W + rj * p.sw;  // token offset of region i's corner
+
+  // ---- queries first: they do not depend on the routing table
   op8 qop[MAXU];
-  floatx4 acc[MAXU][2];
-  float m[MAXU], lsum[MAXU];
-  int64_t qoff[MAXU];
+  // acc[u][0..1]: O^T tiles (channels 8g..8g+3 and 8g+4..8g+7 of the lane's
+  // query); acc[u][2]: an all-ones 16 x 32 A operand against the same P^T, so
+  // every element holds the softmax denominator sum_k P[k] of the lane's query,
+  // computed by the matrix cores from exactly the P the numerator used.
+  floatx4 acc[MAXU][3];
+  float m[MAXU];
+  int qoff[MAXU];
   bool qvalid[MAXU];
 #pragma unroll
   for (int uu = 0; uu < MAXU; ++uu) {
     const int u = wave + NW * uu;
-    const int hl = u / max(ntiles, 1);
+    const int hl = u / ntiles;
     const int t = u - hl * ntiles;
     const int qi = q0 + t * 16 + col;
     qvalid[uu] = (u < U) && (qi < q0 + nq);
     qoff[uu] = 0;
     if (qvalid[uu]) {
-      const int qy = ri * p.sh + qi / p.sw;
-      const int qx = rj * p.sw + (qi - (qi / p.sw) * p.sw);
-      qoff[uu] = (((int64_t)b * p.H + qy) * p.W + qx) * p.C + cb + hl * D + 8 * g;
+      int qx;
+      const int qy = fdiv(qi, p.div_sw, &qx);
+      qoff[uu] = (qcorner + qy * p.W + qx) * p.C + cb + hl * D + 8 * g;
       qop[uu] = TT::load8(Qg + qoff[uu]);
     } else {
       qop[uu] = TT::zero();
     }
     acc[uu][0] = floatx4{0.f, 0.f, 0.f, 0.f};
     acc[uu][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    acc[uu][2] = floatx4{0.f, 0.f, 0.f, 0.f};
     m[uu] = -INFINITY;
-    lsum[uu] = 0.f;
   }
+
+  // ---- routing row of region i -> corner offsets of the routed regions
+  if (tid == 0) sbad = 0;
+  __syncthreads();
+  for (int j = tid; j < p.topk; j += blockDim.x) {
+    const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
+    const bool ok = r >= 0 && r < p.R;
+    const int rr = ok ? r : 0;
+    const int ry = rr / p.S;
+    rbase[j] = ry * p.sh * p.W + (rr - ry * p.S) * p.sw;
+    if (!ok) sbad = 1;
+  }
+  __syncthreads();
 
   if (sbad) {
     // a routing entry outside [0, S*S): never dereferenced; output NaN
@@ -237,33 +291,63 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
     return;
   }
 
-  const int vpk = HGC / VEC;  // 16-byte vectors per key row
-  for (int c0 = 0; c0 < p.kv; c0 += KC) {
-    if (c0) __syncthreads();  // previous chunk fully consumed
-    // ---- gather chunk: K rows as is, V transposed, through the routing table
-    for (int f = tid; f < KC * vpk; f += blockDim.x) {
-      const int kl = f / vpk;
-      const int cv = f - kl * vpk;
-      const int kappa = c0 + kl;
-      uint4 kvv = make_uint4(0u, 0u, 0u, 0u);
-      uint4 vvv = make_uint4(0u, 0u, 0u, 0u);
-      if (kappa < p.kv) {
-        const int jr = kappa / p.n;
-        const int tk = kappa - jr * p.n;
-        const int r = sidx[jr];
-        const int ty = tk / p.sw;
-        const int y = (r / p.S) * p.sh + ty;
-        const int x = (r - (r / p.S) * p.S) * p.sw + (tk - ty * p.sw);
-        const int64_t off = (((int64_t)b * p.H + y) * p.W + x) * p.C + cb + cv * VEC;
-        kvv = *reinterpret_cast<const uint4*>(Kg + off);
-        vvv = *reinterpret_cast<const uint4*>(Vg + off);
-      }
-      *reinterpret_cast<uint4*>(Ks + kl * ldk + cv * VEC) = kvv;
-      const T* ve = reinterpret_cast<const T*>(&vvv);
+  // ---- chunk loads. A thread owns NV/2 (key pair, 16-byte channel vector)
+  // items: pair item f = tid + 256 q covers keys 2p and 2p+1 of channel vector
+  // cv, with 8 consecutive pairs per channel vector so that one wave
+  // instruction reads 8 whole token rows; slot 2q holds key 2p, slot 2q+1 key
+  // 2p+1. Both keys of a pair land in one packed V^T word.
+  const int vpk = HGC / VEC;          // 16-byte vectors per key row
+  const int npair = (KC / 2) * vpk;   // pair items per chunk and tensor
+  uint4 kreg[NV], vreg[NV];
+  int kl0[NV / 2], cvs[NV / 2];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) Vt[(cv * VEC + e) * ldv + kl] = ve[e];
+  for (int q = 0; q < NV / 2; ++q) {
+    const int f = tid + 256 * q;
+    const int oct = f / (8 * vpk);
+    const int rem = f - oct * 8 * vpk;
+    cvs[q] = rem >> 3;
+    kl0[q] = 2 * (oct * 8 + (rem & 7));
+  }
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int s2 = 0; s2 < NV; ++s2) {
+      const int q = s2 >> 1;
+      kreg[s2] = make_uint4(0u, 0u, 0u, 0u);
+      vreg[s2] = make_uint4(0u, 0u, 0u, 0u);
+      const int kappa = c0 + kl0[q] + (s2 & 1);
+      if (tid + 256 * q < npair && kappa < p.kv) {
+        int tk, tx;
+        const int jr = fdiv(kappa, p.div_n, &tk);
+        const int ty = fdiv(tk, p.div_sw, &tx);
+        const int off = (rbase[jr] + ty * p.W + tx) * p.C + cb + cvs[q] * VEC;
+        kreg[s2] = *reinterpret_cast<const uint4*>(Kg + off);
+        vreg[s2] = *reinterpret_cast<const uint4*>(Vg + off);
+      }
     }
+  };
+  auto store_chunk = [&](T* Ks, T* Vt) {
+#pragma unroll
+    for (int q = 0; q < NV / 2; ++q) {
+      if (tid + 256 * q < npair) {
+        const int k0 = kl0[q], cv = cvs[q];
+        *reinterpret_cast<uint4*>(Ks + k0 * ldk + cv * VEC) = kreg[2 * q];
+        *reinterpret_cast<uint4*>(Ks + (k0 + 1) * ldk + cv * VEC) = kreg[2 * q + 1];
+        const int row0 = cv * VEC;
+        store_vt_pair(Vt, ldv, row0, vt_col(row0, k0), vreg[2 * q], vreg[2 * q + 1]);
+      }
+    }
+  };
+
+  const int nchunks = MULTI ? (p.kv + KC - 1) / KC : 1;
+  load_chunk(0);
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * KC;
+    T* Ks = reinterpret_cast<T*>(smem_raw) + (p.nbuf == 2 ? (ch & 1) * bufsz : 0);
+    T* Vt = Ks + KC * ldk;
+    if (ch > 0 && p.nbuf == 1) __syncthreads();  // single buffer: previous chunk consumed
+    store_chunk(Ks, Vt);
     __syncthreads();
+    if (MULTI && ch + 1 < nchunks) load_chunk(c0 + KC);  // next chunk in flight during compute
 
     const int nvalid = min(KC, p.kv - c0);
 #pragma unroll
@@ -288,31 +372,33 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
         }
       }
       // lane group g holds keys st*32 + 8g + e, e = 0..7
+      if (nvalid < KC) {  // ragged last chunk (uniform branch)
+#pragma unroll
+        for (int st = 0; st < KC / 32; ++st)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (st * 32 + 8 * g + e >= nvalid) s[st][e] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int st = 0; st < KC / 32; ++st)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (st * 32 + 8 * g + e >= nvalid) s[st][e] = -INFINITY;
-          mx = fmaxf(mx, s[st][e]);
-        }
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
       mx = wave_max_groups(mx);
-      const float mnew = fmaxf(m[uu], mx);
+      // online softmax: with a single chunk the running max starts at -inf and
+      // the accumulators at 0, so there is nothing to rescale
+      const float mnew = MULTI ? fmaxf(m[uu], mx) : mx;
       const float mc = mnew * p.c;
-      const float alpha = __builtin_amdgcn_exp2f(m[uu] * p.c - mc);
-      float ps = 0.f;
+      if (MULTI) {
+        const float alpha = __builtin_amdgcn_exp2f(m[uu] * p.c - mc);
+#pragma unroll
+        for (int ct = 0; ct < 3; ++ct) acc[uu][ct] *= alpha;
+        m[uu] = mnew;
+      }
 #pragma unroll
       for (int st = 0; st < KC / 32; ++st)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
-          s[st][e] = pe;
-          ps += pe;
-        }
-      lsum[uu] = __builtin_fmaf(lsum[uu], alpha, ps);
-      m[uu] = mnew;
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) acc[uu][ct] *= alpha;
+        for (int e = 0; e < 8; ++e) s[st][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
       // ---- O^T += V^T P^T
       const int vrow = 8 * (rr >> 2) + (rr & 3);  // channel row of tile 0; tile 1 is +4
 #pragma unroll
@@ -320,9 +406,11 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
         const op8 pop = TT::from_f32(s[st]);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const op8 va = TT::load8(Vt + (hl * D + vrow + 4 * ct) * ldv + st * 32 + 8 * g);
+          const int row = hl * D + vrow + 4 * ct;
+          const op8 va = TT::load8(Vt + row * ldv + vt_col(row, st * 32 + 8 * g));
           acc[uu][ct] = TT::mma(va, pop, acc[uu][ct]);
         }
+        acc[uu][2] = TT::mma(TT::ones(), pop, acc[uu][2]);
       }
     }
   }
@@ -332,8 +420,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
   for (int uu = 0; uu < MAXU; ++uu) {
     const int u = wave + NW * uu;
     if (u >= U) continue;
-    const float l = wave_sum_groups(lsum[uu]);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / acc[uu][2][0];
     float o[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -364,16 +451,30 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
   p.HG = HG;
   p.nhg = (s.heads + HG - 1) / HG;
   p.c = 1.4426950408889634f / sqrtf((float)s.d);
+  p.div_n = make_fastdiv(s.n);
+  p.div_sw = make_fastdiv(s.sw);
   const size_t esz = dtype == kBF16 ? 2 : 4;
   const int padk = dtype == kBF16 ? Tr<__bf16>::PADK : Tr<float>::PADK;
   const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
-  const size_t lds = esz * ((size_t)KC * (HG * D + padk) + (size_t)HG * D * (KC + padv));
+  const size_t buf = esz * ((size_t)KC * (HG * D + padk) + (size_t)HG * D * (KC + padv));
+  p.nbuf = (s.kv > KC && 2 * buf <= 65536) ? 2 : 1;
+  const size_t lds = p.nbuf * buf;
   const int64_t nwg = (int64_t)s.B * s.R * p.nqb * p.nhg;
   dim3 grid((unsigned)nwg);
   void* args[] = {&p};
-  if (dtype == kBF16)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&attend_kernel<__bf16>), grid, dim3(NW * 64), args, lds, stream);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&attend_kernel<float>), grid, dim3(NW * 64), args, lds, stream);
+  // vectors per thread: KC keys x (HG*D / VEC) vectors / 256 threads
+  const int vec = dtype == kBF16 ? 8 : 4;
+  const int nv = (KC * (HG * D / vec) + NW * 64 - 1) / (NW * 64);
+  const bool multi = s.kv > KC;
+  const void* fn;
+  if (dtype == kBF16) {
+    if (nv <= 2) fn = multi ? (const void*)&attend_kernel<__bf16, 2, true> : (const void*)&attend_kernel<__bf16, 2, false>;
+    else fn = multi ? (const void*)&attend_kernel<__bf16, 4, true> : (const void*)&attend_kernel<__bf16, 4, false>;
+  } else {
+    if (nv <= 2) fn = multi ? (const void*)&attend_kernel<float, 2, true> : (const void*)&attend_kernel<float, 2, false>;
+    else fn = multi ? (const void*)&attend_kernel<float, 4, true> : (const void*)&attend_kernel<float, 4, false>;
+  }
+  return hipLaunchKernel(fn, grid, dim3(NW * 64), args, lds, stream);
 }
 
 }  // namespace bra

@@ -25,6 +25,7 @@ bra_status check_shape(int B, int H, int W, int C, int heads, int S, int topk, i
   const int64_t R = (int64_t)S * S;
   if (topk > R) return BRA_EINVAL;
   if ((int64_t)B * H * W * C >= (int64_t(1) << 40)) return BRA_EINVAL;
+  if ((int64_t)H * W * C > bra::kMaxImageElems) return BRA_EINVAL;
   if ((int64_t)B * R * topk >= (int64_t(1) << 31)) return BRA_EINVAL;
   if (dtype != bra::kF32 && dtype != bra::kBF16) return BRA_EUNSUPPORTED;
   if (R > bra::kMaxRegions) return BRA_EUNSUPPORTED;
@@ -36,7 +37,7 @@ bra_status check_shape(int B, int H, int W, int C, int heads, int S, int topk, i
   s.sh = H / S; s.sw = W / S; s.n = s.sh * s.sw; s.R = (int)R;
   s.d = heads > 0 ? C / heads : C;
   const int64_t kv = (int64_t)topk * s.n;
-  if (kv >= (int64_t(1) << 30)) return BRA_EINVAL;
+  if (kv >= bra::kMaxFastDiv) return BRA_EINVAL;
   s.kv = (int)kv;
   *out = s;
   return BRA_OK;

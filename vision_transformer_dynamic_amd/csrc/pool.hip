@@ -5,17 +5,20 @@
 // regional representations by average pooling).
 //
 // HBM-bound: every input byte is read once, 2*B*R*C fp32 values are written.
-// One workgroup per (image, region, tensor). A region is sh rows of one
-// contiguous segment of sw*C elements, so each wave load instruction reads
-// whole 16-byte vectors of contiguous row segments. The block size is a
-// multiple of the number of 16-byte channel groups per token, so every thread
+// One workgroup per (image, region) pools both Q and K. A region is sh rows of
+// one contiguous segment of sw*C elements, read as 16-byte vectors; every
+// thread issues all of its loads (up to NL per tensor) before it adds any, so
+// a workgroup has its whole region in flight at once. The block size is a
+// multiple of the number of 16-byte channel groups per token, so a thread
 // always accumulates the same 8 (bf16) or 4 (fp32) channels; the per-thread
-// partial sums are then reduced across threads through LDS in a fixed order
+// sums are then reduced across threads through LDS in a fixed order
 // (deterministic, fp32 throughout).
 #include "bra_internal.h"
 
 namespace bra {
 namespace {
+
+constexpr int NL = 4;  // loads per tensor per thread per batch
 
 struct PoolParams {
   const void* Q;
@@ -26,11 +29,11 @@ struct PoolParams {
 };
 
 template <int VEC>
-__device__ inline void accum16(float (&acc)[8], const uint4 v);
+__device__ inline void accum16(float* acc, const uint4 v);
 
 // bf16: 8 values per 16 bytes; a bf16 is the high half of an fp32.
 template <>
-__device__ inline void accum16<8>(float (&acc)[8], const uint4 v) {
+__device__ inline void accum16<8>(float* acc, const uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -41,7 +44,7 @@ __device__ inline void accum16<8>(float (&acc)[8], const uint4 v) {
 
 // fp32: 4 values per 16 bytes.
 template <>
-__device__ inline void accum16<4>(float (&acc)[8], const uint4 v) {
+__device__ inline void accum16<4>(float* acc, const uint4 v) {
   acc[0] += __uint_as_float(v.x);
   acc[1] += __uint_as_float(v.y);
   acc[2] += __uint_as_float(v.z);
@@ -51,13 +54,11 @@ __device__ inline void accum16<4>(float (&acc)[8], const uint4 v) {
 template <int ESIZE>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   constexpr int VEC = 16 / ESIZE;  // elements per 16-byte vector
-  __shared__ float red[256 * VEC];
+  __shared__ float red[2][256 * VEC];
 
   const int R = p.S * p.S;
   const int b = blockIdx.x / R;
   const int r = blockIdx.x - b * R;
-  const char* X = static_cast<const char*>(blockIdx.y ? p.K : p.Q);
-  float* out = blockIdx.y ? p.Kr : p.Qr;
 
   const int G = p.C / VEC;                // 16-byte channel groups per token
   const int nthr = (blockDim.x / G) * G;  // active threads, multiple of G
@@ -65,32 +66,56 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   const int segv = p.sw * G;              // vectors per region row segment
   const int total = p.sh * segv;
 
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[2][VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[0][e] = acc[1][e] = 0.f;
   if (t < nthr) {
     const int y0 = (r / p.S) * p.sh;
     const int x0 = (r - (r / p.S) * p.S) * p.sw;
     const int64_t row_elems = (int64_t)p.W * p.C;
-    const char* base = X + ((((int64_t)b * p.H + y0) * p.W + x0) * p.C) * ESIZE;
-    for (int f = t; f < total; f += nthr) {
-      const int y = f / segv;
-      const int v = f - y * segv;
-      const uint4 val = *reinterpret_cast<const uint4*>(base + (y * row_elems + (int64_t)v * VEC) * ESIZE);
-      accum16<VEC>(acc, val);
+    const int64_t base = (((int64_t)b * p.H + y0) * p.W + x0) * p.C;
+    const char* Qb = static_cast<const char*>(p.Q) + base * ESIZE;
+    const char* Kb = static_cast<const char*>(p.K) + base * ESIZE;
+    for (int f0 = t; f0 < total; f0 += nthr * NL) {
+      uint4 vq[NL], vk[NL];
+#pragma unroll
+      for (int m = 0; m < NL; ++m) {
+        const int f = f0 + m * nthr;
+        if (f < total) {
+          const int y = f / segv;
+          const int64_t off = (y * row_elems + (int64_t)(f - y * segv) * VEC) * ESIZE;
+          vq[m] = *reinterpret_cast<const uint4*>(Qb + off);
+          vk[m] = *reinterpret_cast<const uint4*>(Kb + off);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NL; ++m) {
+        if (f0 + m * nthr < total) {
+          accum16<VEC>(acc[0], vq[m]);
+          accum16<VEC>(acc[1], vk[m]);
+        }
+      }
     }
   }
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) red[t * VEC + e] = (t < nthr) ? acc[e] : 0.f;
+  for (int e = 0; e < VEC; ++e) {
+    red[0][t * VEC + e] = acc[0][e];
+    red[1][t * VEC + e] = acc[1][e];
+  }
   __syncthreads();
 
   // thread t's channel group is t % G, so channel c = g*VEC + e sums
   // red[(g + j*G)*VEC + e] over j, in increasing j.
   const float inv_n = 1.0f / (float)(p.sh * p.sw);
-  for (int c = t; c < p.C; c += blockDim.x) {
-    const int g = c / VEC;
-    const int e = c - g * VEC;
+  for (int c = t; c < 2 * p.C; c += blockDim.x) {
+    const int which = c >= p.C;
+    const int cc = c - which * p.C;
+    const int g = cc / VEC;
+    const int e = cc - g * VEC;
     float s = 0.f;
-    for (int u = g; u < nthr; u += G) s += red[u * VEC + e];
-    out[((int64_t)b * R + r) * p.C + c] = s * inv_n;
+    for (int u = g; u < nthr; u += G) s += red[which][u * VEC + e];
+    float* out = which ? p.Kr : p.Qr;
+    out[((int64_t)b * R + r) * p.C + cc] = s * inv_n;
   }
 }
 
@@ -102,11 +127,11 @@ hipError_t launch_pool(const void* Q, const void* K, float* Qr, float* Kr,
   const int vec = dtype == kBF16 ? 8 : 4;
   const int G = s.C / vec;
   const int total = s.sh * s.sw * G;
-  // about 4 vector loads per thread, at least one full channel-group set
+  // about 4 vectors per tensor per thread, at least one full channel-group set
   int bs = 64;
   while (bs < 256 && total > 4 * bs) bs *= 2;
   while (bs < G) bs *= 2;
-  dim3 grid((unsigned)(s.B * s.R), 2);
+  dim3 grid((unsigned)(s.B * s.R));
   void* args[] = {&p};
   if (dtype == kBF16)
     return hipLaunchKernel(reinterpret_cast<const void*>(&pool_kernel<2>), grid, dim3(bs), args, 0, stream);
