@@ -196,3 +196,21 @@ def test_deterministic_and_stream_ordered():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("w", [wl.WORKLOADS[0], wl.WORKLOADS[1], wl.WORKLOADS[3], wl.WORKLOADS[4],
+                               wl.custom(1, 16, 16, 32, 1, 16, 7, "bf16", seed=27)],
+                         ids=lambda w: w.name)
+def test_forward_routing_table_equals_bra_route(w):
+    """bra_forward leaves its routing table in the workspace: it must equal the
+    one bra_route computes, bit for bit (whether the forward pass routes in the
+    attention kernel or in the route kernel)."""
+    q, k, v = _gpu(*wl.make_inputs(w))
+    nbytes = bra.workspace_bytes(w.B, w.H, w.W, w.C, w.S, w.topk)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    bra.forward(q, k, v, w.heads, w.S, w.topk, workspace=ws)
+    pooled = -(-4 * w.B * w.R * w.C // 256) * 256
+    table = ws[2 * pooled: 2 * pooled + 4 * w.B * w.R * w.topk].view(torch.int32).reshape(w.B, w.R, w.topk)
+    ref = bra.route(q, k, w.S, w.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(table, ref)

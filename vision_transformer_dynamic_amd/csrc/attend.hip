@@ -10,9 +10,10 @@
 // through the routing table (each token's head-group channels are one
 // contiguous run), and runs both products on MFMA with an online softmax.
 //
-// Work split. One workgroup = (image b, query region i, block of <= 64 of the
-// region's queries, group of HG heads). Its 4 waves own "units" = (head, tile
-// of 16 queries); each wave keeps <= 2 units' accumulators in registers.
+// Work split. One workgroup = one work item (image b, query region i, block
+// of <= 64 of the region's queries, group of HG heads). Its 4 waves own
+// "units" = (head, tile of 16 queries); each wave keeps <= 2 units'
+// accumulators in registers.
 //
 // Transposed products. With d = 32 the score tile is computed as
 //   S^T[16 keys x 16 queries] = K[16 x 32] . Q^T[32 x 16]
@@ -35,6 +36,7 @@
 // accumulation and softmax. fp32: eight v_mfma_f32_16x16x4_f32 per 32-deep
 // contraction, P kept in fp32.
 #include "bra_internal.h"
+#include "route_common.h"
 
 #include <math.h>
 
@@ -139,18 +141,24 @@ struct AttnParams {
   int H, W, C, S, topk;
   int sh, sw, n, R, kv;
   int heads;
-  int nqb;   // query blocks per region
-  int HG;    // heads per workgroup
-  int nhg;   // head groups
-  int nbuf;  // LDS chunk buffers (2: double-buffered, when kv spans several chunks)
-  float c;   // softmax scale * log2(e)
-  FastDiv div_n, div_sw;
+  int nqb;     // query blocks per region
+  int HG;      // heads per workgroup (a power of two)
+  int nhg;     // head groups
+  int nitems;  // B * R * nqb * nhg
+  int lg_oct;  // log2(8 * HG * D / VEC): pair items per 8-pair octet of a chunk
+  int nbuf;    // LDS chunk buffers (2: double-buffered, when kv spans several chunks)
+  float c;     // softmax scale * log2(e)
+  FastDiv div_n, div_sw, div_S, div_c4;
+  const float* Qr;  // region means (routing inside the kernel only)
+  const float* Kr;
+  int32_t* idx_out; // routing table written by the kernel (routing inside only)
 };
 
-__device__ inline float wave_max_groups(float v) {
-  // max over the 4 lane groups that share lane % 16
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
+// Max over the 4 lane groups that share lane % 16; a16/a32 are the byte
+// addresses ((lane ^ 16) * 4, (lane ^ 32) * 4) for ds_bpermute, computed once.
+__device__ inline float wave_max_groups(float v, int a16, int a32) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute(a16, __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute(a32, __float_as_int(v))));
   return v;
 }
 
@@ -183,252 +191,475 @@ __device__ inline void store_vt_pair(float* Vt, int ldv, int row0, int col, cons
     *reinterpret_cast<uint2*>(Vt + (row0 + e) * ldv + col) = make_uint2(wa[e], wb[e]);
 }
 
-// NV: 16-byte vectors per tensor per thread per chunk (2 or 4, even).
-// MULTI: kv spans more than one chunk (prefetch the next chunk during compute).
-template <typename T, int NV, bool MULTI>
-__global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
-  typedef Tr<T> TT;
-  typedef typename TT::op8 op8;
-  constexpr int VEC = TT::VEC;
+// Geometry of one work item; every field is uniform over the workgroup.
+struct Item {
+  bool valid;
+  int b, i, qb, hg;
+  int q0, nq, ntiles, nh, cb, U, qcorner;
+  int64_t img;  // element offset of image b
+};
 
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int rbase[kMaxRegions];  // token offset of each routed region's corner
-  __shared__ int sbad;
+__device__ inline Item item_at(const AttnParams& p, int w) {
+  Item it;
+  it.valid = w < p.nitems;
+  if (!it.valid) w = 0;
+  it.hg = w % p.nhg;  w /= p.nhg;
+  it.qb = w % p.nqb;  w /= p.nqb;
+  it.i = w % p.R;
+  it.b = w / p.R;
+  it.q0 = it.qb * QB;
+  it.nq = min(QB, p.n - it.q0);
+  it.ntiles = (it.nq + 15) >> 4;
+  const int h0 = it.hg * p.HG;
+  it.nh = min(p.HG, p.heads - h0);
+  it.cb = h0 * D;
+  it.U = it.valid ? it.nh * it.ntiles : 0;
+  const int ri = it.i / p.S, rj = it.i - ri * p.S;
+  it.qcorner = ri * p.sh * p.W + rj * p.sw;
+  it.img = (int64_t)it.b * p.H * p.W * p.C;
+  return it;
+}
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int g = lane >> 4;      // lane group: contraction slots 8g..8g+7
-  const int col = lane & 15;    // query column of the 16-query tile
-
-  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
-  // each XCD a contiguous range of work items (same image -> same L2).
-  int w;
-  {
-    const int nwg = gridDim.x, bid = blockIdx.x;
-    const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
-    w = x * q8 + min(x, r8) + loc;
-  }
-  const int hg = w % p.nhg;  w /= p.nhg;
-  const int qb = w % p.nqb;  w /= p.nqb;
-  const int i = w % p.R;
-  const int b = w / p.R;
-
-  const int q0 = qb * QB;
-  const int nq = min(QB, p.n - q0);
-  const int ntiles = (nq + 15) >> 4;
-  const int h0 = hg * p.HG;
-  const int nh = min(p.HG, p.heads - h0);
-  const int HGC = nh * D;             // channels this workgroup touches
-  const int cb = h0 * D;              // first channel
-  const int U = nh * ntiles;          // units
-  const int ldk = p.HG * D + TT::PADK;   // LDS row stride of K (elements)
-  const int ldv = KC + TT::PADV;         // LDS row stride of V^T (elements)
-  const int bufsz = KC * ldk + p.HG * D * ldv;
-
-  // per-image bases; offsets inside an image fit in 32 bits (H*W*C < 2^31)
-  const int64_t img = (int64_t)b * p.H * p.W * p.C;
-  const T* Qg = static_cast<const T*>(p.Q) + img;
-  const T* Kg = static_cast<const T*>(p.K) + img;
-  const T* Vg = static_cast<const T*>(p.V) + img;
-  T* Og = static_cast<T*>(p.O) + img;
-  const int ri = i / p.S, rj = i - (i / p.S) * p.S;
-  const int qcorner = ri * p.sh * p.W + rj * p.sw;  // token offset of region i's corner
-
-  // ---- queries first: they do not depend on the routing table
-  op8 qop[MAXU];
+// Per-wave state of one item: the wave's units (head hl, query tile t).
+template <typename T>
+struct Units {
+  typename Tr<T>::op8 qop[MAXU];
   // acc[u][0..1]: O^T tiles (channels 8g..8g+3 and 8g+4..8g+7 of the lane's
   // query); acc[u][2]: an all-ones 16 x 32 A operand against the same P^T, so
-  // every element holds the softmax denominator sum_k P[k] of the lane's query,
-  // computed by the matrix cores from exactly the P the numerator used.
+  // every element holds the softmax denominator sum_k P[k] of the lane's
+  // query, computed by the matrix cores from exactly the P the numerator used.
   floatx4 acc[MAXU][3];
   float m[MAXU];
   int qoff[MAXU];
   bool qvalid[MAXU];
+};
+
+// Query operands of the wave's units (they do not depend on the routing).
+template <typename T>
+__device__ __forceinline__ void load_queries(const AttnParams& p, const Item& it, int wave, int g, int col,
+                                             Units<T>& us) {
+  typedef Tr<T> TT;
+  const T* Qg = static_cast<const T*>(p.Q) + it.img;
 #pragma unroll
   for (int uu = 0; uu < MAXU; ++uu) {
-    const int u = wave + NW * uu;
-    const int hl = u / ntiles;
-    const int t = u - hl * ntiles;
-    const int qi = q0 + t * 16 + col;
-    qvalid[uu] = (u < U) && (qi < q0 + nq);
-    qoff[uu] = 0;
-    if (qvalid[uu]) {
+    const int u = wave + NW * uu;  // uniform
+    const int hl = u / max(it.ntiles, 1);
+    const int t = u - hl * it.ntiles;
+    const int qi = it.q0 + t * 16 + col;
+    us.qvalid[uu] = (u < it.U) && (qi < it.q0 + it.nq);
+    us.qoff[uu] = 0;
+    if (us.qvalid[uu]) {
       int qx;
       const int qy = fdiv(qi, p.div_sw, &qx);
-      qoff[uu] = (qcorner + qy * p.W + qx) * p.C + cb + hl * D + 8 * g;
-      qop[uu] = TT::load8(Qg + qoff[uu]);
+      us.qoff[uu] = (it.qcorner + qy * p.W + qx) * p.C + it.cb + hl * D + 8 * g;
+      us.qop[uu] = TT::load8(Qg + us.qoff[uu]);
     } else {
-      qop[uu] = TT::zero();
+      us.qop[uu] = TT::zero();
     }
-    acc[uu][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-    acc[uu][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-    acc[uu][2] = floatx4{0.f, 0.f, 0.f, 0.f};
-    m[uu] = -INFINITY;
+#pragma unroll
+    for (int ct = 0; ct < 3; ++ct) us.acc[uu][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+    us.m[uu] = -INFINITY;
   }
+}
 
-  // ---- routing row of region i -> corner offsets of the routed regions
-  if (tid == 0) sbad = 0;
-  __syncthreads();
-  for (int j = tid; j < p.topk; j += blockDim.x) {
-    const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
+// Token offset of region r's top-left corner inside its image.
+__device__ inline int region_corner(const AttnParams& p, int r) {
+  int rx;
+  const int ry = fdiv(r, p.div_S, &rx);
+  return ry * p.sh * p.W + rx * p.sw;
+}
+
+// Routing row of the item's region, read from the table: corner offsets into
+// rb[0..topk); returns (through LDS flag *bad) whether an entry is out of range.
+__device__ __forceinline__ void read_routes(const AttnParams& p, const Item& it, int tid, int* rb, int* bad) {
+  for (int j = tid; j < p.topk; j += NW * 64) {
+    const int r = it.valid ? p.idx[((int64_t)it.b * p.R + it.i) * p.topk + j] : 0;
     const bool ok = r >= 0 && r < p.R;
-    const int rr = ok ? r : 0;
-    const int ry = rr / p.S;
-    rbase[j] = ry * p.sh * p.W + (rr - ry * p.S) * p.sw;
-    if (!ok) sbad = 1;
+    rb[j] = region_corner(p, ok ? r : 0);
+    if (!ok) *bad = 1;
+  }
+}
+
+// Single chunk (kv <= 64): token offset (inside the image) of every routed key
+// kappa < kv, straight from the routing table: tok[kappa] = corner of region
+// idx[b][i][kappa / n] + the (kappa % n)-th token of that region. Sets *bad
+// (LDS) for an entry outside [0, S*S).
+__device__ __forceinline__ void read_route_tokens(const AttnParams& p, const Item& it, int tid, int* tok, int* bad) {
+  for (int kappa = tid; kappa < p.kv; kappa += NW * 64) {
+    int tk, tx;
+    const int jr = fdiv(kappa, p.div_n, &tk);
+    const int ty = fdiv(tk, p.div_sw, &tx);
+    const int r = it.valid ? p.idx[((int64_t)it.b * p.R + it.i) * p.topk + jr] : 0;
+    const bool ok = r >= 0 && r < p.R;
+    tok[kappa] = region_corner(p, ok ? r : 0) + ty * p.W + tx;
+    if (!ok) *bad = 1;
+  }
+}
+
+// Routing row computed in the workgroup from the region means, with the route
+// kernel's arithmetic (shared helpers), staged in the chunk LDS area `stage`.
+// Ends with a barrier; the staging area is free afterwards.
+__device__ __forceinline__ void compute_routes(const AttnParams& p, const Item& it, int tid, float* stage, int* rb) {
+  const int ldc = p.C + 4;
+  float* Kst = stage;
+  float* Qst = Kst + p.R * ldc;
+  float* Ast = Qst + p.C;
+  const int c4n = p.C >> 2;
+  const int ldr = (p.R + 3) & ~3;
+  const float* krb = p.Kr + (int64_t)it.b * p.R * p.C;
+  const float* qri = p.Qr + ((int64_t)it.b * p.R + it.i) * p.C;
+  for (int f = tid; f < p.R * c4n; f += NW * 64) {
+    int c4;
+    const int j = fdiv(f, p.div_c4, &c4);
+    *reinterpret_cast<float4*>(Kst + j * ldc + 4 * c4) = *reinterpret_cast<const float4*>(krb + (int64_t)j * p.C + 4 * c4);
+  }
+  for (int c4 = tid; c4 < c4n; c4 += NW * 64)
+    *reinterpret_cast<float4*>(Qst + 4 * c4) = *reinterpret_cast<const float4*>(qri + 4 * c4);
+  __syncthreads();
+  for (int j = tid; j < ldr; j += NW * 64) {
+    float a = -INFINITY;
+    if (j < p.R) {
+      float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int c4 = 0; c4 < c4n; ++c4)
+        acc4 = affinity_step(acc4, *reinterpret_cast<const float4*>(Qst + 4 * c4),
+                             *reinterpret_cast<const float4*>(Kst + j * ldc + 4 * c4));
+      a = affinity_finish(acc4);
+    }
+    Ast[j] = a;
   }
   __syncthreads();
-
-  if (sbad) {
-    // a routing entry outside [0, S*S): never dereferenced; output NaN
-    float nanv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) nanv[e] = __builtin_nanf("");
-#pragma unroll
-    for (int uu = 0; uu < MAXU; ++uu)
-      if (qvalid[uu]) TT::store8(Og + qoff[uu], nanv);
-    return;
+  for (int j = tid; j < p.R; j += NW * 64) {
+    const int rank = affinity_rank(Ast, ldr, Ast[j], j);
+    if (rank < p.topk) {
+      rb[rank] = region_corner(p, j);
+      if (it.qb == 0 && it.hg == 0) p.idx_out[((int64_t)it.b * p.R + it.i) * p.topk + rank] = j;
+    }
   }
+  __syncthreads();
+}
 
-  // ---- chunk loads. A thread owns NV/2 (key pair, 16-byte channel vector)
-  // items: pair item f = tid + 256 q covers keys 2p and 2p+1 of channel vector
-  // cv, with 8 consecutive pairs per channel vector so that one wave
-  // instruction reads 8 whole token rows; slot 2q holds key 2p, slot 2q+1 key
-  // 2p+1. Both keys of a pair land in one packed V^T word.
-  const int vpk = HGC / VEC;          // 16-byte vectors per key row
-  const int npair = (KC / 2) * vpk;   // pair items per chunk and tensor
-  uint4 kreg[NV], vreg[NV];
-  int kl0[NV / 2], cvs[NV / 2];
-#pragma unroll
-  for (int q = 0; q < NV / 2; ++q) {
-    const int f = tid + 256 * q;
-    const int oct = f / (8 * vpk);
-    const int rem = f - oct * 8 * vpk;
-    cvs[q] = rem >> 3;
-    kl0[q] = 2 * (oct * 8 + (rem & 7));
+// Single chunk: token table of the routed keys from the corner offsets rb.
+__device__ __forceinline__ void route_tokens_from_corners(const AttnParams& p, int tid, const int* rb, int* tok) {
+  for (int kappa = tid; kappa < p.kv; kappa += NW * 64) {
+    int tk, tx;
+    const int jr = fdiv(kappa, p.div_n, &tk);
+    const int ty = fdiv(tk, p.div_sw, &tx);
+    tok[kappa] = rb[jr] + ty * p.W + tx;
   }
-  auto load_chunk = [&](int c0) {
+}
+
+// K/V loads of one 64-key chunk into registers. A thread owns NV/2 (key pair,
+// 16-byte channel vector) items: pair item f = tid + 256 q covers keys 2p and
+// 2p+1 of channel vector cv, with 8 consecutive pairs per channel vector so
+// one wave instruction reads 8 whole token rows; slot 2q holds key 2p, slot
+// 2q+1 key 2p+1. (f -> p, cv by shifts: the head group spans a power-of-two
+// number of 16-byte vectors.)
+// TOK: rb holds the token offset of every key (single chunk) instead of the
+// routed regions' corners.
+template <typename T, int NV, bool TOK>
+__device__ __forceinline__ void load_kv(const AttnParams& p, const Item& it, int tid, const int* rb, int c0,
+                                        uint4 (&kreg)[NV], uint4 (&vreg)[NV]) {
+  constexpr int VEC = Tr<T>::VEC;
+  const T* Kg = static_cast<const T*>(p.K) + it.img;
+  const T* Vg = static_cast<const T*>(p.V) + it.img;
+  const int vpk = it.nh * (D / VEC);  // valid vectors per key row
 #pragma unroll
-    for (int s2 = 0; s2 < NV; ++s2) {
-      const int q = s2 >> 1;
-      kreg[s2] = make_uint4(0u, 0u, 0u, 0u);
-      vreg[s2] = make_uint4(0u, 0u, 0u, 0u);
-      const int kappa = c0 + kl0[q] + (s2 & 1);
-      if (tid + 256 * q < npair && kappa < p.kv) {
+  for (int s2 = 0; s2 < NV; ++s2) {
+    const int f = tid + 256 * (s2 >> 1);
+    const int oct = f >> p.lg_oct;
+    const int rem = f & ((1 << p.lg_oct) - 1);
+    const int cv = rem >> 3;
+    const int kappa = c0 + 2 * (oct * 8 + (rem & 7)) + (s2 & 1);
+    kreg[s2] = make_uint4(0u, 0u, 0u, 0u);
+    vreg[s2] = make_uint4(0u, 0u, 0u, 0u);
+    if (it.valid && oct < KC / 16 && cv < vpk && kappa < p.kv) {
+      int token;
+      if (TOK) {
+        token = rb[kappa];
+      } else {
         int tk, tx;
         const int jr = fdiv(kappa, p.div_n, &tk);
         const int ty = fdiv(tk, p.div_sw, &tx);
-        const int off = (rbase[jr] + ty * p.W + tx) * p.C + cb + cvs[q] * VEC;
-        kreg[s2] = *reinterpret_cast<const uint4*>(Kg + off);
-        vreg[s2] = *reinterpret_cast<const uint4*>(Vg + off);
+        token = rb[jr] + ty * p.W + tx;
       }
-    }
-  };
-  auto store_chunk = [&](T* Ks, T* Vt) {
-#pragma unroll
-    for (int q = 0; q < NV / 2; ++q) {
-      if (tid + 256 * q < npair) {
-        const int k0 = kl0[q], cv = cvs[q];
-        *reinterpret_cast<uint4*>(Ks + k0 * ldk + cv * VEC) = kreg[2 * q];
-        *reinterpret_cast<uint4*>(Ks + (k0 + 1) * ldk + cv * VEC) = kreg[2 * q + 1];
-        const int row0 = cv * VEC;
-        store_vt_pair(Vt, ldv, row0, vt_col(row0, k0), vreg[2 * q], vreg[2 * q + 1]);
-      }
-    }
-  };
-
-  const int nchunks = MULTI ? (p.kv + KC - 1) / KC : 1;
-  load_chunk(0);
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int c0 = ch * KC;
-    T* Ks = reinterpret_cast<T*>(smem_raw) + (p.nbuf == 2 ? (ch & 1) * bufsz : 0);
-    T* Vt = Ks + KC * ldk;
-    if (ch > 0 && p.nbuf == 1) __syncthreads();  // single buffer: previous chunk consumed
-    store_chunk(Ks, Vt);
-    __syncthreads();
-    if (MULTI && ch + 1 < nchunks) load_chunk(c0 + KC);  // next chunk in flight during compute
-
-    const int nvalid = min(KC, p.kv - c0);
-#pragma unroll
-    for (int uu = 0; uu < MAXU; ++uu) {
-      const int u = wave + NW * uu;
-      if (u >= U) continue;  // wave-uniform
-      const int hl = u / ntiles;
-      // ---- scores S^T for 64 keys: two 32-key steps, two 16-row tiles each
-      float s[KC / 32][8];
-      const int rr = col;  // MFMA row supplied by this lane
-      const int krow = 8 * (rr >> 2) + (rr & 3);  // key row of tile a; tile b is +4
-#pragma unroll
-      for (int st = 0; st < KC / 32; ++st) {
-        const op8 ka = TT::load8(Ks + (st * 32 + krow) * ldk + hl * D + 8 * g);
-        const op8 kb = TT::load8(Ks + (st * 32 + krow + 4) * ldk + hl * D + 8 * g);
-        const floatx4 sa = TT::mma(ka, qop[uu], floatx4{0.f, 0.f, 0.f, 0.f});
-        const floatx4 sb = TT::mma(kb, qop[uu], floatx4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[st][e] = sa[e];
-          s[st][4 + e] = sb[e];
-        }
-      }
-      // lane group g holds keys st*32 + 8g + e, e = 0..7
-      if (nvalid < KC) {  // ragged last chunk (uniform branch)
-#pragma unroll
-        for (int st = 0; st < KC / 32; ++st)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (st * 32 + 8 * g + e >= nvalid) s[st][e] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < KC / 32; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
-      mx = wave_max_groups(mx);
-      // online softmax: with a single chunk the running max starts at -inf and
-      // the accumulators at 0, so there is nothing to rescale
-      const float mnew = MULTI ? fmaxf(m[uu], mx) : mx;
-      const float mc = mnew * p.c;
-      if (MULTI) {
-        const float alpha = __builtin_amdgcn_exp2f(m[uu] * p.c - mc);
-#pragma unroll
-        for (int ct = 0; ct < 3; ++ct) acc[uu][ct] *= alpha;
-        m[uu] = mnew;
-      }
-#pragma unroll
-      for (int st = 0; st < KC / 32; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[st][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
-      // ---- O^T += V^T P^T
-      const int vrow = 8 * (rr >> 2) + (rr & 3);  // channel row of tile 0; tile 1 is +4
-#pragma unroll
-      for (int st = 0; st < KC / 32; ++st) {
-        const op8 pop = TT::from_f32(s[st]);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          const int row = hl * D + vrow + 4 * ct;
-          const op8 va = TT::load8(Vt + row * ldv + vt_col(row, st * 32 + 8 * g));
-          acc[uu][ct] = TT::mma(va, pop, acc[uu][ct]);
-        }
-        acc[uu][2] = TT::mma(TT::ones(), pop, acc[uu][2]);
-      }
+      const int off = token * p.C + it.cb + cv * VEC;
+      kreg[s2] = *reinterpret_cast<const uint4*>(Kg + off);
+      vreg[s2] = *reinterpret_cast<const uint4*>(Vg + off);
     }
   }
+}
 
-  // ---- normalise and store: lane holds channels 8g..8g+7 of its query
+template <typename T, int NV>
+__device__ __forceinline__ void store_kv(const AttnParams& p, int tid, T* Ks, T* Vt, int ldk, int ldv,
+                                         const uint4 (&kreg)[NV], const uint4 (&vreg)[NV]) {
+  constexpr int VEC = Tr<T>::VEC;
+#pragma unroll
+  for (int q = 0; q < NV / 2; ++q) {
+    const int f = tid + 256 * q;
+    const int oct = f >> p.lg_oct;
+    if (oct < KC / 16) {
+      const int rem = f & ((1 << p.lg_oct) - 1);
+      const int cv = rem >> 3;
+      const int k0 = 2 * (oct * 8 + (rem & 7));
+      *reinterpret_cast<uint4*>(Ks + k0 * ldk + cv * VEC) = kreg[2 * q];
+      *reinterpret_cast<uint4*>(Ks + (k0 + 1) * ldk + cv * VEC) = kreg[2 * q + 1];
+      const int row0 = cv * VEC;
+      store_vt_pair(Vt, ldv, row0, vt_col(row0, k0), vreg[2 * q], vreg[2 * q + 1]);
+    }
+  }
+}
+
+// Scores, softmax and P.V for the wave's units over one staged chunk.
+template <typename T, bool MULTI, bool RAGGED>
+__device__ __forceinline__ void compute_chunk(const AttnParams& p, const Item& it, int wave, int g, int col,
+                                              const T* Ks, const T* Vt, int ldk, int ldv, int nvalid,
+                                              int a16, int a32, const typename Tr<T>::op8& ones,
+                                              Units<T>& us) {
+  typedef Tr<T> TT;
+  typedef typename TT::op8 op8;
 #pragma unroll
   for (int uu = 0; uu < MAXU; ++uu) {
     const int u = wave + NW * uu;
-    if (u >= U) continue;
-    const float inv = 1.0f / acc[uu][2][0];
-    float o[8];
+    if (u >= it.U) continue;  // uniform
+    const int hl = u / it.ntiles;
+    // ---- scores S^T for 64 keys: two 32-key steps, two 16-row tiles each
+    float s[KC / 32][8];
+    const int rr = col;  // MFMA row supplied by this lane
+    const int krow = 8 * (rr >> 2) + (rr & 3);  // key row of tile a; tile b is +4
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[e] = acc[uu][0][e] * inv;
-      o[4 + e] = acc[uu][1][e] * inv;
+    for (int st = 0; st < KC / 32; ++st) {
+      const op8 ka = TT::load8(Ks + (st * 32 + krow) * ldk + hl * D + 8 * g);
+      const op8 kb = TT::load8(Ks + (st * 32 + krow + 4) * ldk + hl * D + 8 * g);
+      const floatx4 sa = TT::mma(ka, us.qop[uu], floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 sb = TT::mma(kb, us.qop[uu], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[st][e] = sa[e];
+        s[st][4 + e] = sb[e];
+      }
     }
-    if (qvalid[uu]) TT::store8(Og + qoff[uu], o);
+    // lane group g holds keys st*32 + 8g + e, e = 0..7
+    if (RAGGED && nvalid < KC) {  // ragged last chunk (uniform branch)
+#pragma unroll
+      for (int st = 0; st < KC / 32; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (st * 32 + 8 * g + e >= nvalid) s[st][e] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < KC / 32; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
+    mx = wave_max_groups(mx, a16, a32);
+    // online softmax: with a single chunk the running max starts at -inf and
+    // the accumulators at 0, so there is nothing to rescale
+    const float mnew = MULTI ? fmaxf(us.m[uu], mx) : mx;
+    const float mc = mnew * p.c;
+    if (MULTI) {
+      const float alpha = __builtin_amdgcn_exp2f(us.m[uu] * p.c - mc);
+#pragma unroll
+      for (int ct = 0; ct < 3; ++ct) us.acc[uu][ct] *= alpha;
+      us.m[uu] = mnew;
+    }
+#pragma unroll
+    for (int st = 0; st < KC / 32; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[st][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
+    // ---- O^T += V^T P^T (and the all-ones row-sum tile)
+    const int vrow = 8 * (rr >> 2) + (rr & 3);  // channel row of tile 0; tile 1 is +4
+#pragma unroll
+    for (int st = 0; st < KC / 32; ++st) {
+      const op8 pop = TT::from_f32(s[st]);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int row = hl * D + vrow + 4 * ct;
+        const op8 va = TT::load8(Vt + row * ldv + vt_col(row, st * 32 + 8 * g));
+        us.acc[uu][ct] = TT::mma(va, pop, us.acc[uu][ct]);
+      }
+      us.acc[uu][2] = TT::mma(ones, pop, us.acc[uu][2]);
+    }
   }
+}
+
+// Normalise and store: the lane holds channels 8g..8g+7 of its query.
+template <typename T>
+__device__ __forceinline__ void store_outputs(const AttnParams& p, const Item& it, const Units<T>& us, bool nan_rows) {
+  typedef Tr<T> TT;
+  T* Og = static_cast<T*>(p.O) + it.img;
+#pragma unroll
+  for (int uu = 0; uu < MAXU; ++uu) {
+    if (!us.qvalid[uu]) continue;
+    float o[8];
+    if (nan_rows) {
+      // a routing entry outside [0, S*S): never dereferenced; output NaN
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = __builtin_nanf("");
+    } else {
+      const float inv = 1.0f / us.acc[uu][2][0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = us.acc[uu][0][e] * inv;
+        o[4 + e] = us.acc[uu][1][e] * inv;
+      }
+    }
+    TT::store8(Og + us.qoff[uu], o);
+  }
+}
+
+// NV: 16-byte vectors per tensor per thread per chunk (2 or 4, even).
+// MULTI: kv spans more than one chunk (prefetch the next chunk during compute).
+// ROUTE: the workgroup computes its own routing rows from the region means
+// (same arithmetic as the route kernel) instead of reading a routing table.
+// RAGGED: kv is not a multiple of 64 (the last chunk masks its missing keys).
+template <typename T, int NV, bool MULTI, bool ROUTE, bool RAGGED>
+__global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
+  typedef Tr<T> TT;
+  typedef typename TT::op8 op8;
+  // single chunk: the routed keys' token offsets; several chunks: the routed
+  // regions' corner offsets
+  constexpr bool TOK = !MULTI;
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int rtab[kMaxRegions];
+  __shared__ int sbad;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;      // lane group: contraction slots 8g..8g+7
+  const int col = lane & 15;    // query column of the 16-query tile
+  const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
+  const op8 ones = TT::ones();
+
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
+  // each XCD a contiguous range of work items (same image -> same L2).
+  int wg;
+  {
+    const int nwg = gridDim.x, bid = blockIdx.x;
+    const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
+    wg = x * q8 + min(x, r8) + loc;
+  }
+  const int ldk = p.HG * D + TT::PADK;   // LDS row stride of K (elements)
+  const int ldv = KC + TT::PADV;         // LDS row stride of V^T (elements)
+  const int bufsz = KC * ldk + p.HG * D * ldv;
+
+  const Item it = item_at(p, wg);
+  Units<T> us;
+  load_queries<T>(p, it, wave, g, col, us);
+
+  // ---- routing row -> token offsets of the routed keys (or region corners)
+  bool bad = false;
+  if (ROUTE) {
+    if (it.valid) {
+      __shared__ int rcorner[kMaxRegions];
+      compute_routes(p, it, tid, reinterpret_cast<float*>(smem_raw), TOK ? rcorner : rtab);
+      if (TOK) {
+        route_tokens_from_corners(p, tid, rcorner, rtab);
+        __syncthreads();
+      }
+    }
+  } else {
+    if (tid == 0) sbad = 0;
+    __syncthreads();
+    if (TOK) read_route_tokens(p, it, tid, rtab, &sbad);
+    else read_routes(p, it, tid, rtab, &sbad);
+    __syncthreads();
+    bad = sbad;
+  }
+
+  if (!bad) {
+    uint4 kreg[NV], vreg[NV];
+    load_kv<T, NV, TOK>(p, it, tid, rtab, 0, kreg, vreg);
+    const int nchunks = MULTI ? (p.kv + KC - 1) / KC : 1;
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int c0 = ch * KC;
+      T* Ks = reinterpret_cast<T*>(smem_raw) + (p.nbuf == 2 ? (ch & 1) * bufsz : 0);
+      T* Vt = Ks + KC * ldk;
+      if (ch > 0 && p.nbuf == 1) __syncthreads();  // single buffer: previous chunk consumed
+      store_kv<T, NV>(p, tid, Ks, Vt, ldk, ldv, kreg, vreg);
+      __syncthreads();
+      if (MULTI && ch + 1 < nchunks) load_kv<T, NV, TOK>(p, it, tid, rtab, c0 + KC, kreg, vreg);  // next chunk in flight
+      compute_chunk<T, MULTI, RAGGED>(p, it, wave, g, col, Ks, Vt, ldk, ldv, min(KC, p.kv - c0), a16, a32, ones, us);
+    }
+  }
+  store_outputs<T>(p, it, us, bad);
+}
+
+}  // namespace
+
+namespace {
+
+// Attention launch shape: head grouping, LDS, kernel variant.
+struct AttnLaunch {
+  AttnParams p;
+  size_t lds;
+  int nv;
+  bool multi;
+  int64_t nwg;
+};
+
+AttnLaunch plan_attend(const Shape& s, int dtype) {
+  AttnLaunch L;
+  AttnParams& p = L.p;
+  p = AttnParams{};
+  p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S; p.topk = s.topk;
+  p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R; p.kv = s.kv;
+  p.heads = s.heads;
+  p.nqb = (s.n + QB - 1) / QB;
+  const int qtiles = (min(s.n, QB) + 15) / 16;
+  const int cap = dtype == kBF16 ? 4 : 2;  // keeps LDS at or below 64 KiB
+  int HG = 1;  // largest power of two <= min(units budget, cap, heads)
+  while (2 * HG <= (NW * MAXU) / qtiles && 2 * HG <= cap && 2 * HG <= s.heads) HG *= 2;
+  p.HG = HG;
+  p.nhg = (s.heads + HG - 1) / HG;
+  p.nitems = s.B * s.R * p.nqb * p.nhg;
+  const int vec = dtype == kBF16 ? 8 : 4;
+  int lg = 0;
+  while ((1 << lg) < 8 * (HG * D / vec)) ++lg;
+  p.lg_oct = lg;
+  p.c = 1.4426950408889634f / sqrtf((float)s.d);
+  p.div_n = make_fastdiv(s.n);
+  p.div_sw = make_fastdiv(s.sw);
+  p.div_S = make_fastdiv(s.S);
+  p.div_c4 = make_fastdiv(s.C / 4);
+  const size_t esz = dtype == kBF16 ? 2 : 4;
+  const int padk = dtype == kBF16 ? Tr<__bf16>::PADK : Tr<float>::PADK;
+  const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
+  const size_t buf = esz * ((size_t)KC * (HG * D + padk) + (size_t)HG * D * (KC + padv));
+  p.nbuf = (s.kv > KC && 2 * buf <= 65536) ? 2 : 1;
+  L.lds = p.nbuf * buf;
+  L.nv = (KC * (HG * D / vec) + NW * 64 - 1) / (NW * 64);
+  L.multi = s.kv > KC;
+  // One item per workgroup. (Two items per workgroup, with all loads of both
+  // in flight before either is computed, measured slower at the stage-1
+  // shape: the extra registers cut occupancy from 8 to 5 waves per SIMD and
+  // the kernel is issue-bound.)
+  L.nwg = p.nitems;
+  return L;
+}
+
+// LDS the in-kernel routing needs: K^r[b] rows (C + 4 floats each), one query
+// row, and the affinity row.
+size_t route_in_lds(const Shape& s) {
+  return sizeof(float) * ((size_t)s.R * (s.C + 4) + s.C + (size_t)((s.R + 3) & ~3));
+}
+
+template <typename T, bool ROUTE, bool RAGGED>
+const void* pick_attend_r(int nv, bool multi) {
+  if (multi) return nv <= 2 ? (const void*)&attend_kernel<T, 2, true, ROUTE, RAGGED> : (const void*)&attend_kernel<T, 4, true, ROUTE, RAGGED>;
+  return nv <= 2 ? (const void*)&attend_kernel<T, 2, false, ROUTE, RAGGED> : (const void*)&attend_kernel<T, 4, false, ROUTE, RAGGED>;
+}
+
+template <typename T, bool ROUTE>
+const void* pick_attend_t(int nv, bool multi, bool ragged) {
+  return ragged ? pick_attend_r<T, ROUTE, true>(nv, multi) : pick_attend_r<T, ROUTE, false>(nv, multi);
+}
+
+template <bool ROUTE>
+const void* pick_attend(int dtype, const AttnLaunch& L) {
+  const bool ragged = L.p.kv % KC != 0;
+  return dtype == kBF16 ? pick_attend_t<__bf16, ROUTE>(L.nv, L.multi, ragged) : pick_attend_t<float, ROUTE>(L.nv, L.multi, ragged);
 }
 
 }  // namespace
@@ -436,45 +667,24 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
 hipError_t launch_attend(const void* Q, const void* K, const void* V,
                          const int32_t* idx, void* O, const Shape& s, int dtype,
                          hipStream_t stream) {
-  AttnParams p;
-  p.Q = Q; p.K = K; p.V = V; p.idx = idx; p.O = O;
-  p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S; p.topk = s.topk;
-  p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R; p.kv = s.kv;
-  p.heads = s.heads;
-  p.nqb = (s.n + QB - 1) / QB;
-  const int qtiles = (min(s.n, QB) + 15) / 16;
-  const int cap = dtype == kBF16 ? 4 : 2;  // keeps LDS at or below 64 KiB
-  int HG = (NW * MAXU) / qtiles;
-  if (HG > cap) HG = cap;
-  if (HG > s.heads) HG = s.heads;
-  if (HG < 1) HG = 1;
-  p.HG = HG;
-  p.nhg = (s.heads + HG - 1) / HG;
-  p.c = 1.4426950408889634f / sqrtf((float)s.d);
-  p.div_n = make_fastdiv(s.n);
-  p.div_sw = make_fastdiv(s.sw);
-  const size_t esz = dtype == kBF16 ? 2 : 4;
-  const int padk = dtype == kBF16 ? Tr<__bf16>::PADK : Tr<float>::PADK;
-  const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
-  const size_t buf = esz * ((size_t)KC * (HG * D + padk) + (size_t)HG * D * (KC + padv));
-  p.nbuf = (s.kv > KC && 2 * buf <= 65536) ? 2 : 1;
-  const size_t lds = p.nbuf * buf;
-  const int64_t nwg = (int64_t)s.B * s.R * p.nqb * p.nhg;
-  dim3 grid((unsigned)nwg);
-  void* args[] = {&p};
-  // vectors per thread: KC keys x (HG*D / VEC) vectors / 256 threads
-  const int vec = dtype == kBF16 ? 8 : 4;
-  const int nv = (KC * (HG * D / vec) + NW * 64 - 1) / (NW * 64);
-  const bool multi = s.kv > KC;
-  const void* fn;
-  if (dtype == kBF16) {
-    if (nv <= 2) fn = multi ? (const void*)&attend_kernel<__bf16, 2, true> : (const void*)&attend_kernel<__bf16, 2, false>;
-    else fn = multi ? (const void*)&attend_kernel<__bf16, 4, true> : (const void*)&attend_kernel<__bf16, 4, false>;
-  } else {
-    if (nv <= 2) fn = multi ? (const void*)&attend_kernel<float, 2, true> : (const void*)&attend_kernel<float, 2, false>;
-    else fn = multi ? (const void*)&attend_kernel<float, 4, true> : (const void*)&attend_kernel<float, 4, false>;
-  }
-  return hipLaunchKernel(fn, grid, dim3(NW * 64), args, lds, stream);
+  AttnLaunch L = plan_attend(s, dtype);
+  L.p.Q = Q; L.p.K = K; L.p.V = V; L.p.idx = idx; L.p.O = O;
+  void* args[] = {&L.p};
+  return hipLaunchKernel(pick_attend<false>(dtype, L), dim3((unsigned)L.nwg), dim3(NW * 64), args, L.lds, stream);
+}
+
+bool attend_can_route(const Shape& s, int dtype) {
+  return route_in_lds(s) <= plan_attend(s, dtype).lds;
+}
+
+hipError_t launch_attend_routed(const void* Q, const void* K, const void* V, const float* Qr,
+                                const float* Kr, int32_t* idx_out, void* O, const Shape& s,
+                                int dtype, hipStream_t stream) {
+  AttnLaunch L = plan_attend(s, dtype);
+  L.p.Q = Q; L.p.K = K; L.p.V = V; L.p.O = O;
+  L.p.Qr = Qr; L.p.Kr = Kr; L.p.idx_out = idx_out;
+  void* args[] = {&L.p};
+  return hipLaunchKernel(pick_attend<true>(dtype, L), dim3((unsigned)L.nwg), dim3(NW * 64), args, L.lds, stream);
 }
 
 }  // namespace bra

@@ -5,7 +5,8 @@
 // regional representations by average pooling).
 //
 // HBM-bound: every input byte is read once, 2*B*R*C fp32 values are written.
-// One workgroup per (image, region) pools both Q and K. A region is sh rows of
+// One workgroup per (image, region) pools both Q and K. (One wave per region
+// with a lane-shuffle reduction measured slower at the stage-1 shape.) A region is sh rows of
 // one contiguous segment of sw*C elements, read as 16-byte vectors; every
 // thread issues all of its loads (up to NL per tensor) before it adds any, so
 // a workgroup has its whole region in flight at once. The block size is a
@@ -126,6 +127,7 @@ hipError_t launch_pool(const void* Q, const void* K, float* Qr, float* Kr,
   PoolParams p{Q, K, Qr, Kr, s.H, s.W, s.C, s.S, s.sh, s.sw};
   const int vec = dtype == kBF16 ? 8 : 4;
   const int G = s.C / vec;
+
   const int total = s.sh * s.sw * G;
   // about 4 vectors per tensor per thread, at least one full channel-group set
   int bs = 64;

@@ -23,6 +23,7 @@
 // Each lane counts against the whole row (broadcast LDS reads): R compares
 // per candidate, independent of k.
 #include "bra_internal.h"
+#include "route_common.h"
 
 #include <math.h>
 
@@ -117,10 +118,7 @@ __global__ __launch_bounds__(NT) void route_kernel(RouteParams p) {
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const float4 k = *reinterpret_cast<const float4*>(Ks + min(lane + 64 * u, p.R - 1) * LDC + 4 * c4);
-        acc[u].x = __builtin_fmaf(q.x, k.x, acc[u].x);
-        acc[u].y = __builtin_fmaf(q.y, k.y, acc[u].y);
-        acc[u].z = __builtin_fmaf(q.z, k.z, acc[u].z);
-        acc[u].w = __builtin_fmaf(q.w, k.w, acc[u].w);
+        acc[u] = affinity_step(acc[u], q, k);
       }
     }
   }
@@ -131,7 +129,7 @@ __global__ __launch_bounds__(NT) void route_kernel(RouteParams p) {
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const int j = lane + 64 * u;
-    if (j < p.ldr) a[j] = j < p.R ? (acc[u].x + acc[u].y) + (acc[u].z + acc[u].w) : -INFINITY;
+    if (j < p.ldr) a[j] = j < p.R ? affinity_finish(acc[u]) : -INFINITY;
   }
   __syncthreads();
   if (row >= nrows) return;  // wave-uniform; no barrier follows
@@ -142,14 +140,7 @@ __global__ __launch_bounds__(NT) void route_kernel(RouteParams p) {
   for (int u = 0; u < NU; ++u) {
     const int j = lane + 64 * u;
     const float aj = j < p.R ? a[j] : -INFINITY;
-    int rank = 0;
-    for (int m = 0; m < p.ldr; m += 4) {
-      const float4 am = *reinterpret_cast<const float4*>(a + m);
-      rank += (am.x > aj) || (am.x == aj && m + 0 < j);
-      rank += (am.y > aj) || (am.y == aj && m + 1 < j);
-      rank += (am.z > aj) || (am.z == aj && m + 2 < j);
-      rank += (am.w > aj) || (am.w == aj && m + 3 < j);
-    }
+    const int rank = affinity_rank(a, p.ldr, aj, j);
     if (j < p.R && rank < p.topk) out[rank] = j;
   }
 }
