@@ -36,7 +36,6 @@
 // accumulation and softmax. fp32: eight v_mfma_f32_16x16x4_f32 per 32-deep
 // contraction, P kept in fp32.
 #include "bra_internal.h"
-#include "route_common.h"
 
 #include <math.h>
 
@@ -148,10 +147,7 @@ struct AttnParams {
   int lg_oct;  // log2(8 * HG * D / VEC): pair items per 8-pair octet of a chunk
   int nbuf;    // LDS chunk buffers (2: double-buffered, when kv spans several chunks)
   float c;     // softmax scale * log2(e)
-  FastDiv div_n, div_sw, div_S, div_c4;
-  const float* Qr;  // region means (routing inside the kernel only)
-  const float* Kr;
-  int32_t* idx_out; // routing table written by the kernel (routing inside only)
+  FastDiv div_n, div_sw, div_S;
 };
 
 // Max over the 4 lane groups that share lane % 16; a16/a32 are the byte
@@ -293,58 +289,6 @@ __device__ __forceinline__ void read_route_tokens(const AttnParams& p, const Ite
     const bool ok = r >= 0 && r < p.R;
     tok[kappa] = region_corner(p, ok ? r : 0) + ty * p.W + tx;
     if (!ok) *bad = 1;
-  }
-}
-
-// Routing row computed in the workgroup from the region means, with the route
-// kernel's arithmetic (shared helpers), staged in the chunk LDS area `stage`.
-// Ends with a barrier; the staging area is free afterwards.
-__device__ __forceinline__ void compute_routes(const AttnParams& p, const Item& it, int tid, float* stage, int* rb) {
-  const int ldc = p.C + 4;
-  float* Kst = stage;
-  float* Qst = Kst + p.R * ldc;
-  float* Ast = Qst + p.C;
-  const int c4n = p.C >> 2;
-  const int ldr = (p.R + 3) & ~3;
-  const float* krb = p.Kr + (int64_t)it.b * p.R * p.C;
-  const float* qri = p.Qr + ((int64_t)it.b * p.R + it.i) * p.C;
-  for (int f = tid; f < p.R * c4n; f += NW * 64) {
-    int c4;
-    const int j = fdiv(f, p.div_c4, &c4);
-    *reinterpret_cast<float4*>(Kst + j * ldc + 4 * c4) = *reinterpret_cast<const float4*>(krb + (int64_t)j * p.C + 4 * c4);
-  }
-  for (int c4 = tid; c4 < c4n; c4 += NW * 64)
-    *reinterpret_cast<float4*>(Qst + 4 * c4) = *reinterpret_cast<const float4*>(qri + 4 * c4);
-  __syncthreads();
-  for (int j = tid; j < ldr; j += NW * 64) {
-    float a = -INFINITY;
-    if (j < p.R) {
-      float4 acc4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int c4 = 0; c4 < c4n; ++c4)
-        acc4 = affinity_step(acc4, *reinterpret_cast<const float4*>(Qst + 4 * c4),
-                             *reinterpret_cast<const float4*>(Kst + j * ldc + 4 * c4));
-      a = affinity_finish(acc4);
-    }
-    Ast[j] = a;
-  }
-  __syncthreads();
-  for (int j = tid; j < p.R; j += NW * 64) {
-    const int rank = affinity_rank(Ast, ldr, Ast[j], j);
-    if (rank < p.topk) {
-      rb[rank] = region_corner(p, j);
-      if (it.qb == 0 && it.hg == 0) p.idx_out[((int64_t)it.b * p.R + it.i) * p.topk + rank] = j;
-    }
-  }
-  __syncthreads();
-}
-
-// Single chunk: token table of the routed keys from the corner offsets rb.
-__device__ __forceinline__ void route_tokens_from_corners(const AttnParams& p, int tid, const int* rb, int* tok) {
-  for (int kappa = tid; kappa < p.kv; kappa += NW * 64) {
-    int tk, tx;
-    const int jr = fdiv(kappa, p.div_n, &tk);
-    const int ty = fdiv(tk, p.div_sw, &tx);
-    tok[kappa] = rb[jr] + ty * p.W + tx;
   }
 }
 
@@ -509,10 +453,8 @@ __device__ __forceinline__ void store_outputs(const AttnParams& p, const Item& i
 
 // NV: 16-byte vectors per tensor per thread per chunk (2 or 4, even).
 // MULTI: kv spans more than one chunk (prefetch the next chunk during compute).
-// ROUTE: the workgroup computes its own routing rows from the region means
-// (same arithmetic as the route kernel) instead of reading a routing table.
 // RAGGED: kv is not a multiple of 64 (the last chunk masks its missing keys).
-template <typename T, int NV, bool MULTI, bool ROUTE, bool RAGGED>
+template <typename T, int NV, bool MULTI, bool RAGGED>
 __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
@@ -549,24 +491,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
   load_queries<T>(p, it, wave, g, col, us);
 
   // ---- routing row -> token offsets of the routed keys (or region corners)
-  bool bad = false;
-  if (ROUTE) {
-    if (it.valid) {
-      __shared__ int rcorner[kMaxRegions];
-      compute_routes(p, it, tid, reinterpret_cast<float*>(smem_raw), TOK ? rcorner : rtab);
-      if (TOK) {
-        route_tokens_from_corners(p, tid, rcorner, rtab);
-        __syncthreads();
-      }
-    }
-  } else {
-    if (tid == 0) sbad = 0;
-    __syncthreads();
-    if (TOK) read_route_tokens(p, it, tid, rtab, &sbad);
-    else read_routes(p, it, tid, rtab, &sbad);
-    __syncthreads();
-    bad = sbad;
-  }
+  if (tid == 0) sbad = 0;
+  __syncthreads();
+  if (TOK) read_route_tokens(p, it, tid, rtab, &sbad);
+  else read_routes(p, it, tid, rtab, &sbad);
+  __syncthreads();
+  const bool bad = sbad;
 
   if (!bad) {
     uint4 kreg[NV], vreg[NV];
@@ -584,6 +514,188 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
     }
   }
   store_outputs<T>(p, it, us, bad);
+}
+
+// ---------------------------------------------------------------------------
+// Single-chunk kernel (kv <= 64 routed keys per query), one wave per head.
+// A workgroup = one work item with HG heads = HG waves; wave h owns head h of
+// the group and loops over the item's <= 4 query tiles. Its K operands (the
+// A operands of S^T, 64 keys x 32 channels) come straight from HBM into
+// registers once and serve every tile; its V slice goes through the wave's
+// own V^T tile in LDS once (the transpose) and then also lives in registers.
+// Per tile only the query operand is loaded: 10 MFMAs, the softmax and the
+// 16-byte output stores, with no LDS traffic.
+// MAXT: query tiles per item the kernel is built for (1, or 4 = 64 queries).
+template <typename T, bool RAGGED, int MAXT>
+__global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
+  typedef Tr<T> TT;
+  typedef typename TT::op8 op8;
+  constexpr int VEC = TT::VEC;
+  constexpr int CVH = D / VEC;  // 16-byte vectors per key row of one head
+  constexpr int PAIRS = KC / 2 * CVH / 64;  // (key pair, vector) items per lane
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int rtab[KC];
+  __shared__ int sbad;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+  const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
+  const op8 ones = TT::ones();
+  const int ldv = KC + TT::PADV;
+  T* Vt = reinterpret_cast<T*>(smem_raw) + wave * D * ldv;  // this wave's V^T tile
+
+  int wg;
+  {
+    const int nwg = gridDim.x, bid = blockIdx.x;
+    const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
+    wg = x * q8 + min(x, r8) + loc;
+  }
+  const Item it = item_at(p, wg);
+  const bool head_ok = wave < it.nh;
+  const int ch0 = it.cb + wave * D;  // first channel of this wave's head
+  const T* Kg = static_cast<const T*>(p.K) + it.img;
+  const T* Vg = static_cast<const T*>(p.V) + it.img;
+  const T* Qg = static_cast<const T*>(p.Q) + it.img;
+
+  // ---- query operands of all (<= 4) tiles first: they do not depend on the
+  // routing, so their loads overlap the routing-table round trip
+  op8 qop[MAXT];
+  int qoff[MAXT];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    const int qi = it.q0 + t * 16 + col;
+    qoff[t] = -1;
+    qop[t] = TT::zero();
+    if (head_ok && t < it.ntiles && qi < it.q0 + it.nq) {
+      int qx;
+      const int qy = fdiv(qi, p.div_sw, &qx);
+      qoff[t] = (it.qcorner + qy * p.W + qx) * p.C + ch0 + 8 * g;
+      qop[t] = TT::load8(Qg + qoff[t]);
+    }
+  }
+
+  if (tid == 0) sbad = 0;
+  __syncthreads();
+  read_route_tokens(p, it, tid, rtab, &sbad);
+  __syncthreads();
+  const bool bad = sbad;
+
+  // ---- K operands: row rr = col of the tile for (32-key step st, tile tb)
+  // is key st*32 + 8*(rr/4) + (rr%4) + 4*tb; slots = channels 8g..8g+7
+  op8 kop[2][2];
+  uint4 vreg[PAIRS][2];
+  if (head_ok && !bad) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
+        kop[st][tb] = (!RAGGED || key < p.kv) ? TT::load8(Kg + rtab[key] * p.C + ch0 + 8 * g) : TT::zero();
+      }
+    // V slice: pair item f = lane + 64 m -> channel vector cv = f % CVH, key
+    // pair p2 = f / CVH (keys 2 p2, 2 p2 + 1)
+#pragma unroll
+    for (int m = 0; m < PAIRS; ++m) {
+      const int f = lane + 64 * m;
+      const int cv = f % CVH, p2 = f / CVH;
+#pragma unroll
+      for (int k1 = 0; k1 < 2; ++k1) {
+        const int key = 2 * p2 + k1;
+        vreg[m][k1] = (!RAGGED || key < p.kv) ? *reinterpret_cast<const uint4*>(Vg + rtab[key] * p.C + ch0 + cv * VEC)
+                                             : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < PAIRS; ++m) {
+      const int f = lane + 64 * m;
+      const int cv = f % CVH, p2 = f / CVH;
+      const int row0 = cv * VEC;
+      store_vt_pair(Vt, ldv, row0, vt_col(row0, 2 * p2), vreg[m][0], vreg[m][1]);
+    }
+  }
+  __syncthreads();  // V^T tiles written (each wave reads only its own)
+  if (!head_ok) return;
+
+  T* Og = static_cast<T*>(p.O) + it.img;
+  if (bad) {
+    // a routing entry outside [0, S*S): never dereferenced; output NaN
+    float nanv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nanv[e] = __builtin_nanf("");
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+      if (qoff[t] >= 0) TT::store8(Og + qoff[t], nanv);
+    return;
+  }
+
+  // ---- V operands: row rr = col is channel 8*(rr/4) + (rr%4) + 4*ct; slots =
+  // keys st*32 + 8g .. +7
+  op8 vop[2][2];
+  {
+    const int vrow = 8 * (col >> 2) + (col & 3);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int row = vrow + 4 * ct;
+        vop[st][ct] = TT::load8(Vt + row * ldv + vt_col(row, st * 32 + 8 * g));
+      }
+  }
+
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t >= it.ntiles) break;  // uniform
+    float s[2][8];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const floatx4 sa = TT::mma(kop[st][0], qop[t], floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 sb = TT::mma(kop[st][1], qop[t], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[st][e] = sa[e];
+        s[st][4 + e] = sb[e];
+      }
+    }
+    if (RAGGED) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (st * 32 + 8 * g + e >= p.kv) s[st][e] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
+    mx = wave_max_groups(mx, a16, a32);
+    const float mc = mx * p.c;
+    floatx4 acc[3] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float pe[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
+      const op8 pop = TT::from_f32(pe);
+      acc[0] = TT::mma(vop[st][0], pop, acc[0]);
+      acc[1] = TT::mma(vop[st][1], pop, acc[1]);
+      acc[2] = TT::mma(ones, pop, acc[2]);
+    }
+    if (qoff[t] >= 0) {
+      const float inv = 1.0f / acc[2][0];
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = acc[0][e] * inv;
+        o[4 + e] = acc[1][e] * inv;
+      }
+      TT::store8(Og + qoff[t], o);
+    }
+  }
 }
 
 }  // namespace
@@ -622,7 +734,6 @@ AttnLaunch plan_attend(const Shape& s, int dtype) {
   p.div_n = make_fastdiv(s.n);
   p.div_sw = make_fastdiv(s.sw);
   p.div_S = make_fastdiv(s.S);
-  p.div_c4 = make_fastdiv(s.C / 4);
   const size_t esz = dtype == kBF16 ? 2 : 4;
   const int padk = dtype == kBF16 ? Tr<__bf16>::PADK : Tr<float>::PADK;
   const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
@@ -639,27 +750,16 @@ AttnLaunch plan_attend(const Shape& s, int dtype) {
   return L;
 }
 
-// LDS the in-kernel routing needs: K^r[b] rows (C + 4 floats each), one query
-// row, and the affinity row.
-size_t route_in_lds(const Shape& s) {
-  return sizeof(float) * ((size_t)s.R * (s.C + 4) + s.C + (size_t)((s.R + 3) & ~3));
-}
-
-template <typename T, bool ROUTE, bool RAGGED>
+template <typename T, bool RAGGED>
 const void* pick_attend_r(int nv, bool multi) {
-  if (multi) return nv <= 2 ? (const void*)&attend_kernel<T, 2, true, ROUTE, RAGGED> : (const void*)&attend_kernel<T, 4, true, ROUTE, RAGGED>;
-  return nv <= 2 ? (const void*)&attend_kernel<T, 2, false, ROUTE, RAGGED> : (const void*)&attend_kernel<T, 4, false, ROUTE, RAGGED>;
+  if (multi) return nv <= 2 ? (const void*)&attend_kernel<T, 2, true, RAGGED> : (const void*)&attend_kernel<T, 4, true, RAGGED>;
+  return nv <= 2 ? (const void*)&attend_kernel<T, 2, false, RAGGED> : (const void*)&attend_kernel<T, 4, false, RAGGED>;
 }
 
-template <typename T, bool ROUTE>
-const void* pick_attend_t(int nv, bool multi, bool ragged) {
-  return ragged ? pick_attend_r<T, ROUTE, true>(nv, multi) : pick_attend_r<T, ROUTE, false>(nv, multi);
-}
-
-template <bool ROUTE>
 const void* pick_attend(int dtype, const AttnLaunch& L) {
   const bool ragged = L.p.kv % KC != 0;
-  return dtype == kBF16 ? pick_attend_t<__bf16, ROUTE>(L.nv, L.multi, ragged) : pick_attend_t<float, ROUTE>(L.nv, L.multi, ragged);
+  if (dtype == kBF16) return ragged ? pick_attend_r<__bf16, true>(L.nv, L.multi) : pick_attend_r<__bf16, false>(L.nv, L.multi);
+  return ragged ? pick_attend_r<float, true>(L.nv, L.multi) : pick_attend_r<float, false>(L.nv, L.multi);
 }
 
 }  // namespace
@@ -667,24 +767,34 @@ const void* pick_attend(int dtype, const AttnLaunch& L) {
 hipError_t launch_attend(const void* Q, const void* K, const void* V,
                          const int32_t* idx, void* O, const Shape& s, int dtype,
                          hipStream_t stream) {
+  if (s.kv <= KC) {
+    // single chunk: one wave per head, up to 8 heads per workgroup
+    AttnParams p = plan_attend(s, dtype).p;
+    int HG = 1;
+    while (2 * HG <= 8 && 2 * HG <= s.heads) HG *= 2;
+    p.HG = HG;
+    p.nhg = (s.heads + HG - 1) / HG;
+    p.nitems = s.B * s.R * p.nqb * p.nhg;
+    p.Q = Q; p.K = K; p.V = V; p.idx = idx; p.O = O;
+    const size_t esz = dtype == kBF16 ? 2 : 4;
+    const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
+    const size_t lds = esz * (size_t)HG * D * (KC + padv);
+    const bool ragged = s.kv % KC != 0;
+    const bool one = s.n <= 16;  // one query tile per item
+    const void* fn;
+    if (dtype == kBF16)
+      fn = ragged ? (one ? (const void*)&attend_head_kernel<__bf16, true, 1> : (const void*)&attend_head_kernel<__bf16, true, 4>)
+                  : (one ? (const void*)&attend_head_kernel<__bf16, false, 1> : (const void*)&attend_head_kernel<__bf16, false, 4>);
+    else
+      fn = ragged ? (one ? (const void*)&attend_head_kernel<float, true, 1> : (const void*)&attend_head_kernel<float, true, 4>)
+                  : (one ? (const void*)&attend_head_kernel<float, false, 1> : (const void*)&attend_head_kernel<float, false, 4>);
+    void* args[] = {&p};
+    return hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(HG * 64), args, lds, stream);
+  }
   AttnLaunch L = plan_attend(s, dtype);
   L.p.Q = Q; L.p.K = K; L.p.V = V; L.p.idx = idx; L.p.O = O;
   void* args[] = {&L.p};
-  return hipLaunchKernel(pick_attend<false>(dtype, L), dim3((unsigned)L.nwg), dim3(NW * 64), args, L.lds, stream);
-}
-
-bool attend_can_route(const Shape& s, int dtype) {
-  return route_in_lds(s) <= plan_attend(s, dtype).lds;
-}
-
-hipError_t launch_attend_routed(const void* Q, const void* K, const void* V, const float* Qr,
-                                const float* Kr, int32_t* idx_out, void* O, const Shape& s,
-                                int dtype, hipStream_t stream) {
-  AttnLaunch L = plan_attend(s, dtype);
-  L.p.Q = Q; L.p.K = K; L.p.V = V; L.p.O = O;
-  L.p.Qr = Qr; L.p.Kr = Kr; L.p.idx_out = idx_out;
-  void* args[] = {&L.p};
-  return hipLaunchKernel(pick_attend<true>(dtype, L), dim3((unsigned)L.nwg), dim3(NW * 64), args, L.lds, stream);
+  return hipLaunchKernel(pick_attend(dtype, L), dim3((unsigned)L.nwg), dim3(NW * 64), args, L.lds, stream);
 }
 
 }  // namespace bra

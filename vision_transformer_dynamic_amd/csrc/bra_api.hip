@@ -149,15 +149,6 @@ bra_status bra_forward(const void* Q, const void* K, const void* V, void* O,
   st = ws.acquire(workspace, workspace_bytes, workspace_for(s), stream);
   if (st != BRA_OK) return st;
   int32_t* idx = reinterpret_cast<int32_t*>(ws.ptr + 2 * pooled_bytes(s));
-  if (bra::attend_can_route(s, (int)dtype)) {
-    // two launches: pool, then attention that routes each region itself
-    float* Qr = reinterpret_cast<float*>(ws.ptr);
-    float* Kr = reinterpret_cast<float*>(ws.ptr + pooled_bytes(s));
-    if (bra::launch_pool(Q, K, Qr, Kr, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
-    if (bra::launch_attend_routed(Q, K, V, Qr, Kr, idx, O, s, (int)dtype, stream) != hipSuccess)
-      return BRA_EHIP;
-    return BRA_OK;
-  }
   st = enqueue_route(Q, K, idx, s, (int)dtype, ws.ptr, stream);
   if (st != BRA_OK) return st;
   if (bra::launch_attend(Q, K, V, idx, O, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;

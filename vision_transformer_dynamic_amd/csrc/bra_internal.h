@@ -67,14 +67,4 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
                          const int32_t* idx, void* O, const Shape& s, int dtype,
                          hipStream_t stream);
 
-// True when the attention kernel can form its own routing rows (the staged
-// region keys fit in its LDS); then the route kernel is not needed.
-bool attend_can_route(const Shape& s, int dtype);
-
-// Attention that computes each region's routing row from Qr, Kr itself (the
-// route kernel's arithmetic, bit for bit) and writes the table to idx_out.
-hipError_t launch_attend_routed(const void* Q, const void* K, const void* V, const float* Qr,
-                                const float* Kr, int32_t* idx_out, void* O, const Shape& s,
-                                int dtype, hipStream_t stream);
-
 }  // namespace bra

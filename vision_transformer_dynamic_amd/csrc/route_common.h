@@ -1,8 +1,7 @@
-// Arithmetic shared by every kernel that routes (the route kernel and the
-// attention kernel's own routing row), so that all of them produce the same
-// bits: region affinity A[i][j] = Q^r[i,:] . K^r[j,:] and the top-k tie rule
-// (explainer "BiFormer Reshapes Visual Attention with 'Bi-Level Routing'",
-// Part 2.2 pseudocode steps 4-5).
+// Routing arithmetic: region affinity A[i][j] = Q^r[i,:] . K^r[j,:] in one
+// fixed order, and the top-k tie rule (explainer "BiFormer Reshapes Visual
+// Attention with 'Bi-Level Routing'", Part 2.2 pseudocode steps 4-5). Any
+// kernel that routes uses these, so all routing tables agree bit for bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
