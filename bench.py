@@ -257,7 +257,7 @@ def main(argv=None):
                 "frac": round(achieved / peak_tf, 4)}
     traffic = profiled_traffic() if w is wl.HEADLINE else None
     roof["traffic"] = traffic
-    roof["kernel"] = "attend_kernel<bf16>" if w.dtype == "bf16" else "attend_kernel<float>"
+    roof["kernel"] = "attend_head_kernel" if w.kv <= 64 else "attend_kernel"
     roof["algorithmic_bytes_per_launch"] = attn_bytes
     roof["launch_us"] = round(attend_us, 2)
 
