@@ -48,8 +48,13 @@ design notes of the repository):
   * ties in top-k: larger affinity first, lower region index first on
     exact ties (a stable sort of -A);
   * the local context enhancement term (+ dwconv(V), [EXP] pseudocode
-    step 7) is not part of this operator: it needs convolution weights and
-    the operator's interface takes none.
+    step 7) is a separate function, ``lce``, added by ``bra_lce`` /
+    ``attend_lce``: the operator without it takes no convolution weights.
+    Its readings: a 5 x 5 depthwise convolution of V over the whole H x W
+    map (not per region), stride 1, zero padding 2 (output the size of the
+    map), PyTorch's convolution convention (cross-correlation: tap (i, j)
+    of channel c multiplies V[y + i - 2, x + j - 2, c]), one filter per
+    channel and an optional per-channel bias.
 
 Pins (tests/test_oracle_pins.py, all ``-m "not gpu"``):
   region_mean + affinity : equal to the mean of all n*n token-pair dot
@@ -62,7 +67,12 @@ Pins (tests/test_oracle_pins.py, all ``-m "not gpu"``):
                            reshaping (brute); K = 0 gives the mean of the
                            gathered V; V = 1 gives 1; permutation
                            invariance in the route order;
-  attended_tokens        : the [EXP] Part 6.3 table (tests/golden).
+  attended_tokens        : the [EXP] Part 6.3 table (tests/golden);
+  lce                    : torch conv2d with groups = C and scipy.ndimage
+                           correlate (two library routines), single-tap
+                           filters = shifted maps with zero fill (brute
+                           loops), all-ones filter on a map of ones = the
+                           closed-form count of in-map neighbours.
 """
 
 from __future__ import annotations
@@ -238,3 +248,60 @@ def bra(Q, K, V, heads: int, S: int, topk: int, scale: float | None = None):
     """Full BRA forward (without the local-context term): returns (O, routes)."""
     routes = route(Q, K, S, topk)
     return attend(Q, K, V, routes, heads, S, scale), routes
+
+
+# --------------------------------------------------------------------------- #
+# Local context enhancement: the "+ dwconv(value)" term
+# --------------------------------------------------------------------------- #
+LCE_SIZE = 5
+
+
+def lce(V, weight, bias=None) -> np.ndarray:
+    """Local context enhancement: a 5 x 5 depthwise convolution of V.
+
+    [EXP] 2.2 step 4 (the local enhancement term, a 5 x 5 depthwise
+    convolution) and pseudocode step 7 (``+ dwconv(value)``); [SUM] Section 3
+    (token-to-token attention plus a depthwise-convolution local context
+    term). Written out:
+
+        out[b, y, x, c] = bias[c] + sum_{i, j in 0..4} weight[c, i, j]
+                                    * V[b, y + i - 2, x + j - 2, c]
+
+    where terms whose position falls outside the H x W map are omitted (zero
+    padding). V: [B, H, W, C]; weight: [C, 5, 5]; bias: [C] or None.
+    Returns [B, H, W, C] float64.
+    """
+    V = np.asarray(V, dtype=np.float64)
+    weight = np.asarray(weight, dtype=np.float64)
+    B, H, W, C = V.shape
+    if weight.shape != (C, LCE_SIZE, LCE_SIZE):
+        raise ValueError(f"weight must be [C, 5, 5] = {(C, LCE_SIZE, LCE_SIZE)}, got {weight.shape}")
+    out = np.zeros_like(V)
+    if bias is not None:
+        bias = np.asarray(bias, dtype=np.float64)
+        if bias.shape != (C,):
+            raise ValueError(f"bias must be [C] = {(C,)}, got {bias.shape}")
+        out += bias
+    half = LCE_SIZE // 2
+    for i in range(LCE_SIZE):
+        dy = i - half
+        y0, y1 = max(0, -dy), min(H, H - dy)  # rows y with 0 <= y + dy < H
+        for j in range(LCE_SIZE):
+            dx = j - half
+            x0, x1 = max(0, -dx), min(W, W - dx)
+            if y0 >= y1 or x0 >= x1:
+                continue
+            out[:, y0:y1, x0:x1, :] += weight[:, i, j] * V[:, y0 + dy:y1 + dy, x0 + dx:x1 + dx, :]
+    return out
+
+
+def attend_lce(Q, K, V, routes, heads: int, S: int, weight, bias=None, scale: float | None = None) -> np.ndarray:
+    """Token attention over a given routing table plus the local context
+    term: the module output of [EXP] pseudocode step 7."""
+    return attend(Q, K, V, routes, heads, S, scale) + lce(V, weight, bias)
+
+
+def bra_lce(Q, K, V, heads: int, S: int, topk: int, weight, bias=None, scale: float | None = None):
+    """Full BRA forward with the local context term: returns (O, routes)."""
+    O, routes = bra(Q, K, V, heads, S, topk, scale)
+    return O + lce(V, weight, bias), routes

@@ -18,6 +18,7 @@ _orig_affinity = O.affinity
 _orig_softmax = O.softmax_attention
 _orig_mean = O.region_mean
 _orig_attend = O.attend
+_orig_lce = O.lce
 
 
 def _transposed_affinity(Qr, Kr):
@@ -72,7 +73,46 @@ def _interleaved_heads(Q, K, V, routes, heads, S, scale=None):
     return _orig_attend(Q[..., perm], np.asarray(K)[..., perm], np.asarray(V)[..., perm], routes, heads, S, scale)[..., inv]
 
 
+def _convolution_not_correlation(V, weight, bias=None):
+    return _orig_lce(V, np.asarray(weight)[:, ::-1, ::-1], bias)
+
+
+def _transposed_filter(V, weight, bias=None):
+    return _orig_lce(V, np.swapaxes(np.asarray(weight), 1, 2), bias)
+
+
+def _circular_padding(V, weight, bias=None):
+    V = np.asarray(V, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    out = np.zeros_like(V) + (0.0 if bias is None else np.asarray(bias, dtype=np.float64))
+    for i in range(5):
+        for j in range(5):
+            out += w[:, i, j] * np.roll(V, (2 - i, 2 - j), axis=(1, 2))
+    return out
+
+
+def _dropped_bias(V, weight, bias=None):
+    return _orig_lce(V, weight, None)
+
+
+def _off_by_one_padding(V, weight, bias=None):
+    V = np.asarray(V, dtype=np.float64)
+    Vp = np.pad(V, ((0, 0), (1, 3), (1, 3), (0, 0)))  # pads 1 before instead of 2
+    w = np.asarray(weight, dtype=np.float64)
+    B, H, W, C = V.shape
+    out = np.zeros_like(V) + (0.0 if bias is None else np.asarray(bias, dtype=np.float64))
+    for i in range(5):
+        for j in range(5):
+            out += w[:, i, j] * Vp[:, i:i + H, j:j + W, :]
+    return out
+
+
 MUTATIONS = {
+    "lce_convolution_not_correlation": ("lce", _convolution_not_correlation),
+    "lce_transposed_filter": ("lce", _transposed_filter),
+    "lce_circular_padding": ("lce", _circular_padding),
+    "lce_dropped_bias": ("lce", _dropped_bias),
+    "lce_off_by_one_padding": ("lce", _off_by_one_padding),
     "transposed_affinity": ("affinity", _transposed_affinity),
     "ties_higher_index_first": ("topk_route", _ties_higher_index_first),
     "column_major_regions": ("region_token_coords", _column_major_regions),

@@ -247,3 +247,77 @@ def test_check_config_rejects_undefined_shapes():
         O.check_config(1, 56, 56, 64, 2, 7, 50)
     with pytest.raises(ValueError):
         O.check_config(0, 56, 56, 64, 2, 7, 1)
+
+
+# --------------------------------------------------------------------------- #
+# Local context term: 5 x 5 depthwise convolution of V (explainer Part 2.2
+# step 4 and pseudocode step 7; paper summary Section 3)
+# --------------------------------------------------------------------------- #
+LCE_SHAPES = [(2, 7, 9, 8), (1, 3, 2, 4), (1, 1, 6, 3), (1, 12, 5, 16)]
+
+
+@pytest.mark.parametrize("B,H,W,C", LCE_SHAPES)
+def test_lce_equals_torch_depthwise_conv2d(B, H, W, C):
+    V = _rand((B, H, W, C), 40)
+    w = _rand((C, 5, 5), 41)
+    b = _rand((C,), 42)
+    ref = torch.nn.functional.conv2d(torch.from_numpy(V).permute(0, 3, 1, 2), torch.from_numpy(w)[:, None],
+                                     torch.from_numpy(b), padding=2, groups=C)
+    ref = ref.permute(0, 2, 3, 1).numpy()
+    np.testing.assert_allclose(O.lce(V, w, b), ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.lce(V, w), ref - b, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,H,W,C", LCE_SHAPES[:2])
+def test_lce_equals_scipy_correlate(B, H, W, C):
+    from scipy import ndimage
+
+    V = _rand((B, H, W, C), 43)
+    w = _rand((C, 5, 5), 44)
+    out = O.lce(V, w)
+    for bi in range(B):
+        for c in range(C):
+            ref = ndimage.correlate(V[bi, :, :, c], w[c], mode="constant", cval=0.0)
+            np.testing.assert_allclose(out[bi, :, :, c], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("i,j", [(2, 2), (0, 0), (4, 1), (1, 3), (3, 4)])
+def test_lce_single_tap_is_a_shift_with_zero_fill(i, j):
+    B, H, W, C = 1, 5, 6, 2
+    V = _rand((B, H, W, C), 45)
+    w = np.zeros((C, 5, 5))
+    w[:, i, j] = 1.0
+    out = O.lce(V, w)
+    for y in range(H):
+        for x in range(W):
+            yy, xx = y + i - 2, x + j - 2
+            expect = V[0, yy, xx] if (0 <= yy < H and 0 <= xx < W) else np.zeros(C)
+            np.testing.assert_array_equal(out[0, y, x], expect)
+
+
+def test_lce_all_ones_counts_in_map_neighbours():
+    B, H, W, C = 1, 7, 4, 3
+    out = O.lce(np.ones((B, H, W, C)), np.ones((C, 5, 5)), np.full(C, 0.5))
+    for y in range(H):
+        for x in range(W):
+            rows = min(y + 2, H - 1) - max(y - 2, 0) + 1
+            cols = min(x + 2, W - 1) - max(x - 2, 0) + 1
+            assert np.all(out[0, y, x] == rows * cols + 0.5)
+
+
+def test_lce_is_added_to_the_attention_output():
+    B, H, W, C, heads, S, k = 1, 8, 8, 8, 2, 4, 2
+    Q, K, V = (_rand((B, H, W, C), s) for s in (46, 47, 48))
+    w = _rand((C, 5, 5), 49)
+    b = _rand((C,), 50)
+    plain, routes = O.bra(Q, K, V, heads, S, k)
+    full, routes2 = O.bra_lce(Q, K, V, heads, S, k, w, b)
+    np.testing.assert_array_equal(routes, routes2)
+    ref = torch.nn.functional.conv2d(torch.from_numpy(V).permute(0, 3, 1, 2), torch.from_numpy(w)[:, None],
+                                     torch.from_numpy(b), padding=2, groups=C).permute(0, 2, 3, 1).numpy()
+    np.testing.assert_allclose(full - plain, ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(O.attend_lce(Q, K, V, routes, heads, S, w, b), full, rtol=0, atol=0)
+    with pytest.raises(ValueError):
+        O.lce(V, w[:, :4])
+    with pytest.raises(ValueError):
+        O.lce(V, w, b[:3])

@@ -17,6 +17,12 @@ shape [B, H, W, C] for Q, then K, then V. The clustered workload draws, in
 order, region means of Q [B, S*S, C], token noise of Q [B, H, W, C], the same
 two for K, then V; each token of Q (K) is its region's mean plus 0.5 times
 its noise. bf16 workloads are cast (round to nearest even) after composing.
+
+Local-context filters (``make_lce_params``): a generator seeded with
+``seed + 1000`` draws the [C, 5, 5] depthwise weights as ``randn / 5`` (so a
+filter applied to unit-variance values gives roughly unit variance) and the
+[C] bias as ``randn / 10``, both cast to the workload's dtype. No trained
+filter is used.
 """
 
 from __future__ import annotations
@@ -118,6 +124,17 @@ def make_inputs(w: Workload):
         raise ValueError(f"unknown content kind {w.content!r}")
     dt = w.torch_dtype
     return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous()
+
+
+def make_lce_params(w: Workload):
+    """Draw (weight [C, 5, 5], bias [C]) of the local-context depthwise
+    filter on the CPU in the workload's dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(w.seed) + 1000)
+    weight = torch.randn((w.C, 5, 5), generator=gen, dtype=torch.float32) / 5.0
+    bias = torch.randn((w.C,), generator=gen, dtype=torch.float32) / 10.0
+    dt = w.torch_dtype
+    return weight.to(dt).contiguous(), bias.to(dt).contiguous()
 
 
 def to_f64(t: torch.Tensor):
