@@ -6,8 +6,10 @@
  * 'Bi-Level Routing'", Part 2.2 "The Overall BRA Flow" (steps 1-4 and the
  * PyTorch-style pseudocode), and by the paper summary "BiFormer: Vision
  * Transformer with Bi-Level Routing Attention", Section 3 "Our Approach".
- * Q, K, V are taken as already projected (the pseudocode's linear_qkv output);
- * the local-context term (+ dwconv(V)) is not part of this operator.
+ * Q, K, V are taken as already projected (the pseudocode's linear_qkv output).
+ * bra_attend / bra_forward compute the attention alone; bra_attend_lce /
+ * bra_forward_lce add the local-context term (+ dwconv(V)), whose filter
+ * weights they take as arguments.
  *
  * Tensors
  *   Q, K, V, O : [B, H, W, C] row-major, channels fastest, all of one dtype,
@@ -119,6 +121,48 @@ bra_status bra_forward(const void* Q, const void* K, const void* V, void* O,
                        int B, int H, int W, int C, int heads, int S, int topk,
                        bra_dtype dtype, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/*
+ * Local context enhancement (LCE): the "+ dwconv(value)" term of the module
+ * output (explainer Part 2.2 step 4, third bullet, and pseudocode step 7;
+ * paper summary Section 3, the depthwise-convolution local context term):
+ *
+ *   lce[b, y, x, c] = bias[c] + sum_{i, j in 0..4} weight[c][i][j]
+ *                                * V[b, y + i - 2, x + j - 2, c]
+ *
+ * over the whole H x W map with zero padding (terms outside the map are
+ * dropped), stride 1, one 5 x 5 filter per channel (PyTorch's depthwise
+ * Conv2d convention: cross-correlation, weight [C, 1, 5, 5] stored as
+ * [C][5][5]).
+ *
+ *   weight : [C][5][5] in `dtype`, device memory, 4-byte aligned.
+ *   bias   : [C] in `dtype`, device memory, or NULL for no bias.
+ *   Neither may overlap O (BRA_EINVAL). A NULL weight gives BRA_EINVAL.
+ *
+ * Rounding: the attention output and the term are added in fp32 and rounded
+ * once for bf16 regions of at most 8 x 8 tokens with at most 64 routed keys
+ * per query (the term is fused into the attention kernel); otherwise
+ * (fp32, larger regions, more keys) a second kernel adds the term to the
+ * stored attention output, which for bf16 rounds twice.
+ */
+
+/* bra_attend_lce - bra_attend plus the local context term:
+ * O = attention(Q, K, V; idx) + lce(V). Same arguments, checks and
+ * streams as bra_attend, plus weight and bias. */
+bra_status bra_attend_lce(const void* Q, const void* K, const void* V,
+                          const int32_t* idx, const void* weight, const void* bias, void* O,
+                          int B, int H, int W, int C, int heads, int S, int topk,
+                          bra_dtype dtype, hipStream_t stream);
+
+/* bra_forward_lce - the whole module output of explainer pseudocode steps
+ * 1 and 3-7: bra_forward plus the local context term. Same arguments,
+ * checks, workspace and streams as bra_forward, plus weight and bias; its
+ * routing table is bra_route's, bit for bit. */
+bra_status bra_forward_lce(const void* Q, const void* K, const void* V,
+                           const void* weight, const void* bias, void* O,
+                           int B, int H, int W, int C, int heads, int S, int topk,
+                           bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

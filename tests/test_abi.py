@@ -21,6 +21,7 @@ HEADER = os.path.join(ROOT, "include", "bra.h")
 EINVAL, EUNSUP = bra.BRA_EINVAL, bra.BRA_EUNSUPPORTED
 P = 0x10000  # aligned fake device pointers (never dereferenced)
 P2, P3, P4, PW = 0x20000, 0x30000, 0x40000, 0x50000
+PF, PB = 0x60000, 0x70000  # local-context filter weight and bias
 
 
 @pytest.fixture(scope="module")
@@ -80,7 +81,17 @@ def _attend(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P
     return lib.bra_attend(q, kk, v, idx, o, B, H, W, C, heads, S, k, dt, None)
 
 
-@pytest.mark.parametrize("call", [_fwd, _route, _attend])
+def _fwd_lce(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4, ws=PW, wsb=1 << 20,
+             wt=PF, bias=PB):
+    return lib.bra_forward_lce(q, kk, v, wt, bias, o, B, H, W, C, heads, S, k, dt, ws, wsb, None)
+
+
+def _attend_lce(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, idx=P4, o=PW, wt=PF,
+                bias=PB):
+    return lib.bra_attend_lce(q, kk, v, idx, wt, bias, o, B, H, W, C, heads, S, k, dt, None)
+
+
+@pytest.mark.parametrize("call", [_fwd, _route, _attend, _fwd_lce, _attend_lce])
 @pytest.mark.parametrize(
     "kwargs,status",
     [
@@ -103,7 +114,7 @@ def test_host_validation(lib, call, kwargs, status):
     assert call(lib, **kwargs) == status
 
 
-@pytest.mark.parametrize("call", [_fwd, _attend])
+@pytest.mark.parametrize("call", [_fwd, _attend, _fwd_lce, _attend_lce])
 @pytest.mark.parametrize(
     "kwargs,status",
     [
@@ -122,9 +133,27 @@ def test_host_validation_heads_and_outputs(lib, call, kwargs, status):
 def test_attend_null_index_table(lib):
     assert _attend(lib, idx=0) == EINVAL
     assert _attend(lib, idx=P4 + 2) == EINVAL
+    assert _attend_lce(lib, idx=0) == EINVAL
 
 
-@pytest.mark.parametrize("call", [_fwd, _route])
+@pytest.mark.parametrize("call", [_fwd_lce, _attend_lce])
+@pytest.mark.parametrize(
+    "kwargs",
+    [
+        dict(wt=0),                      # the filter is required
+        dict(wt=PF + 2),                 # weight not 4-byte aligned
+        dict(bias=PB + 2),               # fp32 bias not element aligned
+        dict(dt=1, bias=PB + 1),         # bf16 bias not element aligned
+        dict(wt=0x40010, o=0x40000),     # weight inside O
+        dict(bias=0x40100, o=0x40000),   # bias inside O
+        dict(wt=0x40000 - 64, o=0x40000),  # weight runs into O
+    ],
+)
+def test_lce_filter_validation(lib, call, kwargs):
+    assert call(lib, **kwargs) == EINVAL
+
+
+@pytest.mark.parametrize("call", [_fwd, _route, _fwd_lce])
 def test_workspace_validation(lib, call):
     assert call(lib, wsb=16) == EINVAL           # too small
     assert call(lib, ws=PW + 64) == EINVAL       # not 256-byte aligned

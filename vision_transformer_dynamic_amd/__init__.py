@@ -6,11 +6,15 @@ computation runs in the library's HIP kernels. PyTorch supplies device memory
 and the current stream. If the library has not been built, every call raises
 ``RuntimeError``; there is no fallback.
 
-    route(q, k, S, topk)              -> idx [B, S*S, topk] int32
-    attend(q, k, v, idx, heads, S)    -> o   [B, H, W, C]
-    forward(q, k, v, heads, S, topk)  -> o   [B, H, W, C]
+    route(q, k, S, topk)                               -> idx [B, S*S, topk] int32
+    attend(q, k, v, idx, heads, S)                     -> o   [B, H, W, C]
+    forward(q, k, v, heads, S, topk)                   -> o   [B, H, W, C]
+    attend_lce(q, k, v, idx, weight, bias, heads, S)   -> o + 5x5 depthwise conv of v
+    forward_lce(q, k, v, weight, bias, heads, S, topk) -> o + 5x5 depthwise conv of v
 
-q, k, v: contiguous [B, H, W, C] tensors on one GPU, float32 or bfloat16.
+q, k, v: contiguous [B, H, W, C] tensors on one GPU, float32 or bfloat16;
+weight [C, 5, 5] and bias [C] (or None) of the local-context filter in the
+same dtype.
 """
 
 from __future__ import annotations
@@ -28,6 +32,8 @@ __all__ = [
     "route",
     "attend",
     "forward",
+    "attend_lce",
+    "forward_lce",
     "EXPORTS",
 ]
 
@@ -39,7 +45,8 @@ BRA_BF16 = 1
 BRA_OK, BRA_EINVAL, BRA_EUNSUPPORTED, BRA_EHIP, BRA_ENOMEM = range(5)
 
 # Every symbol include/bra.h declares.
-EXPORTS = ("bra_status_string", "bra_workspace_bytes", "bra_route", "bra_attend", "bra_forward")
+EXPORTS = ("bra_status_string", "bra_workspace_bytes", "bra_route", "bra_attend", "bra_forward",
+           "bra_attend_lce", "bra_forward_lce")
 
 _lib = None
 
@@ -79,6 +86,10 @@ def load_library():
     lib.bra_attend.argtypes = [vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
     lib.bra_forward.restype = i32
     lib.bra_forward.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [i32, vp, sz, vp]
+    lib.bra_attend_lce.restype = i32
+    lib.bra_attend_lce.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
+    lib.bra_forward_lce.restype = i32
+    lib.bra_forward_lce.argtypes = [vp, vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -181,4 +192,53 @@ def forward(q, k, v, heads: int, S: int, topk: int, out=None, workspace=None) ->
     _check(lib.bra_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            B, H, W, C, heads, S, topk, _dtype_code(q),
                            ws.data_ptr(), nbytes, _stream(q.device)))
+    return out
+
+
+def _lce_args(q: torch.Tensor, weight: torch.Tensor, bias):
+    C = q.shape[-1]
+    if weight.shape != (C, 5, 5) or weight.dtype != q.dtype or weight.device != q.device or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous [C, 5, 5] tensor of q's dtype on q's device")
+    if bias is None:
+        return weight.data_ptr(), None
+    if bias.shape != (C,) or bias.dtype != q.dtype or bias.device != q.device or not bias.is_contiguous():
+        raise ValueError("bias must be a contiguous [C] tensor of q's dtype on q's device, or None")
+    return weight.data_ptr(), bias.data_ptr()
+
+
+def attend_lce(q, k, v, idx: torch.Tensor, weight: torch.Tensor, bias, heads: int, S: int, out=None) -> torch.Tensor:
+    """attend() plus the local context term: a 5x5 depthwise convolution of v
+    (zero padding, optional per-channel bias) over the whole map."""
+    lib = load_library()
+    _check_maps(q, k, v)
+    B, H, W, C = q.shape
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() != 3 or idx.device != q.device:
+        raise ValueError("idx must be a contiguous int32 [B, S*S, topk] tensor on q's device")
+    if tuple(idx.shape[:2]) != (B, S * S):
+        raise ValueError("idx must be [B, S*S, topk]")
+    topk = idx.shape[2]
+    wp, bp = _lce_args(q, weight, bias)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_maps(q, out)
+    _check(lib.bra_attend_lce(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), wp, bp, out.data_ptr(),
+                              B, H, W, C, heads, S, topk, _dtype_code(q), _stream(q.device)))
+    return out
+
+
+def forward_lce(q, k, v, weight: torch.Tensor, bias, heads: int, S: int, topk: int, out=None,
+                workspace=None) -> torch.Tensor:
+    """forward() plus the local context term (the module output of the
+    pages' pseudocode, after the projections)."""
+    lib = load_library()
+    _check_maps(q, k, v)
+    B, H, W, C = q.shape
+    wp, bp = _lce_args(q, weight, bias)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_maps(q, out)
+    ws, nbytes = _workspace(q, S, topk, workspace)
+    _check(lib.bra_forward_lce(q.data_ptr(), k.data_ptr(), v.data_ptr(), wp, bp, out.data_ptr(),
+                               B, H, W, C, heads, S, topk, _dtype_code(q),
+                               ws.data_ptr(), nbytes, _stream(q.device)))
     return out

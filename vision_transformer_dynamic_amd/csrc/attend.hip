@@ -36,6 +36,7 @@
 // accumulation and softmax. fp32: eight v_mfma_f32_16x16x4_f32 per 32-deep
 // contraction, P kept in fp32.
 #include "bra_internal.h"
+#include "lce_tile.h"
 
 #include <math.h>
 
@@ -148,6 +149,12 @@ struct AttnParams {
   int nbuf;    // LDS chunk buffers (2: double-buffered, when kv spans several chunks)
   float c;     // softmax scale * log2(e)
   FastDiv div_n, div_sw, div_S;
+  // local context term fused into the single-chunk kernel's epilogue
+  const void* lw;   // [C][5][5] depthwise filter
+  const void* lb;   // [C] bias or null
+  int wave_lds;     // LDS bytes per wave (single-chunk kernel)
+  int lce_pw, lce_ps;
+  FastDiv div_lpw;
 };
 
 // Max over the 4 lane groups that share lane % 16; a16/a32 are the byte
@@ -192,6 +199,7 @@ struct Item {
   bool valid;
   int b, i, qb, hg;
   int q0, nq, ntiles, nh, cb, U, qcorner;
+  int ry0, rx0;  // image coordinates of the region's first token
   int64_t img;  // element offset of image b
 };
 
@@ -212,6 +220,8 @@ __device__ inline Item item_at(const AttnParams& p, int w) {
   it.U = it.valid ? it.nh * it.ntiles : 0;
   const int ri = it.i / p.S, rj = it.i - ri * p.S;
   it.qcorner = ri * p.sh * p.W + rj * p.sw;
+  it.ry0 = ri * p.sh;
+  it.rx0 = rj * p.sw;
   it.img = (int64_t)it.b * p.H * p.W * p.C;
   return it;
 }
@@ -526,13 +536,22 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
 // Per tile only the query operand is loaded: 10 MFMAs, the softmax and the
 // 16-byte output stores, with no LDS traffic.
 // MAXT: query tiles per item the kernel is built for (1, or 4 = 64 queries).
-template <typename T, bool RAGGED, int MAXT>
+// LR, LX > 0: the local context term is fused into the epilogue (bf16, region
+// at most LR rows and 2*LX columns): before the V^T transpose, each wave
+// stages its head's V halo around the query region in its LDS area, computes
+// the region's 5x5 depthwise convolution (lce_tile.h), transposes the results
+// through the same LDS and keeps its own lanes' values (8 channels of each of
+// its queries) in registers; the epilogue adds them before the one rounding.
+template <typename T, bool RAGGED, int MAXT, int LR, int LX>
 __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
   constexpr int VEC = TT::VEC;
   constexpr int CVH = D / VEC;  // 16-byte vectors per key row of one head
   constexpr int PAIRS = KC / 2 * CVH / 64;  // (key pair, vector) items per lane
+  constexpr bool LCE = LR > 0;
+  static_assert(!LCE || sizeof(T) == 2, "the fused local context term is built for bf16");
+  constexpr int LNB = LCE ? ((LR + 4) * ((2 * LX + 5) / 2) * 4 + 63) / 64 : 1;  // halo items per lane
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int rtab[KC];
@@ -546,7 +565,8 @@ __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
   const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
   const op8 ones = TT::ones();
   const int ldv = KC + TT::PADV;
-  T* Vt = reinterpret_cast<T*>(smem_raw) + wave * D * ldv;  // this wave's V^T tile
+  unsigned char* warea = smem_raw + wave * p.wave_lds;  // this wave's LDS area
+  T* Vt = reinterpret_cast<T*>(warea);                  // its V^T tile
 
   int wg;
   {
@@ -575,6 +595,24 @@ __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
       const int qy = fdiv(qi, p.div_sw, &qx);
       qoff[t] = (it.qcorner + qy * p.W + qx) * p.C + ch0 + 8 * g;
       qop[t] = TT::load8(Qg + qoff[t]);
+    }
+  }
+
+  // ---- local context term: halo loads and filter weights, also independent
+  // of the routing
+  LceTile lt;
+  uint4 ha[LNB], hb[LNB];
+  LceW<T> lw;
+  if constexpr (LCE) {
+    lt.y0 = it.ry0;
+    lt.x0 = it.rx0;
+    lt.rows = p.sh;
+    lt.cols = p.sw;
+    lt.pw = p.lce_pw;
+    lt.ps = p.lce_ps;
+    if (head_ok) {
+      lce_halo_load<T, LNB>(Vg, p.H, p.W, p.C, ch0, lt, p.div_lpw, 0, lane, ha, hb);
+      lce_weights(static_cast<const T*>(p.lw), static_cast<const T*>(p.lb), ch0 + (lane & 31), lane >> 5, lw);
     }
   }
 
@@ -609,6 +647,39 @@ __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
                                              : make_uint4(0u, 0u, 0u, 0u);
       }
     }
+  }
+
+  // ---- local context term of the wave's queries, through the wave's LDS
+  // area (every wave of the group takes the barriers)
+  float lce[MAXT][8];
+  if constexpr (LCE) {
+    typedef typename Lce<T>::word LWord;
+    LWord* halo = reinterpret_cast<LWord*>(warea);
+    if (head_ok) lce_halo_store<T, LNB>(halo, lt, p.div_lpw, 0, lane, ha, hb);
+    __syncthreads();
+    float acc[LR][LX];
+    if (head_ok) lce_compute<T, LR, LX>(halo + (lane & 31) * lt.ps, lt, lw, acc);
+    __syncthreads();  // halo reads done before the results overwrite it
+    float* res = reinterpret_cast<float*>(warea);
+    if (head_ok) lce_store_results<LR, LX>(res, lt, lane & 31, lane >> 5, acc);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      const int q = t * 16 + col;
+      if (head_ok && q < p.n) {
+        const float4 lo = *reinterpret_cast<const float4*>(res + q * kLceRes + 8 * g);
+        const float4 hi = *reinterpret_cast<const float4*>(res + q * kLceRes + 8 * g + 4);
+        lce[t][0] = lo.x; lce[t][1] = lo.y; lce[t][2] = lo.z; lce[t][3] = lo.w;
+        lce[t][4] = hi.x; lce[t][5] = hi.y; lce[t][6] = hi.z; lce[t][7] = hi.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lce[t][e] = 0.f;
+      }
+    }
+    __syncthreads();  // results read before the V^T tile reuses the area
+  }
+
+  if (head_ok && !bad) {
 #pragma unroll
     for (int m = 0; m < PAIRS; ++m) {
       const int f = lane + 64 * m;
@@ -693,6 +764,10 @@ __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
         o[e] = acc[0][e] * inv;
         o[4 + e] = acc[1][e] * inv;
       }
+      if constexpr (LCE) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += lce[t][e];
+      }
       TT::store8(Og + qoff[t], o);
     }
   }
@@ -765,8 +840,9 @@ const void* pick_attend(int dtype, const AttnLaunch& L) {
 }  // namespace
 
 hipError_t launch_attend(const void* Q, const void* K, const void* V,
-                         const int32_t* idx, void* O, const Shape& s, int dtype,
-                         hipStream_t stream) {
+                         const int32_t* idx, const void* lce_w, const void* lce_b, void* O,
+                         const Shape& s, int dtype, hipStream_t stream) {
+  const bool lce = lce_w != nullptr;
   if (s.kv <= KC) {
     // single chunk: one wave per head, up to 8 heads per workgroup
     AttnParams p = plan_attend(s, dtype).p;
@@ -778,23 +854,45 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
     p.Q = Q; p.K = K; p.V = V; p.idx = idx; p.O = O;
     const size_t esz = dtype == kBF16 ? 2 : 4;
     const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
-    const size_t lds = esz * (size_t)HG * D * (KC + padv);
+    p.wave_lds = (int)(esz * D * (KC + padv));
     const bool ragged = s.kv % KC != 0;
     const bool one = s.n <= 16;  // one query tile per item
+    // the local context term is fused for bf16 regions of at most 8 x 8 tokens
+    const bool fuse = lce && dtype == kBF16 && s.sh <= 8 && s.sw <= 8;
+    const bool small = s.sh <= 4 && s.sw <= 4;
     const void* fn;
-    if (dtype == kBF16)
-      fn = ragged ? (one ? (const void*)&attend_head_kernel<__bf16, true, 1> : (const void*)&attend_head_kernel<__bf16, true, 4>)
-                  : (one ? (const void*)&attend_head_kernel<__bf16, false, 1> : (const void*)&attend_head_kernel<__bf16, false, 4>);
-    else
-      fn = ragged ? (one ? (const void*)&attend_head_kernel<float, true, 1> : (const void*)&attend_head_kernel<float, true, 4>)
-                  : (one ? (const void*)&attend_head_kernel<float, false, 1> : (const void*)&attend_head_kernel<float, false, 4>);
+    if (fuse) {
+      p.lw = lce_w;
+      p.lb = lce_b;
+      p.lce_pw = lce_pw(s.sw);
+      p.lce_ps = lce_ps(s.sh, s.sw);
+      p.div_lpw = make_fastdiv(p.lce_pw);
+      p.wave_lds = max(p.wave_lds, lce_lds_bytes(s.sh, s.sw, 4));
+      if (small)
+        fn = ragged ? (const void*)&attend_head_kernel<__bf16, true, 1, 4, 2> : (const void*)&attend_head_kernel<__bf16, false, 1, 4, 2>;
+      else if (one)
+        fn = ragged ? (const void*)&attend_head_kernel<__bf16, true, 1, 8, 4> : (const void*)&attend_head_kernel<__bf16, false, 1, 8, 4>;
+      else
+        fn = ragged ? (const void*)&attend_head_kernel<__bf16, true, 4, 8, 4> : (const void*)&attend_head_kernel<__bf16, false, 4, 8, 4>;
+    } else if (dtype == kBF16) {
+      fn = ragged ? (one ? (const void*)&attend_head_kernel<__bf16, true, 1, 0, 0> : (const void*)&attend_head_kernel<__bf16, true, 4, 0, 0>)
+                  : (one ? (const void*)&attend_head_kernel<__bf16, false, 1, 0, 0> : (const void*)&attend_head_kernel<__bf16, false, 4, 0, 0>);
+    } else {
+      fn = ragged ? (one ? (const void*)&attend_head_kernel<float, true, 1, 0, 0> : (const void*)&attend_head_kernel<float, true, 4, 0, 0>)
+                  : (one ? (const void*)&attend_head_kernel<float, false, 1, 0, 0> : (const void*)&attend_head_kernel<float, false, 4, 0, 0>);
+    }
     void* args[] = {&p};
-    return hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(HG * 64), args, lds, stream);
+    const size_t lds = (size_t)HG * p.wave_lds;
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(HG * 64), args, lds, stream);
+    if (e != hipSuccess || !lce || fuse) return e;
+    return launch_lce(V, lce_w, lce_b, O, s, dtype, stream);
   }
   AttnLaunch L = plan_attend(s, dtype);
   L.p.Q = Q; L.p.K = K; L.p.V = V; L.p.idx = idx; L.p.O = O;
   void* args[] = {&L.p};
-  return hipLaunchKernel(pick_attend(dtype, L), dim3((unsigned)L.nwg), dim3(NW * 64), args, L.lds, stream);
+  hipError_t e = hipLaunchKernel(pick_attend(dtype, L), dim3((unsigned)L.nwg), dim3(NW * 64), args, L.lds, stream);
+  if (e != hipSuccess || !lce) return e;
+  return launch_lce(V, lce_w, lce_b, O, s, dtype, stream);
 }
 
 }  // namespace bra

@@ -75,6 +75,23 @@ struct Workspace {
 
 bool bad_tensor(const void* p) { return p == nullptr || !aligned(p, 16); }
 
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Local-context filter arguments: weight [C][5][5] (4-byte aligned), bias [C]
+// or null (element aligned); neither may overlap O.
+bra_status check_lce(const void* weight, const void* bias, const void* O, const Shape& s, int dtype) {
+  const size_t esz = dtype == bra::kBF16 ? 2 : 4;
+  if (weight == nullptr || !aligned(weight, 4)) return BRA_EINVAL;
+  if (bias != nullptr && !aligned(bias, esz)) return BRA_EINVAL;
+  const size_t obytes = esz * (size_t)s.B * s.H * s.W * s.C;
+  if (overlaps(weight, esz * 25 * (size_t)s.C, O, obytes)) return BRA_EINVAL;
+  if (bias != nullptr && overlaps(bias, esz * (size_t)s.C, O, obytes)) return BRA_EINVAL;
+  return BRA_OK;
+}
+
 bra_status enqueue_route(const void* Q, const void* K, int32_t* idx, const Shape& s, int dtype,
                          char* ws, hipStream_t stream) {
   float* Qr = reinterpret_cast<float*>(ws);
@@ -120,39 +137,80 @@ bra_status bra_route(const void* Q, const void* K, int32_t* idx,
   return enqueue_route(Q, K, idx, s, (int)dtype, ws.ptr, stream);
 }
 
-bra_status bra_attend(const void* Q, const void* K, const void* V,
-                      const int32_t* idx, void* O,
-                      int B, int H, int W, int C, int heads, int S, int topk,
-                      bra_dtype dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+bra_status attend_impl(const void* Q, const void* K, const void* V, const int32_t* idx, const void* weight,
+                       const void* bias, void* O, int B, int H, int W, int C, int heads, int S, int topk, int dtype,
+                       hipStream_t stream) {
   Shape s;
-  bra_status st = check_shape(B, H, W, C, heads, S, topk, (int)dtype, &s);
+  bra_status st = check_shape(B, H, W, C, heads, S, topk, dtype, &s);
   if (st != BRA_OK) return st;
   if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(V) || bad_tensor(O))
     return BRA_EINVAL;
   if (idx == nullptr || !aligned(idx, 4)) return BRA_EINVAL;
   if (O == Q || O == K || O == V) return BRA_EINVAL;
-  if (bra::launch_attend(Q, K, V, idx, O, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
+  if (weight != nullptr && (st = check_lce(weight, bias, O, s, dtype)) != BRA_OK) return st;
+  if (bra::launch_attend(Q, K, V, idx, weight, bias, O, s, dtype, stream) != hipSuccess) return BRA_EHIP;
   return BRA_OK;
+}
+
+bra_status forward_impl(const void* Q, const void* K, const void* V, const void* weight, const void* bias, void* O,
+                        int B, int H, int W, int C, int heads, int S, int topk, int dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, heads, S, topk, dtype, &s);
+  if (st != BRA_OK) return st;
+  if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(V) || bad_tensor(O))
+    return BRA_EINVAL;
+  if (O == Q || O == K || O == V) return BRA_EINVAL;
+  if (weight != nullptr && (st = check_lce(weight, bias, O, s, dtype)) != BRA_OK) return st;
+  Workspace ws;
+  st = ws.acquire(workspace, workspace_bytes, workspace_for(s), stream);
+  if (st != BRA_OK) return st;
+  int32_t* idx = reinterpret_cast<int32_t*>(ws.ptr + 2 * pooled_bytes(s));
+  st = enqueue_route(Q, K, idx, s, dtype, ws.ptr, stream);
+  if (st != BRA_OK) return st;
+  if (bra::launch_attend(Q, K, V, idx, weight, bias, O, s, dtype, stream) != hipSuccess) return BRA_EHIP;
+  return BRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bra_status bra_attend(const void* Q, const void* K, const void* V,
+                      const int32_t* idx, void* O,
+                      int B, int H, int W, int C, int heads, int S, int topk,
+                      bra_dtype dtype, hipStream_t stream) {
+  return attend_impl(Q, K, V, idx, nullptr, nullptr, O, B, H, W, C, heads, S, topk, (int)dtype, stream);
 }
 
 bra_status bra_forward(const void* Q, const void* K, const void* V, void* O,
                        int B, int H, int W, int C, int heads, int S, int topk,
                        bra_dtype dtype, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-  Shape s;
-  bra_status st = check_shape(B, H, W, C, heads, S, topk, (int)dtype, &s);
-  if (st != BRA_OK) return st;
-  if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(V) || bad_tensor(O))
-    return BRA_EINVAL;
-  if (O == Q || O == K || O == V) return BRA_EINVAL;
-  Workspace ws;
-  st = ws.acquire(workspace, workspace_bytes, workspace_for(s), stream);
-  if (st != BRA_OK) return st;
-  int32_t* idx = reinterpret_cast<int32_t*>(ws.ptr + 2 * pooled_bytes(s));
-  st = enqueue_route(Q, K, idx, s, (int)dtype, ws.ptr, stream);
-  if (st != BRA_OK) return st;
-  if (bra::launch_attend(Q, K, V, idx, O, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
-  return BRA_OK;
+  return forward_impl(Q, K, V, nullptr, nullptr, O, B, H, W, C, heads, S, topk, (int)dtype, workspace,
+                      workspace_bytes, stream);
+}
+
+bra_status bra_attend_lce(const void* Q, const void* K, const void* V,
+                          const int32_t* idx, const void* weight, const void* bias, void* O,
+                          int B, int H, int W, int C, int heads, int S, int topk,
+                          bra_dtype dtype, hipStream_t stream) {
+  if (weight == nullptr) return BRA_EINVAL;
+  return attend_impl(Q, K, V, idx, weight, bias, O, B, H, W, C, heads, S, topk, (int)dtype, stream);
+}
+
+bra_status bra_forward_lce(const void* Q, const void* K, const void* V,
+                           const void* weight, const void* bias, void* O,
+                           int B, int H, int W, int C, int heads, int S, int topk,
+                           bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (weight == nullptr) return BRA_EINVAL;
+  return forward_impl(Q, K, V, weight, bias, O, B, H, W, C, heads, S, topk, (int)dtype, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -62,9 +62,16 @@ hipError_t launch_pool(const void* Q, const void* K, float* Qr, float* Kr,
 hipError_t launch_route(const float* Qr, const float* Kr, int32_t* idx,
                         const Shape& s, hipStream_t stream);
 
-// Token attention over routed regions: O = softmax(q k_g^T / sqrt(d)) v_g.
+// Token attention over routed regions: O = softmax(q k_g^T / sqrt(d)) v_g,
+// plus the local context term lce(V) when lce_w ([C][5][5]) is not null
+// (lce_b: [C] bias or null), fused or by launch_lce afterwards.
 hipError_t launch_attend(const void* Q, const void* K, const void* V,
-                         const int32_t* idx, void* O, const Shape& s, int dtype,
-                         hipStream_t stream);
+                         const int32_t* idx, const void* lce_w, const void* lce_b, void* O,
+                         const Shape& s, int dtype, hipStream_t stream);
+
+// O += lce(V): 5x5 depthwise convolution of V over the whole map, zero
+// padding, per-channel bias (lce_b may be null). C must be a multiple of 32.
+hipError_t launch_lce(const void* V, const void* lce_w, const void* lce_b, void* O,
+                      const Shape& s, int dtype, hipStream_t stream);
 
 }  // namespace bra
