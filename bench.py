@@ -9,7 +9,10 @@ step's working set between two uses of the same copy.
 
 Prints ONE JSON line: whole-job tokens/s, per-step time, TFLOP/s, the
 roofline of the dominant kernel (fused gather + attention) from HIP events on
-the stream it runs on, and the CPU oracle timed on a bounded sample.
+the stream it runs on, and the CPU oracle timed on a bounded sample. The
+``with_lce`` object times the module output with the local context term
+(5x5 depthwise convolution of V, seeded synthetic filter) the same way; it is
+a side measurement, not the headline value.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -47,6 +50,7 @@ def parse_args(argv=None):
     ap.add_argument("--sets", type=int, default=0, help="input copies to rotate over (0 = enough to exceed the MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-lce", action="store_true", help="skip the side measurement with the local context term")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     return ap.parse_args(argv)
@@ -89,13 +93,14 @@ def calibrate_copy(mib: int) -> None:
 class Step:
     """Pre-bound C-ABI calls for one input copy (no per-call allocation)."""
 
-    def __init__(self, w, q, k, v):
+    def __init__(self, w, q, k, v, lce_w=None, lce_b=None):
         import torch
         import vision_transformer_dynamic_amd as bra
 
         self.bra = bra
         self.w = w
         self.q, self.k, self.v = q, k, v
+        self.lce_w, self.lce_b = lce_w, lce_b
         self.out = torch.empty_like(q)
         self.idx = torch.empty((w.B, w.R, w.topk), dtype=torch.int32, device=q.device)
         nbytes = bra.workspace_bytes(w.B, w.H, w.W, w.C, w.S, w.topk)
@@ -106,6 +111,14 @@ class Step:
 
     def attend(self):
         self.bra.attend(self.q, self.k, self.v, self.idx, self.w.heads, self.w.S, out=self.out)
+
+    def attend_lce(self):
+        self.bra.attend_lce(self.q, self.k, self.v, self.idx, self.lce_w, self.lce_b, self.w.heads, self.w.S,
+                            out=self.out)
+
+    def step_lce(self):
+        self.route()
+        self.attend_lce()
 
     def __call__(self):
         self.route()
@@ -184,7 +197,8 @@ def main(argv=None):
     set_bytes = 4 * w.tokens * w.C * esz
     nsets = args.sets or max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / set_bytes)))
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    steps = [Step(w, qd.clone(), kd.clone(), vd.clone()) for _ in range(nsets)]
+    lw, lb = (t.to(dev) for t in wl.make_lce_params(w))
+    steps = [Step(w, qd.clone(), kd.clone(), vd.clone(), lw, lb) for _ in range(nsets)]
     torch.cuda.synchronize()
 
     # eager warm-up of every copy (also the first-launch code loading)
@@ -235,6 +249,30 @@ def main(argv=None):
     attend_us = phase_us(attend_cycle, attend_singles)
     route_us = phase_us(route_cycle, route_singles)
 
+    with_lce = None
+    if not args.no_lce:
+        for s_ in steps:
+            s_.step_lce()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            lce_cycle = capture([s_.step_lce for s_ in steps])
+            lce_singles = [capture([s_.step_lce]) for s_ in steps]
+            alce_cycle = capture([s_.attend_lce for s_ in steps])
+            alce_singles = [capture([s_.attend_lce]) for s_ in steps]
+        torch.cuda.synchronize()
+        lce_step_us = phase_us(lce_cycle, lce_singles)
+        alce_us = phase_us(alce_cycle, alce_singles)
+        ref_lce = bra.forward_lce(qd, kd, vd, lw, lb, w.heads, w.S, w.topk)
+        torch.cuda.synchronize()
+        if not torch.equal(ref_lce, steps[0].out):
+            raise RuntimeError("benchmark output with the local context term differs from bra_forward_lce")
+        with_lce = {"value": round(w.tokens / (lce_step_us * 1e-6), 1), "unit": "tokens/s",
+                    "us_per_step": round(lce_step_us, 2), "attend_lce_us": round(alce_us, 2),
+                    "filter": "seeded synthetic 5x5 depthwise weights and bias"}
+        for s_ in steps:  # leave the plain outputs in place for the check below
+            s_()
+        torch.cuda.synchronize()
+
     # the timed steps computed the real thing: spot-check one copy
     ref = bra.forward(qd, kd, vd, w.heads, w.S, w.topk)
     torch.cuda.synchronize()
@@ -282,6 +320,8 @@ def main(argv=None):
                       "step_wall": round(wall_ms * 1e3, 2), "step_events": round(ev_ms * 1e3, 2)},
         "roofline": roof,
     }
+    if with_lce is not None:
+        result["with_lce"] = with_lce
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(result))

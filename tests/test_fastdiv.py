@@ -31,3 +31,14 @@ def test_fastdiv_exact_on_boundaries_and_random():
         q, r = fdiv(a, d)
         assert np.array_equal(q, a // d), d
         assert np.array_equal(r, a % d), d
+
+
+def test_halo_row_decode_by_float_reciprocal_is_exact():
+    """Halo items of the local-context tiles are decoded as
+    hy = trunc((pi + 0.5) * fl(1/pw)) in float32 with no fix-up; exact for
+    every word count pw a tile can have and pi < 2^16 (far beyond any halo)."""
+    pi = np.arange(1 << 16, dtype=np.int64)
+    for pw in range(1, 40):
+        inv = np.float32(1.0) / np.float32(pw)
+        got = ((pi.astype(np.float32) + np.float32(0.5)) * inv).astype(np.int64)
+        np.testing.assert_array_equal(got, pi // pw, err_msg=f"pw={pw}")

@@ -152,9 +152,9 @@ struct AttnParams {
   // local context term fused into the single-chunk kernel's epilogue
   const void* lw;   // [C][5][5] depthwise filter
   const void* lb;   // [C] bias or null
-  int wave_lds;     // LDS bytes per wave (single-chunk kernel)
+  int wave_lds;     // LDS bytes of one head's convolution area
   int lce_pw, lce_ps;
-  FastDiv div_lpw;
+  float lce_inv_pw;
 };
 
 // Max over the 4 lane groups that share lane % 16; a16/a32 are the byte
@@ -536,14 +536,19 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
 // Per tile only the query operand is loaded: 10 MFMAs, the softmax and the
 // 16-byte output stores, with no LDS traffic.
 // MAXT: query tiles per item the kernel is built for (1, or 4 = 64 queries).
-// LR, LX > 0: the local context term is fused into the epilogue (bf16, region
-// at most LR rows and 2*LX columns): before the V^T transpose, each wave
-// stages its head's V halo around the query region in its LDS area, computes
-// the region's 5x5 depthwise convolution (lce_tile.h), transposes the results
-// through the same LDS and keeps its own lanes' values (8 channels of each of
-// its queries) in registers; the epilogue adds them before the one rounding.
+//
+// LR, LX > 0: the local context term is fused (bf16, regions of at most LR
+// rows and 2*LX columns). The workgroup then has 2*HG waves: waves 0..HG-1
+// compute attention as above, and wave HG + h computes the 5x5 depthwise
+// convolution of head h over the region (lce_tile.h: V halo staged in the
+// wave's own LDS area, results transposed into fp32 [query][channel] rows in
+// the same area) concurrently with the attention waves' loads and products.
+// The attention epilogue of head h reads its lanes' 8 channels per query from
+// that area and adds them before the one rounding to bf16. The two roles
+// never hold registers at the same time, so the kernel's register budget is
+// the larger of the two, not their sum.
 template <typename T, bool RAGGED, int MAXT, int LR, int LX>
-__global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
+__global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
   constexpr int VEC = TT::VEC;
@@ -565,8 +570,6 @@ __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
   const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
   const op8 ones = TT::ones();
   const int ldv = KC + TT::PADV;
-  unsigned char* warea = smem_raw + wave * p.wave_lds;  // this wave's LDS area
-  T* Vt = reinterpret_cast<T*>(warea);                  // its V^T tile
 
   int wg;
   {
@@ -575,44 +578,49 @@ __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
     wg = x * q8 + min(x, r8) + loc;
   }
   const Item it = item_at(p, wg);
-  const bool head_ok = wave < it.nh;
-  const int ch0 = it.cb + wave * D;  // first channel of this wave's head
+  // role: attention wave for head `head`, or (LCE) convolution wave for it
+  const bool att = !LCE || wave < p.HG;
+  const int head = att ? wave : wave - p.HG;
+  const bool head_ok = head < it.nh;
+  const int ch0 = it.cb + head * D;  // first channel of the wave's head
+  T* Vt = reinterpret_cast<T*>(smem_raw) + head * D * ldv;  // head's V^T tile
+  unsigned char* larea = smem_raw + p.HG * D * ldv * (int)sizeof(T) + head * p.wave_lds;  // head's LCE area
   const T* Kg = static_cast<const T*>(p.K) + it.img;
   const T* Vg = static_cast<const T*>(p.V) + it.img;
   const T* Qg = static_cast<const T*>(p.Q) + it.img;
 
-  // ---- query operands of all (<= 4) tiles first: they do not depend on the
-  // routing, so their loads overlap the routing-table round trip
+  // ---- attention waves: query operands of all (<= 4) tiles first (they do
+  // not depend on the routing, so their loads overlap the routing-table
+  // round trip); convolution waves: the V halo and the filter
   op8 qop[MAXT];
   int qoff[MAXT];
-#pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    const int qi = it.q0 + t * 16 + col;
-    qoff[t] = -1;
-    qop[t] = TT::zero();
-    if (head_ok && t < it.ntiles && qi < it.q0 + it.nq) {
-      int qx;
-      const int qy = fdiv(qi, p.div_sw, &qx);
-      qoff[t] = (it.qcorner + qy * p.W + qx) * p.C + ch0 + 8 * g;
-      qop[t] = TT::load8(Qg + qoff[t]);
-    }
-  }
-
-  // ---- local context term: halo loads and filter weights, also independent
-  // of the routing
   LceTile lt;
   uint4 ha[LNB], hb[LNB];
   LceW<T> lw;
-  if constexpr (LCE) {
+  if (att) {
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      const int qi = it.q0 + t * 16 + col;
+      qoff[t] = -1;
+      qop[t] = TT::zero();
+      if (head_ok && t < it.ntiles && qi < it.q0 + it.nq) {
+        int qx;
+        const int qy = fdiv(qi, p.div_sw, &qx);
+        qoff[t] = (it.qcorner + qy * p.W + qx) * p.C + ch0 + 8 * g;
+        qop[t] = TT::load8(Qg + qoff[t]);
+      }
+    }
+  } else if constexpr (LCE) {
     lt.y0 = it.ry0;
     lt.x0 = it.rx0;
     lt.rows = p.sh;
     lt.cols = p.sw;
     lt.pw = p.lce_pw;
     lt.ps = p.lce_ps;
+    lt.inv_pw = p.lce_inv_pw;
     if (head_ok) {
-      lce_halo_load<T, LNB>(Vg, p.H, p.W, p.C, ch0, lt, p.div_lpw, 0, lane, ha, hb);
-      lce_weights(static_cast<const T*>(p.lw), static_cast<const T*>(p.lb), ch0 + (lane & 31), lane >> 5, lw);
+      lce_halo_load<T, LNB>(Vg, p.H, p.W, p.C, ch0, lt, 0, lane, ha, hb);
+      lce_weights(static_cast<const T*>(p.lw), static_cast<const T*>(p.lb), ch0 + (lane & 31), (lane >> 5) & 1, lw);
     }
   }
 
@@ -622,74 +630,59 @@ __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
   __syncthreads();
   const bool bad = sbad;
 
-  // ---- K operands: row rr = col of the tile for (32-key step st, tile tb)
-  // is key st*32 + 8*(rr/4) + (rr%4) + 4*tb; slots = channels 8g..8g+7
   op8 kop[2][2];
-  uint4 vreg[PAIRS][2];
-  if (head_ok && !bad) {
+  if (att) {
+    if (head_ok && !bad) {
+      // ---- K operands: row rr = col of the tile for (32-key step st, tile
+      // tb) is key st*32 + 8*(rr/4) + (rr%4) + 4*tb; slots = channels 8g..8g+7
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
-        kop[st][tb] = (!RAGGED || key < p.kv) ? TT::load8(Kg + rtab[key] * p.C + ch0 + 8 * g) : TT::zero();
+        for (int tb = 0; tb < 2; ++tb) {
+          const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
+          kop[st][tb] = (!RAGGED || key < p.kv) ? TT::load8(Kg + rtab[key] * p.C + ch0 + 8 * g) : TT::zero();
+        }
+      // V slice: pair item f = lane + 64 m -> channel vector cv = f % CVH, key
+      // pair p2 = f / CVH (keys 2 p2, 2 p2 + 1)
+      uint4 vreg[PAIRS][2];
+#pragma unroll
+      for (int m = 0; m < PAIRS; ++m) {
+        const int f = lane + 64 * m;
+        const int cv = f % CVH, p2 = f / CVH;
+#pragma unroll
+        for (int k1 = 0; k1 < 2; ++k1) {
+          const int key = 2 * p2 + k1;
+          vreg[m][k1] = (!RAGGED || key < p.kv) ? *reinterpret_cast<const uint4*>(Vg + rtab[key] * p.C + ch0 + cv * VEC)
+                                               : make_uint4(0u, 0u, 0u, 0u);
+        }
       }
-    // V slice: pair item f = lane + 64 m -> channel vector cv = f % CVH, key
-    // pair p2 = f / CVH (keys 2 p2, 2 p2 + 1)
 #pragma unroll
-    for (int m = 0; m < PAIRS; ++m) {
-      const int f = lane + 64 * m;
-      const int cv = f % CVH, p2 = f / CVH;
-#pragma unroll
-      for (int k1 = 0; k1 < 2; ++k1) {
-        const int key = 2 * p2 + k1;
-        vreg[m][k1] = (!RAGGED || key < p.kv) ? *reinterpret_cast<const uint4*>(Vg + rtab[key] * p.C + ch0 + cv * VEC)
-                                             : make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  }
-
-  // ---- local context term of the wave's queries, through the wave's LDS
-  // area (every wave of the group takes the barriers)
-  float lce[MAXT][8];
-  if constexpr (LCE) {
-    typedef typename Lce<T>::word LWord;
-    LWord* halo = reinterpret_cast<LWord*>(warea);
-    if (head_ok) lce_halo_store<T, LNB>(halo, lt, p.div_lpw, 0, lane, ha, hb);
-    __syncthreads();
-    float acc[LR][LX];
-    if (head_ok) lce_compute<T, LR, LX>(halo + (lane & 31) * lt.ps, lt, lw, acc);
-    __syncthreads();  // halo reads done before the results overwrite it
-    float* res = reinterpret_cast<float*>(warea);
-    if (head_ok) lce_store_results<LR, LX>(res, lt, lane & 31, lane >> 5, acc);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-      const int q = t * 16 + col;
-      if (head_ok && q < p.n) {
-        const float4 lo = *reinterpret_cast<const float4*>(res + q * kLceRes + 8 * g);
-        const float4 hi = *reinterpret_cast<const float4*>(res + q * kLceRes + 8 * g + 4);
-        lce[t][0] = lo.x; lce[t][1] = lo.y; lce[t][2] = lo.z; lce[t][3] = lo.w;
-        lce[t][4] = hi.x; lce[t][5] = hi.y; lce[t][6] = hi.z; lce[t][7] = hi.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lce[t][e] = 0.f;
+      for (int m = 0; m < PAIRS; ++m) {
+        const int f = lane + 64 * m;
+        const int cv = f % CVH, p2 = f / CVH;
+        const int row0 = cv * VEC;
+        store_vt_pair(Vt, ldv, row0, vt_col(row0, 2 * p2), vreg[m][0], vreg[m][1]);
       }
     }
-    __syncthreads();  // results read before the V^T tile reuses the area
-  }
-
-  if (head_ok && !bad) {
-#pragma unroll
-    for (int m = 0; m < PAIRS; ++m) {
-      const int f = lane + 64 * m;
-      const int cv = f % CVH, p2 = f / CVH;
-      const int row0 = cv * VEC;
-      store_vt_pair(Vt, ldv, row0, vt_col(row0, 2 * p2), vreg[m][0], vreg[m][1]);
+  } else if constexpr (LCE) {
+    // ---- convolution of the region for this head, all inside the wave's
+    // own LDS area (LDS operations of one wave complete in order; the fences
+    // keep the compiler from reordering them across the phase changes)
+    if (head_ok) {
+      typedef typename Lce<T>::word LWord;
+      LWord* halo = reinterpret_cast<LWord*>(larea);
+      lce_halo_store<T, LNB>(halo, lt, 0, lane, ha, hb);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      float acc[LR][LX];
+      lce_compute<T, LR, LX>(halo + (lane & 31) * lt.ps, lt, lw, acc);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      lce_store_results<LR, LX>(reinterpret_cast<float*>(larea), lt, lane & 31, (lane >> 5) & 1, acc);
     }
   }
-  __syncthreads();  // V^T tiles written (each wave reads only its own)
-  if (!head_ok) return;
+  __syncthreads();  // V^T tiles and convolution results written
+  if (!att || !head_ok) return;
 
   T* Og = static_cast<T*>(p.O) + it.img;
   if (bad) {
@@ -765,8 +758,12 @@ __global__ __launch_bounds__(512) void attend_head_kernel(AttnParams p) {
         o[4 + e] = acc[1][e] * inv;
       }
       if constexpr (LCE) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += lce[t][e];
+        // the head's convolution results, query t*16 + col, channels 8g..8g+7
+        const float* r = reinterpret_cast<const float*>(larea) + (t * 16 + col) * kLceRes + 8 * g;
+        const float4 lo = *reinterpret_cast<const float4*>(r);
+        const float4 hi = *reinterpret_cast<const float4*>(r + 4);
+        o[0] += lo.x; o[1] += lo.y; o[2] += lo.z; o[3] += lo.w;
+        o[4] += hi.x; o[5] += hi.y; o[6] += hi.z; o[7] += hi.w;
       }
       TT::store8(Og + qoff[t], o);
     }
@@ -854,20 +851,35 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
     p.Q = Q; p.K = K; p.V = V; p.idx = idx; p.O = O;
     const size_t esz = dtype == kBF16 ? 2 : 4;
     const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
-    p.wave_lds = (int)(esz * D * (KC + padv));
     const bool ragged = s.kv % KC != 0;
     const bool one = s.n <= 16;  // one query tile per item
-    // the local context term is fused for bf16 regions of at most 8 x 8 tokens
-    const bool fuse = lce && dtype == kBF16 && s.sh <= 8 && s.sw <= 8;
+    // The local context term is fused for bf16 regions of 16 to 64 tokens
+    // (at most 8 x 8). For smaller regions the halo is several times the
+    // region (6 x 6 positions around 2 x 2) and the separate pass after the
+    // attention kernel measured faster (14x14 map, 2 x 2 regions: 38 us for
+    // attention + pass vs 47 us fused).
+    const bool fuse = lce && dtype == kBF16 && s.sh <= 8 && s.sw <= 8 && s.n >= 16;
     const bool small = s.sh <= 4 && s.sw <= 4;
+    size_t lds = esz * (size_t)HG * D * (KC + padv);  // V^T tiles
+    int waves = HG;
     const void* fn;
     if (fuse) {
+      // one convolution wave per head beside each attention wave; at most 4
+      // heads per workgroup keeps workgroups at 8 waves
+      if (HG > 4) {
+        HG = 4;
+        p.HG = HG;
+        p.nhg = (s.heads + HG - 1) / HG;
+        p.nitems = s.B * s.R * p.nqb * p.nhg;
+      }
       p.lw = lce_w;
       p.lb = lce_b;
       p.lce_pw = lce_pw(s.sw);
       p.lce_ps = lce_ps(s.sh, s.sw);
-      p.div_lpw = make_fastdiv(p.lce_pw);
-      p.wave_lds = max(p.wave_lds, lce_lds_bytes(s.sh, s.sw, 4));
+      p.lce_inv_pw = 1.0f / p.lce_pw;
+      p.wave_lds = lce_lds_bytes(s.sh, s.sw, 4);
+      lds = esz * (size_t)HG * D * (KC + padv) + (size_t)HG * p.wave_lds;
+      waves = 2 * HG;
       if (small)
         fn = ragged ? (const void*)&attend_head_kernel<__bf16, true, 1, 4, 2> : (const void*)&attend_head_kernel<__bf16, false, 1, 4, 2>;
       else if (one)
@@ -882,8 +894,7 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
                   : (one ? (const void*)&attend_head_kernel<float, false, 1, 0, 0> : (const void*)&attend_head_kernel<float, false, 4, 0, 0>);
     }
     void* args[] = {&p};
-    const size_t lds = (size_t)HG * p.wave_lds;
-    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(HG * 64), args, lds, stream);
+    hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(waves * 64), args, lds, stream);
     if (e != hipSuccess || !lce || fuse) return e;
     return launch_lce(V, lce_w, lce_b, O, s, dtype, stream);
   }

@@ -24,7 +24,6 @@ struct LceParams {
   int H, W, C;
   int tiles_x, tiles_y, ncg;
   int nitems;
-  FastDiv div_pw;
 };
 
 template <typename T>
@@ -56,14 +55,28 @@ __global__ __launch_bounds__(64) void lce_kernel(LceParams p) {
   t.cols = TC;
   t.pw = lce_pw(TC);
   t.ps = lce_ps(TR, TC);
+  t.inv_pw = 1.0f / lce_pw(TC);
   const int64_t img = (int64_t)b * p.H * p.W * p.C;
   const int ch0 = cg * 32;
   const int c = lane & 31, par = lane >> 5;
 
+  // the attention output this tile adds to: loads issued first, consumed last
+  T* Og = static_cast<T*>(p.O) + img;
+  constexpr int NO = TR * TC * CVN / 64;  // 16-byte output vectors per lane
+  uint4 ov[NO];
+  int ooff[NO];
+#pragma unroll
+  for (int m = 0; m < NO; ++m) {
+    const int f = lane + 64 * m;
+    const int cv = f % CVN, q = f / CVN;
+    const int yy = t.y0 + q / TC, xx = t.x0 + q % TC;
+    ooff[m] = (yy < p.H && xx < p.W) ? (yy * p.W + xx) * p.C + ch0 + cv * VEC : -1;
+    ov[m] = ooff[m] >= 0 ? *reinterpret_cast<const uint4*>(Og + ooff[m]) : make_uint4(0u, 0u, 0u, 0u);
+  }
   LceW<T> lw;
   lce_weights(static_cast<const T*>(p.w), static_cast<const T*>(p.bias), ch0 + c, par, lw);
   typename L::word* halo = reinterpret_cast<typename L::word*>(smem_raw);
-  lce_halo_fill<T, NB>(static_cast<const T*>(p.V) + img, p.H, p.W, p.C, ch0, t, p.div_pw, lane, halo);
+  lce_halo_fill<T, NB>(static_cast<const T*>(p.V) + img, p.H, p.W, p.C, ch0, t, lane, halo);
   __syncthreads();
   float acc[TR][TC / 2];
   lce_compute<T, TR, TC / 2>(halo + c * t.ps, t, lw, acc);
@@ -72,29 +85,25 @@ __global__ __launch_bounds__(64) void lce_kernel(LceParams p) {
   lce_store_results<TR, TC / 2>(res, t, c, par, acc);
   __syncthreads();
 
-  T* Og = static_cast<T*>(p.O) + img;
 #pragma unroll
-  for (int m = 0; m < TR * TC * CVN / 64; ++m) {
+  for (int m = 0; m < NO; ++m) {
     const int f = lane + 64 * m;
     const int cv = f % CVN, q = f / CVN;
-    const int y = q / TC, x = q % TC;
-    const int yy = t.y0 + y, xx = t.x0 + x;
-    if (yy < p.H && xx < p.W) {
-      T* o = Og + (yy * p.W + xx) * p.C + ch0 + cv * VEC;
+    if (ooff[m] >= 0) {
       const float* r = res + q * kLceRes + cv * VEC;
       if constexpr (VEC == 8) {
         typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(o);
+        bf16x8 v = __builtin_bit_cast(bf16x8, ov[m]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] + r[e]);
-        *reinterpret_cast<bf16x8*>(o) = v;
+        *reinterpret_cast<bf16x8*>(Og + ooff[m]) = v;
       } else {
-        float4 v = *reinterpret_cast<const float4*>(o);
+        float4 v = __builtin_bit_cast(float4, ov[m]);
         v.x += r[0];
         v.y += r[1];
         v.z += r[2];
         v.w += r[3];
-        *reinterpret_cast<float4*>(o) = v;
+        *reinterpret_cast<float4*>(Og + ooff[m]) = v;
       }
     }
   }
@@ -118,7 +127,6 @@ hipError_t launch_lce(const void* V, const void* weight, const void* bias, void*
   const int64_t n = (int64_t)s.B * p.tiles_y * p.tiles_x * p.ncg;
   if (n >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   p.nitems = (int)n;
-  p.div_pw = make_fastdiv(lce_pw(TC));
   const size_t lds = lce_lds_bytes(TR, TC, dtype == kBF16 ? 4 : 8);
   const void* fn = dtype == kBF16 ? (const void*)&lce_kernel<__bf16> : (const void*)&lce_kernel<float>;
   void* args[] = {&p};

@@ -74,37 +74,48 @@ struct LceTile {
   int y0, x0;      // image coordinates of the tile's first output
   int rows, cols;  // tile size
   int pw, ps;      // lce_pw(cols), lce_ps(rows, cols)
+  float inv_pw;    // 1 / pw
 };
 
-// Halo items: (halo row hy, word px, channel vector cv); each loads the two
-// positions of word px (16 bytes each) or leaves zeros outside the map.
+// Halo items: f -> (halo row hy, word px, channel vector cv). The row is
+// (pi + 0.5) / pw rounded down, with pi = f / CVN: for pi < 2^16 the float
+// product is far closer to the true quotient than the 0.5 / pw that separates
+// it from an integer, so it truncates exactly without a remainder fix-up.
 template <typename T>
-__device__ __forceinline__ void lce_halo_item(const LceTile& t, FastDiv div_pw, int f, int* hy, int* px, int* cv) {
+__device__ __forceinline__ void lce_halo_item(const LceTile& t, int f, int* hy, int* px, int* cv) {
   constexpr int CVN = 32 / Lce<T>::VEC;  // 4 (bf16) or 8 (fp32)
   *cv = f & (CVN - 1);
-  *hy = fdiv(f / CVN, div_pw, px);
+  const int pi = f / CVN;
+  *hy = (int)(((float)pi + 0.5f) * t.inv_pw);
+  *px = pi - *hy * t.pw;
 }
 
+// Each item loads the two positions of word px (16 bytes each). Positions
+// outside the map are clamped to the map for the load (always in bounds, no
+// branch) and their values replaced by zeros.
 template <typename T, int NB>
 __device__ __forceinline__ void lce_halo_load(const T* Vimg, int H, int W, int C, int ch0, const LceTile& t,
-                                              FastDiv div_pw, int base, int lane, uint4 (&a)[NB], uint4 (&b)[NB]) {
+                                              int base, int lane, uint4 (&a)[NB], uint4 (&b)[NB]) {
   constexpr int CVN = 32 / Lce<T>::VEC;
   const int nitems = (t.rows + 4) * t.pw * CVN;
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int m = 0; m < NB; ++m) {
     const int f = base + lane + 64 * m;
-    a[m] = make_uint4(0u, 0u, 0u, 0u);
-    b[m] = make_uint4(0u, 0u, 0u, 0u);
-    if (f < nitems) {
-      int hy, px, cv;
-      lce_halo_item<T>(t, div_pw, f, &hy, &px, &cv);
-      const int yy = t.y0 - 2 + hy, xx = t.x0 - 2 + 2 * px;
-      if (yy >= 0 && yy < H) {
-        const T* row = Vimg + (yy * W) * C + ch0 + cv * Lce<T>::VEC;
-        if (xx >= 0 && xx < W) a[m] = *reinterpret_cast<const uint4*>(row + xx * C);
-        if (xx + 1 >= 0 && xx + 1 < W) b[m] = *reinterpret_cast<const uint4*>(row + (xx + 1) * C);
-      }
-    }
+    const bool in = f < nitems;
+    int hy, px, cv;
+    lce_halo_item<T>(t, in ? f : 0, &hy, &px, &cv);
+    const int yy = t.y0 - 2 + hy, xx = t.x0 - 2 + 2 * px;
+    const bool rok = in && (unsigned)yy < (unsigned)H;
+    const bool aok = rok && (unsigned)xx < (unsigned)W;
+    const bool bok = rok && (unsigned)(xx + 1) < (unsigned)W;
+    const int yc = min(max(yy, 0), H - 1);
+    const int xa = min(max(xx, 0), W - 1), xb = min(max(xx + 1, 0), W - 1);
+    const T* row = Vimg + (yc * W) * C + ch0 + cv * Lce<T>::VEC;
+    const uint4 va = *reinterpret_cast<const uint4*>(row + xa * C);
+    const uint4 vb = *reinterpret_cast<const uint4*>(row + xb * C);
+    a[m] = aok ? va : z;
+    b[m] = bok ? vb : z;
   }
 }
 
@@ -126,8 +137,8 @@ __device__ __forceinline__ void lce_put(float2* halo, int ps, int ch, int w, con
 }
 
 template <typename T, int NB>
-__device__ __forceinline__ void lce_halo_store(typename Lce<T>::word* halo, const LceTile& t, FastDiv div_pw, int base,
-                                               int lane, const uint4 (&a)[NB], const uint4 (&b)[NB]) {
+__device__ __forceinline__ void lce_halo_store(typename Lce<T>::word* halo, const LceTile& t, int base, int lane,
+                                               const uint4 (&a)[NB], const uint4 (&b)[NB]) {
   constexpr int CVN = 32 / Lce<T>::VEC;
   const int nitems = (t.rows + 4) * t.pw * CVN;
 #pragma unroll
@@ -135,7 +146,7 @@ __device__ __forceinline__ void lce_halo_store(typename Lce<T>::word* halo, cons
     const int f = base + lane + 64 * m;
     if (f < nitems) {
       int hy, px, cv;
-      lce_halo_item<T>(t, div_pw, f, &hy, &px, &cv);
+      lce_halo_item<T>(t, f, &hy, &px, &cv);
       lce_put(halo, t.ps, cv * Lce<T>::VEC, hy * t.pw + px, a[m], b[m]);
     }
   }
@@ -143,15 +154,15 @@ __device__ __forceinline__ void lce_halo_store(typename Lce<T>::word* halo, cons
 
 // Whole halo, load then store in batches of NB items per lane.
 template <typename T, int NB>
-__device__ __forceinline__ void lce_halo_fill(const T* Vimg, int H, int W, int C, int ch0, const LceTile& t,
-                                              FastDiv div_pw, int lane, typename Lce<T>::word* halo) {
+__device__ __forceinline__ void lce_halo_fill(const T* Vimg, int H, int W, int C, int ch0, const LceTile& t, int lane,
+                                              typename Lce<T>::word* halo) {
   constexpr int CVN = 32 / Lce<T>::VEC;
   const int nitems = (t.rows + 4) * t.pw * CVN;
 #pragma unroll 1
   for (int base = 0; base < nitems; base += 64 * NB) {
     uint4 a[NB], b[NB];
-    lce_halo_load<T, NB>(Vimg, H, W, C, ch0, t, div_pw, base, lane, a, b);
-    lce_halo_store<T, NB>(halo, t, div_pw, base, lane, a, b);
+    lce_halo_load<T, NB>(Vimg, H, W, C, ch0, t, base, lane, a, b);
+    lce_halo_store<T, NB>(halo, t, base, lane, a, b);
   }
 }
 
@@ -228,24 +239,28 @@ __device__ __forceinline__ void lce_compute(const typename Lce<T>::word* plane, 
       const int y = hy - i;  // output row fed by halo row hy through filter row i
       if (y < 0 || y >= LR) continue;
       if (y >= t.rows) continue;  // uniform
+      // consecutive instructions update different accumulators
 #pragma unroll
-      for (int m = 0; m < LX; ++m)
-        acc[y][m] = L::dot(wd[m + 2], lw.w[i][2], L::dot(wd[m + 1], lw.w[i][1], L::dot(wd[m], lw.w[i][0], acc[y][m])));
+      for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int m = 0; m < LX; ++m) acc[y][m] = L::dot(wd[m + k], lw.w[i][k], acc[y][m]);
     }
   }
 }
 
-// Results to LDS rows res[(y * cols + x) * kLceRes + c].
+// Results to LDS rows res[(y * cols + x) * kLceRes + c]. Outputs past the
+// tile's last column go to a padding slot of row 0 (no branch per store).
 template <int LR, int LX>
 __device__ __forceinline__ void lce_store_results(float* res, const LceTile& t, int c, int par,
                                                   const float (&acc)[LR][LX]) {
 #pragma unroll
   for (int y = 0; y < LR; ++y) {
-    if (y >= t.rows) break;
+    if (y >= t.rows) break;  // uniform
 #pragma unroll
     for (int m = 0; m < LX; ++m) {
       const int x = 2 * m + par;
-      if (x < t.cols) res[(y * t.cols + x) * kLceRes + c] = acc[y][m];
+      const int at = x < t.cols ? (y * t.cols + x) * kLceRes + c : 32 + (c & 3);
+      res[at] = acc[y][m];
     }
   }
 }
