@@ -68,6 +68,11 @@ Pins (tests/test_oracle_pins.py, all ``-m "not gpu"``):
                            gathered V; V = 1 gives 1; permutation
                            invariance in the route order;
   attended_tokens        : the [EXP] Part 6.3 table (tests/golden);
+  attend_backward        : central finite differences of ``attend``
+                           itself (no gradient formula involved), torch
+                           autograd through SDPA in fp64 when every region
+                           is routed, and the sum rules sum(dK) = 0 and
+                           sum(dV) = sum(dO) per image and head;
   lce                    : torch conv2d with groups = C and scipy.ndimage
                            correlate (two library routines), single-tap
                            filters = shifted maps with zero fill (brute
@@ -305,3 +310,71 @@ def bra_lce(Q, K, V, heads: int, S: int, topk: int, weight, bias=None, scale: fl
     """Full BRA forward with the local context term: returns (O, routes)."""
     O, routes = bra(Q, K, V, heads, S, topk, scale)
     return O + lce(V, weight, bias), routes
+
+
+# --------------------------------------------------------------------------- #
+# Backward of the token attention with the routing held fixed
+# --------------------------------------------------------------------------- #
+def softmax_attention_backward(q: np.ndarray, kg: np.ndarray, vg: np.ndarray, do: np.ndarray, scale: float):
+    """Gradients of O = softmax(q kg^T * scale) vg for one (image, region,
+    head), given dL/dO = do. Written out from the chain rule:
+
+        P    = softmax(Z),  Z = scale * q kg^T          (rows normalised)
+        dvg  = P^T do
+        dP   = do vg^T
+        dZ   = P * (dP - rowsum(P * dP))                (softmax Jacobian)
+        dq   = scale * dZ kg
+        dkg  = scale * dZ^T q
+
+    Returns (dq [n, d], dkg [m, d], dvg [m, dv]).
+    """
+    z = (q @ kg.T) * scale
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)
+    dvg = p.T @ do
+    dp = do @ vg.T
+    dz = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    dq = scale * (dz @ kg)
+    dkg = scale * (dz.T @ q)
+    return dq, dkg, dvg
+
+
+def attend_backward(Q, K, V, routes, dO, heads: int, S: int, scale: float | None = None):
+    """Gradients of ``attend`` with respect to Q, K and V, the routing table
+    held fixed (top-k indices carry no gradient, so the region pooling gets
+    none either). A key/value token routed to by several query regions
+    accumulates the gradient of every one of them. Returns (dQ, dK, dV),
+    each [B, H, W, C] float64."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    routes = np.asarray(routes)
+    B, H, W, C = Q.shape
+    R = S * S
+    k = routes.shape[-1]
+    check_config(B, H, W, C, heads, S, k)
+    if routes.shape != (B, R, k):
+        raise ValueError(f"routes must be [B, S*S, k] = {(B, R, k)}, got {routes.shape}")
+    if routes.min() < 0 or routes.max() >= R:
+        raise ValueError("route indices out of range")
+    d = C // heads
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for i in range(R):
+            qy, qx = region_token_coords(H, W, S, i)
+            gy, gx = gather_coords(H, W, S, routes[b, i])
+            for m in range(heads):
+                ch = slice(m * d, (m + 1) * d)
+                dq, dkg, dvg = softmax_attention_backward(Q[b, qy, qx, ch], K[b, gy, gx, ch], V[b, gy, gx, ch],
+                                                          dO[b, qy, qx, ch], scale)
+                dQ[b, qy, qx, ch] = dq
+                # the routed regions are distinct, so (gy, gx) has no repeats
+                # inside one row and += adds each token once
+                dK[b, gy, gx, ch] += dkg
+                dV[b, gy, gx, ch] += dvg
+    return dQ, dK, dV

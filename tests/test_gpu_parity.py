@@ -111,6 +111,26 @@ def test_edge_shapes(w):
     _check_case(w, q, k, v, images=list(range(w.B)))
 
 
+# The (S, k) schedules of the explainer's Part 6.3 table over the four stage
+# maps of a 224 x 224 input (56, 28, 14, 7; C = 64 * 2^stage, head dim 32):
+# S = 7 with k = [1, 4, 16, 49], S = 7 with k = [1, 2, 8, 32], and
+# S = [8, 4, 2, 1] with k = [2, 2, 2, 1]. Two images each.
+_STAGE_MAPS = [(56, 64), (28, 128), (14, 256), (7, 512)]
+_SCHEDULES = [((7, 7, 7, 7), (1, 4, 16, 49)), ((7, 7, 7, 7), (1, 2, 8, 32)), ((8, 4, 2, 1), (2, 2, 2, 1))]
+PAGE_SCHEDULES = [
+    wl.custom(2, hw, hw, c, c // 32, S[st], k[st], "bf16", seed=40 + 4 * row + st)
+    for row, (S, k) in enumerate(_SCHEDULES)
+    for st, (hw, c) in enumerate(_STAGE_MAPS)
+]
+
+
+@pytest.mark.parametrize("w", PAGE_SCHEDULES, ids=[w.name for w in PAGE_SCHEDULES])
+def test_page_schedules(w):
+    q, k, v = wl.make_inputs(w)
+    mism, _, _ = _check_case(w, q, k, v, images=list(range(w.B)))
+    assert mism == 0
+
+
 def test_one_region_equals_global_attention():
     w = wl.custom(2, 8, 8, 64, 2, 1, 1, "f32", seed=21)
     q, k, v = wl.make_inputs(w)

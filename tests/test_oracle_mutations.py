@@ -19,6 +19,7 @@ _orig_softmax = O.softmax_attention
 _orig_mean = O.region_mean
 _orig_attend = O.attend
 _orig_lce = O.lce
+_orig_sab = O.softmax_attention_backward
 
 
 def _transposed_affinity(Qr, Kr):
@@ -107,7 +108,51 @@ def _off_by_one_padding(V, weight, bias=None):
     return out
 
 
+def _bwd_no_rowsum_term(q, kg, vg, do, scale):
+    z = (q @ kg.T) * scale
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dz = p * (do @ vg.T)
+    return scale * (dz @ kg), scale * (dz.T @ q), p.T @ do
+
+
+def _bwd_unscaled_dq(q, kg, vg, do, scale):
+    dq, dk, dv = _orig_sab(q, kg, vg, do, scale)
+    return dq / scale, dk, dv
+
+
+def _bwd_value_grad_from_logits(q, kg, vg, do, scale):
+    dq, dk, dv = _orig_sab(q, kg, vg, do, scale)
+    z = (q @ kg.T) * scale
+    return dq, dk, np.exp(z - z.max()).T @ do  # unnormalised probabilities
+
+
+def _bwd_scatter_overwrites(Q, K, V, routes, dO, heads, S, scale=None):
+    # last query region wins instead of accumulating
+    Q = np.asarray(Q, dtype=np.float64)
+    B, H, W, C = Q.shape
+    d = C // heads
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    dQ, dK, dV = (np.zeros_like(Q) for _ in range(3))
+    for b in range(B):
+        for i in range(S * S):
+            qy, qx = O.region_token_coords(H, W, S, i)
+            gy, gx = O.gather_coords(H, W, S, routes[b, i])
+            for m in range(heads):
+                ch = slice(m * d, (m + 1) * d)
+                dq, dk, dv = _orig_sab(Q[b, qy, qx, ch], np.asarray(K)[b, gy, gx, ch], np.asarray(V)[b, gy, gx, ch],
+                                       np.asarray(dO)[b, qy, qx, ch], scale)
+                dQ[b, qy, qx, ch] = dq
+                dK[b, gy, gx, ch] = dk
+                dV[b, gy, gx, ch] = dv
+    return dQ, dK, dV
+
+
 MUTATIONS = {
+    "bwd_no_rowsum_term": ("softmax_attention_backward", _bwd_no_rowsum_term),
+    "bwd_unscaled_dq": ("softmax_attention_backward", _bwd_unscaled_dq),
+    "bwd_value_grad_unnormalised": ("softmax_attention_backward", _bwd_value_grad_from_logits),
+    "bwd_scatter_overwrites": ("attend_backward", _bwd_scatter_overwrites),
     "lce_convolution_not_correlation": ("lce", _convolution_not_correlation),
     "lce_transposed_filter": ("lce", _transposed_filter),
     "lce_circular_padding": ("lce", _circular_padding),

@@ -321,3 +321,95 @@ def test_lce_is_added_to_the_attention_output():
         O.lce(V, w[:, :4])
     with pytest.raises(ValueError):
         O.lce(V, w, b[:3])
+
+
+# --------------------------------------------------------------------------- #
+# Backward with the routing held fixed
+# --------------------------------------------------------------------------- #
+def _fixed_route_loss_grads_fd(Q, K, V, routes, G, heads, S, h=1e-6):
+    """Central finite differences of L = sum(attend(Q, K, V) * G) with the
+    routing table fixed: uses only the forward oracle."""
+    grads = []
+    for which in range(3):
+        X = [Q.copy(), K.copy(), V.copy()]
+        g = np.zeros_like(X[which])
+        for idx in np.ndindex(*X[which].shape):
+            orig = X[which][idx]
+            X[which][idx] = orig + h
+            up = (O.attend(*X, routes, heads, S) * G).sum()
+            X[which][idx] = orig - h
+            dn = (O.attend(*X, routes, heads, S) * G).sum()
+            X[which][idx] = orig
+            g[idx] = (up - dn) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("B,H,W,C,heads,S,k", [(1, 4, 4, 4, 2, 2, 2), (1, 4, 6, 2, 1, 2, 3)])
+def test_backward_matches_finite_differences(B, H, W, C, heads, S, k):
+    Q, K, V, G = (_rand((B, H, W, C), s) for s in (60, 61, 62, 63))
+    routes = O.route(Q, K, S, k)
+    fd = _fixed_route_loss_grads_fd(Q, K, V, routes, G, heads, S)
+    an = O.attend_backward(Q, K, V, routes, G, heads, S)
+    for name, a, f in zip("QKV", an, fd):
+        np.testing.assert_allclose(a, f, rtol=1e-6, atol=1e-8, err_msg=f"d{name}")
+
+
+def test_backward_full_routing_equals_sdpa_autograd():
+    B, H, W, C, heads, S = 2, 4, 4, 8, 2, 2
+    Q, K, V, G = (_rand((B, H, W, C), s) for s in (64, 65, 66, 67))
+    routes = np.broadcast_to(np.arange(S * S, dtype=np.int32), (B, S * S, S * S)).copy()
+    dQ, dK, dV = O.attend_backward(Q, K, V, routes, G, heads, S)
+    ts = [torch.from_numpy(x).reshape(B, H * W, heads, C // heads).permute(0, 2, 1, 3).requires_grad_(True)
+          for x in (Q, K, V)]
+    out = torch.nn.functional.scaled_dot_product_attention(*ts)
+    g = torch.from_numpy(G).reshape(B, H * W, heads, C // heads).permute(0, 2, 1, 3)
+    (out * g).sum().backward()
+    for a, t, name in zip((dQ, dK, dV), ts, "QKV"):
+        ref = t.grad.permute(0, 2, 1, 3).reshape(B, H, W, C).numpy()
+        np.testing.assert_allclose(a, ref, rtol=1e-10, atol=1e-12, err_msg=f"d{name}")
+
+
+def test_backward_matches_autograd_through_a_torch_gather():
+    """General routes (k < S^2, overlapping): torch autograd through
+    advanced indexing + SDPA, per region, in fp64."""
+    B, H, W, C, heads, S, k = 1, 6, 6, 4, 2, 3, 2
+    Q, K, V, G = (_rand((B, H, W, C), s) for s in (68, 69, 70, 71))
+    routes = O.route(Q, K, S, k)
+    tq, tk, tv = (torch.from_numpy(x).clone().requires_grad_(True) for x in (Q, K, V))
+    sh, sw = H // S, W // S
+    loss = 0.0
+    for i in range(S * S):
+        ri, rj = divmod(i, S)
+        qy, qx = np.meshgrid(np.arange(ri * sh, (ri + 1) * sh), np.arange(rj * sw, (rj + 1) * sw), indexing="ij")
+        ys, xs = [], []
+        for r in routes[0, i]:
+            a, c = divmod(int(r), S)
+            y, x = np.meshgrid(np.arange(a * sh, (a + 1) * sh), np.arange(c * sw, (c + 1) * sw), indexing="ij")
+            ys.append(y.ravel())
+            xs.append(x.ravel())
+        gy, gx = torch.from_numpy(np.concatenate(ys)), torch.from_numpy(np.concatenate(xs))
+        qy_t, qx_t = torch.from_numpy(qy.ravel()), torch.from_numpy(qx.ravel())
+        d = C // heads
+        q = tq[0, qy_t, qx_t].reshape(-1, heads, d).transpose(0, 1)
+        kk = tk[0, gy, gx].reshape(-1, heads, d).transpose(0, 1)
+        vv = tv[0, gy, gx].reshape(-1, heads, d).transpose(0, 1)
+        o = torch.nn.functional.scaled_dot_product_attention(q, kk, vv).transpose(0, 1).reshape(-1, C)
+        loss = loss + (o * torch.from_numpy(G[0, qy.ravel(), qx.ravel()])).sum()
+    loss.backward()
+    dQ, dK, dV = O.attend_backward(Q, K, V, routes, G, heads, S)
+    for a, t, name in zip((dQ, dK, dV), (tq, tk, tv), "QKV"):
+        np.testing.assert_allclose(a, t.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=f"d{name}")
+
+
+def test_backward_sum_rules():
+    """Softmax rows sum to one: per image and head the key gradients sum to
+    zero and the value gradients sum to the output gradients."""
+    B, H, W, C, heads, S, k = 2, 8, 8, 8, 2, 4, 3
+    Q, K, V, G = (_rand((B, H, W, C), s) for s in (72, 73, 74, 75))
+    routes = O.route(Q, K, S, k)
+    dQ, dK, dV = O.attend_backward(Q, K, V, routes, G, heads, S)
+    np.testing.assert_allclose(dK.sum(axis=(1, 2)), 0.0, atol=1e-10)
+    np.testing.assert_allclose(dV.sum(axis=(1, 2)), G.sum(axis=(1, 2)), rtol=1e-10, atol=1e-10)
+    z = O.attend_backward(Q, K, V, routes, np.zeros_like(G), heads, S)
+    assert all(np.all(x == 0) for x in z)

@@ -23,6 +23,9 @@ Local-context filters (``make_lce_params``): a generator seeded with
 filter applied to unit-variance values gives roughly unit variance) and the
 [C] bias as ``randn / 10``, both cast to the workload's dtype. No trained
 filter is used.
+
+Output gradients for the backward pass (``make_grad_output``): a generator
+seeded with ``seed + 2000`` draws ``randn`` [B, H, W, C], cast to the dtype.
 """
 
 from __future__ import annotations
@@ -135,6 +138,14 @@ def make_lce_params(w: Workload):
     bias = torch.randn((w.C,), generator=gen, dtype=torch.float32) / 10.0
     dt = w.torch_dtype
     return weight.to(dt).contiguous(), bias.to(dt).contiguous()
+
+
+def make_grad_output(w: Workload):
+    """Draw dL/dO [B, H, W, C] on the CPU in the workload's dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(w.seed) + 2000)
+    g = torch.randn((w.B, w.H, w.W, w.C), generator=gen, dtype=torch.float32)
+    return g.to(w.torch_dtype).contiguous()
 
 
 def to_f64(t: torch.Tensor):
