@@ -164,6 +164,43 @@ bra_status bra_forward_lce(const void* Q, const void* K, const void* V,
                            bra_dtype dtype, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/*
+ * Backward of the token attention, routing held fixed (the pages report
+ * training throughput: explainer Part 7 and paper summary Appendix B; the
+ * forward is explainer Part 2.2 step 4, pseudocode steps 6-7). The top-k
+ * indices are not differentiable, so the region pooling receives no gradient.
+ * For every image, region i and head m, with P = softmax(scale q k_g^T):
+ *
+ *   dV_g += P^T dO,  dZ = P * (dO V_g^T - rowsum(dO * O)),
+ *   dQ = scale dZ K_g,  dK_g += scale dZ^T Q
+ *
+ * where K_g, V_g are the tokens of regions idx[b][i][.] and a token's dK, dV
+ * sum over every query region routed to its region.
+ *
+ *   Q, K, V  : the forward inputs; O: the forward output (bra_attend /
+ *              bra_forward with the same idx); dO: dL/dO. All [B, H, W, C]
+ *              in `dtype`, 16-byte aligned, read only.
+ *   idx      : the routing table of the forward, [B, S*S, topk] int32, with
+ *              distinct entries per row (as bra_route writes them). A row
+ *              with an entry outside [0, S*S) makes that region's dQ NaN and
+ *              its queries contribute nothing to dK, dV.
+ *   dQ, dK, dV : outputs [B, H, W, C] in `dtype`, 16-byte aligned, pairwise
+ *              distinct and distinct from the inputs (BRA_EINVAL). Every
+ *              element is written (tokens no region routes to get 0 in dK
+ *              and dV).
+ *   workspace  : bra_backward_workspace_bytes(...) bytes, 256-byte aligned,
+ *              or NULL/0 for a stream-ordered allocation as in bra_forward.
+ *
+ * Deterministic: no atomics touch the gradients; fp32 accumulation.
+ */
+size_t bra_backward_workspace_bytes(int B, int H, int W, int C, int heads, int S, int topk);
+
+bra_status bra_attend_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                               const int32_t* idx, void* dQ, void* dK, void* dV,
+                               int B, int H, int W, int C, int heads, int S, int topk,
+                               bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

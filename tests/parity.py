@@ -98,3 +98,25 @@ def assert_lce_output_close(out: np.ndarray, ref: np.ndarray, dtype: str, what: 
         assert worst <= 0, f"{what}: bf16 error exceeds 2e-2 + 2^-7 |ref| by {worst:.3e} (max-abs {max_abs:.3e})"
         assert mean_rel <= BF16_MEAN_REL, f"{what}: bf16 mean-rel {mean_rel:.3e} > {BF16_MEAN_REL}"
     return max_abs, mean_rel
+
+
+GRAD_F32_REL = 1e-4
+GRAD_BF16_REL = 2e-2
+GRAD_BF16_MEAN_REL = 1e-2
+
+
+def assert_grad_close(out: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    """Parity bound for gradients. Their size depends on the data, so the
+    elementwise bound scales with the tensor's largest reference value: fp32
+    1e-4 * max(1, max|ref|); bf16 2e-2 * max(1, max|ref|) (bf16 rounding of
+    the probabilities and of dZ inside the products, 2^-8 relative each, and
+    of the stored gradient) plus mean-rel <= 1e-2."""
+    assert np.all(np.isfinite(out)), f"{what}: non-finite gradients"
+    max_abs, mean_rel = output_errors(out, ref)
+    scale = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
+    if dtype == "f32":
+        assert max_abs <= GRAD_F32_REL * scale, f"{what}: fp32 max-abs {max_abs:.3e} > {GRAD_F32_REL} * {scale:.2f}"
+    else:
+        assert max_abs <= GRAD_BF16_REL * scale, f"{what}: bf16 max-abs {max_abs:.3e} > {GRAD_BF16_REL} * {scale:.2f}"
+        assert mean_rel <= GRAD_BF16_MEAN_REL, f"{what}: bf16 mean-rel {mean_rel:.3e} > {GRAD_BF16_MEAN_REL}"
+    return max_abs, mean_rel

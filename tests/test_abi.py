@@ -91,7 +91,12 @@ def _attend_lce(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2,
     return lib.bra_attend_lce(q, kk, v, idx, wt, bias, o, B, H, W, C, heads, S, k, dt, None)
 
 
-@pytest.mark.parametrize("call", [_fwd, _route, _attend, _fwd_lce, _attend_lce])
+def _bwd(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4, do=PF, idx=PB,
+         dq=0x80000, dk=0x90000, dv=0xA0000, ws=PW, wsb=1 << 20):
+    return lib.bra_attend_backward(q, kk, v, o, do, idx, dq, dk, dv, B, H, W, C, heads, S, k, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("call", [_fwd, _route, _attend, _fwd_lce, _attend_lce, _bwd])
 @pytest.mark.parametrize(
     "kwargs,status",
     [
@@ -114,7 +119,7 @@ def test_host_validation(lib, call, kwargs, status):
     assert call(lib, **kwargs) == status
 
 
-@pytest.mark.parametrize("call", [_fwd, _attend, _fwd_lce, _attend_lce])
+@pytest.mark.parametrize("call", [_fwd, _attend, _fwd_lce, _attend_lce, _bwd])
 @pytest.mark.parametrize(
     "kwargs,status",
     [
@@ -127,6 +132,8 @@ def test_host_validation(lib, call, kwargs, status):
     ],
 )
 def test_host_validation_heads_and_outputs(lib, call, kwargs, status):
+    if call is _bwd and "o" in kwargs:
+        kwargs = dict(dq=kwargs["o"])  # the backward's o is an input: alias an output instead
     assert call(lib, **kwargs) == status
 
 
@@ -153,7 +160,22 @@ def test_lce_filter_validation(lib, call, kwargs):
     assert call(lib, **kwargs) == EINVAL
 
 
-@pytest.mark.parametrize("call", [_fwd, _route, _fwd_lce])
+@pytest.mark.parametrize("kwargs", [dict(dq=P), dict(dk=P3), dict(dv=PF), dict(dq=0x90000), dict(dk=0xA0000),
+                                    dict(do=0), dict(idx=0), dict(idx=PB + 2), dict(dv=0xA0000 + 8)])
+def test_backward_validation(lib, kwargs):
+    assert _bwd(lib, **kwargs) == EINVAL
+
+
+def test_backward_workspace_bytes(lib):
+    B, H, W, C, heads, S, k = 2, 16, 16, 64, 2, 4, 2
+    tok = B * H * W * heads
+    up = lambda x: -(-x // 256) * 256
+    assert lib.bra_backward_workspace_bytes(B, H, W, C, heads, S, k) == 2 * up(4 * tok) + 2 * up(4 * B * 16) + up(4 * B * 16 * 16)
+    assert lib.bra_backward_workspace_bytes(B, H, W, C, 0, S, k) == 0
+    assert lib.bra_backward_workspace_bytes(B, H, W, C, 3, S, k) == 0
+
+
+@pytest.mark.parametrize("call", [_fwd, _route, _fwd_lce, _bwd])
 def test_workspace_validation(lib, call):
     assert call(lib, wsb=16) == EINVAL           # too small
     assert call(lib, ws=PW + 64) == EINVAL       # not 256-byte aligned

@@ -11,6 +11,7 @@ and the current stream. If the library has not been built, every call raises
     forward(q, k, v, heads, S, topk)                   -> o   [B, H, W, C]
     attend_lce(q, k, v, idx, weight, bias, heads, S)   -> o + 5x5 depthwise conv of v
     forward_lce(q, k, v, weight, bias, heads, S, topk) -> o + 5x5 depthwise conv of v
+    attend_backward(q, k, v, o, do, idx, heads, S)     -> (dq, dk, dv), routing held fixed
 
 q, k, v: contiguous [B, H, W, C] tensors on one GPU, float32 or bfloat16;
 weight [C, 5, 5] and bias [C] (or None) of the local-context filter in the
@@ -34,6 +35,7 @@ __all__ = [
     "forward",
     "attend_lce",
     "forward_lce",
+    "attend_backward",
     "EXPORTS",
 ]
 
@@ -46,7 +48,7 @@ BRA_OK, BRA_EINVAL, BRA_EUNSUPPORTED, BRA_EHIP, BRA_ENOMEM = range(5)
 
 # Every symbol include/bra.h declares.
 EXPORTS = ("bra_status_string", "bra_workspace_bytes", "bra_route", "bra_attend", "bra_forward",
-           "bra_attend_lce", "bra_forward_lce")
+           "bra_attend_lce", "bra_forward_lce", "bra_backward_workspace_bytes", "bra_attend_backward")
 
 _lib = None
 
@@ -90,6 +92,10 @@ def load_library():
     lib.bra_attend_lce.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
     lib.bra_forward_lce.restype = i32
     lib.bra_forward_lce.argtypes = [vp, vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp, sz, vp]
+    lib.bra_backward_workspace_bytes.restype = sz
+    lib.bra_backward_workspace_bytes.argtypes = [i32] * 7
+    lib.bra_attend_backward.restype = i32
+    lib.bra_attend_backward.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -242,3 +248,37 @@ def forward_lce(q, k, v, weight: torch.Tensor, bias, heads: int, S: int, topk: i
                                B, H, W, C, heads, S, topk, _dtype_code(q),
                                ws.data_ptr(), nbytes, _stream(q.device)))
     return out
+
+
+def backward_workspace_bytes(B: int, H: int, W: int, C: int, heads: int, S: int, topk: int) -> int:
+    n = load_library().bra_backward_workspace_bytes(B, H, W, C, heads, S, topk)
+    if n == 0:
+        raise ValueError("invalid sizes for the BRA backward")
+    return int(n)
+
+
+def attend_backward(q, k, v, o, do, idx: torch.Tensor, heads: int, S: int, out=None, workspace=None):
+    """Gradients (dq, dk, dv) of the token attention given dL/dO = do, the
+    routing table idx held fixed; o is the forward output for the same idx."""
+    lib = load_library()
+    _check_maps(q, k, v, o, do)
+    B, H, W, C = q.shape
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.dim() != 3 or idx.device != q.device:
+        raise ValueError("idx must be a contiguous int32 [B, S*S, topk] tensor on q's device")
+    if tuple(idx.shape[:2]) != (B, S * S):
+        raise ValueError("idx must be [B, S*S, topk]")
+    topk = idx.shape[2]
+    if out is None:
+        out = tuple(torch.empty_like(q) for _ in range(3))
+    dq, dk, dv = out
+    _check_maps(q, dq, dk, dv)
+    need = backward_workspace_bytes(B, H, W, C, heads, S, topk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes")
+    _check(lib.bra_attend_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                   idx.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   B, H, W, C, heads, S, topk, _dtype_code(q),
+                                   workspace.data_ptr(), need, _stream(q.device)))
+    return dq, dk, dv

@@ -1,0 +1,616 @@
+// Backward of the token attention over routed regions, with the routing
+// table held fixed (explainer "BiFormer Reshapes Visual Attention with
+// 'Bi-Level Routing'", Part 2.2 step 4 and pseudocode steps 6-7 for the
+// forward; Part 7 reports training throughput, i.e. the module is trained
+// through this path). The top-k indices carry no gradient, so neither does the
+// region pooling; the gradients are those of ordinary softmax attention of
+// every region's queries over its routed keys:
+//
+//   P = softmax(Z), Z = scale * q k^T;  dV_g = P^T dO;  dP = dO V_g^T;
+//   dZ = P * (dP - D), D = rowsum(dO * O) = rowsum(P * dP);
+//   dQ = scale * dZ K_g;  dK_g = scale * dZ^T Q
+//
+// with dK, dV of a token summed over every query region routed to its region.
+//
+// Three kernels, all deterministic (no atomics on gradients):
+//  1. bwd_routes_kernel: per image, the inverse routing table - for every key
+//     region, the ascending list of query regions whose rows hold it. A row
+//     with an entry outside [0, S*S) is marked bad and left out.
+//  2. bwd_dq_kernel: one wave per (head, 16-query tile), the forward's
+//     transposed products (S^T = K Q^T, dP^T = V dO^T, dQ^T = K^T dZ^T with
+//     K^T through LDS), D from O and dO, and the base-2 log-sum-exp of every
+//     query, written for kernel 3. Several 64-key chunks take two passes
+//     (log-sum-exp first).
+//  3. bwd_dkv_kernel: one wave per (head, 32 keys of one key region), looping
+//     over the query regions of the inverse table: S = Q K^T and dP = dO V^T
+//     put each lane on one key with 4 queries, exactly the contraction slots
+//     of the 16-deep products dV^T += dO^T P and dK^T += Q^T dZ (dO^T, Q^T
+//     through LDS), so P and dZ never leave registers.
+#include "attn_common.h"
+
+#include <math.h>
+
+namespace bra {
+namespace {
+
+struct BwdParams {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const int32_t* idx;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* lse;     // [B*H*W*heads]: base-2 log-sum-exp of c * q.k over the query's keys
+  float* dd;      // [B*H*W*heads]: D = dO . O
+  int* inv_cnt;   // [B*R]
+  int* inv_list;  // [B*R*R]
+  int* bad;       // [B*R]
+  int H, W, C, S, topk;
+  int sh, sw, n, R, kv, heads;
+  int HG, nhg, nqb, ntq, nitems_q;    // dq kernel
+  int HGk, nhgk, nkb, nitems_kv;      // dkv kernel
+  float c;      // scale * log2(e)
+  float scale;  // 1 / sqrt(d)
+  FastDiv div_n, div_sw, div_S;
+};
+
+__device__ inline int corner_of(const BwdParams& p, int r) {
+  int rx;
+  const int ry = fdiv(r, p.div_S, &rx);
+  return ry * p.sh * p.W + rx * p.sw;
+}
+
+__device__ inline int xcd_remap() {
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
+  return x * q8 + min(x, r8) + loc;  // consecutive work items to one XCD
+}
+
+// ---------------------------------------------------------------------------
+// 1. Inverse routing table, one workgroup per image.
+__global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
+  __shared__ int cnt[kMaxRegions];
+  __shared__ int rowbad[kMaxRegions];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int32_t* idx = p.idx + (int64_t)b * p.R * p.topk;
+  for (int r = tid; r < p.R; r += 256) {
+    cnt[r] = 0;
+    rowbad[r] = 0;
+  }
+  __syncthreads();
+  const int nent = p.R * p.topk;
+  for (int e = tid; e < nent; e += 256) {
+    const int r = idx[e];
+    if (r < 0 || r >= p.R) rowbad[e / p.topk] = 1;
+  }
+  __syncthreads();
+  int* list = p.inv_list + (int64_t)b * p.R * p.R;
+  for (int e = tid; e < nent; e += 256) {
+    const int i = e / p.topk;
+    const int r = idx[e];
+    if (!rowbad[i]) {
+      const int slot = atomicAdd(&cnt[r], 1);
+      if (slot < p.R) list[r * p.R + slot] = i;  // a row repeating r cannot overflow the list
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < p.R; r += 256) {
+    const int m = min(cnt[r], p.R);
+    int* L = list + r * p.R;
+    // ascending order, whatever order the slots were taken in
+    for (int a = 1; a < m; ++a) {
+      const int v = L[a];
+      int j = a - 1;
+      while (j >= 0 && L[j] > v) {
+        L[j + 1] = L[j];
+        --j;
+      }
+      L[j + 1] = v;
+    }
+    p.inv_cnt[b * p.R + r] = m;
+    p.bad[b * p.R + r] = rowbad[r];
+  }
+}
+
+// Chunk token table: tok[kappa - c0] = token (inside the image) of routed key
+// kappa of the chunk starting at c0, -1 past kv. rb holds the routed regions'
+// corners.
+__device__ __forceinline__ void build_tok(int* tok, const int* rb, int tid, int c0, int kv, int W, FastDiv div_n,
+                                          FastDiv div_sw) {
+  if (tid < KC) {
+    const int kappa = c0 + tid;
+    int t = -1;
+    if (kappa < kv) {
+      int tk, tx;
+      const int jr = fdiv(kappa, div_n, &tk);
+      const int ty = fdiv(tk, div_sw, &tx);
+      t = rb[jr] + ty * W + tx;
+    }
+    tok[tid] = t;
+  }
+}
+
+// A-operand row rr = col of the (32-key step st, tile tb) is key
+// st*32 + 8*(rr/4) + (rr%4) + 4*tb, so lane group g holds keys 8g..8g+7 of
+// every 32-key step: the slots of the dZ^T operand.
+__device__ __forceinline__ int key_of(int col, int st, int tb) { return st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb; }
+
+// ---------------------------------------------------------------------------
+// 2. dQ, log-sum-exp and D. Workgroup = (image b, query region i, block of
+// <= 64 queries, group of HG heads); wave w = (head w / ntq, tile w % ntq).
+template <typename T, bool MULTI, bool RAGGED>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
+  typedef Tr<T> TT;
+  typedef typename TT::op8 op8;
+  constexpr int VEC = TT::VEC;
+  constexpr int CVH = D / VEC;
+  constexpr int ITEMS = KC / 2 * CVH;  // (key pair, vector) items of one K^T tile
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int tok[KC];
+  __shared__ int rb[kMaxRegions];
+  __shared__ int sbad;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, col = lane & 15;
+  const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
+  const int ldk = KC + TT::PADV;
+
+  int w = xcd_remap();
+  const int hg = w % p.nhg;
+  w /= p.nhg;
+  const int qb = w % p.nqb;
+  w /= p.nqb;
+  const int i = w % p.R;
+  const int b = w / p.R;
+  const int hl = wave / p.ntq, t = wave - hl * p.ntq;
+  const int head = hg * p.HG + hl;
+  const bool head_ok = head < p.heads;
+  const int ch0 = head * D;
+  const int64_t img = (int64_t)b * p.H * p.W * p.C;
+  const T* Kg = static_cast<const T*>(p.K) + img;
+  const T* Vg = static_cast<const T*>(p.V) + img;
+  T* Kt = reinterpret_cast<T*>(smem_raw) + hl * D * ldk;  // K^T tile of this wave's head
+
+  // routed regions' corners
+  if (tid == 0) sbad = 0;
+  __syncthreads();
+  for (int j = tid; j < p.topk; j += blockDim.x) {
+    const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
+    const bool ok = r >= 0 && r < p.R;
+    rb[j] = corner_of(p, ok ? r : 0);
+    if (!ok) sbad = 1;
+  }
+
+  // the wave's queries: B operands of q and dO, and D = dO . O per query
+  const int q0 = qb * 64;
+  const int qi = q0 + t * 16 + col;
+  const bool qvalid = head_ok && t * 16 < min(64, p.n - q0) && qi < p.n;
+  int qtok = 0;
+  op8 qop = TT::zero(), dop = TT::zero();
+  float dpart = 0.f;
+  {
+    int qx;
+    const int qy = fdiv(qi < p.n ? qi : 0, p.div_sw, &qx);
+    int rx;
+    const int ry = fdiv(i, p.div_S, &rx);
+    qtok = (ry * p.sh + qy) * p.W + rx * p.sw + qx;
+    if (qvalid) {
+      const int off = qtok * p.C + ch0 + 8 * g;
+      qop = TT::load8(static_cast<const T*>(p.Q) + img + off);
+      dop = TT::load8(static_cast<const T*>(p.dO) + img + off);
+      const op8 o = TT::load8(static_cast<const T*>(p.O) + img + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart += (float)dop[e] * (float)o[e];
+    }
+  }
+  const float Dq = wave_sum_groups(dpart, a16, a32);
+  __syncthreads();
+  const bool bad = sbad;
+  T* dQg = static_cast<T*>(p.dQ) + img;
+  if (bad) {
+    // a routing entry outside [0, S*S): gradient NaN for the region's queries
+    if (qvalid) {
+      float nanv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) nanv[e] = __builtin_nanf("");
+      TT::store8(dQg + qtok * p.C + ch0 + 8 * g, nanv);
+    }
+    return;  // uniform over the workgroup
+  }
+
+  const int nchunks = MULTI ? (p.kv + KC - 1) / KC : 1;
+  const int kv = p.kv, W = p.W;
+  const FastDiv div_n = p.div_n, div_sw = p.div_sw;
+
+  // ---- pass 1 (several chunks): running max and sum per query
+  float m = -INFINITY, l = 0.f;
+  if (MULTI) {
+    for (int ch = 0; ch < nchunks; ++ch) {
+      build_tok(tok, rb, tid, ch * KC, kv, W, div_n, div_sw);
+      __syncthreads();
+      float s[2][8];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        op8 ka = TT::zero(), kb = TT::zero();
+        const int t0 = tok[key_of(col, st, 0)], t1 = tok[key_of(col, st, 1)];
+        if (head_ok && t0 >= 0) ka = TT::load8(Kg + t0 * p.C + ch0 + 8 * g);
+        if (head_ok && t1 >= 0) kb = TT::load8(Kg + t1 * p.C + ch0 + 8 * g);
+        const floatx4 sa = TT::mma(ka, qop, floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 sb = TT::mma(kb, qop, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[st][e] = sa[e];
+          s[st][4 + e] = sb[e];
+        }
+      }
+      const int c0 = ch * KC;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (RAGGED && c0 + st * 32 + 8 * g + e >= p.kv) s[st][e] = -INFINITY;
+          mx = fmaxf(mx, s[st][e]);
+        }
+      mx = wave_max_groups(mx, a16, a32);
+      const float mn = fmaxf(m, mx);
+      float add = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) add += __builtin_amdgcn_exp2f((s[st][e] - mn) * p.c);
+      l = l * __builtin_amdgcn_exp2f((m - mn) * p.c) + add;
+      m = mn;
+      __syncthreads();  // tok reused by the next chunk
+    }
+  }
+  float lse = MULTI ? m * p.c + __builtin_log2f(wave_sum_groups(l, a16, a32)) : 0.f;
+
+  // ---- pass 2: P, dP, dZ and dQ^T += K^T dZ^T
+  floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * KC;
+    build_tok(tok, rb, tid, c0, kv, W, div_n, div_sw);
+    __syncthreads();
+    // K^T tile of this head, written by the head's ntq waves together
+    for (int f = t * 64 + lane; f < ITEMS; f += p.ntq * 64) {
+      const int cv = f % CVH, p2 = f / CVH;
+      const int ta = tok[2 * p2], tb2 = tok[2 * p2 + 1];
+      uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = va;
+      if (head_ok && ta >= 0) va = *reinterpret_cast<const uint4*>(Kg + ta * p.C + ch0 + cv * VEC);
+      if (head_ok && tb2 >= 0) vb = *reinterpret_cast<const uint4*>(Kg + tb2 * p.C + ch0 + cv * VEC);
+      const int row0 = cv * VEC;
+      store_vt_pair(Kt, ldk, row0, vt_col(row0, 2 * p2), va, vb);
+    }
+    float s[2][8], dp[2][8];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int t0 = tok[key_of(col, st, 0)], t1 = tok[key_of(col, st, 1)];
+      op8 ka = TT::zero(), kb = TT::zero(), va = TT::zero(), vb = TT::zero();
+      if (head_ok && t0 >= 0) {
+        ka = TT::load8(Kg + t0 * p.C + ch0 + 8 * g);
+        va = TT::load8(Vg + t0 * p.C + ch0 + 8 * g);
+      }
+      if (head_ok && t1 >= 0) {
+        kb = TT::load8(Kg + t1 * p.C + ch0 + 8 * g);
+        vb = TT::load8(Vg + t1 * p.C + ch0 + 8 * g);
+      }
+      const floatx4 sa = TT::mma(ka, qop, floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 sb = TT::mma(kb, qop, floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 pa = TT::mma(va, dop, floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 pb = TT::mma(vb, dop, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[st][e] = sa[e];
+        s[st][4 + e] = sb[e];
+        dp[st][e] = pa[e];
+        dp[st][4 + e] = pb[e];
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (RAGGED && c0 + st * 32 + 8 * g + e >= p.kv) s[st][e] = -INFINITY;
+    if (!MULTI) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
+      mx = wave_max_groups(mx, a16, a32);
+      float sum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f((s[st][e] - mx) * p.c);
+      lse = mx * p.c + __builtin_log2f(wave_sum_groups(sum, a16, a32));
+    }
+    __syncthreads();  // K^T tile complete
+    const int vrow = 8 * (col >> 2) + (col & 3);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float dz[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -lse));
+        dz[e] = pr * (dp[st][e] - Dq);
+      }
+      const op8 zop = TT::from_f32(dz);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int row = vrow + 4 * ct;
+        const op8 kt = TT::load8(Kt + row * ldk + vt_col(row, st * 32 + 8 * g));
+        dq[ct] = TT::mma(kt, zop, dq[ct]);
+      }
+    }
+    __syncthreads();  // tok and K^T reused by the next chunk
+  }
+
+  if (qvalid) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = dq[0][e] * p.scale;
+      o[4 + e] = dq[1][e] * p.scale;
+    }
+    TT::store8(dQg + qtok * p.C + ch0 + 8 * g, o);
+    if (g == 0) {
+      const int64_t at = ((int64_t)b * p.H * p.W + qtok) * p.heads + head;
+      p.lse[at] = lse;
+      p.dd[at] = Dq;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dK, dV. Workgroup = (image b, key region r, block of <= 64 of its keys,
+// group of HGk heads); wave w = (head w / 2, key half w % 2: 32 keys).
+template <typename T>
+__global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
+  typedef Tr<T> TT;
+  typedef typename TT::op8 op8;
+  typedef typename TT::op4 op4;
+  constexpr int VEC = TT::VEC;
+  constexpr int CVH = D / VEC;
+  constexpr int LDT = 16 + (sizeof(T) == 2 ? 8 : 4);  // transposed query tiles: row = channel
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, col = lane & 15;
+
+  int w = xcd_remap();
+  const int hg = w % p.nhgk;
+  w /= p.nhgk;
+  const int kb = w % p.nkb;
+  w /= p.nkb;
+  const int r = w % p.R;
+  const int b = w / p.R;
+  const int hl = wave >> 1, kh = wave & 1;
+  const int head = hg * p.HGk + hl;
+  const bool head_ok = head < p.heads;
+  const int ch0 = head * D;
+  const int64_t img = (int64_t)b * p.H * p.W * p.C;
+  const int64_t imgrow = (int64_t)b * p.H * p.W;
+  T* Qt = reinterpret_cast<T*>(smem_raw) + hl * 2 * D * LDT;  // Q^T of the current query tile
+  T* dOt = Qt + D * LDT;                                       // dO^T
+
+  // the wave's 32 keys: key tile kt2 column col is key kb*64 + kh*32 + kt2*16 + col
+  const int rcorner = corner_of(p, r);
+  op8 kB[2], vB[2];
+  int ktok[2];
+  bool kval[2];
+#pragma unroll
+  for (int kt2 = 0; kt2 < 2; ++kt2) {
+    const int key = kb * 64 + kh * 32 + kt2 * 16 + col;
+    kval[kt2] = head_ok && key < p.n;
+    int tx;
+    const int ty = fdiv(key < p.n ? key : 0, p.div_sw, &tx);
+    ktok[kt2] = rcorner + ty * p.W + tx;
+    const int off = ktok[kt2] * p.C + ch0 + 8 * g;
+    kB[kt2] = kval[kt2] ? TT::load8(static_cast<const T*>(p.K) + img + off) : TT::zero();
+    vB[kt2] = kval[kt2] ? TT::load8(static_cast<const T*>(p.V) + img + off) : TT::zero();
+  }
+  floatx4 dv[2][2], dk[2][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+      dv[ct][kt2] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dk[ct][kt2] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  const int cnt = p.inv_cnt[b * p.R + r];
+  const int* list = p.inv_list + ((int64_t)b * p.R + r) * p.R;
+  const int ntiles = (p.n + 15) >> 4;
+  const T* Qg = static_cast<const T*>(p.Q) + img;
+  const T* dOg = static_cast<const T*>(p.dO) + img;
+  const int vrow = 8 * (col >> 2) + (col & 3);
+  for (int e = 0; e < cnt; ++e) {
+    const int qi_region = list[e];
+    const int qcorner = corner_of(p, qi_region);
+    for (int t = 0; t < ntiles; ++t) {
+      // transposed Q (key half 0) and dO (key half 1) tiles of this head:
+      // item f = (query pair f / CVH, channel vector f % CVH)
+      {
+        const T* src = kh == 0 ? Qg : dOg;
+        T* dst = kh == 0 ? Qt : dOt;
+        for (int f = lane; f < 8 * CVH; f += 64) {
+          const int cv = f % CVH, qp = f / CVH;
+          uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = va;
+          const int qa = t * 16 + 2 * qp;
+          if (head_ok && qa < p.n) {
+            int x;
+            const int y = fdiv(qa, p.div_sw, &x);
+            va = *reinterpret_cast<const uint4*>(src + (qcorner + y * p.W + x) * p.C + ch0 + cv * VEC);
+          }
+          if (head_ok && qa + 1 < p.n) {
+            int x;
+            const int y = fdiv(qa + 1, p.div_sw, &x);
+            vb = *reinterpret_cast<const uint4*>(src + (qcorner + y * p.W + x) * p.C + ch0 + cv * VEC);
+          }
+          store_vt_pair(dst, LDT, cv * VEC, 2 * qp, va, vb);
+        }
+      }
+      // A operands of S = Q K^T and dP = dO V^T: row = query col
+      const int qa = t * 16 + col;
+      op8 qA = TT::zero(), dA = TT::zero();
+      if (head_ok && qa < p.n) {
+        int x;
+        const int y = fdiv(qa, p.div_sw, &x);
+        const int off = (qcorner + y * p.W + x) * p.C + ch0 + 8 * g;
+        qA = TT::load8(Qg + off);
+        dA = TT::load8(dOg + off);
+      }
+      // log-sum-exp and D of the lane's 4 queries (rows 4g..4g+3)
+      float lq[4], dq4[4];
+      bool qv[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int q = t * 16 + 4 * g + ii;
+        qv[ii] = head_ok && q < p.n;
+        lq[ii] = 0.f;
+        dq4[ii] = 0.f;
+        if (qv[ii]) {
+          int x;
+          const int y = fdiv(q, p.div_sw, &x);
+          const int64_t at = (imgrow + qcorner + y * p.W + x) * p.heads + head;
+          lq[ii] = p.lse[at];
+          dq4[ii] = p.dd[at];
+        }
+      }
+      __syncthreads();  // transposed tiles written
+      op4 pB[2], zB[2];
+#pragma unroll
+      for (int kt2 = 0; kt2 < 2; ++kt2) {
+        const floatx4 s = TT::mma(qA, kB[kt2], floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 dpv = TT::mma(dA, vB[kt2], floatx4{0.f, 0.f, 0.f, 0.f});
+        float pr[4], dz[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          pr[ii] = qv[ii] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[ii], p.c, -lq[ii])) : 0.f;
+          dz[ii] = pr[ii] * (dpv[ii] - dq4[ii]);
+        }
+        pB[kt2] = TT::from_f32_4(pr);
+        zB[kt2] = TT::from_f32_4(dz);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int row = vrow + 4 * ct;  // channel of A row col
+        const op4 dOA = TT::load4(dOt + row * LDT + 4 * g);
+        const op4 QA = TT::load4(Qt + row * LDT + 4 * g);
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) {
+          dv[ct][kt2] = TT::mma16(dOA, pB[kt2], dv[ct][kt2]);
+          dk[ct][kt2] = TT::mma16(QA, zB[kt2], dk[ct][kt2]);
+        }
+      }
+      __syncthreads();  // tiles consumed before the next query tile
+    }
+  }
+
+  T* dKg = static_cast<T*>(p.dK) + img;
+  T* dVg = static_cast<T*>(p.dV) + img;
+#pragma unroll
+  for (int kt2 = 0; kt2 < 2; ++kt2) {
+    if (!kval[kt2]) continue;
+    float ov[8], ok[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ov[e] = dv[0][kt2][e];
+      ov[4 + e] = dv[1][kt2][e];
+      ok[e] = dk[0][kt2][e] * p.scale;
+      ok[4 + e] = dk[1][kt2][e] * p.scale;
+    }
+    const int off = ktok[kt2] * p.C + ch0 + 8 * g;
+    TT::store8(dVg + off, ov);
+    TT::store8(dKg + off, ok);
+  }
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t backward_workspace_bytes(const Shape& s) {
+  const size_t tok = (size_t)s.B * s.H * s.W * s.heads;
+  const size_t reg = (size_t)s.B * s.R;
+  return 2 * align256(4 * tok) + 2 * align256(4 * reg) + align256(4 * reg * s.R);
+}
+
+hipError_t launch_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                           const int32_t* idx, void* dQ, void* dK, void* dV, void* ws, const Shape& s, int dtype,
+                           hipStream_t stream) {
+  BwdParams p{};
+  p.Q = Q; p.K = K; p.V = V; p.O = O; p.dO = dO; p.idx = idx;
+  p.dQ = dQ; p.dK = dK; p.dV = dV;
+  char* w = static_cast<char*>(ws);
+  const size_t tok = (size_t)s.B * s.H * s.W * s.heads;
+  const size_t reg = (size_t)s.B * s.R;
+  p.lse = reinterpret_cast<float*>(w);
+  w += align256(4 * tok);
+  p.dd = reinterpret_cast<float*>(w);
+  w += align256(4 * tok);
+  p.inv_cnt = reinterpret_cast<int*>(w);
+  w += align256(4 * reg);
+  p.bad = reinterpret_cast<int*>(w);
+  w += align256(4 * reg);
+  p.inv_list = reinterpret_cast<int*>(w);
+  p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S; p.topk = s.topk;
+  p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R; p.kv = s.kv; p.heads = s.heads;
+  p.scale = 1.0f / sqrtf((float)s.d);
+  p.c = p.scale * 1.4426950408889634f;
+  p.div_n = make_fastdiv(s.n);
+  p.div_sw = make_fastdiv(s.sw);
+  p.div_S = make_fastdiv(s.S);
+  // dq kernel: query blocks of 64, one wave per (head, tile), <= 8 waves
+  p.nqb = (s.n + 63) / 64;
+  p.ntq = (min(s.n, 64) + 15) / 16;
+  int HG = 1;
+  while (2 * HG * p.ntq <= 8 && 2 * HG <= s.heads) HG *= 2;
+  p.HG = HG;
+  p.nhg = (s.heads + HG - 1) / HG;
+  const int64_t nq = (int64_t)s.B * s.R * p.nqb * p.nhg;
+  // dkv kernel: key blocks of 64, two waves per head, <= 8 waves
+  p.nkb = (s.n + 63) / 64;
+  int HGk = 1;
+  while (2 * HGk <= 4 && 2 * HGk <= s.heads) HGk *= 2;
+  p.HGk = HGk;
+  p.nhgk = (s.heads + HGk - 1) / HGk;
+  const int64_t nk = (int64_t)s.B * s.R * p.nkb * p.nhgk;
+  if (nq >= (int64_t(1) << 31) || nk >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  p.nitems_q = (int)nq;
+  p.nitems_kv = (int)nk;
+  const size_t esz = dtype == kBF16 ? 2 : 4;
+  const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
+
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel((const void*)&bwd_routes_kernel, dim3(s.B), dim3(256), args, 0, stream);
+  if (e != hipSuccess) return e;
+
+  const bool multi = s.kv > KC, ragged = s.kv % KC != 0;
+  const void* fq;
+  if (dtype == kBF16)
+    fq = multi ? (ragged ? (const void*)&bwd_dq_kernel<__bf16, true, true> : (const void*)&bwd_dq_kernel<__bf16, true, false>)
+               : (ragged ? (const void*)&bwd_dq_kernel<__bf16, false, true> : (const void*)&bwd_dq_kernel<__bf16, false, false>);
+  else
+    fq = multi ? (ragged ? (const void*)&bwd_dq_kernel<float, true, true> : (const void*)&bwd_dq_kernel<float, true, false>)
+               : (ragged ? (const void*)&bwd_dq_kernel<float, false, true> : (const void*)&bwd_dq_kernel<float, false, false>);
+  const size_t ldsq = esz * (size_t)HG * D * (KC + padv);
+  e = hipLaunchKernel(fq, dim3((unsigned)p.nitems_q), dim3(HG * p.ntq * 64), args, ldsq, stream);
+  if (e != hipSuccess) return e;
+
+  const void* fk = dtype == kBF16 ? (const void*)&bwd_dkv_kernel<__bf16> : (const void*)&bwd_dkv_kernel<float>;
+  const int ldt = 16 + (dtype == kBF16 ? 8 : 4);
+  const size_t ldsk = esz * (size_t)HGk * 2 * D * ldt;
+  return hipLaunchKernel(fk, dim3((unsigned)p.nitems_kv), dim3(HGk * 2 * 64), args, ldsk, stream);
+}
+
+}  // namespace bra

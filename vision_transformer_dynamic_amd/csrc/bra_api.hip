@@ -214,3 +214,40 @@ bra_status bra_forward_lce(const void* Q, const void* K, const void* V,
 }
 
 }  // extern "C"
+
+extern "C" {
+
+size_t bra_backward_workspace_bytes(int B, int H, int W, int C, int heads, int S, int topk) {
+  Shape s;
+  if (heads <= 0 || check_shape(B, H, W, C, heads, S, topk, bra::kBF16, &s) != BRA_OK) return 0;
+  return bra::backward_workspace_bytes(s);
+}
+
+bra_status bra_attend_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                               const int32_t* idx, void* dQ, void* dK, void* dV,
+                               int B, int H, int W, int C, int heads, int S, int topk,
+                               bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, heads, S, topk, (int)dtype, &s);
+  if (st != BRA_OK) return st;
+  const void* ins[] = {Q, K, V, O, dO};
+  void* outs[] = {dQ, dK, dV};
+  for (const void* t : ins)
+    if (bad_tensor(t)) return BRA_EINVAL;
+  for (void* t : outs) {
+    if (bad_tensor(t)) return BRA_EINVAL;
+    for (const void* u : ins)
+      if (t == u) return BRA_EINVAL;
+  }
+  if (dQ == dK || dQ == dV || dK == dV) return BRA_EINVAL;
+  if (idx == nullptr || !aligned(idx, 4)) return BRA_EINVAL;
+  Workspace ws;
+  st = ws.acquire(workspace, workspace_bytes, bra::backward_workspace_bytes(s), stream);
+  if (st != BRA_OK) return st;
+  if (bra::launch_backward(Q, K, V, O, dO, idx, dQ, dK, dV, ws.ptr, s, (int)dtype, stream) != hipSuccess)
+    return BRA_EHIP;
+  return BRA_OK;
+}
+
+}  // extern "C"

@@ -74,4 +74,11 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
 hipError_t launch_lce(const void* V, const void* lce_w, const void* lce_b, void* O,
                       const Shape& s, int dtype, hipStream_t stream);
 
+// Backward of the token attention, routing table idx held fixed: dQ, dK, dV
+// from dO (and the forward output O). ws holds backward_workspace_bytes(s).
+size_t backward_workspace_bytes(const Shape& s);
+hipError_t launch_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                           const int32_t* idx, void* dQ, void* dK, void* dV, void* ws, const Shape& s, int dtype,
+                           hipStream_t stream);
+
 }  // namespace bra
