@@ -22,7 +22,8 @@
 //     query, written for kernel 3. Several 64-key chunks take two passes
 //     (log-sum-exp first).
 //  3. bwd_dkv_kernel: one wave per (head, 32 keys of one key region), looping
-//     over the query regions of the inverse table: S = Q K^T and dP = dO V^T
+//     over the queries of the inverse table's regions, staged 64 at a time
+//     in LDS (small regions share a tile): S = Q K^T and dP = dO V^T
 //     put each lane on one key with 4 queries, exactly the contraction slots
 //     of the 16-deep products dV^T += dO^T P and dK^T += Q^T dZ (dO^T, Q^T
 //     through LDS), so P and dZ never leave registers.
@@ -70,48 +71,34 @@ __device__ inline int xcd_remap() {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Inverse routing table, one workgroup per image.
+// 1. Inverse routing table, one workgroup per image. Each routing row becomes
+// a bit mask of its regions in LDS (bitwise OR is order-free); thread r then
+// walks the rows in order and appends every good row whose mask holds r, so
+// each list comes out ascending with one LDS read per row.
 __global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
-  __shared__ int cnt[kMaxRegions];
+  __shared__ uint32_t mask[kMaxRegions][kMaxRegions / 32];
   __shared__ int rowbad[kMaxRegions];
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int32_t* idx = p.idx + (int64_t)b * p.R * p.topk;
-  for (int r = tid; r < p.R; r += 256) {
-    cnt[r] = 0;
-    rowbad[r] = 0;
+  const int R = p.R, k = p.topk;
+  const int32_t* idx = p.idx + (int64_t)b * R * k;
+  for (int e = tid; e < R * (kMaxRegions / 32); e += 256) mask[e / (kMaxRegions / 32)][e % (kMaxRegions / 32)] = 0u;
+  for (int i = tid; i < R; i += 256) rowbad[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < R * k; e += 256) {
+    const int i = e / k, r = idx[e];
+    if (r < 0 || r >= R)
+      rowbad[i] = 1;
+    else
+      atomicOr(&mask[i][r >> 5], 1u << (r & 31));
   }
   __syncthreads();
-  const int nent = p.R * p.topk;
-  for (int e = tid; e < nent; e += 256) {
-    const int r = idx[e];
-    if (r < 0 || r >= p.R) rowbad[e / p.topk] = 1;
-  }
-  __syncthreads();
-  int* list = p.inv_list + (int64_t)b * p.R * p.R;
-  for (int e = tid; e < nent; e += 256) {
-    const int i = e / p.topk;
-    const int r = idx[e];
-    if (!rowbad[i]) {
-      const int slot = atomicAdd(&cnt[r], 1);
-      if (slot < p.R) list[r * p.R + slot] = i;  // a row repeating r cannot overflow the list
-    }
-  }
-  __syncthreads();
-  for (int r = tid; r < p.R; r += 256) {
-    const int m = min(cnt[r], p.R);
-    int* L = list + r * p.R;
-    // ascending order, whatever order the slots were taken in
-    for (int a = 1; a < m; ++a) {
-      const int v = L[a];
-      int j = a - 1;
-      while (j >= 0 && L[j] > v) {
-        L[j + 1] = L[j];
-        --j;
-      }
-      L[j + 1] = v;
-    }
-    p.inv_cnt[b * p.R + r] = m;
-    p.bad[b * p.R + r] = rowbad[r];
+  if (tid < R) {
+    int* L = p.inv_list + ((int64_t)b * R + tid) * R;
+    int m = 0;
+    for (int i = 0; i < R; ++i)
+      if (!rowbad[i] && ((mask[i][tid >> 5] >> (tid & 31)) & 1u)) L[m++] = i;
+    p.inv_cnt[b * R + tid] = m;
+    p.bad[b * R + tid] = rowbad[tid];
   }
 }
 
@@ -370,7 +357,82 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // 3. dK, dV. Workgroup = (image b, key region r, block of <= 64 of its keys,
-// group of HGk heads); wave w = (head w / 2, key half w % 2: 32 keys).
+// group of HGk heads); wave = (head, key half of 32 keys).
+// The queries of the key region's incoming query regions (inverse table, in
+// order) form one flat sequence of slots, taken 64 at a time ("stages"):
+// each stage's Q and dO rows go to LDS twice, as rows (A operands of
+// S = Q K^T and dP = dO V^T) and transposed (A operands of dV^T += dO^T P and
+// dK^T += Q^T dZ), with the slots' log-sum-exp and D, all loads of a stage in
+// flight together; the next stage's loads are issued before the current one
+// is computed. Small regions share a 16-query tile.
+constexpr int kStage = 64;  // query slots per stage
+
+// slot s -> token of the query (inside the image), or -1 past the last slot
+__device__ __forceinline__ int slot_token(int s, int nslots, const int* corners, FastDiv div_n, FastDiv div_sw,
+                                          int W) {
+  if (s >= nslots) return -1;
+  int qi, qx;
+  const int e = fdiv(s, div_n, &qi);
+  const int qy = fdiv(qi, div_sw, &qx);
+  return corners[e] + qy * W + qx;
+}
+
+// Per-lane share of one stage's loads: NI (slot pair, channel vector, tensor)
+// items of two 16-byte vectors, plus one log-sum-exp or D value.
+template <int NI>
+struct StageRegs {
+  uint4 a[NI], b[NI];
+  float v;
+};
+
+template <typename T, int NI>
+__device__ __forceinline__ void stage_load(const BwdParams& p, int s0, int nslots, const int* corners, bool head_ok,
+                                           int lt, int ch0, int64_t img, int64_t imgrow, int head,
+                                           StageRegs<NI>& R) {
+  constexpr int VEC = Tr<T>::VEC;
+  constexpr int CVH = D / VEC;
+  const T* Qg = static_cast<const T*>(p.Q) + img;
+  const T* dOg = static_cast<const T*>(p.dO) + img;
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int f = lt + 128 * m;  // < 2 * (kStage / 2) * CVH
+    const int cv = f % CVH, rest = f / CVH;
+    const int qp = rest % (kStage / 2), tensor = rest / (kStage / 2);
+    const T* src = tensor == 0 ? Qg : dOg;
+    R.a[m] = make_uint4(0u, 0u, 0u, 0u);
+    R.b[m] = R.a[m];
+    const int ta = slot_token(s0 + 2 * qp, nslots, corners, p.div_n, p.div_sw, p.W);
+    const int tb = slot_token(s0 + 2 * qp + 1, nslots, corners, p.div_n, p.div_sw, p.W);
+    if (head_ok && ta >= 0) R.a[m] = *reinterpret_cast<const uint4*>(src + ta * p.C + ch0 + cv * VEC);
+    if (head_ok && tb >= 0) R.b[m] = *reinterpret_cast<const uint4*>(src + tb * p.C + ch0 + cv * VEC);
+  }
+  // lanes 0..63: log-sum-exp of slot s0 + lt; lanes 64..127: D of slot s0 + lt - 64
+  const int sl = lt & 63;
+  const int tr = slot_token(s0 + sl, nslots, corners, p.div_n, p.div_sw, p.W);
+  R.v = lt < 64 ? INFINITY : 0.f;  // past the last slot: P = 0 and dZ = 0
+  if (head_ok && tr >= 0) R.v = (lt < 64 ? p.lse : p.dd)[(imgrow + tr) * p.heads + head];
+}
+
+template <typename T, int NI>
+__device__ __forceinline__ void stage_store(T* Qn, T* dOn, T* Qt, T* dOt, float* lse, float* dd, int lt,
+                                            const StageRegs<NI>& R) {
+  constexpr int VEC = Tr<T>::VEC;
+  constexpr int CVH = D / VEC;
+  constexpr int LDN = D + 16 / (int)sizeof(T);  // row tiles: one 16-byte pad per row
+  constexpr int LDT = kStage + 16 / (int)sizeof(T);
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int f = lt + 128 * m;
+    const int cv = f % CVH, rest = f / CVH;
+    const int qp = rest % (kStage / 2), tensor = rest / (kStage / 2);
+    T* rows = tensor == 0 ? Qn : dOn;
+    *reinterpret_cast<uint4*>(rows + (2 * qp) * LDN + cv * VEC) = R.a[m];
+    *reinterpret_cast<uint4*>(rows + (2 * qp + 1) * LDN + cv * VEC) = R.b[m];
+    store_vt_pair(tensor == 0 ? Qt : dOt, LDT, cv * VEC, 2 * qp, R.a[m], R.b[m]);
+  }
+  (lt < 64 ? lse : dd)[lt & 63] = R.v;
+}
+
 template <typename T>
 __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   typedef Tr<T> TT;
@@ -378,8 +440,12 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   typedef typename TT::op4 op4;
   constexpr int VEC = TT::VEC;
   constexpr int CVH = D / VEC;
-  constexpr int LDT = 16 + (sizeof(T) == 2 ? 8 : 4);  // transposed query tiles: row = channel
+  constexpr int NI = 2 * (kStage / 2) * CVH / 128;  // stage items per lane (2 bf16, 4 fp32)
+  constexpr int LDN = D + 16 / (int)sizeof(T);
+  constexpr int LDT = kStage + 16 / (int)sizeof(T);
+  constexpr int HEAD_ELEMS = 2 * kStage * LDN + 2 * D * LDT;  // Qn, dOn, Qt, dOt
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int corners[kMaxRegions];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -394,13 +460,24 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   const int r = w % p.R;
   const int b = w / p.R;
   const int hl = wave >> 1, kh = wave & 1;
+  const int lt = kh * 64 + lane;  // lane within the head's two waves
   const int head = hg * p.HGk + hl;
   const bool head_ok = head < p.heads;
   const int ch0 = head * D;
   const int64_t img = (int64_t)b * p.H * p.W * p.C;
   const int64_t imgrow = (int64_t)b * p.H * p.W;
-  T* Qt = reinterpret_cast<T*>(smem_raw) + hl * 2 * D * LDT;  // Q^T of the current query tile
-  T* dOt = Qt + D * LDT;                                       // dO^T
+  T* Qn = reinterpret_cast<T*>(smem_raw) + hl * HEAD_ELEMS;
+  T* dOn = Qn + kStage * LDN;
+  T* Qt = dOn + kStage * LDN;
+  T* dOt = Qt + D * LDT;
+  float* lse = reinterpret_cast<float*>(reinterpret_cast<T*>(smem_raw) + p.HGk * HEAD_ELEMS) + hl * 2 * kStage;
+  float* dd = lse + kStage;
+
+  const int cnt = p.inv_cnt[b * p.R + r];
+  const int* list = p.inv_list + ((int64_t)b * p.R + r) * p.R;
+  for (int e = tid; e < cnt; e += blockDim.x) corners[e] = corner_of(p, list[e]);
+  const int nslots = cnt * p.n;
+  const int nstages = (nslots + kStage - 1) / kStage;
 
   // the wave's 32 keys: key tile kt2 column col is key kb*64 + kh*32 + kt2*16 + col
   const int rcorner = corner_of(p, r);
@@ -418,6 +495,9 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
     kB[kt2] = kval[kt2] ? TT::load8(static_cast<const T*>(p.K) + img + off) : TT::zero();
     vB[kt2] = kval[kt2] ? TT::load8(static_cast<const T*>(p.V) + img + off) : TT::zero();
   }
+  // key tiles with no key of the region skip their products (uniform per wave)
+  const bool kt_live0 = kb * 64 + kh * 32 < p.n;
+  const bool kt_live1 = kb * 64 + kh * 32 + 16 < p.n;
   floatx4 dv[2][2], dk[2][2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -426,94 +506,55 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
       dv[ct][kt2] = floatx4{0.f, 0.f, 0.f, 0.f};
       dk[ct][kt2] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+  __syncthreads();  // corners
 
-  const int cnt = p.inv_cnt[b * p.R + r];
-  const int* list = p.inv_list + ((int64_t)b * p.R + r) * p.R;
-  const int ntiles = (p.n + 15) >> 4;
-  const T* Qg = static_cast<const T*>(p.Q) + img;
-  const T* dOg = static_cast<const T*>(p.dO) + img;
   const int vrow = 8 * (col >> 2) + (col & 3);
-  for (int e = 0; e < cnt; ++e) {
-    const int qi_region = list[e];
-    const int qcorner = corner_of(p, qi_region);
-    for (int t = 0; t < ntiles; ++t) {
-      // transposed Q (key half 0) and dO (key half 1) tiles of this head:
-      // item f = (query pair f / CVH, channel vector f % CVH)
-      {
-        const T* src = kh == 0 ? Qg : dOg;
-        T* dst = kh == 0 ? Qt : dOt;
-        for (int f = lane; f < 8 * CVH; f += 64) {
-          const int cv = f % CVH, qp = f / CVH;
-          uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = va;
-          const int qa = t * 16 + 2 * qp;
-          if (head_ok && qa < p.n) {
-            int x;
-            const int y = fdiv(qa, p.div_sw, &x);
-            va = *reinterpret_cast<const uint4*>(src + (qcorner + y * p.W + x) * p.C + ch0 + cv * VEC);
-          }
-          if (head_ok && qa + 1 < p.n) {
-            int x;
-            const int y = fdiv(qa + 1, p.div_sw, &x);
-            vb = *reinterpret_cast<const uint4*>(src + (qcorner + y * p.W + x) * p.C + ch0 + cv * VEC);
-          }
-          store_vt_pair(dst, LDT, cv * VEC, 2 * qp, va, vb);
-        }
-      }
-      // A operands of S = Q K^T and dP = dO V^T: row = query col
-      const int qa = t * 16 + col;
-      op8 qA = TT::zero(), dA = TT::zero();
-      if (head_ok && qa < p.n) {
-        int x;
-        const int y = fdiv(qa, p.div_sw, &x);
-        const int off = (qcorner + y * p.W + x) * p.C + ch0 + 8 * g;
-        qA = TT::load8(Qg + off);
-        dA = TT::load8(dOg + off);
-      }
-      // log-sum-exp and D of the lane's 4 queries (rows 4g..4g+3)
-      float lq[4], dq4[4];
-      bool qv[4];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int q = t * 16 + 4 * g + ii;
-        qv[ii] = head_ok && q < p.n;
-        lq[ii] = 0.f;
-        dq4[ii] = 0.f;
-        if (qv[ii]) {
-          int x;
-          const int y = fdiv(q, p.div_sw, &x);
-          const int64_t at = (imgrow + qcorner + y * p.W + x) * p.heads + head;
-          lq[ii] = p.lse[at];
-          dq4[ii] = p.dd[at];
-        }
-      }
-      __syncthreads();  // transposed tiles written
-      op4 pB[2], zB[2];
-#pragma unroll
-      for (int kt2 = 0; kt2 < 2; ++kt2) {
-        const floatx4 s = TT::mma(qA, kB[kt2], floatx4{0.f, 0.f, 0.f, 0.f});
-        const floatx4 dpv = TT::mma(dA, vB[kt2], floatx4{0.f, 0.f, 0.f, 0.f});
-        float pr[4], dz[4];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          pr[ii] = qv[ii] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[ii], p.c, -lq[ii])) : 0.f;
-          dz[ii] = pr[ii] * (dpv[ii] - dq4[ii]);
-        }
-        pB[kt2] = TT::from_f32_4(pr);
-        zB[kt2] = TT::from_f32_4(dz);
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int row = vrow + 4 * ct;  // channel of A row col
-        const op4 dOA = TT::load4(dOt + row * LDT + 4 * g);
-        const op4 QA = TT::load4(Qt + row * LDT + 4 * g);
+  StageRegs<NI> st;
+  if (nstages > 0) stage_load<T, NI>(p, 0, nslots, corners, head_ok, lt, ch0, img, imgrow, head, st);
+  for (int sg = 0; sg < nstages; ++sg) {
+    stage_store<T, NI>(Qn, dOn, Qt, dOt, lse, dd, lt, st);
+    __syncthreads();  // stage in LDS
+    if (sg + 1 < nstages)
+      stage_load<T, NI>(p, (sg + 1) * kStage, nslots, corners, head_ok, lt, ch0, img, imgrow, head, st);
+    const int tiles = min(4, (nslots - sg * kStage + 15) >> 4);
+    if (kt_live0) {
+      for (int t = 0; t < tiles; ++t) {
+        const op8 qA = TT::load8(Qn + (t * 16 + col) * LDN + 8 * g);
+        const op8 dA = TT::load8(dOn + (t * 16 + col) * LDN + 8 * g);
+        const float4 lq = *reinterpret_cast<const float4*>(lse + t * 16 + 4 * g);
+        const float4 dq4 = *reinterpret_cast<const float4*>(dd + t * 16 + 4 * g);
+        const float lqa[4] = {lq.x, lq.y, lq.z, lq.w};
+        const float dqa[4] = {dq4.x, dq4.y, dq4.z, dq4.w};
+        op4 pB[2], zB[2];
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2) {
-          dv[ct][kt2] = TT::mma16(dOA, pB[kt2], dv[ct][kt2]);
-          dk[ct][kt2] = TT::mma16(QA, zB[kt2], dk[ct][kt2]);
+          if (kt2 == 1 && !kt_live1) continue;
+          const floatx4 sc = TT::mma(qA, kB[kt2], floatx4{0.f, 0.f, 0.f, 0.f});
+          const floatx4 dpv = TT::mma(dA, vB[kt2], floatx4{0.f, 0.f, 0.f, 0.f});
+          float pr[4], dz[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            pr[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[ii], p.c, -lqa[ii]));
+            dz[ii] = pr[ii] * (dpv[ii] - dqa[ii]);
+          }
+          pB[kt2] = TT::from_f32_4(pr);
+          zB[kt2] = TT::from_f32_4(dz);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const int row = vrow + 4 * ct;  // channel of A row col
+          const op4 dOA = TT::load4(dOt + row * LDT + t * 16 + 4 * g);
+          const op4 QA = TT::load4(Qt + row * LDT + t * 16 + 4 * g);
+#pragma unroll
+          for (int kt2 = 0; kt2 < 2; ++kt2) {
+            if (kt2 == 1 && !kt_live1) continue;
+            dv[ct][kt2] = TT::mma16(dOA, pB[kt2], dv[ct][kt2]);
+            dk[ct][kt2] = TT::mma16(QA, zB[kt2], dk[ct][kt2]);
+          }
         }
       }
-      __syncthreads();  // tiles consumed before the next query tile
     }
+    __syncthreads();  // stage consumed before the next one is stored
   }
 
   T* dKg = static_cast<T*>(p.dK) + img;
@@ -578,10 +619,9 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   p.HG = HG;
   p.nhg = (s.heads + HG - 1) / HG;
   const int64_t nq = (int64_t)s.B * s.R * p.nqb * p.nhg;
-  // dkv kernel: key blocks of 64, two waves per head, <= 8 waves
+  // dkv kernel: key blocks of 64, two waves per head, up to 2 heads
   p.nkb = (s.n + 63) / 64;
-  int HGk = 1;
-  while (2 * HGk <= 4 && 2 * HGk <= s.heads) HGk *= 2;
+  const int HGk = s.heads >= 2 ? 2 : 1;
   p.HGk = HGk;
   p.nhgk = (s.heads + HGk - 1) / HGk;
   const int64_t nk = (int64_t)s.B * s.R * p.nkb * p.nhgk;
@@ -608,8 +648,11 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   if (e != hipSuccess) return e;
 
   const void* fk = dtype == kBF16 ? (const void*)&bwd_dkv_kernel<__bf16> : (const void*)&bwd_dkv_kernel<float>;
-  const int ldt = 16 + (dtype == kBF16 ? 8 : 4);
-  const size_t ldsk = esz * (size_t)HGk * 2 * D * ldt;
+  // per head: Q and dO stage rows [64][32 + pad] and transposed [32][64 + pad],
+  // then the stage's log-sum-exp and D
+  const size_t pad = 16 / esz;
+  const size_t head_elems = 2 * 64 * (D + pad) + 2 * D * (64 + pad);
+  const size_t ldsk = esz * HGk * head_elems + sizeof(float) * HGk * 2 * 64;
   return hipLaunchKernel(fk, dim3((unsigned)p.nitems_kv), dim3(HGk * 2 * 64), args, ldsk, stream);
 }
 
