@@ -12,7 +12,9 @@ roofline of the dominant kernel (fused gather + attention) from HIP events on
 the stream it runs on, and the CPU oracle timed on a bounded sample. The
 ``with_lce`` object times the module output with the local context term
 (5x5 depthwise convolution of V, seeded synthetic filter) the same way; it is
-a side measurement, not the headline value.
+a side measurement, not the headline value. The ``train`` object times a
+training step of the same operator the same way: routing, attention and the
+backward pass (dQ, dK, dV for a seeded output gradient, routing held fixed).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -37,7 +39,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 F32_PEAK_TFLOPS = 157.3     # MI355X dense fp32 matrix, published
 CACHE_DEFEAT_BYTES = 640 << 20  # rotate input copies over more than the 256 MB MALL
-ATTEND_SOURCES = ["attend.hip"]
+ATTEND_SOURCES = ["attend.hip", "attn_common.h", "lce_tile.h", "bra_internal.h"]  # what the attention kernels are built from
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "attend_stage1_b64_56x56_pmc.md")
 
 
@@ -51,6 +53,7 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle sample budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lce", action="store_true", help="skip the side measurement with the local context term")
+    ap.add_argument("--no-train", action="store_true", help="skip the side measurement of the training step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     return ap.parse_args(argv)
@@ -93,7 +96,7 @@ def calibrate_copy(mib: int) -> None:
 class Step:
     """Pre-bound C-ABI calls for one input copy (no per-call allocation)."""
 
-    def __init__(self, w, q, k, v, lce_w=None, lce_b=None):
+    def __init__(self, w, q, k, v, lce_w=None, lce_b=None, grad=None):
         import torch
         import vision_transformer_dynamic_amd as bra
 
@@ -101,6 +104,9 @@ class Step:
         self.w = w
         self.q, self.k, self.v = q, k, v
         self.lce_w, self.lce_b = lce_w, lce_b
+        self.grad = grad
+        self.grads = None
+        self.bws = None
         self.out = torch.empty_like(q)
         self.idx = torch.empty((w.B, w.R, w.topk), dtype=torch.int32, device=q.device)
         nbytes = bra.workspace_bytes(w.B, w.H, w.W, w.C, w.S, w.topk)
@@ -119,6 +125,22 @@ class Step:
     def step_lce(self):
         self.route()
         self.attend_lce()
+
+    def backward(self):
+        import torch
+
+        if self.grads is None:
+            w = self.w
+            self.grads = tuple(torch.empty_like(self.q) for _ in range(3))
+            n = self.bra.backward_workspace_bytes(w.B, w.H, w.W, w.C, w.heads, w.S, w.topk)
+            self.bws = torch.empty(n, dtype=torch.uint8, device=self.q.device)
+        self.bra.attend_backward(self.q, self.k, self.v, self.out, self.grad, self.idx, self.w.heads, self.w.S,
+                                 out=self.grads, workspace=self.bws)
+
+    def step_train(self):
+        self.route()
+        self.attend()
+        self.backward()
 
     def __call__(self):
         self.route()
@@ -198,7 +220,8 @@ def main(argv=None):
     nsets = args.sets or max(1, min(32, math.ceil(CACHE_DEFEAT_BYTES / set_bytes)))
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     lw, lb = (t.to(dev) for t in wl.make_lce_params(w))
-    steps = [Step(w, qd.clone(), kd.clone(), vd.clone(), lw, lb) for _ in range(nsets)]
+    gd = wl.make_grad_output(w).to(dev)
+    steps = [Step(w, qd.clone(), kd.clone(), vd.clone(), lw, lb, gd) for _ in range(nsets)]
     torch.cuda.synchronize()
 
     # eager warm-up of every copy (also the first-launch code loading)
@@ -273,6 +296,28 @@ def main(argv=None):
             s_()
         torch.cuda.synchronize()
 
+    train = None
+    if not args.no_train:
+        for s_ in steps:
+            s_.step_train()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            tr_cycle = capture([s_.step_train for s_ in steps])
+            tr_singles = [capture([s_.step_train]) for s_ in steps]
+            bw_cycle = capture([s_.backward for s_ in steps])
+            bw_singles = [capture([s_.backward]) for s_ in steps]
+        torch.cuda.synchronize()
+        train_us = phase_us(tr_cycle, tr_singles)
+        bw_us = phase_us(bw_cycle, bw_singles)
+        s0 = steps[0]
+        ref = bra.attend_backward(s0.q, s0.k, s0.v, s0.out, gd, s0.idx, w.heads, w.S)
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(ref, s0.grads)):
+            raise RuntimeError("benchmark gradients differ from bra_attend_backward")
+        train = {"value": round(w.tokens / (train_us * 1e-6), 1), "unit": "tokens/s",
+                 "us_per_step": round(train_us, 2), "backward_us": round(bw_us, 2),
+                 "step": "pool + route + attention + backward (dQ, dK, dV), routing held fixed"}
+
     # the timed steps computed the real thing: spot-check one copy
     ref = bra.forward(qd, kd, vd, w.heads, w.S, w.topk)
     torch.cuda.synchronize()
@@ -322,6 +367,8 @@ def main(argv=None):
     }
     if with_lce is not None:
         result["with_lce"] = with_lce
+    if train is not None:
+        result["train"] = train
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(result))
