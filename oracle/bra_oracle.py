@@ -73,6 +73,9 @@ Pins (tests/test_oracle_pins.py, all ``-m "not gpu"``):
                            autograd through SDPA in fp64 when every region
                            is routed, and the sum rules sum(dK) = 0 and
                            sum(dV) = sum(dO) per image and head;
+  qkv_project            : torch.nn.functional.linear in fp64, identity
+                           weight blocks (Q = X, K = 2X, V = 3X) that fix
+                           the chunk order, a bias-only projection;
   lce                    : torch conv2d with groups = C and scipy.ndimage
                            correlate (two library routines), single-tap
                            filters = shifted maps with zero fill (brute
@@ -378,3 +381,38 @@ def attend_backward(Q, K, V, routes, dO, heads: int, S: int, scale: float | None
                 dK[b, gy, gx, ch] += dkg
                 dV[b, gy, gx, ch] += dvg
     return dQ, dK, dV
+
+
+# --------------------------------------------------------------------------- #
+# The linear projection in front of the routing
+# --------------------------------------------------------------------------- #
+def qkv_project(X, Wqkv, bqkv=None):
+    """Q, K, V = linear_qkv(X).chunk(3, dim=-1).
+
+    [EXP] 2.2 step 2 (Q, K, V from linear projections) and pseudocode step 2;
+    [EXP] Part 3 counts it as the 3HWC^2 projection term. X: [B, H, W, C];
+    Wqkv: [3C, C], rows are output features (a torch Linear weight), so the
+    projection is X Wqkv^T; bqkv: [3C] or None. The output features are Q's
+    C channels, then K's, then V's. Returns (Q, K, V), each [B, H, W, C]
+    float64.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    Wqkv = np.asarray(Wqkv, dtype=np.float64)
+    C = X.shape[-1]
+    if Wqkv.shape != (3 * C, C):
+        raise ValueError(f"Wqkv must be [3C, C] = {(3 * C, C)}, got {Wqkv.shape}")
+    Y = np.matmul(X, Wqkv.T)
+    if bqkv is not None:
+        bqkv = np.asarray(bqkv, dtype=np.float64)
+        if bqkv.shape != (3 * C,):
+            raise ValueError(f"bqkv must be [3C] = {(3 * C,)}, got {bqkv.shape}")
+        Y = Y + bqkv
+    return Y[..., :C], Y[..., C:2 * C], Y[..., 2 * C:]
+
+
+def bra_from_x(X, Wqkv, bqkv, heads: int, S: int, topk: int, scale: float | None = None):
+    """Projection, routing and attention from the block input X: returns
+    (O, routes, (Q, K, V))."""
+    Q, K, V = qkv_project(X, Wqkv, bqkv)
+    O, routes = bra(Q, K, V, heads, S, topk, scale)
+    return O, routes, (Q, K, V)

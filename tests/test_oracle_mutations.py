@@ -20,6 +20,7 @@ _orig_mean = O.region_mean
 _orig_attend = O.attend
 _orig_lce = O.lce
 _orig_sab = O.softmax_attention_backward
+_orig_qkv = O.qkv_project
 
 
 def _transposed_affinity(Qr, Kr):
@@ -148,7 +149,24 @@ def _bwd_scatter_overwrites(Q, K, V, routes, dO, heads, S, scale=None):
     return dQ, dK, dV
 
 
+def _qkv_chunk_order_kqv(X, Wqkv, bqkv=None):
+    q, k, v = _orig_qkv(X, Wqkv, bqkv)
+    return k, q, v
+
+
+def _qkv_weight_read_column_major(X, Wqkv, bqkv=None):
+    W = np.asarray(Wqkv)
+    return _orig_qkv(X, W.reshape(W.shape[1], W.shape[0]).T, bqkv)
+
+
+def _qkv_dropped_bias(X, Wqkv, bqkv=None):
+    return _orig_qkv(X, Wqkv, None)
+
+
 MUTATIONS = {
+    "qkv_chunk_order": ("qkv_project", _qkv_chunk_order_kqv),
+    "qkv_weight_column_major": ("qkv_project", _qkv_weight_read_column_major),
+    "qkv_dropped_bias": ("qkv_project", _qkv_dropped_bias),
     "bwd_no_rowsum_term": ("softmax_attention_backward", _bwd_no_rowsum_term),
     "bwd_unscaled_dq": ("softmax_attention_backward", _bwd_unscaled_dq),
     "bwd_value_grad_unnormalised": ("softmax_attention_backward", _bwd_value_grad_from_logits),

@@ -413,3 +413,41 @@ def test_backward_sum_rules():
     np.testing.assert_allclose(dV.sum(axis=(1, 2)), G.sum(axis=(1, 2)), rtol=1e-10, atol=1e-10)
     z = O.attend_backward(Q, K, V, routes, np.zeros_like(G), heads, S)
     assert all(np.all(x == 0) for x in z)
+
+
+# --------------------------------------------------------------------------- #
+# Linear projection (explainer Part 2.2 step 2, pseudocode step 2)
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("B,H,W,C", [(2, 4, 6, 8), (1, 3, 3, 16)])
+def test_qkv_projection_equals_torch_linear(B, H, W, C):
+    X = _rand((B, H, W, C), 90)
+    Wq = _rand((3 * C, C), 91)
+    bq = _rand((3 * C,), 92)
+    ref = torch.nn.functional.linear(torch.from_numpy(X), torch.from_numpy(Wq), torch.from_numpy(bq)).numpy()
+    Q, K, V = O.qkv_project(X, Wq, bq)
+    np.testing.assert_allclose(np.concatenate([Q, K, V], axis=-1), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_qkv_identity_blocks_fix_the_chunk_order_and_bias():
+    B, H, W, C = 1, 4, 4, 8
+    X = _rand((B, H, W, C), 93)
+    eye = np.eye(C)
+    Q, K, V = O.qkv_project(X, np.concatenate([eye, 2 * eye, 3 * eye]))
+    np.testing.assert_array_equal(Q, X)
+    np.testing.assert_array_equal(K, 2 * X)
+    np.testing.assert_array_equal(V, 3 * X)
+    b = np.arange(3 * C, dtype=np.float64)
+    Q, K, V = O.qkv_project(X, np.zeros((3 * C, C)), b)
+    assert np.all(Q == b[:C]) and np.all(K == b[C:2 * C]) and np.all(V == b[2 * C:])
+    with pytest.raises(ValueError):
+        O.qkv_project(X, np.zeros((C, 3 * C)))
+
+
+def test_bra_from_x_composes_projection_and_bra():
+    B, H, W, C, heads, S, k = 1, 8, 8, 8, 2, 4, 2
+    X = _rand((B, H, W, C), 94)
+    Wq = _rand((3 * C, C), 95) / np.sqrt(C)
+    out, routes, (Q, K, V) = O.bra_from_x(X, Wq, None, heads, S, k)
+    ref, ref_routes = O.bra(X @ Wq[:C].T, X @ Wq[C:2 * C].T, X @ Wq[2 * C:].T, heads, S, k)
+    np.testing.assert_array_equal(routes, ref_routes)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)

@@ -26,6 +26,11 @@ filter is used.
 
 Output gradients for the backward pass (``make_grad_output``): a generator
 seeded with ``seed + 2000`` draws ``randn`` [B, H, W, C], cast to the dtype.
+
+Projection inputs (``make_projection``): a generator seeded with
+``seed + 3000`` draws the block input X as ``randn`` [B, H, W, C], the
+[3C, C] weight as ``randn / sqrt(C)`` (unit-variance outputs) and the [3C]
+bias as ``randn / 10``, all cast to the dtype.
 """
 
 from __future__ import annotations
@@ -146,6 +151,18 @@ def make_grad_output(w: Workload):
     gen.manual_seed(int(w.seed) + 2000)
     g = torch.randn((w.B, w.H, w.W, w.C), generator=gen, dtype=torch.float32)
     return g.to(w.torch_dtype).contiguous()
+
+
+def make_projection(w: Workload):
+    """Draw (X [B, H, W, C], Wqkv [3C, C], bqkv [3C]) on the CPU in the
+    workload's dtype."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(w.seed) + 3000)
+    x = torch.randn((w.B, w.H, w.W, w.C), generator=gen, dtype=torch.float32)
+    wq = torch.randn((3 * w.C, w.C), generator=gen, dtype=torch.float32) / float(w.C) ** 0.5
+    bq = torch.randn((3 * w.C,), generator=gen, dtype=torch.float32) / 10.0
+    dt = w.torch_dtype
+    return x.to(dt).contiguous(), wq.to(dt).contiguous(), bq.to(dt).contiguous()
 
 
 def to_f64(t: torch.Tensor):
