@@ -201,6 +201,40 @@ bra_status bra_attend_backward(const void* Q, const void* K, const void* V, cons
                                bra_dtype dtype, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/*
+ * The linear projection in front of the routing, with the region pooling
+ * fused into its epilogue (explainer Part 2.2 steps 2-3 and pseudocode steps
+ * 2-3; Part 3's 3HWC^2 projection term):
+ *
+ *   [Q | K | V] = X Wqkv^T + bqkv   (linear_qkv(x).chunk(3, dim=-1))
+ *
+ *   X      : [B, H, W, C] block input in `dtype`, 16-byte aligned.
+ *   Wqkv   : [3C][C] in `dtype` (a torch Linear weight: row = output
+ *            feature; Q's C features first, then K's, then V's), 16-byte
+ *            aligned. bqkv: [3C] in `dtype` or NULL.
+ *   Q, K, V: [B, H, W, C] outputs in `dtype`, 16-byte aligned, rounded once
+ *            from fp32 accumulation.
+ * Supported: C a multiple of 32, C <= 256 for bf16 and <= 128 for fp32
+ * (BRA_EUNSUPPORTED otherwise).
+ * Outputs may not overlap each other, X or the weights (BRA_EINVAL).
+ */
+
+/* bra_qkv_pool - Q, K, V and the region means Qr, Kr ([B, S*S, C] fp32,
+ * 4-byte aligned) of the ROUNDED Q and K, i.e. what bra_route pools from the
+ * stored Q and K (up to fp32 summation order), without reading them again. */
+bra_status bra_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, void* Q, void* K, void* V,
+                        float* Qr, float* Kr, int B, int H, int W, int C, int S,
+                        bra_dtype dtype, hipStream_t stream);
+
+/* bra_forward_qkv - the module from its input: bra_qkv_pool into Q, K, V
+ * (kept for the caller, e.g. for the backward) and the workspace's region
+ * means, routing from those means, then attention into O. Workspace and
+ * streams as bra_forward (bra_workspace_bytes bytes). */
+bra_status bra_forward_qkv(const void* X, const void* Wqkv, const void* bqkv, void* Q, void* K, void* V, void* O,
+                           int B, int H, int W, int C, int heads, int S, int topk,
+                           bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -120,3 +120,23 @@ def assert_grad_close(out: np.ndarray, ref: np.ndarray, dtype: str, what: str = 
         assert max_abs <= GRAD_BF16_REL * scale, f"{what}: bf16 max-abs {max_abs:.3e} > {GRAD_BF16_REL} * {scale:.2f}"
         assert mean_rel <= GRAD_BF16_MEAN_REL, f"{what}: bf16 mean-rel {mean_rel:.3e} > {GRAD_BF16_MEAN_REL}"
     return max_abs, mean_rel
+
+
+PROJ_F32_REL = 1e-4
+PROJ_BF16_ABS = 1e-3
+
+
+def assert_proj_close(out: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    """Parity bound for the projection outputs: one rounding of an fp32 sum of
+    exact products. fp32: max-abs <= 1e-4 * max(1, max|ref|); bf16:
+    |out - ref| <= 2^-8 |ref| + 1e-3 elementwise (the rounding, plus room for
+    the fp32 accumulation)."""
+    assert np.all(np.isfinite(out)), f"{what}: non-finite outputs"
+    max_abs, mean_rel = output_errors(out, ref)
+    if dtype == "f32":
+        scale = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
+        assert max_abs <= PROJ_F32_REL * scale, f"{what}: fp32 max-abs {max_abs:.3e}"
+    else:
+        excess = np.abs(out - ref) - (BF16_UNIT_ROUNDOFF * np.abs(ref) + PROJ_BF16_ABS)
+        assert float(excess.max()) <= 0, f"{what}: bf16 error exceeds 2^-8 |ref| + 1e-3 by {float(excess.max()):.3e}"
+    return max_abs, mean_rel

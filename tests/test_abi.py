@@ -160,6 +160,45 @@ def test_lce_filter_validation(lib, call, kwargs):
     assert call(lib, **kwargs) == EINVAL
 
 
+def _qkv(lib, B=1, H=16, W=16, C=32, S=4, dt=0, x=P, w=P2, b=0, q=P3, k=P4, v=PW, qr=PF, kr=PB):
+    return lib.bra_qkv_pool(x, w, b, q, k, v, qr, kr, B, H, W, C, S, dt, None)
+
+
+def _fqkv(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, x=P, w=P2, b=0, q=P3, kk=P4, v=PW, o=PF,
+          ws=0xC0000, wsb=1 << 20):
+    return lib.bra_forward_qkv(x, w, b, q, kk, v, o, B, H, W, C, heads, S, k, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("call", [_qkv, _fqkv])
+@pytest.mark.parametrize(
+    "kwargs,status",
+    [
+        (dict(C=40), EUNSUP),             # C not a multiple of 32
+        (dict(C=512, H=8, W=8, S=2), EUNSUP),  # C above the projection's limit
+        (dict(C=256, H=8, W=8, S=2), EUNSUP),  # fp32 above 128
+        (dict(x=0), EINVAL),
+        (dict(x=P + 8), EINVAL),          # misaligned input
+        (dict(w=P2 + 4), EINVAL),         # misaligned weight
+        (dict(b=PB + 2), EINVAL),         # misaligned fp32 bias
+        (dict(q=P), EINVAL),              # output aliases the input
+        (dict(q=P2), EINVAL),             # output overlaps the weight
+        (dict(S=5), EINVAL),
+        (dict(dt=3), EUNSUP),
+    ],
+)
+def test_projection_validation(lib, call, kwargs, status):
+    if call is _fqkv and "C" in kwargs and kwargs["C"] in (256, 512):
+        kwargs = dict(kwargs, heads=kwargs["C"] // 32)
+    assert call(lib, **kwargs) == status
+
+
+def test_projection_pooled_outputs_validation(lib):
+    assert _qkv(lib, qr=0) == EINVAL
+    assert _qkv(lib, kr=PF + 64) == EINVAL  # region means overlap
+    assert _fqkv(lib, o=P3) == EINVAL       # O aliases Q
+    assert _fqkv(lib, wsb=16) == EINVAL
+
+
 @pytest.mark.parametrize("kwargs", [dict(dq=P), dict(dk=P3), dict(dv=PF), dict(dq=0x90000), dict(dk=0xA0000),
                                     dict(do=0), dict(idx=0), dict(idx=PB + 2), dict(dv=0xA0000 + 8)])
 def test_backward_validation(lib, kwargs):

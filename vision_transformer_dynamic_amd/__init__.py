@@ -12,6 +12,8 @@ and the current stream. If the library has not been built, every call raises
     attend_lce(q, k, v, idx, weight, bias, heads, S)   -> o + 5x5 depthwise conv of v
     forward_lce(q, k, v, weight, bias, heads, S, topk) -> o + 5x5 depthwise conv of v
     attend_backward(q, k, v, o, do, idx, heads, S)     -> (dq, dk, dv), routing held fixed
+    qkv_pool(x, w_qkv, b_qkv, S)                       -> (q, k, v, q_r, k_r) region means of q, k
+    forward_qkv(x, w_qkv, b_qkv, heads, S, topk)       -> (o, q, k, v) from the block input
 
 q, k, v: contiguous [B, H, W, C] tensors on one GPU, float32 or bfloat16;
 weight [C, 5, 5] and bias [C] (or None) of the local-context filter in the
@@ -36,6 +38,8 @@ __all__ = [
     "attend_lce",
     "forward_lce",
     "attend_backward",
+    "qkv_pool",
+    "forward_qkv",
     "EXPORTS",
 ]
 
@@ -48,7 +52,8 @@ BRA_OK, BRA_EINVAL, BRA_EUNSUPPORTED, BRA_EHIP, BRA_ENOMEM = range(5)
 
 # Every symbol include/bra.h declares.
 EXPORTS = ("bra_status_string", "bra_workspace_bytes", "bra_route", "bra_attend", "bra_forward",
-           "bra_attend_lce", "bra_forward_lce", "bra_backward_workspace_bytes", "bra_attend_backward")
+           "bra_attend_lce", "bra_forward_lce", "bra_backward_workspace_bytes", "bra_attend_backward",
+           "bra_qkv_pool", "bra_forward_qkv")
 
 _lib = None
 
@@ -96,6 +101,10 @@ def load_library():
     lib.bra_backward_workspace_bytes.argtypes = [i32] * 7
     lib.bra_attend_backward.restype = i32
     lib.bra_attend_backward.argtypes = [vp] * 9 + [i32] * 7 + [i32, vp, sz, vp]
+    lib.bra_qkv_pool.restype = i32
+    lib.bra_qkv_pool.argtypes = [vp] * 8 + [i32] * 5 + [i32, vp]
+    lib.bra_forward_qkv.restype = i32
+    lib.bra_forward_qkv.argtypes = [vp] * 7 + [i32] * 7 + [i32, vp, sz, vp]
     _lib = lib
     return lib
 
@@ -282,3 +291,53 @@ def attend_backward(q, k, v, o, do, idx: torch.Tensor, heads: int, S: int, out=N
                                    B, H, W, C, heads, S, topk, _dtype_code(q),
                                    workspace.data_ptr(), need, _stream(q.device)))
     return dq, dk, dv
+
+
+def _proj_args(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv):
+    C = x.shape[-1]
+    if w_qkv.shape != (3 * C, C) or w_qkv.dtype != x.dtype or w_qkv.device != x.device or not w_qkv.is_contiguous():
+        raise ValueError("w_qkv must be a contiguous [3C, C] tensor of x's dtype on x's device")
+    if b_qkv is None:
+        return w_qkv.data_ptr(), None
+    if b_qkv.shape != (3 * C,) or b_qkv.dtype != x.dtype or b_qkv.device != x.device or not b_qkv.is_contiguous():
+        raise ValueError("b_qkv must be a contiguous [3C] tensor of x's dtype on x's device, or None")
+    return w_qkv.data_ptr(), b_qkv.data_ptr()
+
+
+def qkv_pool(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv, S: int, out=None):
+    """Q, K, V = x w_qkv^T + b_qkv (chunked q, k, v) and the region means
+    q_r, k_r [B, S*S, C] float32 of the rounded Q and K."""
+    lib = load_library()
+    _check_maps(x)
+    B, H, W, C = x.shape
+    wp, bp = _proj_args(x, w_qkv, b_qkv)
+    if out is None:
+        out = tuple(torch.empty_like(x) for _ in range(3)) + tuple(
+            torch.empty((B, S * S, C), dtype=torch.float32, device=x.device) for _ in range(2))
+    q, k, v, qr, kr = out
+    _check_maps(x, q, k, v)
+    for t in (qr, kr):
+        if t.dtype != torch.float32 or t.shape != (B, S * S, C) or not t.is_contiguous() or t.device != x.device:
+            raise ValueError("q_r, k_r must be contiguous float32 [B, S*S, C] tensors on x's device")
+    _check(lib.bra_qkv_pool(x.data_ptr(), wp, bp, q.data_ptr(), k.data_ptr(), v.data_ptr(), qr.data_ptr(),
+                            kr.data_ptr(), B, H, W, C, S, _dtype_code(x), _stream(x.device)))
+    return q, k, v, qr, kr
+
+
+def forward_qkv(x: torch.Tensor, w_qkv: torch.Tensor, b_qkv, heads: int, S: int, topk: int, out=None,
+                workspace=None):
+    """The module from its input x: projection (with the pooling fused),
+    routing and attention. Returns (o, q, k, v)."""
+    lib = load_library()
+    _check_maps(x)
+    B, H, W, C = x.shape
+    wp, bp = _proj_args(x, w_qkv, b_qkv)
+    if out is None:
+        out = tuple(torch.empty_like(x) for _ in range(4))
+    o, q, k, v = out
+    _check_maps(x, o, q, k, v)
+    ws, nbytes = _workspace(x, S, topk, workspace)
+    _check(lib.bra_forward_qkv(x.data_ptr(), wp, bp, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               B, H, W, C, heads, S, topk, _dtype_code(x), ws.data_ptr(), nbytes,
+                               _stream(x.device)))
+    return o, q, k, v

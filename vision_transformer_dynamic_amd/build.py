@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libbra.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["pool.hip", "route.hip", "attend.hip", "lce.hip", "backward.hip", "bra_api.hip"]
+SOURCES = ["pool.hip", "route.hip", "attend.hip", "lce.hip", "backward.hip", "qkv.hip", "bra_api.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

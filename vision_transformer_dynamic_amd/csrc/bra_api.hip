@@ -251,3 +251,70 @@ bra_status bra_attend_backward(const void* Q, const void* K, const void* V, cons
 }
 
 }  // extern "C"
+
+namespace {
+
+// Projection arguments: C a multiple of 32 and at most 256 (bf16) or 128 (fp32);
+// X and the outputs 16-byte aligned and distinct; the weight 16-byte
+// aligned, the bias element-aligned or null; no output overlapping X or the
+// weights.
+bra_status check_proj(const void* X, const void* Wqkv, const void* bqkv, void* const* outs, int nout,
+                      const Shape& s, int dtype) {
+  if (s.C % 32 != 0 || s.C > (dtype == bra::kBF16 ? bra::kMaxProjChannelsBf16 : bra::kMaxProjChannelsF32))
+    return BRA_EUNSUPPORTED;
+  const size_t esz = dtype == bra::kBF16 ? 2 : 4;
+  if (bad_tensor(X) || bad_tensor(Wqkv)) return BRA_EINVAL;
+  if (bqkv != nullptr && !aligned(bqkv, esz)) return BRA_EINVAL;
+  const size_t map = esz * (size_t)s.B * s.H * s.W * s.C;
+  for (int i = 0; i < nout; ++i) {
+    if (bad_tensor(outs[i])) return BRA_EINVAL;
+    if (overlaps(outs[i], map, X, map)) return BRA_EINVAL;
+    if (overlaps(outs[i], map, Wqkv, esz * 3 * (size_t)s.C * s.C)) return BRA_EINVAL;
+    if (bqkv != nullptr && overlaps(outs[i], map, bqkv, esz * 3 * (size_t)s.C)) return BRA_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], map, outs[j], map)) return BRA_EINVAL;
+  }
+  return BRA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bra_status bra_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, void* Q, void* K, void* V,
+                        float* Qr, float* Kr, int B, int H, int W, int C, int S,
+                        bra_dtype dtype, hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, -1, S, 1, (int)dtype, &s);
+  if (st != BRA_OK) return st;
+  void* outs[] = {Q, K, V};
+  if ((st = check_proj(X, Wqkv, bqkv, outs, 3, s, (int)dtype)) != BRA_OK) return st;
+  if (Qr == nullptr || Kr == nullptr || !aligned(Qr, 4) || !aligned(Kr, 4)) return BRA_EINVAL;
+  const size_t pooled = sizeof(float) * (size_t)s.B * s.R * s.C;
+  if (overlaps(Qr, pooled, Kr, pooled)) return BRA_EINVAL;
+  if (bra::launch_qkv_pool(X, Wqkv, bqkv, Q, K, V, Qr, Kr, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
+  return BRA_OK;
+}
+
+bra_status bra_forward_qkv(const void* X, const void* Wqkv, const void* bqkv, void* Q, void* K, void* V, void* O,
+                           int B, int H, int W, int C, int heads, int S, int topk,
+                           bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, heads, S, topk, (int)dtype, &s);
+  if (st != BRA_OK) return st;
+  void* outs[] = {Q, K, V, O};
+  if ((st = check_proj(X, Wqkv, bqkv, outs, 4, s, (int)dtype)) != BRA_OK) return st;
+  Workspace ws;
+  st = ws.acquire(workspace, workspace_bytes, workspace_for(s), stream);
+  if (st != BRA_OK) return st;
+  float* Qr = reinterpret_cast<float*>(ws.ptr);
+  float* Kr = reinterpret_cast<float*>(ws.ptr + pooled_bytes(s));
+  int32_t* idx = reinterpret_cast<int32_t*>(ws.ptr + 2 * pooled_bytes(s));
+  if (bra::launch_qkv_pool(X, Wqkv, bqkv, Q, K, V, Qr, Kr, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
+  if (bra::launch_route(Qr, Kr, idx, s, stream) != hipSuccess) return BRA_EHIP;
+  if (bra::launch_attend(Q, K, V, idx, nullptr, nullptr, O, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
+  return BRA_OK;
+}
+
+}  // extern "C"

@@ -74,6 +74,14 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
 hipError_t launch_lce(const void* V, const void* lce_w, const void* lce_b, void* O,
                       const Shape& s, int dtype, hipStream_t stream);
 
+// Q, K, V = X Wqkv^T + bqkv (Wqkv [3C][C]; bqkv [3C] or null) and the region
+// means Qr, Kr [B, R, C] of the rounded Q and K. C % 32 == 0, C <= 256 (bf16)
+// or 128 (fp32): the X rows, region sums and per-wave tiles fit in LDS.
+hipError_t launch_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, void* Q, void* K, void* V, float* Qr,
+                           float* Kr, const Shape& s, int dtype, hipStream_t stream);
+constexpr int kMaxProjChannelsBf16 = 256;
+constexpr int kMaxProjChannelsF32 = 128;
+
 // Backward of the token attention, routing table idx held fixed: dQ, dK, dV
 // from dO (and the forward output O). ws holds backward_workspace_bytes(s).
 size_t backward_workspace_bytes(const Shape& s);
