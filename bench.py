@@ -15,6 +15,9 @@ the stream it runs on, and the CPU oracle timed on a bounded sample. The
 a side measurement, not the headline value. The ``train`` object times a
 training step of the same operator the same way: routing, attention and the
 backward pass (dQ, dK, dV for a seeded output gradient, routing held fixed).
+The ``from_input`` object times the module from its block input X: the QKV
+projection with the region pooling fused into it, routing from the fused
+means, and attention (seeded synthetic projection weights).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -54,6 +57,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-lce", action="store_true", help="skip the side measurement with the local context term")
     ap.add_argument("--no-train", action="store_true", help="skip the side measurement of the training step")
+    ap.add_argument("--no-proj", action="store_true", help="skip the side measurement from the block input")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     return ap.parse_args(argv)
@@ -318,6 +322,38 @@ def main(argv=None):
                  "us_per_step": round(train_us, 2), "backward_us": round(bw_us, 2),
                  "step": "pool + route + attention + backward (dQ, dK, dV), routing held fixed"}
 
+    from_input = None
+    if not args.no_proj and w.C % 32 == 0 and w.C <= (256 if w.dtype == "bf16" else 128):
+        xh, wq, bq = wl.make_projection(w)
+        wq, bq = wq.to(dev), bq.to(dev)
+        xs = [xh.to(dev) for _ in range(nsets)]
+        outs = [tuple(torch.empty_like(xs[0]) for _ in range(4)) for _ in range(nsets)]
+        pouts = [tuple(torch.empty_like(xs[0]) for _ in range(3)) + tuple(
+            torch.empty((w.B, w.R, w.C), dtype=torch.float32, device=dev) for _ in range(2)) for _ in range(nsets)]
+        fws = [torch.empty(bra.workspace_bytes(w.B, w.H, w.W, w.C, w.S, w.topk), dtype=torch.uint8, device=dev)
+               for _ in range(nsets)]
+        fwd_x = [lambda i=i: bra.forward_qkv(xs[i], wq, bq, w.heads, w.S, w.topk, out=outs[i], workspace=fws[i])
+                 for i in range(nsets)]
+        proj = [lambda i=i: bra.qkv_pool(xs[i], wq, bq, w.S, out=pouts[i]) for i in range(nsets)]
+        for f in fwd_x + proj:
+            f()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            fx_cycle = capture(fwd_x)
+            fx_singles = [capture([f]) for f in fwd_x]
+            pj_cycle = capture(proj)
+            pj_singles = [capture([f]) for f in proj]
+        torch.cuda.synchronize()
+        fx_us = phase_us(fx_cycle, fx_singles)
+        pj_us = phase_us(pj_cycle, pj_singles)
+        o0, q0, k0, v0 = outs[0]
+        if not torch.equal(o0, bra.forward(q0, k0, v0, w.heads, w.S, w.topk)):
+            raise RuntimeError("output from the block input differs from bra_forward on its projections")
+        from_input = {"value": round(w.tokens / (fx_us * 1e-6), 1), "unit": "tokens/s", "us_per_step": round(fx_us, 2),
+                      "qkv_pool_us": round(pj_us, 2),
+                      "step": "QKV projection with fused region pooling + route + attention, seeded synthetic weights"}
+        del xs, outs, pouts, fws
+
     # the timed steps computed the real thing: spot-check one copy
     ref = bra.forward(qd, kd, vd, w.heads, w.S, w.topk)
     torch.cuda.synchronize()
@@ -365,6 +401,8 @@ def main(argv=None):
                       "step_wall": round(wall_ms * 1e3, 2), "step_events": round(ev_ms * 1e3, 2)},
         "roofline": roof,
     }
+    if from_input is not None:
+        result["from_input"] = from_input
     if with_lce is not None:
         result["with_lce"] = with_lce
     if train is not None:

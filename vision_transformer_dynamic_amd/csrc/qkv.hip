@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kTokBlock = 64;  // tokens per block
 constexpr int kQkvWaves = 8;   // waves per workgroup (at most)
+constexpr int kXLoads = 2;     // X-row loads in flight per thread
 
 struct QkvParams {
   const void* X;
@@ -65,16 +66,35 @@ __device__ __forceinline__ int block_token(int sub, int tw, int r0, int nreg, in
   return (ry * sh + qy) * W + rx * sw + qx;
 }
 
-template <typename T>
+// Sum of v over aligned runs of `seg` lanes (seg = 1, 2, 4, 8 or 16) inside
+// each row of 16 lanes, with DPP moves (no LDS traffic): quad permutes for
+// pairs and quads, then the half-row and row mirrors, which pair every lane
+// with one of the other half. The run's first lane reads the sum.
+template <int SEG>
+__device__ __forceinline__ float run_sum(float v) {
+  constexpr int seg = SEG;
+  if (seg >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  if (seg >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  if (seg >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)); // row_half_mirror
+  if (seg >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)); // row_mirror
+  return v;
+}
+
+// SEG > 0: the region size n is a multiple of 16 or divides 16, so the tokens
+// of one region inside a 16-token tile are aligned runs of SEG = min(n, 16)
+// lanes and their sums come from DPP moves across those lanes. SEG = 0: the
+// rounded values go through a per-wave LDS tile and are summed from there.
+template <typename T, int SEG>
 __global__ __launch_bounds__(512) void qkv_pool_kernel(QkvParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
   constexpr int VEC = TT::VEC;
+  constexpr int KPF = 2;  // k-steps whose weight operands are loaded together
   const int LDX = p.C + 16 / (int)sizeof(T);  // X rows in LDS, 16-byte pad
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* xs = reinterpret_cast<T*>(smem_raw);                                         // [64][LDX]
-  float* pool = reinterpret_cast<float*>(xs + kTokBlock * LDX);                    // [rpw][2C] sums
-  float* ptile = pool + p.rpw * 2 * p.C + (threadIdx.x >> 6) * kTokBlock * 33;     // wave's [64][33]
+  T* xs = reinterpret_cast<T*>(smem_raw);                                      // [64][LDX]
+  float* pool = reinterpret_cast<float*>(xs + kTokBlock * LDX);                 // [rpw][2C] sums
+  float* ptile = pool + p.rpw * 2 * p.C + (threadIdx.x >> 6) * kTokBlock * 33;  // SEG = 0: wave's [64][33]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -102,81 +122,123 @@ __global__ __launch_bounds__(512) void qkv_pool_kernel(QkvParams p) {
   const int ntok = p.nsub > 1 ? kTokBlock : nreg * p.n;  // tokens per block
   const int ks_n = p.C / 32;
   const int cvec = p.C / VEC;  // 16-byte vectors per X row
+  constexpr bool BFLY = SEG > 0;
   for (int sub = 0; sub < p.nsub; ++sub) {
     __syncthreads();  // previous block's X rows consumed
-    for (int f = tid; f < kTokBlock * cvec; f += blockDim.x) {
-      const int tw = f / cvec, cv = f - tw * cvec;
-      const int t = tw < ntok ? block_token(sub, tw, r0, nreg, p.nsub, p.n, p.sh, p.sw, p.W, p.div_n, p.div_sw, p.div_S) : -1;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (t >= 0) v = *reinterpret_cast<const uint4*>(Xg + t * p.C + cv * VEC);
-      *reinterpret_cast<uint4*>(xs + tw * LDX + cv * VEC) = v;
+    // X rows of the block: every load of a thread issued before any store
+    for (int f0 = 0; f0 < kTokBlock * cvec; f0 += kXLoads * blockDim.x) {
+      uint4 xv[kXLoads];
+#pragma unroll
+      for (int m = 0; m < kXLoads; ++m) {
+        const int f = f0 + m * blockDim.x + tid;
+        const int tw = f / cvec, cv = f - tw * cvec;
+        const int t = (f < kTokBlock * cvec && tw < ntok)
+                          ? block_token(sub, tw, r0, nreg, p.nsub, p.n, p.sh, p.sw, p.W, p.div_n, p.div_sw, p.div_S)
+                          : -1;
+        xv[m] = make_uint4(0u, 0u, 0u, 0u);
+        if (t >= 0) xv[m] = *reinterpret_cast<const uint4*>(Xg + t * p.C + cv * VEC);
+      }
+#pragma unroll
+      for (int m = 0; m < kXLoads; ++m) {
+        const int f = f0 + m * blockDim.x + tid;
+        if (f < kTokBlock * cvec) {
+          const int tw = f / cvec, cv = f - tw * cvec;
+          *reinterpret_cast<uint4*>(xs + tw * LDX + cv * VEC) = xv[m];
+        }
+      }
     }
     __syncthreads();
-    const int mtiles = (ntok + 15) >> 4;
-    // token of this lane in each 16-token tile (stores)
     for (int fg = wave; fg < p.nfg; fg += nw) {
       // A rows: row rr = col of feature tile ct is feature 32 fg + 8 (rr/4) +
       // (rr%4) + 4 ct, so lane group g ends with features 8g..8g+7
       const int frow = fg * 32 + 8 * (col >> 2) + (col & 3);
       floatx4 acc[4][2];
-      for (int m0 = 0; m0 < mtiles; m0 += 4) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) acc[mt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks < ks_n; ++ks) {
-          const op8 wa = TT::load8(Wg + (frow + 0) * p.C + ks * 32 + 8 * g);
-          const op8 wb = TT::load8(Wg + (frow + 4) * p.C + ks * 32 + 8 * g);
+        for (int ct = 0; ct < 2; ++ct) acc[mt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < ks_n; k0 += KPF) {
+        op8 wa[KPF], wb[KPF];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            if (m0 + mt >= mtiles) break;  // uniform
-            const op8 xb = TT::load8(xs + ((m0 + mt) * 16 + col) * LDX + ks * 32 + 8 * g);
-            acc[mt][0] = TT::mma(wa, xb, acc[mt][0]);
-            acc[mt][1] = TT::mma(wb, xb, acc[mt][1]);
+        for (int kk = 0; kk < KPF; ++kk) {
+          wa[kk] = TT::zero();
+          wb[kk] = TT::zero();
+          if (k0 + kk < ks_n) {
+            wa[kk] = TT::load8(Wg + (frow + 0) * p.C + (k0 + kk) * 32 + 8 * g);
+            wb[kk] = TT::load8(Wg + (frow + 4) * p.C + (k0 + kk) * 32 + 8 * g);
           }
         }
-        // epilogue: bias, one rounding, store; Q/K groups also keep the
-        // rounded values for the region sums
-        const int feat = fg * 32 + 8 * g;  // lane's first feature
-        const int tensor = feat / p.C, ch = feat - tensor * p.C;
-        float bv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bv[e] = Bg ? (float)Bg[feat + e] : 0.f;
-        T* dst = static_cast<T*>(tensor == 0 ? p.Q : tensor == 1 ? p.K : p.V) + img;
+        for (int kk = 0; kk < KPF; ++kk) {
+          if (k0 + kk >= ks_n) break;  // uniform
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          if (m0 + mt >= mtiles) break;
-          const int tw = (m0 + mt) * 16 + col;
-          const int t = tw < ntok ? block_token(sub, tw, r0, nreg, p.nsub, p.n, p.sh, p.sw, p.W, p.div_n, p.div_sw, p.div_S) : -1;
-          float o[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] = acc[mt][0][e] + bv[e];
-            o[4 + e] = acc[mt][1][e] + bv[4 + e];
-          }
-          typename TT::op8 r = TT::from_f32(o);  // the rounded outputs
-          if (t >= 0) *reinterpret_cast<op8*>(dst + t * p.C + ch) = r;
-          if (fg * 32 < 2 * p.C) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ptile[tw * 33 + 8 * g + e] = t >= 0 ? (float)r[e] : 0.f;
+          for (int mt = 0; mt < 4; ++mt) {  // rows past the block are zeros in LDS
+            const op8 xb = TT::load8(xs + (mt * 16 + col) * LDX + (k0 + kk) * 32 + 8 * g);
+            acc[mt][0] = TT::mma(wa[kk], xb, acc[mt][0]);
+            acc[mt][1] = TT::mma(wb[kk], xb, acc[mt][1]);
           }
         }
-        if (fg * 32 < 2 * p.C) {
-          // region sums over this block's tokens, one (region, feature) per
-          // lane step, tokens in order
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          const int t0 = m0 * 16, t1 = min(ntok, (m0 + 4) * 16);
-          for (int jf = lane; jf < p.rpw * 32; jf += 64) {
-            const int j = jf >> 5, f = jf & 31;
-            const int a = max(t0, p.nsub > 1 ? 0 : j * p.n), z = min(t1, p.nsub > 1 ? ntok : (j + 1) * p.n);
-            float sacc = 0.f;
-            for (int tw = a; tw < z; ++tw) sacc += ptile[tw * 33 + f];
-            if (a < z) pool[j * 2 * p.C + fg * 32 + f] += sacc;
-          }
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          __builtin_amdgcn_wave_barrier();
+      }
+      // epilogue: bias, one rounding, store; Q/K groups also sum the rounded
+      // values per region
+      const int feat = fg * 32 + 8 * g;  // lane's first feature
+      const int tensor = feat / p.C, ch = feat - tensor * p.C;
+      const bool pooled = fg * 32 < 2 * p.C;  // uniform
+      float bv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bv[e] = Bg ? (float)Bg[feat + e] : 0.f;
+      T* dst = static_cast<T*>(tensor == 0 ? p.Q : tensor == 1 ? p.K : p.V) + img;
+#pragma unroll 1
+      for (int mt = 0; mt < 4; ++mt) {
+        const int twl = mt * 16 + col;
+        const int t = twl < ntok ? block_token(sub, twl, r0, nreg, p.nsub, p.n, p.sh, p.sw, p.W, p.div_n, p.div_sw, p.div_S)
+                                 : -1;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = acc[mt][0][e] + bv[e];
+          o[4 + e] = acc[mt][1][e] + bv[4 + e];
         }
+        const op8 r = TT::from_f32(o);  // the rounded outputs
+        if (t >= 0) *reinterpret_cast<op8*>(dst + t * p.C + ch) = r;
+        if (pooled) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = t >= 0 ? (float)r[e] : 0.f;
+          if (BFLY) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = run_sum<SEG>(v[e]);
+            // the first lane of each run holds its region's sum for this tile
+            const int tw = mt * 16 + col;
+            if ((col & (SEG - 1)) == 0 && tw < ntok) {
+              const int j = p.nsub > 1 ? 0 : tw / p.n;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) pool[j * 2 * p.C + feat + e] += v[e];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ptile[(mt * 16 + col) * 33 + 8 * g + e] = v[e];
+          }
+        }
+      }
+      if (!BFLY && pooled) {
+        // region sums from the wave's tile, (region, feature) pairs over the
+        // lanes, tokens in order in 4 interleaved partial sums
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        for (int jf = lane; jf < p.rpw * 32; jf += 64) {
+          const int j = jf >> 5, f = jf & 31;
+          const int a = p.nsub > 1 ? 0 : j * p.n, z = min(ntok, p.nsub > 1 ? ntok : (j + 1) * p.n);
+          float s4[4] = {0.f, 0.f, 0.f, 0.f};
+          int tw = a;
+          for (; tw + 4 <= z; tw += 4)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s4[u] += ptile[(tw + u) * 33 + f];
+          for (; tw < z; ++tw) s4[0] += ptile[tw * 33 + f];
+          if (a < z) pool[j * 2 * p.C + fg * 32 + f] += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
       }
     }
   }
@@ -217,9 +279,22 @@ hipError_t launch_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, vo
   if (nwg >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int waves = p.nfg < kQkvWaves ? p.nfg : kQkvWaves;
   const size_t esz = dtype == kBF16 ? 2 : 4;
+  // lanes per region run inside a 16-token tile, 0 when runs do not align
+  const int seg = s.n % 16 == 0 ? 16 : (s.n < 16 && 16 % s.n == 0) ? s.n : 0;
   const size_t lds = esz * kTokBlock * (s.C + 16 / esz) + sizeof(float) * p.rpw * 2 * s.C +
-                     sizeof(float) * waves * kTokBlock * 33;
-  const void* fn = dtype == kBF16 ? (const void*)&qkv_pool_kernel<__bf16> : (const void*)&qkv_pool_kernel<float>;
+                     (seg ? 0 : sizeof(float) * waves * kTokBlock * 33);
+  const void* fn;
+  if (dtype == kBF16) {
+    const void* k[] = {(const void*)&qkv_pool_kernel<__bf16, 0>, (const void*)&qkv_pool_kernel<__bf16, 1>,
+                       (const void*)&qkv_pool_kernel<__bf16, 2>, (const void*)&qkv_pool_kernel<__bf16, 4>,
+                       (const void*)&qkv_pool_kernel<__bf16, 8>, (const void*)&qkv_pool_kernel<__bf16, 16>};
+    fn = k[seg == 0 ? 0 : 1 + __builtin_ctz(seg)];
+  } else {
+    const void* k[] = {(const void*)&qkv_pool_kernel<float, 0>, (const void*)&qkv_pool_kernel<float, 1>,
+                       (const void*)&qkv_pool_kernel<float, 2>, (const void*)&qkv_pool_kernel<float, 4>,
+                       (const void*)&qkv_pool_kernel<float, 8>, (const void*)&qkv_pool_kernel<float, 16>};
+    fn = k[seg == 0 ? 0 : 1 + __builtin_ctz(seg)];
+  }
   void* args[] = {&p};
   return hipLaunchKernel(fn, dim3((unsigned)nwg), dim3(waves * 64), args, lds, stream);
 }
