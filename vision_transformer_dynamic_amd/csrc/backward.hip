@@ -72,9 +72,9 @@ __device__ inline int xcd_remap() {
 
 // ---------------------------------------------------------------------------
 // 1. Inverse routing table, one workgroup per image. Each routing row becomes
-// a bit mask of its regions in LDS (bitwise OR is order-free); thread r then
-// walks the rows in order and appends every good row whose mask holds r, so
-// each list comes out ascending with one LDS read per row.
+// a bit mask of its regions in LDS (bitwise OR is order-free); then one wave
+// per key region tests 64 rows at a time and places the good rows that hold
+// it with a ballot prefix count, so each list comes out ascending.
 __global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
   __shared__ uint32_t mask[kMaxRegions][kMaxRegions / 32];
   __shared__ int rowbad[kMaxRegions];
@@ -92,14 +92,23 @@ __global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
       atomicOr(&mask[i][r >> 5], 1u << (r & 31));
   }
   __syncthreads();
-  if (tid < R) {
-    int* L = p.inv_list + ((int64_t)b * R + tid) * R;
+  // wave w compacts the lists of key regions w, w + 4, ...: 64 rows per step,
+  // hits placed by a ballot prefix count, so each list is ascending
+  const int wave = tid >> 6, lane = tid & 63;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int r = wave; r < R; r += 4) {
+    int* L = p.inv_list + ((int64_t)b * R + r) * R;
     int m = 0;
-    for (int i = 0; i < R; ++i)
-      if (!rowbad[i] && ((mask[i][tid >> 5] >> (tid & 31)) & 1u)) L[m++] = i;
-    p.inv_cnt[b * R + tid] = m;
-    p.bad[b * R + tid] = rowbad[tid];
+    for (int i0 = 0; i0 < R; i0 += 64) {
+      const int i = i0 + lane;
+      const bool hit = i < R && !rowbad[i] && ((mask[i][r >> 5] >> (r & 31)) & 1u);
+      const uint64_t bal = __ballot(hit);
+      if (hit) L[m + __popcll(bal & below)] = i;
+      m += __popcll(bal);
+    }
+    if (lane == 0) p.inv_cnt[b * R + r] = m;
   }
+  for (int r = tid; r < R; r += 256) p.bad[b * R + r] = rowbad[r];
 }
 
 // Chunk token table: tok[kappa - c0] = token (inside the image) of routed key
@@ -163,14 +172,29 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const T* Vg = static_cast<const T*>(p.V) + img;
   T* Kt = reinterpret_cast<T*>(smem_raw) + hl * D * ldk;  // K^T tile of this wave's head
 
-  // routed regions' corners
+  // routed regions' corners (several chunks) or, with one chunk, the token
+  // of every routed key straight from the routing row
   if (tid == 0) sbad = 0;
   __syncthreads();
-  for (int j = tid; j < p.topk; j += blockDim.x) {
-    const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
-    const bool ok = r >= 0 && r < p.R;
-    rb[j] = corner_of(p, ok ? r : 0);
-    if (!ok) sbad = 1;
+  if (MULTI) {
+    for (int j = tid; j < p.topk; j += blockDim.x) {
+      const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
+      const bool ok = r >= 0 && r < p.R;
+      rb[j] = corner_of(p, ok ? r : 0);
+      if (!ok) sbad = 1;
+    }
+  } else if (tid < KC) {
+    int t = -1;
+    if (tid < p.kv) {
+      int tk, tx;
+      const int jr = fdiv(tid, p.div_n, &tk);
+      const int ty = fdiv(tk, p.div_sw, &tx);
+      const int r = p.idx[((int64_t)b * p.R + i) * p.topk + jr];
+      const bool ok = r >= 0 && r < p.R;
+      t = corner_of(p, ok ? r : 0) + ty * p.W + tx;
+      if (!ok) sbad = 1;
+    }
+    tok[tid] = t;
   }
 
   // the wave's queries: B operands of q and dO, and D = dO . O per query
@@ -262,8 +286,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
   for (int ch = 0; ch < nchunks; ++ch) {
     const int c0 = ch * KC;
-    build_tok(tok, rb, tid, c0, kv, W, div_n, div_sw);
-    __syncthreads();
+    if (MULTI) {
+      build_tok(tok, rb, tid, c0, kv, W, div_n, div_sw);
+      __syncthreads();
+    }
     // K^T tile of this head, written by the head's ntq waves together
     for (int f = t * 64 + lane; f < ITEMS; f += p.ntq * 64) {
       const int cv = f % CVH, p2 = f / CVH;
