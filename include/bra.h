@@ -220,7 +220,7 @@ bra_status bra_attend_backward(const void* Q, const void* K, const void* V, cons
  */
 
 /* bra_qkv_pool - Q, K, V and the region means Qr, Kr ([B, S*S, C] fp32,
- * 4-byte aligned) of the ROUNDED Q and K, i.e. what bra_route pools from the
+ * 16-byte aligned, not overlapping) of the ROUNDED Q and K, i.e. what bra_route pools from the
  * stored Q and K (up to fp32 summation order), without reading them again. */
 bra_status bra_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, void* Q, void* K, void* V,
                         float* Qr, float* Kr, int B, int H, int W, int C, int S,

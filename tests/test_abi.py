@@ -195,6 +195,7 @@ def test_projection_validation(lib, call, kwargs, status):
 def test_projection_pooled_outputs_validation(lib):
     assert _qkv(lib, qr=0) == EINVAL
     assert _qkv(lib, kr=PF + 64) == EINVAL  # region means overlap
+    assert _qkv(lib, qr=0x90004) == EINVAL  # region means not 16-byte aligned
     assert _fqkv(lib, o=P3) == EINVAL       # O aliases Q
     assert _fqkv(lib, wsb=16) == EINVAL
 

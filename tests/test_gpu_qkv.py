@@ -54,6 +54,22 @@ def test_edge_shapes_projection(w):
     _check_projection(w, images=list(range(w.B)))
 
 
+# region sizes and channel counts of both projection kernels: n = 2, 4, 8
+# (runs inside a 16-token tile), C = 96 (two feature groups per wave)
+PROJ_SHAPES = [
+    wl.custom(2, 8, 4, 64, 2, 4, 3, "bf16", seed=95),     # n = 2
+    wl.custom(2, 8, 8, 64, 2, 4, 3, "bf16", seed=96),     # n = 4
+    wl.custom(1, 16, 8, 32, 1, 4, 2, "bf16", seed=97),    # n = 8
+    wl.custom(2, 16, 16, 96, 3, 4, 2, "bf16", seed=98),   # C = 96, n = 16
+    wl.custom(1, 24, 24, 128, 4, 3, 2, "bf16", seed=99),  # n = 64, C = 128
+]
+
+
+@pytest.mark.parametrize("w", PROJ_SHAPES, ids=[w.name for w in PROJ_SHAPES])
+def test_projection_region_sizes(w):
+    _check_projection(w, images=list(range(w.B)))
+
+
 def test_projection_without_bias():
     _check_projection(wl.WORKLOADS[2], bias=False)
 

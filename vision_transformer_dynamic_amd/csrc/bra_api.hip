@@ -289,7 +289,7 @@ bra_status bra_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, void*
   if (st != BRA_OK) return st;
   void* outs[] = {Q, K, V};
   if ((st = check_proj(X, Wqkv, bqkv, outs, 3, s, (int)dtype)) != BRA_OK) return st;
-  if (Qr == nullptr || Kr == nullptr || !aligned(Qr, 4) || !aligned(Kr, 4)) return BRA_EINVAL;
+  if (bad_tensor(Qr) || bad_tensor(Kr)) return BRA_EINVAL;
   const size_t pooled = sizeof(float) * (size_t)s.B * s.R * s.C;
   if (overlaps(Qr, pooled, Kr, pooled)) return BRA_EINVAL;
   if (bra::launch_qkv_pool(X, Wqkv, bqkv, Q, K, V, Qr, Kr, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;

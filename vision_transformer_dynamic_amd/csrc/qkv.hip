@@ -22,6 +22,8 @@
 // sum is formed in a fixed order (deterministic, no atomics).
 #include "attn_common.h"
 
+#include <algorithm>
+
 namespace bra {
 namespace {
 
@@ -43,6 +45,7 @@ struct QkvParams {
   int nsub;     // 64-token blocks per region (n > 64), else 1
   int ngroups;  // workgroups per image
   int nfg;      // feature groups (3C / 32)
+  int nunits;   // persistent form: images x groups
   FastDiv div_n, div_sw, div_S;
 };
 
@@ -255,6 +258,162 @@ __global__ __launch_bounds__(512) void qkv_pool_kernel(QkvParams p) {
   }
 }
 
+// Persistent form (bf16, C <= 128, regions of at most 64 tokens whose runs
+// align with 16-token tiles): the grid is sized to the machine and every
+// workgroup walks units (image, region group) u, u + gridDim.x, ... Each
+// wave loads the weight rows and bias of its feature groups once and keeps
+// them in registers; X blocks alternate between two LDS buffers, the next
+// block's loads in flight while the current one is computed (one barrier per
+// block); region sums stay in the run leader's registers and are written as
+// means when the region is complete.
+constexpr int kPersistKS = 4;  // k-steps kept in registers (C <= 128)
+constexpr int kPersistXL = 4;  // X loads per thread per block (the host checks they cover it)
+
+// X rows of unit u (image u / ngroups, regions from (u % ngroups) * rpw):
+// this thread's loads
+__device__ __forceinline__ void persist_load_x(const QkvParams& p, int u, int total, int tid, int nthr, int cvec,
+                                               uint4 (&xr)[kPersistXL]) {
+  const int b = u / p.ngroups;
+  const int r0 = (u - b * p.ngroups) * p.rpw;
+  const int nreg = min(p.rpw, p.R - r0);
+  const __bf16* Xg = static_cast<const __bf16*>(p.X) + (int64_t)b * p.H * p.W * p.C;
+#pragma unroll
+  for (int m = 0; m < kPersistXL; ++m) {
+    const int f = tid + m * nthr;
+    const int tw = f / cvec, cv = f - tw * cvec;
+    xr[m] = make_uint4(0u, 0u, 0u, 0u);
+    if (u < total && f < kTokBlock * cvec && tw < nreg * p.n) {
+      const int t = block_token(0, tw, r0, nreg, 1, p.n, p.sh, p.sw, p.W, p.div_n, p.div_sw, p.div_S);
+      xr[m] = *reinterpret_cast<const uint4*>(Xg + t * p.C + cv * 8);
+    }
+  }
+}
+
+template <int FPW, int KSM, int SEG>
+__global__ __launch_bounds__(512) void qkv_pool_persistent(QkvParams p) {
+  typedef Tr<__bf16> TT;
+  typedef TT::op8 op8;
+  const int LDX = p.C + 8;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __bf16* xbuf = reinterpret_cast<__bf16*>(smem_raw);  // [2][64][LDX]
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, col = lane & 15;
+  const int nthr = blockDim.x;
+  const int ks_n = p.C / 32;
+  const int cvec = p.C / 8;
+  const int total = p.nunits;
+  const __bf16* Wg = static_cast<const __bf16*>(p.Wt);
+  const __bf16* Bg = static_cast<const __bf16*>(p.bias);
+
+  // the wave's feature groups: weight rows (A operands) and bias, kept
+  op8 wa[FPW][KSM], wb[FPW][KSM];
+  float bv[FPW][8];
+#pragma unroll
+  for (int fi = 0; fi < FPW; ++fi) {
+    const int fg = wave * FPW + fi;
+    const int frow = fg * 32 + 8 * (col >> 2) + (col & 3);
+#pragma unroll
+    for (int ks = 0; ks < KSM; ++ks) {
+      wa[fi][ks] = TT::zero();
+      wb[fi][ks] = TT::zero();
+      if (fg < p.nfg && ks < ks_n) {
+        wa[fi][ks] = TT::load8(Wg + (frow + 0) * p.C + ks * 32 + 8 * g);
+        wb[fi][ks] = TT::load8(Wg + (frow + 4) * p.C + ks * 32 + 8 * g);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bv[fi][e] = (Bg && fg < p.nfg) ? (float)Bg[fg * 32 + 8 * g + e] : 0.f;
+  }
+
+  uint4 xr[kPersistXL];
+  int u = blockIdx.x;
+  persist_load_x(p, u, total, tid, nthr, cvec, xr);
+  int buf = 0;
+  for (; u < total; u += gridDim.x, buf ^= 1) {
+    // this block's X rows into LDS, then the next block's loads in flight
+#pragma unroll
+    for (int m = 0; m < kPersistXL; ++m) {
+      const int f = tid + m * nthr;
+      if (f < kTokBlock * cvec) {
+        const int tw = f / cvec, cv = f - tw * cvec;
+        *reinterpret_cast<uint4*>(xbuf + (buf * kTokBlock + tw) * LDX + cv * 8) = xr[m];
+      }
+    }
+    __syncthreads();
+    persist_load_x(p, u + gridDim.x, total, tid, nthr, cvec, xr);
+
+    const int b = u / p.ngroups;
+    const int r0 = (u - b * p.ngroups) * p.rpw;
+    const int nreg = min(p.rpw, p.R - r0);
+    const int ntok = nreg * p.n;
+    const int64_t img = (int64_t)b * p.H * p.W * p.C;
+    const __bf16* xs = xbuf + buf * kTokBlock * LDX;
+#pragma unroll
+    for (int fi = 0; fi < FPW; ++fi) {
+      const int fg = wave * FPW + fi;
+      if (fg >= p.nfg) break;  // uniform
+      floatx4 acc[4][2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        acc[mt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+        acc[mt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KSM; ++ks) {
+        if (ks >= ks_n) break;  // uniform
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {  // rows past the block are zeros
+          const op8 xb = TT::load8(xs + (mt * 16 + col) * LDX + ks * 32 + 8 * g);
+          acc[mt][0] = TT::mma(wa[fi][ks], xb, acc[mt][0]);
+          acc[mt][1] = TT::mma(wb[fi][ks], xb, acc[mt][1]);
+        }
+      }
+      const int feat = fg * 32 + 8 * g;
+      const int tensor = feat / p.C, ch = feat - tensor * p.C;
+      const bool pooled = fg * 32 < 2 * p.C;  // uniform
+      __bf16* dst = static_cast<__bf16*>(tensor == 0 ? p.Q : tensor == 1 ? p.K : p.V) + img;
+      float* means = tensor == 0 ? p.Qr : p.Kr;
+      float racc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) racc[e] = 0.f;
+#pragma unroll 1
+      for (int mt = 0; mt < 4; ++mt) {
+        const int tw = mt * 16 + col;
+        const int t = tw < ntok ? block_token(0, tw, r0, nreg, 1, p.n, p.sh, p.sw, p.W, p.div_n, p.div_sw, p.div_S) : -1;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = acc[mt][0][e] + bv[fi][e];
+          o[4 + e] = acc[mt][1][e] + bv[fi][4 + e];
+        }
+        const op8 r = TT::from_f32(o);
+        if (t >= 0) *reinterpret_cast<op8*>(dst + t * p.C + ch) = r;
+        if (pooled) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) racc[e] += run_sum<SEG>(t >= 0 ? (float)r[e] : 0.f);
+          // the run leader owns its region's sum; a region ends at the run's
+          // end (SEG < 16) or when its last 16-token tile is done
+          const bool ends = SEG < 16 || ((mt + 1) * 16) % p.n == 0;
+          const int j = tw / p.n;
+          if (ends) {
+            if ((col & (SEG - 1)) == 0 && tw < ntok) {
+              float* m = means + ((int64_t)b * p.R + r0 + j) * p.C + ch;
+              const float inv = 1.0f / (float)p.n;
+              *reinterpret_cast<float4*>(m) = make_float4(racc[0] * inv, racc[1] * inv, racc[2] * inv, racc[3] * inv);
+              *reinterpret_cast<float4*>(m + 4) = make_float4(racc[4] * inv, racc[5] * inv, racc[6] * inv, racc[7] * inv);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) racc[e] = 0.f;
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, void* Q, void* K, void* V, float* Qr,
@@ -277,6 +436,34 @@ hipError_t launch_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, vo
   p.div_S = make_fastdiv(s.S);
   const int64_t nwg = (int64_t)s.B * p.ngroups;
   if (nwg >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  p.nunits = (int)nwg;
+  // persistent form: bf16, C <= 128, regions of <= 64 tokens in aligned runs
+  const int seg0 = s.n % 16 == 0 ? 16 : (s.n < 16 && 16 % s.n == 0) ? s.n : 0;
+  const int fpw = p.nfg <= kQkvWaves ? 1 : 2;
+  const int pwaves = (p.nfg + fpw - 1) / fpw;
+  const bool covered = pwaves * 64 * kPersistXL >= kTokBlock * (s.C / 8);
+  if (dtype == kBF16 && s.C <= 32 * kPersistKS && s.n <= kTokBlock && seg0 > 0 && covered) {
+    const int waves = pwaves;
+    const size_t lds = 2 * sizeof(__bf16) * kTokBlock * (s.C + 8);
+    const void* k12[] = {(const void*)&qkv_pool_persistent<1, 2, 1>, (const void*)&qkv_pool_persistent<1, 2, 2>,
+                         (const void*)&qkv_pool_persistent<1, 2, 4>, (const void*)&qkv_pool_persistent<1, 2, 8>,
+                         (const void*)&qkv_pool_persistent<1, 2, 16>};
+    const void* k14[] = {(const void*)&qkv_pool_persistent<1, 4, 1>, (const void*)&qkv_pool_persistent<1, 4, 2>,
+                         (const void*)&qkv_pool_persistent<1, 4, 4>, (const void*)&qkv_pool_persistent<1, 4, 8>,
+                         (const void*)&qkv_pool_persistent<1, 4, 16>};
+    const void* k24[] = {(const void*)&qkv_pool_persistent<2, 4, 1>, (const void*)&qkv_pool_persistent<2, 4, 2>,
+                         (const void*)&qkv_pool_persistent<2, 4, 4>, (const void*)&qkv_pool_persistent<2, 4, 8>,
+                         (const void*)&qkv_pool_persistent<2, 4, 16>};
+    const void* fn = (fpw == 2 ? k24 : s.C <= 64 ? k12 : k14)[__builtin_ctz(seg0)];
+    // as many workgroups as fit at once, each walking many units
+    int dev = 0, ncu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, waves * 64, lds) != hipSuccess)
+      return hipErrorInvalidValue;
+    const int grid = (int)std::min<int64_t>(nwg, (int64_t)ncu * std::max(1, per_cu));
+    void* args[] = {&p};
+    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(waves * 64), args, lds, stream);
+  }
   const int waves = p.nfg < kQkvWaves ? p.nfg : kQkvWaves;
   const size_t esz = dtype == kBF16 ? 2 : 4;
   // lanes per region run inside a 16-token tile, 0 when runs do not align
