@@ -266,29 +266,64 @@ __global__ __launch_bounds__(512) void qkv_pool_kernel(QkvParams p) {
 // block's loads in flight while the current one is computed (one barrier per
 // block); region sums stay in the run leader's registers and are written as
 // means when the region is complete.
+//
+// Token geometry that is the same for every unit is decoded once per thread:
+// a token of slot tw of a unit lies in the unit's region slot j = tw / n at
+// offset q = tw % n inside that region, and j is kept split as j = jy S + jx,
+// so the region of slot j follows from the unit's first region (ry0, rx0)
+// with one carry and no division.
 constexpr int kPersistKS = 4;  // k-steps kept in registers (C <= 128)
 constexpr int kPersistXL = 4;  // X loads per thread per block (the host checks they cover it)
 
-// X rows of unit u (image u / ngroups, regions from (u % ngroups) * rpw):
-// this thread's loads
-__device__ __forceinline__ void persist_load_x(const QkvParams& p, int u, int total, int tid, int nthr, int cvec,
-                                               uint4 (&xr)[kPersistXL]) {
-  const int b = u / p.ngroups;
-  const int r0 = (u - b * p.ngroups) * p.rpw;
-  const int nreg = min(p.rpw, p.R - r0);
-  const __bf16* Xg = static_cast<const __bf16*>(p.X) + (int64_t)b * p.H * p.W * p.C;
-#pragma unroll
-  for (int m = 0; m < kPersistXL; ++m) {
-    const int f = tid + m * nthr;
-    const int tw = f / cvec, cv = f - tw * cvec;
-    xr[m] = make_uint4(0u, 0u, 0u, 0u);
-    if (u < total && f < kTokBlock * cvec && tw < nreg * p.n) {
-      const int t = block_token(0, tw, r0, nreg, 1, p.n, p.sh, p.sw, p.W, p.div_n, p.div_sw, p.div_S);
-      xr[m] = *reinterpret_cast<const uint4*>(Xg + t * p.C + cv * 8);
-    }
+// packed slot word: bits 0-10 LDS vector index (element offset / 8), 11-16 jx,
+// 17-22 jy, 23-29 j (kNoSlot: no token)
+constexpr int kNoSlot = 127;
+
+__device__ __forceinline__ int slot_j(int w) { return (w >> 23) & 127; }
+__device__ __forceinline__ int slot_v8(int w) { return w & 2047; }
+
+// First token (index inside the image) of the region in slot w's region slot
+__device__ __forceinline__ int slot_region_token(int w, int ry0, int rx0, const QkvParams& p) {
+  int rx = rx0 + ((w >> 11) & 63), ry = ry0 + ((w >> 17) & 63);
+  if (rx >= p.S) {
+    rx -= p.S;
+    ++ry;
   }
+  return ry * p.sh * p.W + rx * p.sw;
 }
 
+__device__ __forceinline__ int pack_slot(int v8, int j, int S) {
+  if (j >= kNoSlot) return kNoSlot << 23;
+  const int jy = j / S, jx = j - jy * S;  // j < 64: jx, jy < 64
+  return v8 | (jx << 11) | (jy << 17) | (j << 23);
+}
+
+// The unit's image, first region (and its region row and column) and count
+struct UnitGeo {
+  int b, r0, nreg, ry0, rx0;
+};
+__device__ __forceinline__ UnitGeo unit_geo(int u, const QkvParams& p) {
+  UnitGeo q;
+  q.b = u / p.ngroups;
+  q.r0 = (u - q.b * p.ngroups) * p.rpw;
+  q.nreg = min(p.rpw, p.R - q.r0);
+  q.ry0 = q.r0 / p.S;
+  q.rx0 = q.r0 - q.ry0 * p.S;
+  return q;
+}
+
+// This thread's X loads of unit u (zeros for slots with no token)
+__device__ __forceinline__ void persist_load_x(const QkvParams& p, int u, const UnitGeo& q,
+                                               const int (&xoff)[kPersistXL], const int (&xslot)[kPersistXL],
+                                               uint4 (&xr)[kPersistXL]) {
+  const __bf16* Xg = static_cast<const __bf16*>(p.X) + (int64_t)q.b * p.H * p.W * p.C;
+#pragma unroll
+  for (int m = 0; m < kPersistXL; ++m) {
+    xr[m] = make_uint4(0u, 0u, 0u, 0u);
+    if (u < p.nunits && slot_j(xslot[m]) < q.nreg)
+      xr[m] = *reinterpret_cast<const uint4*>(Xg + slot_region_token(xslot[m], q.ry0, q.rx0, p) * p.C + xoff[m]);
+  }
+}
 template <int FPW, int KSM, int SEG>
 __global__ __launch_bounds__(512) void qkv_pool_persistent(QkvParams p) {
   typedef Tr<__bf16> TT;
@@ -328,29 +363,45 @@ __global__ __launch_bounds__(512) void qkv_pool_persistent(QkvParams p) {
     for (int e = 0; e < 8; ++e) bv[fi][e] = (Bg && fg < p.nfg) ? (float)Bg[fg * 32 + 8 * g + e] : 0.f;
   }
 
+  // this thread's X loads: image offset past the region's first token, slot
+  int xoff[kPersistXL], xslot[kPersistXL];
+#pragma unroll
+  for (int m = 0; m < kPersistXL; ++m) {
+    const int f = tid + m * nthr;
+    const int tw = f / cvec, cv = f - tw * cvec;
+    const int q = tw % p.n, qy = q / p.sw, qx = q - qy * p.sw;
+    xoff[m] = (qy * p.W + qx) * p.C + cv * 8;
+    xslot[m] = pack_slot((tw * LDX + cv * 8) >> 3, f < kTokBlock * cvec ? tw / p.n : kNoSlot, p.S);
+  }
+  // this lane's output tokens (slot mt * 16 + col): offset past the region's
+  // first token, slot
+  int eoff[4], eslot[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int tw = mt * 16 + col;
+    const int q = tw % p.n, qy = q / p.sw, qx = q - qy * p.sw;
+    eoff[mt] = (qy * p.W + qx) * p.C;
+    eslot[mt] = pack_slot(0, tw / p.n, p.S);
+  }
+
   uint4 xr[kPersistXL];
   int u = blockIdx.x;
-  persist_load_x(p, u, total, tid, nthr, cvec, xr);
+  UnitGeo nxt = unit_geo(u, p);
+  persist_load_x(p, u, nxt, xoff, xslot, xr);
   int buf = 0;
   for (; u < total; u += gridDim.x, buf ^= 1) {
     // this block's X rows into LDS, then the next block's loads in flight
+    __bf16* xs = xbuf + buf * kTokBlock * LDX;
 #pragma unroll
-    for (int m = 0; m < kPersistXL; ++m) {
-      const int f = tid + m * nthr;
-      if (f < kTokBlock * cvec) {
-        const int tw = f / cvec, cv = f - tw * cvec;
-        *reinterpret_cast<uint4*>(xbuf + (buf * kTokBlock + tw) * LDX + cv * 8) = xr[m];
-      }
-    }
+    for (int m = 0; m < kPersistXL; ++m)
+      if (slot_j(xslot[m]) != kNoSlot) *reinterpret_cast<uint4*>(xs + slot_v8(xslot[m]) * 8) = xr[m];
     __syncthreads();
-    persist_load_x(p, u + gridDim.x, total, tid, nthr, cvec, xr);
+    const UnitGeo cur = nxt;
+    nxt = unit_geo(u + gridDim.x, p);
+    persist_load_x(p, u + gridDim.x, nxt, xoff, xslot, xr);
 
-    const int b = u / p.ngroups;
-    const int r0 = (u - b * p.ngroups) * p.rpw;
-    const int nreg = min(p.rpw, p.R - r0);
-    const int ntok = nreg * p.n;
+    const int b = cur.b, r0 = cur.r0, nreg = cur.nreg, ry0 = cur.ry0, rx0 = cur.rx0;
     const int64_t img = (int64_t)b * p.H * p.W * p.C;
-    const __bf16* xs = xbuf + buf * kTokBlock * LDX;
 #pragma unroll
     for (int fi = 0; fi < FPW; ++fi) {
       const int fg = wave * FPW + fi;
@@ -374,34 +425,34 @@ __global__ __launch_bounds__(512) void qkv_pool_persistent(QkvParams p) {
       const int feat = fg * 32 + 8 * g;
       const int tensor = feat / p.C, ch = feat - tensor * p.C;
       const bool pooled = fg * 32 < 2 * p.C;  // uniform
-      __bf16* dst = static_cast<__bf16*>(tensor == 0 ? p.Q : tensor == 1 ? p.K : p.V) + img;
-      float* means = tensor == 0 ? p.Qr : p.Kr;
+      __bf16* dst = static_cast<__bf16*>(tensor == 0 ? p.Q : tensor == 1 ? p.K : p.V) + img + ch;
+      float* means = (tensor == 0 ? p.Qr : p.Kr) + ((int64_t)b * p.R + r0) * p.C + ch;
+      const float inv = 1.0f / (float)p.n;
       float racc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) racc[e] = 0.f;
-#pragma unroll 1
+#pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const int tw = mt * 16 + col;
-        const int t = tw < ntok ? block_token(0, tw, r0, nreg, 1, p.n, p.sh, p.sw, p.W, p.div_n, p.div_sw, p.div_S) : -1;
+        const int j = slot_j(eslot[mt]);
+        const bool ok = j < nreg;
         float o[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           o[e] = acc[mt][0][e] + bv[fi][e];
           o[4 + e] = acc[mt][1][e] + bv[fi][4 + e];
         }
-        const op8 r = TT::from_f32(o);
-        if (t >= 0) *reinterpret_cast<op8*>(dst + t * p.C + ch) = r;
+        const op8 r = TT::from_f32(o);  // the rounded outputs
+        if (ok) *reinterpret_cast<op8*>(dst + slot_region_token(eslot[mt], ry0, rx0, p) * p.C + eoff[mt]) = r;
         if (pooled) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) racc[e] += run_sum<SEG>(t >= 0 ? (float)r[e] : 0.f);
-          // the run leader owns its region's sum; a region ends at the run's
-          // end (SEG < 16) or when its last 16-token tile is done
-          const bool ends = SEG < 16 || ((mt + 1) * 16) % p.n == 0;
-          const int j = tw / p.n;
-          if (ends) {
-            if ((col & (SEG - 1)) == 0 && tw < ntok) {
-              float* m = means + ((int64_t)b * p.R + r0 + j) * p.C + ch;
-              const float inv = 1.0f / (float)p.n;
+          for (int e = 0; e < 8; ++e) racc[e] += ok ? (float)r[e] : 0.f;
+          // a region ends at its run's end (SEG < 16) or with its last
+          // 16-token tile; its run leader then holds the sum
+          if (SEG < 16 || ((mt + 1) * 16) % p.n == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) racc[e] = run_sum<SEG>(racc[e]);
+            if ((col & (SEG - 1)) == 0 && ok) {
+              float* m = means + j * p.C;
               *reinterpret_cast<float4*>(m) = make_float4(racc[0] * inv, racc[1] * inv, racc[2] * inv, racc[3] * inv);
               *reinterpret_cast<float4*>(m + 4) = make_float4(racc[4] * inv, racc[5] * inv, racc[6] * inv, racc[7] * inv);
             }
