@@ -63,6 +63,7 @@ struct AttnParams {
   int nitems;  // B * R * nqb * nhg
   int lg_oct;  // log2(8 * HG * D / VEC): pair items per 8-pair octet of a chunk
   int nbuf;    // LDS chunk buffers (2: double-buffered, when kv spans several chunks)
+  int own_tab; // single-chunk kernel: every attention wave builds its own key table
   float c;     // softmax scale * log2(e)
   FastDiv div_n, div_sw, div_S;
   // local context term fused into the single-chunk kernel's epilogue
@@ -246,7 +247,7 @@ __device__ __forceinline__ void store_kv(const AttnParams& p, int tid, T* Ks, T*
 template <typename T, bool MULTI, bool RAGGED>
 __device__ __forceinline__ void compute_chunk(const AttnParams& p, const Item& it, int wave, int g, int col,
                                               const T* Ks, const T* Vt, int ldk, int ldv, int nvalid,
-                                              int a16, int a32, const typename Tr<T>::op8& ones,
+                                              const typename Tr<T>::op8& ones,
                                               Units<T>& us) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
@@ -284,7 +285,7 @@ __device__ __forceinline__ void compute_chunk(const AttnParams& p, const Item& i
     for (int st = 0; st < KC / 32; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
-    mx = wave_max_groups(mx, a16, a32);
+    mx = wave_max_groups(mx);
     // online softmax: with a single chunk the running max starts at -inf and
     // the accumulators at 0, so there is nothing to rescale
     const float mnew = MULTI ? fmaxf(us.m[uu], mx) : mx;
@@ -360,7 +361,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
   const int lane = tid & 63;
   const int g = lane >> 4;      // lane group: contraction slots 8g..8g+7
   const int col = lane & 15;    // query column of the 16-query tile
-  const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
   const op8 ones = TT::ones();
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
       store_kv<T, NV>(p, tid, Ks, Vt, ldk, ldv, kreg, vreg);
       __syncthreads();
       if (MULTI && ch + 1 < nchunks) load_kv<T, NV, TOK>(p, it, tid, rtab, c0 + KC, kreg, vreg);  // next chunk in flight
-      compute_chunk<T, MULTI, RAGGED>(p, it, wave, g, col, Ks, Vt, ldk, ldv, min(KC, p.kv - c0), a16, a32, ones, us);
+      compute_chunk<T, MULTI, RAGGED>(p, it, wave, g, col, Ks, Vt, ldk, ldv, min(KC, p.kv - c0), ones, us);
     }
   }
   store_outputs<T>(p, it, us, bad);
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   constexpr int LNB = LCE ? ((LR + 4) * ((2 * LX + 5) / 2) * 4 + 63) / 64 : 1;  // halo items per lane
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int rtab[KC];
+  __shared__ int rtab[8 * KC];  // token offset of every routed key (per attention wave, or one shared)
   __shared__ int sbad;
 
   const int tid = threadIdx.x;
@@ -446,7 +446,6 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int col = lane & 15;
-  const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
   const op8 ones = TT::ones();
   const int ldv = KC + TT::PADV;
 
@@ -471,12 +470,27 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   // ---- attention waves: query operands of all (<= 4) tiles first (they do
   // not depend on the routing, so their loads overlap the routing-table
   // round trip); convolution waves: the V halo and the filter
+  // ---- attention waves that build a key table: the routing entry of key
+  // kappa = lane first (the K/V addresses wait on it; vector loads complete in
+  // order, so anything issued before it would delay it); attention waves: the
+  // query operands of all (<= 4) tiles; convolution waves: the V halo and the
+  // filter
+  const bool own = p.own_tab;  // uniform: every attention wave builds its own key table
+  const bool builds = att && head_ok && (own || head == 0);
   op8 qop[MAXT];
   int qoff[MAXT];
+  int rid = 0, ktok = 0;  // key lane's routed region, token offset inside it
   LceTile lt;
   uint4 ha[LNB], hb[LNB];
   LceW<T> lw;
   if (att) {
+    if (builds && lane < p.kv) {
+      int tk, tx;
+      const int jr = fdiv(lane, p.div_n, &tk);
+      const int ty = fdiv(tk, p.div_sw, &tx);
+      ktok = ty * p.W + tx;
+      rid = p.idx[((int64_t)it.b * p.R + it.i) * p.topk + jr];
+    }
 #pragma unroll
     for (int t = 0; t < MAXT; ++t) {
       const int qi = it.q0 + t * 16 + col;
@@ -503,26 +517,30 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
     }
   }
 
-  if (tid == 0) sbad = 0;
-  __syncthreads();
-  read_route_tokens(p, it, tid, rtab, &sbad);
-  __syncthreads();
-  const bool bad = sbad;
-
+  // ---- the routing row -> a table of key token offsets: built by every
+  // attention wave for itself (no workgroup barrier; measured faster with 8
+  // heads per workgroup) or by wave 0 for the whole workgroup
+  bool bad = false;
+  if (builds) {
+    const bool ok = rid >= 0 && rid < p.R;
+    bad = __builtin_amdgcn_ballot_w64(lane < p.kv && !ok) != 0;  // uniform
+    rtab[(own ? head : 0) * KC + lane] = region_corner(p, ok ? rid : 0) + ktok;
+    if (!own && lane == 0) sbad = bad;
+  }
+  if (own) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  } else {
+    __syncthreads();
+    bad = sbad;
+  }
   op8 kop[2][2];
-  if (att) {
-    if (head_ok && !bad) {
-      // ---- K operands: row rr = col of the tile for (32-key step st, tile
-      // tb) is key st*32 + 8*(rr/4) + (rr%4) + 4*tb; slots = channels 8g..8g+7
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
-          kop[st][tb] = (!RAGGED || key < p.kv) ? TT::load8(Kg + rtab[key] * p.C + ch0 + 8 * g) : TT::zero();
-        }
-      // V slice: pair item f = lane + 64 m -> channel vector cv = f % CVH, key
-      // pair p2 = f / CVH (keys 2 p2, 2 p2 + 1)
+  if (att && head_ok) {
+    const int* wtab = rtab + (own ? head : 0) * KC;
+    if (!bad) {
+      // V slice first (it is transposed through LDS before any product):
+      // pair item f = lane + 64 m -> channel vector cv = f % CVH, key pair
+      // p2 = f / CVH (keys 2 p2, 2 p2 + 1)
       uint4 vreg[PAIRS][2];
 #pragma unroll
       for (int m = 0; m < PAIRS; ++m) {
@@ -531,10 +549,19 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
 #pragma unroll
         for (int k1 = 0; k1 < 2; ++k1) {
           const int key = 2 * p2 + k1;
-          vreg[m][k1] = (!RAGGED || key < p.kv) ? *reinterpret_cast<const uint4*>(Vg + rtab[key] * p.C + ch0 + cv * VEC)
+          vreg[m][k1] = (!RAGGED || key < p.kv) ? *reinterpret_cast<const uint4*>(Vg + wtab[key] * p.C + ch0 + cv * VEC)
                                                : make_uint4(0u, 0u, 0u, 0u);
         }
       }
+      // K operands: row rr = col of the tile for (32-key step st, tile tb) is
+      // key st*32 + 8*(rr/4) + (rr%4) + 4*tb; slots = channels 8g..8g+7
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
+          kop[st][tb] = (!RAGGED || key < p.kv) ? TT::load8(Kg + wtab[key] * p.C + ch0 + 8 * g) : TT::zero();
+        }
 #pragma unroll
       for (int m = 0; m < PAIRS; ++m) {
         const int f = lane + 64 * m;
@@ -560,7 +587,13 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
       lce_store_results<LR, LX>(reinterpret_cast<float*>(larea), lt, lane & 31, (lane >> 5) & 1, acc);
     }
   }
-  __syncthreads();  // V^T tiles and convolution results written
+  if constexpr (LCE) {
+    __syncthreads();  // convolution results (and V^T tiles) written
+  } else {
+    // the wave reads only its own V^T tile
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
   if (!att || !head_ok) return;
 
   T* Og = static_cast<T*>(p.O) + it.img;
@@ -615,7 +648,7 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
-    mx = wave_max_groups(mx, a16, a32);
+    mx = wave_max_groups(mx);
     const float mc = mx * p.c;
     floatx4 acc[3] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -772,6 +805,9 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
       fn = ragged ? (one ? (const void*)&attend_head_kernel<float, true, 1, 0, 0> : (const void*)&attend_head_kernel<float, true, 4, 0, 0>)
                   : (one ? (const void*)&attend_head_kernel<float, false, 1, 0, 0> : (const void*)&attend_head_kernel<float, false, 4, 0, 0>);
     }
+    // per-wave key tables pay off when many head waves would otherwise wait on
+    // one: 8 heads per workgroup measured faster, 2 and 4 slower
+    p.own_tab = p.HG >= 8;
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(waves * 64), args, lds, stream);
     if (e != hipSuccess || !lce || fuse) return e;

@@ -126,13 +126,30 @@ struct Tr<float> {
   }
 };
 
-// Max over the 4 lane groups that share lane % 16; a16/a32 are the byte
-// addresses ((lane ^ 16) * 4, (lane ^ 32) * 4) for ds_bpermute, computed once.
-__device__ inline float wave_max_groups(float v, int a16, int a32) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute(a16, __float_as_int(v))));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_bpermute(a32, __float_as_int(v))));
-  return v;
+// Cross-lane-group exchanges without LDS: v_permlane16_swap with both
+// operands equal leaves {v[lane], v[lane ^ 16]} in the lane's two results,
+// and v_permlane32_swap {v[lane], v[lane ^ 32]}. The two values are combined
+// by a commutative operation, so the order in which the lane receives them
+// does not matter and every lane of a group gets the same bits.
+__device__ inline float xor16_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ inline float xor32_pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor16_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float xor32_pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max over the 4 lane groups that share lane % 16.
+__device__ inline float wave_max_groups(float v) { return xor32_pair_max(xor16_pair_max(v)); }
 
 // Channel-row swizzle of the V^T tile: column blocks of 8 keys are permuted
 // by an XOR that depends on the row's 8-row group, so the transposed writes of
@@ -163,11 +180,7 @@ __device__ inline void store_vt_pair(float* Vt, int ldv, int row0, int col, cons
     *reinterpret_cast<uint2*>(Vt + (row0 + e) * ldv + col) = make_uint2(wa[e], wb[e]);
 }
 
-// Sum over the 4 lane groups that share lane % 16 (addresses as above).
-__device__ inline float wave_sum_groups(float v, int a16, int a32) {
-  v += __int_as_float(__builtin_amdgcn_ds_bpermute(a16, __float_as_int(v)));
-  v += __int_as_float(__builtin_amdgcn_ds_bpermute(a32, __float_as_int(v)));
-  return v;
-}
+// Sum over the 4 lane groups that share lane % 16, as (g0 + g1) + (g2 + g3).
+__device__ inline float wave_sum_groups(float v) { return xor32_pair_sum(xor16_pair_sum(v)); }
 
 }  // namespace bra

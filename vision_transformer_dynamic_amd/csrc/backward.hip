@@ -153,7 +153,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, col = lane & 15;
-  const int a16 = (lane ^ 16) << 2, a32 = (lane ^ 32) << 2;
   const int ldk = KC + TT::PADV;
 
   int w = xcd_remap();
@@ -219,7 +218,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       for (int e = 0; e < 8; ++e) dpart += (float)dop[e] * (float)o[e];
     }
   }
-  const float Dq = wave_sum_groups(dpart, a16, a32);
+  const float Dq = wave_sum_groups(dpart);
   __syncthreads();
   const bool bad = sbad;
   T* dQg = static_cast<T*>(p.dQ) + img;
@@ -268,7 +267,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
           if (RAGGED && c0 + st * 32 + 8 * g + e >= p.kv) s[st][e] = -INFINITY;
           mx = fmaxf(mx, s[st][e]);
         }
-      mx = wave_max_groups(mx, a16, a32);
+      mx = wave_max_groups(mx);
       const float mn = fmaxf(m, mx);
       float add = 0.f;
 #pragma unroll
@@ -280,7 +279,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       __syncthreads();  // tok reused by the next chunk
     }
   }
-  float lse = MULTI ? m * p.c + __builtin_log2f(wave_sum_groups(l, a16, a32)) : 0.f;
+  float lse = MULTI ? m * p.c + __builtin_log2f(wave_sum_groups(l)) : 0.f;
 
   // ---- pass 2: P, dP, dZ and dQ^T += K^T dZ^T
   floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
@@ -336,13 +335,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
-      mx = wave_max_groups(mx, a16, a32);
+      mx = wave_max_groups(mx);
       float sum = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f((s[st][e] - mx) * p.c);
-      lse = mx * p.c + __builtin_log2f(wave_sum_groups(sum, a16, a32));
+      lse = mx * p.c + __builtin_log2f(wave_sum_groups(sum));
     }
     __syncthreads();  // K^T tile complete
     const int vrow = 8 * (col >> 2) + (col & 3);
