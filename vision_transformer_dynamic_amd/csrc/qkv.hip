@@ -41,11 +41,13 @@ struct QkvParams {
   float* Qr;  // [B, R, C]
   float* Kr;
   int H, W, C, S, sh, sw, n, R;
+  int B;
   int rpw;      // regions per workgroup (n <= 64), else 1
   int nsub;     // 64-token blocks per region (n > 64), else 1
   int ngroups;  // workgroups per image
   int nfg;      // feature groups (3C / 32)
   int nunits;   // persistent form: images x groups
+  int end_mask; // persistent form: bit t set when a region ends with 16-token tile t
   FastDiv div_n, div_sw, div_S;
 };
 
@@ -261,11 +263,11 @@ __global__ __launch_bounds__(512) void qkv_pool_kernel(QkvParams p) {
 // Persistent form (bf16, C <= 128, regions of at most 64 tokens whose runs
 // align with 16-token tiles): the grid is sized to the machine and every
 // workgroup walks units (image, region group) u, u + gridDim.x, ... Each
-// wave loads the weight rows and bias of its feature groups once and keeps
-// them in registers; X blocks alternate between two LDS buffers, the next
-// block's loads in flight while the current one is computed (one barrier per
-// block); region sums stay in the run leader's registers and are written as
-// means when the region is complete.
+// wave owns one feature group of 32 outputs (3C/32 waves) and loads its
+// weight rows and bias once, keeping them in registers; X blocks alternate
+// between two LDS buffers, the next block's loads in flight while the current
+// one is computed (one barrier per block); region sums stay in the run
+// leader's registers and are written as means when the region is complete.
 //
 // Token geometry that is the same for every unit is decoded once per thread:
 // a token of slot tw of a unit lies in the unit's region slot j = tw / n at
@@ -273,6 +275,7 @@ __global__ __launch_bounds__(512) void qkv_pool_kernel(QkvParams p) {
 // so the region of slot j follows from the unit's first region (ry0, rx0)
 // with one carry and no division.
 constexpr int kPersistKS = 4;  // k-steps kept in registers (C <= 128)
+constexpr int kPersistMaxWaves = 3 * kPersistKS;  // one wave per feature group of 32 outputs
 constexpr int kPersistXL = 4;  // X loads per thread per block (the host checks they cover it)
 
 // packed slot word: bits 0-10 LDS vector index (element offset / 8), 11-16 jx,
@@ -312,20 +315,39 @@ __device__ __forceinline__ UnitGeo unit_geo(int u, const QkvParams& p) {
   return q;
 }
 
+// Raw buffer accesses. A lane with nothing to load or store uses an offset
+// past the buffer's range: the buffer unit returns zeros for such a load and
+// drops such a store, so every load and store instruction is issued
+// unconditionally. That keeps the number of memory operations after the X
+// prefetch fixed, so the wait for the prefetch at the top of the next unit
+// does not also wait for this unit's output stores (vector memory counters
+// count stores too).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kRawBufferWord3 = 0x00020000;  // raw (untyped) access, 32-bit data format
+constexpr int kOutOfRange = (int)0x80000000u;  // past every range the host allows (< 2^31 bytes)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
 // This thread's X loads of unit u (zeros for slots with no token)
 __device__ __forceinline__ void persist_load_x(const QkvParams& p, int u, const UnitGeo& q,
                                                const int (&xoff)[kPersistXL], const int (&xslot)[kPersistXL],
                                                uint4 (&xr)[kPersistXL]) {
-  const __bf16* Xg = static_cast<const __bf16*>(p.X) + (int64_t)q.b * p.H * p.W * p.C;
+  const uint32_t img_bytes = (uint32_t)p.H * p.W * p.C * 2u;
+  const __amdgpu_buffer_rsrc_t rx =
+      raw_buffer(static_cast<const __bf16*>(p.X) + (int64_t)min(q.b, p.B - 1) * p.H * p.W * p.C, img_bytes);
 #pragma unroll
   for (int m = 0; m < kPersistXL; ++m) {
-    xr[m] = make_uint4(0u, 0u, 0u, 0u);
-    if (u < p.nunits && slot_j(xslot[m]) < q.nreg)
-      xr[m] = *reinterpret_cast<const uint4*>(Xg + slot_region_token(xslot[m], q.ry0, q.rx0, p) * p.C + xoff[m]);
+    const bool ok = u < p.nunits && slot_j(xslot[m]) < q.nreg;
+    const int off = ok ? (slot_region_token(xslot[m], q.ry0, q.rx0, p) * p.C + xoff[m]) * 2 : kOutOfRange;
+    xr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
   }
 }
-template <int FPW, int KSM, int SEG>
-__global__ __launch_bounds__(512) void qkv_pool_persistent(QkvParams p) {
+
+template <int KSM, int SEG>
+__global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(QkvParams p) {
+  constexpr int FPW = 1;  // feature groups per wave
   typedef Tr<__bf16> TT;
   typedef TT::op8 op8;
   const int LDX = p.C + 8;
@@ -384,84 +406,112 @@ __global__ __launch_bounds__(512) void qkv_pool_persistent(QkvParams p) {
     eslot[mt] = pack_slot(0, tw / p.n, p.S);
   }
 
+  // X rows of this thread's slots into buffer `bufi` of LDS
+  auto stage_x = [&](int bufi, const uint4 (&v)[kPersistXL]) {
+    __bf16* xs = xbuf + bufi * kTokBlock * LDX;
+#pragma unroll
+    for (int m = 0; m < kPersistXL; ++m)
+      if (slot_j(xslot[m]) != kNoSlot) *reinterpret_cast<uint4*>(xs + slot_v8(xslot[m]) * 8) = v[m];
+  };
   uint4 xr[kPersistXL];
   int u = blockIdx.x;
   UnitGeo nxt = unit_geo(u, p);
   persist_load_x(p, u, nxt, xoff, xslot, xr);
+  stage_x(0, xr);
   int buf = 0;
   for (; u < total; u += gridDim.x, buf ^= 1) {
-    // this block's X rows into LDS, then the next block's loads in flight
-    __bf16* xs = xbuf + buf * kTokBlock * LDX;
-#pragma unroll
-    for (int m = 0; m < kPersistXL; ++m)
-      if (slot_j(xslot[m]) != kNoSlot) *reinterpret_cast<uint4*>(xs + slot_v8(xslot[m]) * 8) = xr[m];
+    // buffer `buf` holds this unit's X rows; every wave is done with the other
+    // buffer (the previous unit), which receives the next unit's rows at the
+    // end of this iteration, after this unit's stores (so waiting for those
+    // loads there does not wait for the stores)
     __syncthreads();
+    const __bf16* xs = xbuf + buf * kTokBlock * LDX;
     const UnitGeo cur = nxt;
     nxt = unit_geo(u + gridDim.x, p);
     persist_load_x(p, u + gridDim.x, nxt, xoff, xslot, xr);
 
     const int b = cur.b, r0 = cur.r0, nreg = cur.nreg, ry0 = cur.ry0, rx0 = cur.rx0;
     const int64_t img = (int64_t)b * p.H * p.W * p.C;
+    const uint32_t img_bytes = (uint32_t)p.H * p.W * p.C * 2u;
+    const uint32_t mean_bytes = (uint32_t)p.R * p.C * 4u;
 #pragma unroll
     for (int fi = 0; fi < FPW; ++fi) {
-      const int fg = wave * FPW + fi;
-      if (fg >= p.nfg) break;  // uniform
-      floatx4 acc[4][2];
+      // a wave past the last feature group computes on zero weights and its
+      // stores go out of range (no branch: the store count stays fixed)
+      const bool fvalid = wave * FPW + fi < p.nfg;  // uniform
+      const int fg = fvalid ? wave * FPW + fi : p.nfg - 1;
+      const int feat = fg * 32 + 8 * g;
+      const int tensor = fg * 32 / p.C;  // uniform: the wave's 32 features lie in one of Q, K, V
+      const int ch = feat - tensor * p.C;
+      const bool pooled = fvalid && tensor < 2;  // uniform
+      const __amdgpu_buffer_rsrc_t rdst =
+          raw_buffer(static_cast<__bf16*>(tensor == 0 ? p.Q : tensor == 1 ? p.K : p.V) + img, img_bytes);
+      const float inv = 1.0f / (float)p.n;
+      float racc[8];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        acc[mt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-        acc[mt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 8; ++e) racc[e] = 0.f;
+      // two halves of two 16-token tiles each: products, then their epilogue
+      // (half the accumulators live at a time; the first half's epilogue
+      // overlaps the second half's products)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+      floatx4 acc[2][2];  // accumulated onto the bias
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        acc[m2][0] = floatx4{bv[fi][0], bv[fi][1], bv[fi][2], bv[fi][3]};
+        acc[m2][1] = floatx4{bv[fi][4], bv[fi][5], bv[fi][6], bv[fi][7]};
       }
 #pragma unroll
       for (int ks = 0; ks < KSM; ++ks) {
         if (ks >= ks_n) break;  // uniform
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {  // rows past the block are zeros
+        for (int m2 = 0; m2 < 2; ++m2) {  // rows past the block are zeros
+          const int mt = 2 * hh + m2;
           const op8 xb = TT::load8(xs + (mt * 16 + col) * LDX + ks * 32 + 8 * g);
-          acc[mt][0] = TT::mma(wa[fi][ks], xb, acc[mt][0]);
-          acc[mt][1] = TT::mma(wb[fi][ks], xb, acc[mt][1]);
+          acc[m2][0] = TT::mma(wa[fi][ks], xb, acc[m2][0]);
+          acc[m2][1] = TT::mma(wb[fi][ks], xb, acc[m2][1]);
         }
       }
-      const int feat = fg * 32 + 8 * g;
-      const int tensor = feat / p.C, ch = feat - tensor * p.C;
-      const bool pooled = fg * 32 < 2 * p.C;  // uniform
-      __bf16* dst = static_cast<__bf16*>(tensor == 0 ? p.Q : tensor == 1 ? p.K : p.V) + img + ch;
-      float* means = (tensor == 0 ? p.Qr : p.Kr) + ((int64_t)b * p.R + r0) * p.C + ch;
-      const float inv = 1.0f / (float)p.n;
-      float racc[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) racc[e] = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int mt = 2 * hh + m2;
         const int j = slot_j(eslot[mt]);
         const bool ok = j < nreg;
         float o[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[e] = acc[mt][0][e] + bv[fi][e];
-          o[4 + e] = acc[mt][1][e] + bv[fi][4 + e];
+          o[e] = acc[m2][0][e];
+          o[4 + e] = acc[m2][1][e];
         }
         const op8 r = TT::from_f32(o);  // the rounded outputs
-        if (ok) *reinterpret_cast<op8*>(dst + slot_region_token(eslot[mt], ry0, rx0, p) * p.C + eoff[mt]) = r;
+        const int soff =
+            ok && fvalid ? (slot_region_token(eslot[mt], ry0, rx0, p) * p.C + eoff[mt] + ch) * 2 : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), rdst, soff, 0, 0);
         if (pooled) {
+          // a run that is not a region of this unit sums garbage that is never written
 #pragma unroll
-          for (int e = 0; e < 8; ++e) racc[e] += ok ? (float)r[e] : 0.f;
+          for (int e = 0; e < 8; ++e) racc[e] += (float)r[e];
           // a region ends at its run's end (SEG < 16) or with its last
           // 16-token tile; its run leader then holds the sum
-          if (SEG < 16 || ((mt + 1) * 16) % p.n == 0) {
+          if ((p.end_mask >> mt) & 1) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) racc[e] = run_sum<SEG>(racc[e]);
-            if ((col & (SEG - 1)) == 0 && ok) {
-              float* m = means + j * p.C;
-              *reinterpret_cast<float4*>(m) = make_float4(racc[0] * inv, racc[1] * inv, racc[2] * inv, racc[3] * inv);
-              *reinterpret_cast<float4*>(m + 4) = make_float4(racc[4] * inv, racc[5] * inv, racc[6] * inv, racc[7] * inv);
-            }
+            for (int e = 0; e < 8; ++e) racc[e] = run_sum<SEG>(racc[e]) * inv;
+            const __amdgpu_buffer_rsrc_t rmean =
+                raw_buffer((tensor == 0 ? p.Qr : p.Kr) + (int64_t)b * p.R * p.C, mean_bytes);
+            const int moff = ((col & (SEG - 1)) == 0 && ok) ? ((r0 + j) * p.C + ch) * 4 : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, make_float4(racc[0], racc[1], racc[2], racc[3])), rmean, moff, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, make_float4(racc[4], racc[5], racc[6], racc[7])), rmean,
+                moff == kOutOfRange ? kOutOfRange : moff + 16, 0, 0);
 #pragma unroll
             for (int e = 0; e < 8; ++e) racc[e] = 0.f;
           }
         }
       }
+      }  // hh
     }
+    stage_x(buf ^ 1, xr);
   }
 }
 
@@ -471,7 +521,7 @@ hipError_t launch_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, vo
                            float* Kr, const Shape& s, int dtype, hipStream_t stream) {
   QkvParams p;
   p.X = X; p.Wt = Wqkv; p.bias = bqkv; p.Q = Q; p.K = K; p.V = V; p.Qr = Qr; p.Kr = Kr;
-  p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S; p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R;
+  p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S; p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R; p.B = s.B;
   if (s.n <= kTokBlock) {
     // whole regions up to 64 tokens, with their sums in at most 32 KB of LDS
     p.rpw = min(kTokBlock / s.n, max(1, 4096 / s.C));
@@ -490,22 +540,23 @@ hipError_t launch_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, vo
   p.nunits = (int)nwg;
   // persistent form: bf16, C <= 128, regions of <= 64 tokens in aligned runs
   const int seg0 = s.n % 16 == 0 ? 16 : (s.n < 16 && 16 % s.n == 0) ? s.n : 0;
-  const int fpw = p.nfg <= kQkvWaves ? 1 : 2;
-  const int pwaves = (p.nfg + fpw - 1) / fpw;
+  const int pwaves = p.nfg;  // one wave per feature group
   const bool covered = pwaves * 64 * kPersistXL >= kTokBlock * (s.C / 8);
-  if (dtype == kBF16 && s.C <= 32 * kPersistKS && s.n <= kTokBlock && seg0 > 0 && covered) {
+  // (raw buffer offsets: one image's bytes below 2^31)
+  const bool fits = 2 * (int64_t)s.H * s.W * s.C < (int64_t(1) << 31);
+  if (dtype == kBF16 && s.C <= 32 * kPersistKS && s.n <= kTokBlock && seg0 > 0 && covered && fits) {
     const int waves = pwaves;
     const size_t lds = 2 * sizeof(__bf16) * kTokBlock * (s.C + 8);
-    const void* k12[] = {(const void*)&qkv_pool_persistent<1, 2, 1>, (const void*)&qkv_pool_persistent<1, 2, 2>,
-                         (const void*)&qkv_pool_persistent<1, 2, 4>, (const void*)&qkv_pool_persistent<1, 2, 8>,
-                         (const void*)&qkv_pool_persistent<1, 2, 16>};
-    const void* k14[] = {(const void*)&qkv_pool_persistent<1, 4, 1>, (const void*)&qkv_pool_persistent<1, 4, 2>,
-                         (const void*)&qkv_pool_persistent<1, 4, 4>, (const void*)&qkv_pool_persistent<1, 4, 8>,
-                         (const void*)&qkv_pool_persistent<1, 4, 16>};
-    const void* k24[] = {(const void*)&qkv_pool_persistent<2, 4, 1>, (const void*)&qkv_pool_persistent<2, 4, 2>,
-                         (const void*)&qkv_pool_persistent<2, 4, 4>, (const void*)&qkv_pool_persistent<2, 4, 8>,
-                         (const void*)&qkv_pool_persistent<2, 4, 16>};
-    const void* fn = (fpw == 2 ? k24 : s.C <= 64 ? k12 : k14)[__builtin_ctz(seg0)];
+    p.end_mask = 0;
+    for (int t = 0; t < 4; ++t)
+      if (seg0 < 16 || ((t + 1) * 16) % s.n == 0) p.end_mask |= 1 << t;
+    const void* k2[] = {(const void*)&qkv_pool_persistent<2, 1>, (const void*)&qkv_pool_persistent<2, 2>,
+                        (const void*)&qkv_pool_persistent<2, 4>, (const void*)&qkv_pool_persistent<2, 8>,
+                        (const void*)&qkv_pool_persistent<2, 16>};
+    const void* k4[] = {(const void*)&qkv_pool_persistent<4, 1>, (const void*)&qkv_pool_persistent<4, 2>,
+                        (const void*)&qkv_pool_persistent<4, 4>, (const void*)&qkv_pool_persistent<4, 8>,
+                        (const void*)&qkv_pool_persistent<4, 16>};
+    const void* fn = (s.C <= 64 ? k2 : k4)[__builtin_ctz(seg0)];
     // as many workgroups as fit at once, each walking many units
     int dev = 0, ncu = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
