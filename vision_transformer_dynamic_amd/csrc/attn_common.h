@@ -20,6 +20,8 @@ typedef float floatx8 __attribute__((ext_vector_type(8)));
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 constexpr int KC = 64;       // keys per chunk
 constexpr int D = kHeadDim;  // 32
@@ -37,10 +39,16 @@ struct Tr<__bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static inline op8 load8(const __bf16* p) { return *reinterpret_cast<const op8*>(p); }
+  // converted in pairs: one v_cvt_pk_bf16_f32 (round to nearest even) per
+  // pair, with no repacking of single conversions
   __device__ static inline op8 from_f32(const float* v) {
     op8 r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (__bf16)v[e];
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 t = __builtin_convertvector(floatx2{v[e], v[e + 1]}, bf16x2);
+      r[e] = t[0];
+      r[e + 1] = t[1];
+    }
     return r;
   }
   __device__ static inline op8 zero() {
@@ -66,7 +74,11 @@ struct Tr<__bf16> {
   __device__ static inline op4 from_f32_4(const float* v) {
     bf16x4 r;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = (__bf16)v[e];
+    for (int e = 0; e < 4; e += 2) {
+      const bf16x2 t = __builtin_convertvector(floatx2{v[e], v[e + 1]}, bf16x2);
+      r[e] = t[0];
+      r[e + 1] = t[1];
+    }
     return __builtin_bit_cast(op4, r);
   }
   __device__ static inline op4 load4(const __bf16* p) { return *reinterpret_cast<const op4*>(p); }

@@ -74,14 +74,16 @@ __device__ __forceinline__ int block_token(int sub, int tw, int r0, int nreg, in
 // Sum of v over aligned runs of `seg` lanes (seg = 1, 2, 4, 8 or 16) inside
 // each row of 16 lanes, with DPP moves (no LDS traffic): quad permutes for
 // pairs and quads, then the half-row and row mirrors, which pair every lane
-// with one of the other half. The run's first lane reads the sum.
+// with one of the other half. The run's first lane reads the sum. (Every
+// source lane lies in the row, so the out-of-row setting never applies; it is
+// set so the moves fuse into the adds.)
 template <int SEG>
 __device__ __forceinline__ float run_sum(float v) {
   constexpr int seg = SEG;
-  if (seg >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-  if (seg >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-  if (seg >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)); // row_half_mirror
-  if (seg >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)); // row_mirror
+  if (seg >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+  if (seg >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+  if (seg >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)); // row_half_mirror
+  if (seg >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)); // row_mirror
   return v;
 }
 
@@ -276,6 +278,7 @@ __global__ __launch_bounds__(512) void qkv_pool_kernel(QkvParams p) {
 // with one carry and no division.
 constexpr int kPersistKS = 4;  // k-steps kept in registers (C <= 128)
 constexpr int kPersistMaxWaves = 3 * kPersistKS;  // one wave per feature group of 32 outputs
+constexpr int kTilesPerStep = 2;  // 16-token tiles per products + epilogue step
 constexpr int kPersistXL = 4;  // X loads per thread per block (the host checks they cover it)
 
 // packed slot word: bits 0-10 LDS vector index (element offset / 8), 11-16 jx,
@@ -305,11 +308,12 @@ __device__ __forceinline__ int pack_slot(int v8, int j, int S) {
 struct UnitGeo {
   int b, r0, nreg, ry0, rx0;
 };
+// (a unit past the last has no regions)
 __device__ __forceinline__ UnitGeo unit_geo(int u, const QkvParams& p) {
   UnitGeo q;
   q.b = u / p.ngroups;
   q.r0 = (u - q.b * p.ngroups) * p.rpw;
-  q.nreg = min(p.rpw, p.R - q.r0);
+  q.nreg = u < p.nunits ? min(p.rpw, p.R - q.r0) : 0;
   q.ry0 = q.r0 / p.S;
   q.rx0 = q.r0 - q.ry0 * p.S;
   return q;
@@ -330,8 +334,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, u
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
 }
 
-// This thread's X loads of unit u (zeros for slots with no token)
-__device__ __forceinline__ void persist_load_x(const QkvParams& p, int u, const UnitGeo& q,
+// This thread's X loads of a unit (zeros for slots with no token)
+__device__ __forceinline__ void persist_load_x(const QkvParams& p, const UnitGeo& q,
                                                const int (&xoff)[kPersistXL], const int (&xslot)[kPersistXL],
                                                uint4 (&xr)[kPersistXL]) {
   const uint32_t img_bytes = (uint32_t)p.H * p.W * p.C * 2u;
@@ -339,13 +343,13 @@ __device__ __forceinline__ void persist_load_x(const QkvParams& p, int u, const 
       raw_buffer(static_cast<const __bf16*>(p.X) + (int64_t)min(q.b, p.B - 1) * p.H * p.W * p.C, img_bytes);
 #pragma unroll
   for (int m = 0; m < kPersistXL; ++m) {
-    const bool ok = u < p.nunits && slot_j(xslot[m]) < q.nreg;
+    const bool ok = slot_j(xslot[m]) < q.nreg;
     const int off = ok ? (slot_region_token(xslot[m], q.ry0, q.rx0, p) * p.C + xoff[m]) * 2 : kOutOfRange;
     xr[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
   }
 }
 
-template <int KSM, int SEG>
+template <int KSM, int SEG, int PD>
 __global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(QkvParams p) {
   constexpr int FPW = 1;  // feature groups per wave
   typedef Tr<__bf16> TT;
@@ -396,14 +400,19 @@ __global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(Qkv
     xslot[m] = pack_slot((tw * LDX + cv * 8) >> 3, f < kTokBlock * cvec ? tw / p.n : kNoSlot, p.S);
   }
   // this lane's output tokens (slot mt * 16 + col): offset past the region's
-  // first token, slot
-  int eoff[4], eslot[4];
+  // first token, slot. With runs of 16 (n a multiple of 16) a tile lies in one
+  // region, so its region slot is uniform (sj, split as sjy S + sjx) and the
+  // region's address is scalar arithmetic.
+  int eoff[4], eslot[4], sj[4], sjx[4], sjy[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int tw = mt * 16 + col;
     const int q = tw % p.n, qy = q / p.sw, qx = q - qy * p.sw;
     eoff[mt] = (qy * p.W + qx) * p.C;
     eslot[mt] = pack_slot(0, tw / p.n, p.S);
+    sj[mt] = (mt * 16) / p.n;
+    sjy[mt] = sj[mt] / p.S;
+    sjx[mt] = sj[mt] - sjy[mt] * p.S;
   }
 
   // X rows of this thread's slots into buffer `bufi` of LDS
@@ -413,22 +422,30 @@ __global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(Qkv
     for (int m = 0; m < kPersistXL; ++m)
       if (slot_j(xslot[m]) != kNoSlot) *reinterpret_cast<uint4*>(xs + slot_v8(xslot[m]) * 8) = v[m];
   };
-  uint4 xr[kPersistXL];
+  // X rows are loaded PD units ahead. PD = 1: xr receives the next unit's
+  // rows during this unit. PD = 2: xr holds the next unit's rows (loaded
+  // during the previous unit) and xn receives the rows of the unit after it.
+  uint4 xr[kPersistXL], xn[PD == 2 ? kPersistXL : 1];
   int u = blockIdx.x;
-  UnitGeo nxt = unit_geo(u, p);
-  persist_load_x(p, u, nxt, xoff, xslot, xr);
+  UnitGeo cur = unit_geo(u, p), nxt = unit_geo(u + gridDim.x, p);
+  persist_load_x(p, cur, xoff, xslot, xr);
   stage_x(0, xr);
+  if constexpr (PD == 2) persist_load_x(p, nxt, xoff, xslot, xr);
   int buf = 0;
   for (; u < total; u += gridDim.x, buf ^= 1) {
     // buffer `buf` holds this unit's X rows; every wave is done with the other
     // buffer (the previous unit), which receives the next unit's rows at the
     // end of this iteration, after this unit's stores (so waiting for those
-    // loads there does not wait for the stores)
+    // loads there does not wait for the stores, nor for loads issued later)
     __syncthreads();
     const __bf16* xs = xbuf + buf * kTokBlock * LDX;
-    const UnitGeo cur = nxt;
-    nxt = unit_geo(u + gridDim.x, p);
-    persist_load_x(p, u + gridDim.x, nxt, xoff, xslot, xr);
+    UnitGeo nn;
+    if constexpr (PD == 2) {
+      nn = unit_geo(u + 2 * gridDim.x, p);
+      persist_load_x(p, nn, xoff, xslot, xn);
+    } else {
+      persist_load_x(p, nxt, xoff, xslot, xr);
+    }
 
     const int b = cur.b, r0 = cur.r0, nreg = cur.nreg, ry0 = cur.ry0, rx0 = cur.rx0;
     const int64_t img = (int64_t)b * p.H * p.W * p.C;
@@ -450,14 +467,14 @@ __global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(Qkv
       float racc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) racc[e] = 0.f;
-      // two halves of two 16-token tiles each: products, then their epilogue
-      // (half the accumulators live at a time; the first half's epilogue
-      // overlaps the second half's products)
+      // steps of kTilesPerStep 16-token tiles: products, then their epilogue
+      // (only one step's accumulators live at a time, and a step's epilogue
+      // overlaps the next step's products)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-      floatx4 acc[2][2];  // accumulated onto the bias
+      for (int hh = 0; hh < 4 / kTilesPerStep; ++hh) {
+      floatx4 acc[kTilesPerStep][2];  // accumulated onto the bias
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
+      for (int m2 = 0; m2 < kTilesPerStep; ++m2) {
         acc[m2][0] = floatx4{bv[fi][0], bv[fi][1], bv[fi][2], bv[fi][3]};
         acc[m2][1] = floatx4{bv[fi][4], bv[fi][5], bv[fi][6], bv[fi][7]};
       }
@@ -465,17 +482,29 @@ __global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(Qkv
       for (int ks = 0; ks < KSM; ++ks) {
         if (ks >= ks_n) break;  // uniform
 #pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {  // rows past the block are zeros
-          const int mt = 2 * hh + m2;
+        for (int m2 = 0; m2 < kTilesPerStep; ++m2) {  // rows past the block are zeros
+          const int mt = kTilesPerStep * hh + m2;
           const op8 xb = TT::load8(xs + (mt * 16 + col) * LDX + ks * 32 + 8 * g);
           acc[m2][0] = TT::mma(wa[fi][ks], xb, acc[m2][0]);
           acc[m2][1] = TT::mma(wb[fi][ks], xb, acc[m2][1]);
         }
       }
 #pragma unroll
-      for (int m2 = 0; m2 < 2; ++m2) {
-        const int mt = 2 * hh + m2;
-        const int j = slot_j(eslot[mt]);
+      for (int m2 = 0; m2 < kTilesPerStep; ++m2) {
+        const int mt = kTilesPerStep * hh + m2;
+        int j, rtok;  // the lane's region slot and the region's first token
+        if constexpr (SEG == 16) {
+          j = sj[mt];
+          int rx = rx0 + sjx[mt], ry = ry0 + sjy[mt];
+          if (rx >= p.S) {
+            rx -= p.S;
+            ++ry;
+          }
+          rtok = ry * p.sh * p.W + rx * p.sw;
+        } else {
+          j = slot_j(eslot[mt]);
+          rtok = slot_region_token(eslot[mt], ry0, rx0, p);
+        }
         const bool ok = j < nreg;
         float o[8];
 #pragma unroll
@@ -484,8 +513,7 @@ __global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(Qkv
           o[4 + e] = acc[m2][1][e];
         }
         const op8 r = TT::from_f32(o);  // the rounded outputs
-        const int soff =
-            ok && fvalid ? (slot_region_token(eslot[mt], ry0, rx0, p) * p.C + eoff[mt] + ch) * 2 : kOutOfRange;
+        const int soff = ok && fvalid ? rtok * p.C * 2 + (eoff[mt] + ch) * 2 : kOutOfRange;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, r), rdst, soff, 0, 0);
         if (pooled) {
           // a run that is not a region of this unit sums garbage that is never written
@@ -498,7 +526,7 @@ __global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(Qkv
             for (int e = 0; e < 8; ++e) racc[e] = run_sum<SEG>(racc[e]) * inv;
             const __amdgpu_buffer_rsrc_t rmean =
                 raw_buffer((tensor == 0 ? p.Qr : p.Kr) + (int64_t)b * p.R * p.C, mean_bytes);
-            const int moff = ((col & (SEG - 1)) == 0 && ok) ? ((r0 + j) * p.C + ch) * 4 : kOutOfRange;
+            const int moff = ((col & (SEG - 1)) == 0 && ok) ? (r0 + j) * p.C * 4 + ch * 4 : kOutOfRange;
             __builtin_amdgcn_raw_buffer_store_b128(
                 __builtin_bit_cast(u32x4, make_float4(racc[0], racc[1], racc[2], racc[3])), rmean, moff, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b128(
@@ -512,6 +540,14 @@ __global__ __launch_bounds__(kPersistMaxWaves * 64) void qkv_pool_persistent(Qkv
       }  // hh
     }
     stage_x(buf ^ 1, xr);
+    cur = nxt;
+    if constexpr (PD == 2) {
+#pragma unroll
+      for (int m = 0; m < kPersistXL; ++m) xr[m] = xn[m];
+      nxt = nn;
+    } else {
+      nxt = unit_geo(u + 2 * gridDim.x, p);
+    }
   }
 }
 
@@ -543,19 +579,22 @@ hipError_t launch_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, vo
   const int pwaves = p.nfg;  // one wave per feature group
   const bool covered = pwaves * 64 * kPersistXL >= kTokBlock * (s.C / 8);
   // (raw buffer offsets: one image's bytes below 2^31)
-  const bool fits = 2 * (int64_t)s.H * s.W * s.C < (int64_t(1) << 31);
+  // (unit indices up to two grid strides past the last unit stay below 2^31)
+  const bool fits = 2 * (int64_t)s.H * s.W * s.C < (int64_t(1) << 31) && nwg < (int64_t(1) << 30);
   if (dtype == kBF16 && s.C <= 32 * kPersistKS && s.n <= kTokBlock && seg0 > 0 && covered && fits) {
     const int waves = pwaves;
     const size_t lds = 2 * sizeof(__bf16) * kTokBlock * (s.C + 8);
     p.end_mask = 0;
     for (int t = 0; t < 4; ++t)
       if (seg0 < 16 || ((t + 1) * 16) % s.n == 0) p.end_mask |= 1 << t;
-    const void* k2[] = {(const void*)&qkv_pool_persistent<2, 1>, (const void*)&qkv_pool_persistent<2, 2>,
-                        (const void*)&qkv_pool_persistent<2, 4>, (const void*)&qkv_pool_persistent<2, 8>,
-                        (const void*)&qkv_pool_persistent<2, 16>};
-    const void* k4[] = {(const void*)&qkv_pool_persistent<4, 1>, (const void*)&qkv_pool_persistent<4, 2>,
-                        (const void*)&qkv_pool_persistent<4, 4>, (const void*)&qkv_pool_persistent<4, 8>,
-                        (const void*)&qkv_pool_persistent<4, 16>};
+    // X prefetched one unit ahead for C <= 64 and two for C > 64 (measured:
+    // 56x56 C=64 34.5 vs 39.1 us with two; 28x28 C=128 25.6 vs 26.9 us)
+    const void* k2[] = {(const void*)&qkv_pool_persistent<2, 1, 1>, (const void*)&qkv_pool_persistent<2, 2, 1>,
+                        (const void*)&qkv_pool_persistent<2, 4, 1>, (const void*)&qkv_pool_persistent<2, 8, 1>,
+                        (const void*)&qkv_pool_persistent<2, 16, 1>};
+    const void* k4[] = {(const void*)&qkv_pool_persistent<4, 1, 2>, (const void*)&qkv_pool_persistent<4, 2, 2>,
+                        (const void*)&qkv_pool_persistent<4, 4, 2>, (const void*)&qkv_pool_persistent<4, 8, 2>,
+                        (const void*)&qkv_pool_persistent<4, 16, 2>};
     const void* fn = (s.C <= 64 ? k2 : k4)[__builtin_ctz(seg0)];
     // as many workgroups as fit at once, each walking many units
     int dev = 0, ncu = 0, per_cu = 0;
