@@ -381,6 +381,214 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// 2b. dQ, log-sum-exp and D with a single chunk (at most 64 routed keys per
+// query): the forward head kernel's work split. Workgroup = (image b, query
+// region i, block of <= 64 queries, group of HG heads), one wave per head that
+// loops over the block's <= 4 query tiles. The K and V operands of the 64 keys
+// are loaded once per head wave and serve every tile; K^T goes through the
+// wave's own LDS tile once; each wave turns the routing row into its own key
+// table, so the kernel has no workgroup barrier.
+template <typename T, bool RAGGED, int MAXT>
+__global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
+  typedef Tr<T> TT;
+  typedef typename TT::op8 op8;
+  constexpr int VEC = TT::VEC;
+  constexpr int CVH = D / VEC;
+  constexpr int PAIRS = KC / 2 * CVH / 64;  // (key pair, vector) items of the K^T tile per lane
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __shared__ int wtok[8 * KC];  // per wave: token of every routed key, -1 past kv
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  const int ldk = KC + TT::PADV;
+
+  int w = xcd_remap();
+  const int hg = w % p.nhg;
+  w /= p.nhg;
+  const int qb = w % p.nqb;
+  w /= p.nqb;
+  const int i = w % p.R;
+  const int b = w / p.R;
+  const int head = hg * p.HG + wave;
+  if (head >= p.heads) return;  // wave-uniform; no barrier in this kernel
+  const int ch0 = head * D;
+  const int64_t img = (int64_t)b * p.H * p.W * p.C;
+  const T* Kg = static_cast<const T*>(p.K) + img;
+  const T* Vg = static_cast<const T*>(p.V) + img;
+  T* Kt = reinterpret_cast<T*>(smem_raw) + wave * D * ldk;  // this head's K^T tile
+
+  // routing entry of key kappa = lane first (the K/V addresses wait on it)
+  int rid = 0, ktok = 0;
+  if (lane < p.kv) {
+    int tk, tx;
+    const int jr = fdiv(lane, p.div_n, &tk);
+    const int ty = fdiv(tk, p.div_sw, &tx);
+    ktok = ty * p.W + tx;
+    rid = p.idx[((int64_t)b * p.R + i) * p.topk + jr];
+  }
+  // then the query rows of every tile: q and dO as B operands, O for D
+  const int q0 = qb * 64;
+  const int nq = min(64, p.n - q0);
+  const int ntiles = (nq + 15) >> 4;
+  int qcorner;
+  {
+    int rx;
+    const int ry = fdiv(i, p.div_S, &rx);
+    qcorner = ry * p.sh * p.W + rx * p.sw;
+  }
+  op8 qop[MAXT], dop[MAXT];
+  int qtok[MAXT];
+  float Dq[MAXT];
+  {
+    op8 oop[MAXT];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      const int qi = q0 + t * 16 + col;
+      qtok[t] = -1;
+      qop[t] = TT::zero();
+      dop[t] = TT::zero();
+      oop[t] = TT::zero();
+      if (t < ntiles && qi < q0 + nq) {
+        int qx;
+        const int qy = fdiv(qi, p.div_sw, &qx);
+        qtok[t] = qcorner + qy * p.W + qx;
+        const int off = qtok[t] * p.C + ch0 + 8 * g;
+        qop[t] = TT::load8(static_cast<const T*>(p.Q) + img + off);
+        dop[t] = TT::load8(static_cast<const T*>(p.dO) + img + off);
+        oop[t] = TT::load8(static_cast<const T*>(p.O) + img + off);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+      float dpart = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart += (float)dop[t][e] * (float)oop[t][e];
+      Dq[t] = wave_sum_groups(dpart);
+    }
+  }
+
+  // the wave's key table
+  const bool ok = rid >= 0 && rid < p.R;
+  const bool bad = __builtin_amdgcn_ballot_w64(lane < p.kv && !ok) != 0;  // uniform
+  int* wt = wtok + wave * KC;
+  wt[lane] = lane < p.kv ? corner_of(p, ok ? rid : 0) + ktok : -1;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  T* dQg = static_cast<T*>(p.dQ) + img;
+  if (bad) {
+    // a routing entry outside [0, S*S): gradient NaN for the region's queries
+    float nanv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nanv[e] = __builtin_nanf("");
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t)
+      if (qtok[t] >= 0) TT::store8(dQg + qtok[t] * p.C + ch0 + 8 * g, nanv);
+    return;
+  }
+
+  // K and V operands (A operands of S^T = K Q^T and dP^T = V dO^T), then the
+  // K^T tile (A operands of dQ^T += K^T dZ^T) through LDS
+  op8 kop[2][2], vop[2][2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int tk = wt[key_of(col, st, tb)];
+      kop[st][tb] = TT::zero();
+      vop[st][tb] = TT::zero();
+      if (tk >= 0) {
+        kop[st][tb] = TT::load8(Kg + tk * p.C + ch0 + 8 * g);
+        vop[st][tb] = TT::load8(Vg + tk * p.C + ch0 + 8 * g);
+      }
+    }
+#pragma unroll
+  for (int m = 0; m < PAIRS; ++m) {
+    const int f = lane + 64 * m;
+    const int cv = f % CVH, p2 = f / CVH;
+    const int ta = wt[2 * p2], tb2 = wt[2 * p2 + 1];
+    uint4 va = make_uint4(0u, 0u, 0u, 0u), vb = va;
+    if (ta >= 0) va = *reinterpret_cast<const uint4*>(Kg + ta * p.C + ch0 + cv * VEC);
+    if (tb2 >= 0) vb = *reinterpret_cast<const uint4*>(Kg + tb2 * p.C + ch0 + cv * VEC);
+    const int row0 = cv * VEC;
+    store_vt_pair(Kt, ldk, row0, vt_col(row0, 2 * p2), va, vb);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int vrow = 8 * (col >> 2) + (col & 3);
+
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    if (t >= ntiles) break;  // uniform
+    float s[2][8], dp[2][8];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const floatx4 sa = TT::mma(kop[st][0], qop[t], floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 sb = TT::mma(kop[st][1], qop[t], floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 pa = TT::mma(vop[st][0], dop[t], floatx4{0.f, 0.f, 0.f, 0.f});
+      const floatx4 pb = TT::mma(vop[st][1], dop[t], floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[st][e] = sa[e];
+        s[st][4 + e] = sb[e];
+        dp[st][e] = pa[e];
+        dp[st][4 + e] = pb[e];
+      }
+    }
+    if (RAGGED) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (st * 32 + 8 * g + e >= p.kv) s[st][e] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
+    mx = wave_max_groups(mx);
+    float sum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f((s[st][e] - mx) * p.c);
+    const float lse = mx * p.c + __builtin_log2f(wave_sum_groups(sum));
+    floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      float dz[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -lse));
+        dz[e] = pr * (dp[st][e] - Dq[t]);
+      }
+      const op8 zop = TT::from_f32(dz);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int row = vrow + 4 * ct;
+        const op8 kt = TT::load8(Kt + row * ldk + vt_col(row, st * 32 + 8 * g));
+        dq[ct] = TT::mma(kt, zop, dq[ct]);
+      }
+    }
+    if (qtok[t] >= 0) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = dq[0][e] * p.scale;
+        o[4 + e] = dq[1][e] * p.scale;
+      }
+      TT::store8(dQg + qtok[t] * p.C + ch0 + 8 * g, o);
+      if (g == 0) {
+        const int64_t at = ((int64_t)b * p.H * p.W + qtok[t]) * p.heads + head;
+        p.lse[at] = lse;
+        p.dd[at] = Dq[t];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3. dK, dV. Workgroup = (image b, key region r, block of <= 64 of its keys,
 // group of HGk heads); wave = (head, key half of 32 keys).
 // The queries of the key region's incoming query regions (inverse table, in
@@ -662,14 +870,37 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
 
   const bool multi = s.kv > KC, ragged = s.kv % KC != 0;
   const void* fq;
-  if (dtype == kBF16)
-    fq = multi ? (ragged ? (const void*)&bwd_dq_kernel<__bf16, true, true> : (const void*)&bwd_dq_kernel<__bf16, true, false>)
-               : (ragged ? (const void*)&bwd_dq_kernel<__bf16, false, true> : (const void*)&bwd_dq_kernel<__bf16, false, false>);
-  else
-    fq = multi ? (ragged ? (const void*)&bwd_dq_kernel<float, true, true> : (const void*)&bwd_dq_kernel<float, true, false>)
-               : (ragged ? (const void*)&bwd_dq_kernel<float, false, true> : (const void*)&bwd_dq_kernel<float, false, false>);
-  const size_t ldsq = esz * (size_t)HG * D * (KC + padv);
-  e = hipLaunchKernel(fq, dim3((unsigned)p.nitems_q), dim3(HG * p.ntq * 64), args, ldsq, stream);
+  size_t ldsq;
+  unsigned q_threads;
+  if (!multi) {
+    // one wave per head, up to 8 heads per workgroup, looping over the tiles
+    BwdParams ph = p;
+    int H8 = 1;
+    while (2 * H8 <= 8 && 2 * H8 <= s.heads) H8 *= 2;
+    ph.HG = H8;
+    ph.nhg = (s.heads + H8 - 1) / H8;
+    const int64_t nqh = (int64_t)s.B * s.R * p.nqb * ph.nhg;
+    if (nqh >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    ph.nitems_q = (int)nqh;
+    const bool one = s.n <= 16;
+    if (dtype == kBF16)
+      fq = ragged ? (one ? (const void*)&bwd_dq_head_kernel<__bf16, true, 1> : (const void*)&bwd_dq_head_kernel<__bf16, true, 4>)
+                  : (one ? (const void*)&bwd_dq_head_kernel<__bf16, false, 1> : (const void*)&bwd_dq_head_kernel<__bf16, false, 4>);
+    else
+      fq = ragged ? (one ? (const void*)&bwd_dq_head_kernel<float, true, 1> : (const void*)&bwd_dq_head_kernel<float, true, 4>)
+                  : (one ? (const void*)&bwd_dq_head_kernel<float, false, 1> : (const void*)&bwd_dq_head_kernel<float, false, 4>);
+    ldsq = esz * (size_t)H8 * D * (KC + padv);
+    void* hargs[] = {&ph};
+    e = hipLaunchKernel(fq, dim3((unsigned)ph.nitems_q), dim3(H8 * 64), hargs, ldsq, stream);
+  } else {
+    if (dtype == kBF16)
+      fq = ragged ? (const void*)&bwd_dq_kernel<__bf16, true, true> : (const void*)&bwd_dq_kernel<__bf16, true, false>;
+    else
+      fq = ragged ? (const void*)&bwd_dq_kernel<float, true, true> : (const void*)&bwd_dq_kernel<float, true, false>;
+    ldsq = esz * (size_t)HG * D * (KC + padv);
+    q_threads = HG * p.ntq * 64;
+    e = hipLaunchKernel(fq, dim3((unsigned)p.nitems_q), dim3(q_threads), args, ldsq, stream);
+  }
   if (e != hipSuccess) return e;
 
   const void* fk = dtype == kBF16 ? (const void*)&bwd_dkv_kernel<__bf16> : (const void*)&bwd_dkv_kernel<float>;
