@@ -55,13 +55,17 @@ def test_edge_shapes_projection(w):
 
 
 # region sizes and channel counts of both projection kernels: n = 2, 4, 8
-# (runs inside a 16-token tile), C = 96 (two feature groups per wave)
+# (runs inside a 16-token tile), 32 and 48 (regions over several tiles, a
+# block's last tile empty), C = 96 and 128 (9 and 12 waves; two-unit prefetch)
 PROJ_SHAPES = [
     wl.custom(2, 8, 4, 64, 2, 4, 3, "bf16", seed=95),     # n = 2
     wl.custom(2, 8, 8, 64, 2, 4, 3, "bf16", seed=96),     # n = 4
     wl.custom(1, 16, 8, 32, 1, 4, 2, "bf16", seed=97),    # n = 8
     wl.custom(2, 16, 16, 96, 3, 4, 2, "bf16", seed=98),   # C = 96, n = 16
     wl.custom(1, 24, 24, 128, 4, 3, 2, "bf16", seed=99),  # n = 64, C = 128
+    wl.custom(2, 16, 8, 64, 2, 2, 2, "bf16", seed=100),   # n = 32: a region spans two 16-token tiles
+    wl.custom(1, 16, 12, 64, 2, 2, 2, "bf16", seed=101),  # n = 48: one region per block, the last tile empty
+    wl.custom(1, 16, 12, 128, 4, 2, 3, "bf16", seed=102), # n = 48, C = 128 (two-unit prefetch)
 ]
 
 

@@ -16,10 +16,12 @@
 //  1. bwd_routes_kernel: per image, the inverse routing table - for every key
 //     region, the ascending list of query regions whose rows hold it. A row
 //     with an entry outside [0, S*S) is marked bad and left out.
-//  2. bwd_dq_kernel: one wave per (head, 16-query tile), the forward's
-//     transposed products (S^T = K Q^T, dP^T = V dO^T, dQ^T = K^T dZ^T with
-//     K^T through LDS), D from O and dO, and the base-2 log-sum-exp of every
-//     query, written for kernel 3. Several 64-key chunks take two passes
+//  2. dQ: the forward's transposed products (S^T = K Q^T, dP^T = V dO^T,
+//     dQ^T = K^T dZ^T with K^T through LDS), D from O and dO, and the base-2
+//     log-sum-exp of every query, written for kernel 3. With at most 64 keys
+//     per query, bwd_dq_head_kernel: one wave per head looping over the
+//     query tiles, as in the forward. With several 64-key chunks,
+//     bwd_dq_kernel: one wave per (head, 16-query tile), two passes
 //     (log-sum-exp first).
 //  3. bwd_dkv_kernel: one wave per (head, 32 keys of one key region), looping
 //     over the queries of the inverse table's regions, staged 64 at a time
@@ -135,9 +137,11 @@ __device__ __forceinline__ void build_tok(int* tok, const int* rb, int tid, int 
 __device__ __forceinline__ int key_of(int col, int st, int tb) { return st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb; }
 
 // ---------------------------------------------------------------------------
-// 2. dQ, log-sum-exp and D. Workgroup = (image b, query region i, block of
-// <= 64 queries, group of HG heads); wave w = (head w / ntq, tile w % ntq).
-template <typename T, bool MULTI, bool RAGGED>
+// 2. dQ, log-sum-exp and D when the keys span several 64-key chunks.
+// Workgroup = (image b, query region i, block of <= 64 queries, group of HG
+// heads); wave w = (head w / ntq, tile w % ntq). Pass 1 takes the log-sum-exp
+// over all chunks, pass 2 the gradient.
+template <typename T, bool RAGGED>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
@@ -171,29 +175,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   const T* Vg = static_cast<const T*>(p.V) + img;
   T* Kt = reinterpret_cast<T*>(smem_raw) + hl * D * ldk;  // K^T tile of this wave's head
 
-  // routed regions' corners (several chunks) or, with one chunk, the token
-  // of every routed key straight from the routing row
+  // the routed regions' corners
   if (tid == 0) sbad = 0;
   __syncthreads();
-  if (MULTI) {
-    for (int j = tid; j < p.topk; j += blockDim.x) {
-      const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
-      const bool ok = r >= 0 && r < p.R;
-      rb[j] = corner_of(p, ok ? r : 0);
-      if (!ok) sbad = 1;
-    }
-  } else if (tid < KC) {
-    int t = -1;
-    if (tid < p.kv) {
-      int tk, tx;
-      const int jr = fdiv(tid, p.div_n, &tk);
-      const int ty = fdiv(tk, p.div_sw, &tx);
-      const int r = p.idx[((int64_t)b * p.R + i) * p.topk + jr];
-      const bool ok = r >= 0 && r < p.R;
-      t = corner_of(p, ok ? r : 0) + ty * p.W + tx;
-      if (!ok) sbad = 1;
-    }
-    tok[tid] = t;
+  for (int j = tid; j < p.topk; j += blockDim.x) {
+    const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
+    const bool ok = r >= 0 && r < p.R;
+    rb[j] = corner_of(p, ok ? r : 0);
+    if (!ok) sbad = 1;
   }
 
   // the wave's queries: B operands of q and dO, and D = dO . O per query
@@ -233,13 +222,13 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
     return;  // uniform over the workgroup
   }
 
-  const int nchunks = MULTI ? (p.kv + KC - 1) / KC : 1;
+  const int nchunks = (p.kv + KC - 1) / KC;
   const int kv = p.kv, W = p.W;
   const FastDiv div_n = p.div_n, div_sw = p.div_sw;
 
-  // ---- pass 1 (several chunks): running max and sum per query
+  // ---- pass 1: running max and sum per query
   float m = -INFINITY, l = 0.f;
-  if (MULTI) {
+  {
     for (int ch = 0; ch < nchunks; ++ch) {
       build_tok(tok, rb, tid, ch * KC, kv, W, div_n, div_sw);
       __syncthreads();
@@ -279,16 +268,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       __syncthreads();  // tok reused by the next chunk
     }
   }
-  float lse = MULTI ? m * p.c + __builtin_log2f(wave_sum_groups(l)) : 0.f;
+  const float lse = m * p.c + __builtin_log2f(wave_sum_groups(l));
 
   // ---- pass 2: P, dP, dZ and dQ^T += K^T dZ^T
   floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
   for (int ch = 0; ch < nchunks; ++ch) {
     const int c0 = ch * KC;
-    if (MULTI) {
-      build_tok(tok, rb, tid, c0, kv, W, div_n, div_sw);
-      __syncthreads();
-    }
+    build_tok(tok, rb, tid, c0, kv, W, div_n, div_sw);
+    __syncthreads();
     // K^T tile of this head, written by the head's ntq waves together
     for (int f = t * 64 + lane; f < ITEMS; f += p.ntq * 64) {
       const int cv = f % CVH, p2 = f / CVH;
@@ -329,20 +316,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (RAGGED && c0 + st * 32 + 8 * g + e >= p.kv) s[st][e] = -INFINITY;
-    if (!MULTI) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
-      mx = wave_max_groups(mx);
-      float sum = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f((s[st][e] - mx) * p.c);
-      lse = mx * p.c + __builtin_log2f(wave_sum_groups(sum));
-    }
     __syncthreads();  // K^T tile complete
     const int vrow = 8 * (col >> 2) + (col & 3);
 #pragma unroll
@@ -844,7 +817,7 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   p.div_n = make_fastdiv(s.n);
   p.div_sw = make_fastdiv(s.sw);
   p.div_S = make_fastdiv(s.S);
-  // dq kernel: query blocks of 64, one wave per (head, tile), <= 8 waves
+  // several-chunk dq kernel: query blocks of 64, one wave per (head, tile), <= 8 waves
   p.nqb = (s.n + 63) / 64;
   p.ntq = (min(s.n, 64) + 15) / 16;
   int HG = 1;
@@ -871,7 +844,6 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   const bool multi = s.kv > KC, ragged = s.kv % KC != 0;
   const void* fq;
   size_t ldsq;
-  unsigned q_threads;
   if (!multi) {
     // one wave per head, up to 8 heads per workgroup, looping over the tiles
     BwdParams ph = p;
@@ -894,12 +866,11 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
     e = hipLaunchKernel(fq, dim3((unsigned)ph.nitems_q), dim3(H8 * 64), hargs, ldsq, stream);
   } else {
     if (dtype == kBF16)
-      fq = ragged ? (const void*)&bwd_dq_kernel<__bf16, true, true> : (const void*)&bwd_dq_kernel<__bf16, true, false>;
+      fq = ragged ? (const void*)&bwd_dq_kernel<__bf16, true> : (const void*)&bwd_dq_kernel<__bf16, false>;
     else
-      fq = ragged ? (const void*)&bwd_dq_kernel<float, true, true> : (const void*)&bwd_dq_kernel<float, true, false>;
+      fq = ragged ? (const void*)&bwd_dq_kernel<float, true> : (const void*)&bwd_dq_kernel<float, false>;
     ldsq = esz * (size_t)HG * D * (KC + padv);
-    q_threads = HG * p.ntq * 64;
-    e = hipLaunchKernel(fq, dim3((unsigned)p.nitems_q), dim3(q_threads), args, ldsq, stream);
+    e = hipLaunchKernel(fq, dim3((unsigned)p.nitems_q), dim3(HG * p.ntq * 64), args, ldsq, stream);
   }
   if (e != hipSuccess) return e;
 
