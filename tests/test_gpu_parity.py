@@ -92,7 +92,7 @@ def test_full_size_route_all_images(w):
 # full routing, one region, one token per region.
 EDGE = [
     wl.custom(2, 6, 6, 32, 1, 2, 3, "bf16", seed=10),      # n=9, kv=27
-    wl.custom(1, 20, 20, 64, 2, 2, 2, "bf16", seed=11),    # n=100: two query blocks, ragged
+    wl.custom(1, 20, 20, 64, 2, 2, 2, "bf16", seed=11),    # n=100: a partial query block, ragged chunks
     wl.custom(1, 8, 12, 192, 6, 4, 5, "bf16", seed=12),    # H!=W, 6 heads: partial head group
     wl.custom(1, 16, 16, 32, 1, 16, 7, "bf16", seed=13),   # 256 regions, n=1
     wl.custom(1, 16, 16, 32, 1, 16, 256, "bf16", seed=14), # full routing over 256 regions
@@ -100,8 +100,15 @@ EDGE = [
     wl.custom(2, 9, 9, 64, 2, 1, 1, "bf16", seed=16),      # one region: global attention
     wl.custom(1, 14, 14, 256, 8, 7, 16, "f32", seed=17),   # fp32, stage-3 shape
     wl.custom(2, 24, 24, 64, 2, 3, 2, "f32", seed=18),     # fp32, n=64, two head group of 1
-    wl.custom(1, 32, 32, 64, 2, 2, 2, "f32", seed=19),     # fp32, n=256, 4 query blocks
+    wl.custom(1, 32, 32, 64, 2, 2, 2, "f32", seed=19),     # fp32, n=256, two 128-query blocks
     wl.custom(3, 10, 15, 96, 3, 5, 4, "bf16", seed=20, content="clustered"),
+    # chunked kernel (more than 64 keys per query) launch shapes: 4 heads of
+    # one 16-query tile each in 4 waves (each thread stages four 16-byte
+    # vectors of a chunk), the same in fp32, and a full plus a partial
+    # 128-query block
+    wl.custom(2, 28, 28, 128, 4, 7, 6, "bf16", seed=21),   # n=16, kv=96
+    wl.custom(1, 16, 16, 64, 2, 4, 6, "f32", seed=22),     # fp32, n=16, kv=96
+    wl.custom(1, 20, 30, 64, 2, 2, 2, "bf16", seed=23),    # n=150: blocks of 128 and 22 queries
 ]
 
 

@@ -10,10 +10,12 @@
 // through the routing table (each token's head-group channels are one
 // contiguous run), and runs both products on MFMA with an online softmax.
 //
-// Work split. One workgroup = one work item (image b, query region i, block
-// of <= 64 of the region's queries, group of HG heads). Its 4 waves own
-// "units" = (head, tile of 16 queries); each wave keeps <= 2 units'
-// accumulators in registers.
+// Work split (the chunked kernel, more than 64 keys per query). One
+// workgroup = one work item (image b, query region i, block of <= 128 of the
+// region's queries, group of HG heads); each of its waves owns one "unit" =
+// (head, tile of 16 queries) and keeps its accumulators in registers, and the
+// waves share every staged 64-key chunk. The single-chunk kernel below has
+// its own split.
 //
 // Transposed products. With d = 32 the score tile is computed as
 //   S^T[16 keys x 16 queries] = K[16 x 32] . Q^T[32 x 16]
@@ -41,12 +43,16 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace bra {
 namespace {
 
-constexpr int NW = 4;       // waves per workgroup
-constexpr int MAXU = 2;     // units per wave
-constexpr int QB = 64;      // queries per workgroup (<= 4 tiles of 16)
+constexpr int MAXU = 1;       // chunked kernel: (head, 16-query tile) units per wave
+constexpr int kMaxUnits = 16; // chunked kernel: units (= waves) per workgroup
+constexpr int kMinWaves = 4;  // chunked kernel: waves per workgroup at least (they share the chunk loads)
+constexpr int QB = 64;        // single-chunk kernel: queries per work item (<= 4 tiles of 16)
+constexpr int QBM = 128;      // chunked kernel: queries per work item (<= 8 tiles of 16)
 
 struct AttnParams {
   const void* Q;
@@ -64,6 +70,7 @@ struct AttnParams {
   int lg_oct;  // log2(8 * HG * D / VEC): pair items per 8-pair octet of a chunk
   int nbuf;    // LDS chunk buffers (2: double-buffered, when kv spans several chunks)
   int own_tab; // single-chunk kernel: every attention wave builds its own key table
+  int qblk;    // queries per work item
   float c;     // softmax scale * log2(e)
   FastDiv div_n, div_sw, div_S;
   // local context term fused into the single-chunk kernel's epilogue
@@ -91,8 +98,8 @@ __device__ inline Item item_at(const AttnParams& p, int w) {
   it.qb = w % p.nqb;  w /= p.nqb;
   it.i = w % p.R;
   it.b = w / p.R;
-  it.q0 = it.qb * QB;
-  it.nq = min(QB, p.n - it.q0);
+  it.q0 = it.qb * p.qblk;
+  it.nq = min(p.qblk, p.n - it.q0);
   it.ntiles = (it.nq + 15) >> 4;
   const int h0 = it.hg * p.HG;
   it.nh = min(p.HG, p.heads - h0);
@@ -128,7 +135,7 @@ __device__ __forceinline__ void load_queries(const AttnParams& p, const Item& it
   const T* Qg = static_cast<const T*>(p.Q) + it.img;
 #pragma unroll
   for (int uu = 0; uu < MAXU; ++uu) {
-    const int u = wave + NW * uu;  // uniform
+    const int u = wave + (int)(blockDim.x >> 6) * uu;  // uniform
     const int hl = u / max(it.ntiles, 1);
     const int t = u - hl * it.ntiles;
     const int qi = it.q0 + t * 16 + col;
@@ -158,7 +165,7 @@ __device__ inline int region_corner(const AttnParams& p, int r) {
 // Routing row of the item's region, read from the table: corner offsets into
 // rb[0..topk); returns (through LDS flag *bad) whether an entry is out of range.
 __device__ __forceinline__ void read_routes(const AttnParams& p, const Item& it, int tid, int* rb, int* bad) {
-  for (int j = tid; j < p.topk; j += NW * 64) {
+  for (int j = tid; j < p.topk; j += blockDim.x) {
     const int r = it.valid ? p.idx[((int64_t)it.b * p.R + it.i) * p.topk + j] : 0;
     const bool ok = r >= 0 && r < p.R;
     rb[j] = region_corner(p, ok ? r : 0);
@@ -171,7 +178,7 @@ __device__ __forceinline__ void read_routes(const AttnParams& p, const Item& it,
 // idx[b][i][kappa / n] + the (kappa % n)-th token of that region. Sets *bad
 // (LDS) for an entry outside [0, S*S).
 __device__ __forceinline__ void read_route_tokens(const AttnParams& p, const Item& it, int tid, int* tok, int* bad) {
-  for (int kappa = tid; kappa < p.kv; kappa += NW * 64) {
+  for (int kappa = tid; kappa < p.kv; kappa += blockDim.x) {
     int tk, tx;
     const int jr = fdiv(kappa, p.div_n, &tk);
     const int ty = fdiv(tk, p.div_sw, &tx);
@@ -183,7 +190,7 @@ __device__ __forceinline__ void read_route_tokens(const AttnParams& p, const Ite
 }
 
 // K/V loads of one 64-key chunk into registers. A thread owns NV/2 (key pair,
-// 16-byte channel vector) items: pair item f = tid + 256 q covers keys 2p and
+// 16-byte channel vector) items: pair item f = tid + blockDim.x q covers keys 2p and
 // 2p+1 of channel vector cv, with 8 consecutive pairs per channel vector so
 // one wave instruction reads 8 whole token rows; slot 2q holds key 2p, slot
 // 2q+1 key 2p+1. (f -> p, cv by shifts: the head group spans a power-of-two
@@ -199,7 +206,7 @@ __device__ __forceinline__ void load_kv(const AttnParams& p, const Item& it, int
   const int vpk = it.nh * (D / VEC);  // valid vectors per key row
 #pragma unroll
   for (int s2 = 0; s2 < NV; ++s2) {
-    const int f = tid + 256 * (s2 >> 1);
+    const int f = tid + blockDim.x * (s2 >> 1);
     const int oct = f >> p.lg_oct;
     const int rem = f & ((1 << p.lg_oct) - 1);
     const int cv = rem >> 3;
@@ -229,7 +236,7 @@ __device__ __forceinline__ void store_kv(const AttnParams& p, int tid, T* Ks, T*
   constexpr int VEC = Tr<T>::VEC;
 #pragma unroll
   for (int q = 0; q < NV / 2; ++q) {
-    const int f = tid + 256 * q;
+    const int f = tid + blockDim.x * q;
     const int oct = f >> p.lg_oct;
     if (oct < KC / 16) {
       const int rem = f & ((1 << p.lg_oct) - 1);
@@ -253,7 +260,7 @@ __device__ __forceinline__ void compute_chunk(const AttnParams& p, const Item& i
   typedef typename TT::op8 op8;
 #pragma unroll
   for (int uu = 0; uu < MAXU; ++uu) {
-    const int u = wave + NW * uu;
+    const int u = wave + (int)(blockDim.x >> 6) * uu;
     if (u >= it.U) continue;  // uniform
     const int hl = u / it.ntiles;
     // ---- scores S^T for 64 keys: two 32-key steps, two 16-row tiles each
@@ -345,7 +352,7 @@ __device__ __forceinline__ void store_outputs(const AttnParams& p, const Item& i
 // MULTI: kv spans more than one chunk (prefetch the next chunk during compute).
 // RAGGED: kv is not a multiple of 64 (the last chunk masks its missing keys).
 template <typename T, int NV, bool MULTI, bool RAGGED>
-__global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
+__global__ __launch_bounds__(NV == 2 ? kMaxUnits * 64 : 512) void attend_kernel(AttnParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
   // single chunk: the routed keys' token offsets; several chunks: the routed
@@ -388,18 +395,41 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnParams p) {
   const bool bad = sbad;
 
   if (!bad) {
-    uint4 kreg[NV], vreg[NV];
-    load_kv<T, NV, TOK>(p, it, tid, rtab, 0, kreg, vreg);
+    // chunks are loaded two ahead into two register sets, A for even chunks
+    // and B for odd ones (the loop is unrolled by two, so neither set is
+    // copied, which would wait for its loads early); only the waves that hold
+    // chunk items do the loads and the LDS staging
+    uint4 kA[NV], vA[NV], kB[NV], vB[NV];
     const int nchunks = MULTI ? (p.kv + KC - 1) / KC : 1;
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int c0 = ch * KC;
-      T* Ks = reinterpret_cast<T*>(smem_raw) + (p.nbuf == 2 ? (ch & 1) * bufsz : 0);
-      T* Vt = Ks + KC * ldk;
-      if (ch > 0 && p.nbuf == 1) __syncthreads();  // single buffer: previous chunk consumed
-      store_kv<T, NV>(p, tid, Ks, Vt, ldk, ldv, kreg, vreg);
-      __syncthreads();
-      if (MULTI && ch + 1 < nchunks) load_kv<T, NV, TOK>(p, it, tid, rtab, c0 + KC, kreg, vreg);  // next chunk in flight
-      compute_chunk<T, MULTI, RAGGED>(p, it, wave, g, col, Ks, Vt, ldk, ldv, min(KC, p.kv - c0), ones, us);
+    const bool loader = wave * 64 < ((KC / 16) << p.lg_oct);  // uniform
+    if (loader) {
+      load_kv<T, NV, TOK>(p, it, tid, rtab, 0, kA, vA);
+      if (MULTI && nchunks > 1) load_kv<T, NV, TOK>(p, it, tid, rtab, KC, kB, vB);
+    }
+    for (int ch = 0; ch < nchunks; ch += 2) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int cc = ch + half;
+        if (cc >= nchunks) break;  // uniform
+        const int c0 = cc * KC;
+        T* Ks = reinterpret_cast<T*>(smem_raw) + (p.nbuf == 2 ? (cc & 1) * bufsz : 0);
+        T* Vt = Ks + KC * ldk;
+        if (cc > 0 && p.nbuf == 1) __syncthreads();  // single buffer: previous chunk consumed
+        if (loader) {
+          if (half == 0)
+            store_kv<T, NV>(p, tid, Ks, Vt, ldk, ldv, kA, vA);
+          else
+            store_kv<T, NV>(p, tid, Ks, Vt, ldk, ldv, kB, vB);
+        }
+        __syncthreads();
+        if (loader && MULTI && cc + 2 < nchunks) {  // the chunk after next in flight
+          if (half == 0)
+            load_kv<T, NV, TOK>(p, it, tid, rtab, c0 + 2 * KC, kA, vA);
+          else
+            load_kv<T, NV, TOK>(p, it, tid, rtab, c0 + 2 * KC, kB, vB);
+        }
+        compute_chunk<T, MULTI, RAGGED>(p, it, wave, g, col, Ks, Vt, ldk, ldv, min(KC, p.kv - c0), ones, us);
+      }
     }
   }
   store_outputs<T>(p, it, us, bad);
@@ -690,6 +720,7 @@ namespace {
 struct AttnLaunch {
   AttnParams p;
   size_t lds;
+  int waves;
   int nv;
   bool multi;
   int64_t nwg;
@@ -702,11 +733,16 @@ AttnLaunch plan_attend(const Shape& s, int dtype) {
   p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S; p.topk = s.topk;
   p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R; p.kv = s.kv;
   p.heads = s.heads;
-  p.nqb = (s.n + QB - 1) / QB;
-  const int qtiles = (min(s.n, QB) + 15) / 16;
+  // chunked kernel: 128-query items, one wave per (head, 16-query tile) unit
+  // (more queries per staged chunk measured faster at the dense 128x128
+  // shape: 30.1 us with 128, 39.4 with 64 queries and two units per wave,
+  // 43.3 with 32)
+  p.qblk = s.kv > KC ? QBM : QB;
+  p.nqb = (s.n + p.qblk - 1) / p.qblk;
+  const int qtiles = (min(s.n, p.qblk) + 15) / 16;
   const int cap = dtype == kBF16 ? 4 : 2;  // keeps LDS at or below 64 KiB
   int HG = 1;  // largest power of two <= min(units budget, cap, heads)
-  while (2 * HG <= (NW * MAXU) / qtiles && 2 * HG <= cap && 2 * HG <= s.heads) HG *= 2;
+  while (2 * HG <= (kMaxUnits * MAXU) / qtiles && 2 * HG <= cap && 2 * HG <= s.heads) HG *= 2;
   p.HG = HG;
   p.nhg = (s.heads + HG - 1) / HG;
   p.nitems = s.B * s.R * p.nqb * p.nhg;
@@ -724,7 +760,8 @@ AttnLaunch plan_attend(const Shape& s, int dtype) {
   const size_t buf = esz * ((size_t)KC * (HG * D + padk) + (size_t)HG * D * (KC + padv));
   p.nbuf = (s.kv > KC && 2 * buf <= 65536) ? 2 : 1;
   L.lds = p.nbuf * buf;
-  L.nv = (KC * (HG * D / vec) + NW * 64 - 1) / (NW * 64);
+  L.waves = std::max(kMinWaves, std::min(kMaxUnits, HG * qtiles));
+  L.nv = (KC * (HG * D / vec) + L.waves * 64 - 1) / (L.waves * 64);  // <= 4: at least 4 waves
   L.multi = s.kv > KC;
   // One item per workgroup. (Two items per workgroup, with all loads of both
   // in flight before either is computed, measured slower at the stage-1
@@ -816,7 +853,8 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
   AttnLaunch L = plan_attend(s, dtype);
   L.p.Q = Q; L.p.K = K; L.p.V = V; L.p.idx = idx; L.p.O = O;
   void* args[] = {&L.p};
-  hipError_t e = hipLaunchKernel(pick_attend(dtype, L), dim3((unsigned)L.nwg), dim3(NW * 64), args, L.lds, stream);
+  if (L.nv > 4 || (L.nv > 2 && L.waves > 8)) return hipErrorInvalidValue;  // the kernels' launch bounds
+  hipError_t e = hipLaunchKernel(pick_attend(dtype, L), dim3((unsigned)L.nwg), dim3(L.waves * 64), args, L.lds, stream);
   if (e != hipSuccess || !lce) return e;
   return launch_lce(V, lce_w, lce_b, O, s, dtype, stream);
 }
