@@ -276,6 +276,21 @@ def main(argv=None):
     attend_us = phase_us(attend_cycle, attend_singles)
     route_us = phase_us(route_cycle, route_singles)
 
+    # a plain streaming reference with the attention kernel's traffic: read
+    # three tensors of Q's shape and dtype, write a fourth (torch.addcmul),
+    # over the same input copies and timed the same way
+    ref_outs = [torch.empty_like(s_.q) for s_ in steps]
+    stream_fns = [lambda s_=s_, o_=o_: torch.addcmul(s_.q, s_.k, s_.v, out=o_) for s_, o_ in zip(steps, ref_outs)]
+    for f in stream_fns:
+        f()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        stream_cycle = capture(stream_fns)
+        stream_singles = [capture([f]) for f in stream_fns]
+    torch.cuda.synchronize()
+    stream_us = phase_us(stream_cycle, stream_singles)
+    del ref_outs
+
     with_lce = None
     if not args.no_lce:
         for s_ in steps:
@@ -379,6 +394,10 @@ def main(argv=None):
     roof["kernel"] = "attend_head_kernel" if w.kv <= 64 else "attend_kernel"
     roof["algorithmic_bytes_per_launch"] = attn_bytes
     roof["launch_us"] = round(attend_us, 2)
+    # the same bytes moved by a plain streaming kernel on this GPU, and the
+    # attention kernel's rate as a fraction of that
+    roof["stream_reference_us"] = round(stream_us, 2)
+    roof["frac_of_stream_reference"] = round(stream_us / attend_us, 4)
 
     result = {
         "metric": METRIC,
