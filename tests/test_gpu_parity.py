@@ -87,6 +87,29 @@ def test_full_size_route_all_images(w):
     assert parity.exact_route_mismatches(O.topk_route(A, w.topk), idx) == 0
 
 
+# bra_route takes any C that is a multiple of 8 (routing has no head split).
+# Shapes whose C is not a multiple of 32 route with the vector kernel, as do
+# those with more than 64 regions; the workloads above use the matrix-core one.
+ROUTE_ANY_C = [
+    wl.custom(2, 6, 6, 8, 1, 3, 3, "bf16", seed=50),      # 9 regions, C = 8
+    wl.custom(2, 14, 14, 40, 1, 7, 4, "f32", seed=51),    # 49 regions, C = 40
+    wl.custom(1, 16, 16, 24, 1, 8, 64, "bf16", seed=52),  # 64 regions, full routing
+    wl.custom(1, 16, 16, 48, 1, 16, 9, "bf16", seed=53),  # 256 regions, C = 48
+    wl.custom(3, 8, 8, 96, 3, 8, 1, "bf16", seed=54),     # 64 regions, k = 1, 3 x 32 channels
+]
+
+
+@pytest.mark.parametrize("w", ROUTE_ANY_C, ids=[w.name for w in ROUTE_ANY_C])
+def test_route_any_channel_count(w):
+    q, k, _ = wl.make_inputs(w)
+    qd, kd = _gpu(q, k)
+    idx = bra.route(qd, kd, w.S, w.topk).cpu().numpy()
+    A = _oracle_affinity(_f64(q), _f64(k), w.S)
+    bad = parity.route_violations(A, idx, w.topk)
+    assert not bad, bad[:5]
+    assert parity.exact_route_mismatches(O.topk_route(A, w.topk), idx) == 0
+
+
 # Ragged and edge shapes: n not a multiple of 16, kv not a multiple of 64,
 # more than 64 queries per region, a partial head group, H != W, many regions,
 # full routing, one region, one token per region.

@@ -4,24 +4,38 @@
 // Routing Attention", Section 3: row i of the routing index holds the k
 // regions most relevant to region i).
 //
-// One workgroup per (image b, block of 4 affinity rows); each of its 4 waves
-// owns one row, and lane j owns the candidates j, j+64, j+128, j+192 (at most
-// 256 regions). Channels are streamed in slices of CC: each slice of K^r[b]
-// (all R rows) and of the block's query rows is staged in LDS with coalesced
-// loads, the next slice's loads being in flight while the current one is used.
-// A[i][j] = Q^r[b,i,:] . K^r[b,j,:] is accumulated as four fused
-// multiply-add chains, one per channel residue mod 4, in increasing channel
-// order, and combined as (s0 + s1) + (s2 + s3): a fixed order, so the values
-// are bit-reproducible. The query row is read as a broadcast, K^r row j by
-// lane j. The row never reaches HBM.
-//
 // Top-k by rank: candidate j of row i is beaten by m when A[i][m] > A[i][j],
 // or A[i][m] == A[i][j] and m < j. This is a strict total order, so the number
 // of candidates that beat j is a unique rank in [0, R); j is routed iff its
 // rank is below k, and it is written to slot `rank`, which lists the routed
 // regions in descending affinity with the lower index first on exact ties.
-// Each lane counts against the whole row (broadcast LDS reads): R compares
-// per candidate, independent of k.
+// The affinity rows never reach HBM.
+//
+// Two forms; each shape always takes the same one, so every routing table of
+// a shape is the same bits.
+//
+// R <= 64 and C a multiple of 32 (matrix-core form; every shape with heads of
+// 32 channels). The affinity of one image is a 64 x 64 (padded)
+// fp32 product over C channels, done with 16x16x4 fp32 MFMA. One workgroup
+// per (image, block of 16 rows), 8 waves: wave w computes the 16 x 16 tile of
+// candidates 16 (w % 4) .. +15 over channel half w / 4, its operands loaded
+// straight from memory as 16-byte vectors (one round trip for C <= 256); the
+// two halves are added in a fixed order through LDS. Each affinity becomes a
+// 64-bit key (order-preserving bits of the value, then 63 - j), so "beats" is
+// one unsigned compare; k = 1 is a wave-wide maximum of the keys. The row
+// blocks of one image are given workgroup ids that are equal mod 8, so they
+// run on one XCD and share its L2 copy of K^r[b].
+//
+// Other shapes (vector form). One workgroup per (image b, block of 4 affinity rows);
+// each of its 4 waves owns one row, and lane j owns the candidates j, j+64,
+// j+128, j+192 (at most 256 regions). Channels are streamed in slices of CC:
+// each slice of K^r[b] (all R rows) and of the block's query rows is staged
+// in LDS with coalesced loads, the next slice's loads being in flight while
+// the current one is used. A[i][j] is accumulated as four fused multiply-add
+// chains, one per channel residue mod 4, in increasing channel order, and
+// combined as (s0 + s1) + (s2 + s3). The query row is read as a broadcast,
+// K^r row j by lane j. Each lane counts its rank against the whole row
+// (broadcast LDS reads): R compares per candidate, independent of k.
 #include "bra_internal.h"
 #include "route_common.h"
 
@@ -37,11 +51,12 @@ struct RouteParams {
   const float* Qr;
   const float* Kr;
   int32_t* idx;
-  int R, C, topk;
+  int B, R, C, topk;
   int row_blocks;  // ceil(R / RB): workgroups per image
   int ldr;         // LDS row stride of the affinity block (R rounded up to 4)
 };
 
+// ---- vector form ----
 // NU: candidates per lane (1 when R <= 64, 4 when R <= 256).
 // CC: channels per staged slice (fewer when there are more candidate rows).
 template <int NU> struct RouteCfg {
@@ -145,8 +160,146 @@ __global__ __launch_bounds__(NT) void route_kernel(RouteParams p) {
   }
 }
 
+// ---- matrix-core form (R <= 64, C a multiple of 32) ----
+constexpr int MR = 16;    // affinity rows per workgroup
+constexpr int MW = 8;     // waves: 4 candidate tiles x 2 channel halves
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Order-preserving key of candidate j with affinity a: a larger key beats a
+// smaller one exactly when the affinity is larger, or equal with a lower
+// index. -0 is folded into +0 first, so zeros tie as they compare.
+__device__ inline uint64_t affinity_key(float a, int j) {
+  uint32_t u = __float_as_uint(a == 0.f ? 0.f : a);
+  u = (u >> 31) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(63 - j);
+}
+
+// the larger of a and the key with halves (lo, hi)
+__device__ inline uint64_t key_max(uint64_t a, uint32_t lo, uint32_t hi) {
+  const uint64_t b = ((uint64_t)hi << 32) | lo;
+  return b > a ? b : a;
+}
+
+// Largest key over the 64 lanes, in every lane: DPP within rows of 16 (swap
+// neighbours, swap pairs, rotate by 4, rotate by 8), then the permlane swaps
+// across rows. max is exact, so the order of combination does not matter.
+__device__ inline uint64_t wave_max_key(uint64_t v) {
+#define BRA_KEY_DPP(ctrl)                                                                         \
+  v = key_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, ctrl, 0xF, 0xF, false),      \
+              (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false))
+  BRA_KEY_DPP(0xB1);   // quad_perm 1,0,3,2
+  BRA_KEY_DPP(0x4E);   // quad_perm 2,3,0,1
+  BRA_KEY_DPP(0x124);  // row_ror:4
+  BRA_KEY_DPP(0x128);  // row_ror:8
+#undef BRA_KEY_DPP
+  {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    v = key_max(key_max(v, lo[0], hi[0]), lo[1], hi[1]);
+  }
+  {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    v = key_max(key_max(v, lo[0], hi[0]), lo[1], hi[1]);
+  }
+  return v;
+}
+
+// NS: 16-channel steps per wave loaded at once (a divisor of C / 32; all of a
+// chunk's loads are issued before its products)
+template <int NS>
+__global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
+  __shared__ float part[MR][64];                    // channel half 1 of each tile
+  __shared__ __align__(16) uint64_t keys[MR][64];   // keys of the block's rows
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tile = wave & 3, half = wave >> 2;
+  const int g = lane >> 4, l16 = lane & 15;
+  // workgroup x -> image (x % 8) + 8 * (x / 8 / row_blocks), row block (x / 8) % row_blocks
+  const int slot = blockIdx.x >> 3;
+  const int bq = slot / p.row_blocks;
+  const int b = (blockIdx.x & 7) + 8 * bq;
+  if (b >= p.B) return;  // whole workgroup
+  const int i0 = (slot - bq * p.row_blocks) * MR;
+  const int ncol = (p.R + 15) & ~15;
+  const int j0 = tile * 16;
+  const bool active = j0 < ncol;
+
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    // A operand: lane supplies query row i0 + l16, B operand candidate row
+    // j0 + l16, both the channels 16 t + 4 g .. + 3 of the half at step t
+    // (rows past R read row R - 1; their results are never used)
+    const int nh = p.C >> 5;  // 16-channel steps per half
+    const int64_t img = (int64_t)b * p.R;
+    const float* qrow = p.Qr + (img + min(i0 + l16, p.R - 1)) * p.C + half * (p.C >> 1) + 4 * g;
+    const float* krow = p.Kr + (img + min(j0 + l16, p.R - 1)) * p.C + half * (p.C >> 1) + 4 * g;
+    for (int t0 = 0; t0 < nh; t0 += NS) {
+      float4 a[NS], k[NS];
+#pragma unroll
+      for (int m = 0; m < NS; ++m) {
+        a[m] = *reinterpret_cast<const float4*>(qrow + 16 * (t0 + m));
+        k[m] = *reinterpret_cast<const float4*>(krow + 16 * (t0 + m));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk ahead of the products
+#pragma unroll
+      for (int m = 0; m < NS; ++m) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].x, k[m].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].y, k[m].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].z, k[m].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].w, k[m].w, acc, 0, 0, 0);
+      }
+    }
+    // lane holds rows 4 g .. 4 g + 3 of candidate column j0 + l16
+    if (half == 1) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) part[4 * g + ii][j0 + l16] = acc[ii];
+    }
+  }
+  __syncthreads();
+  if (active && half == 0) {
+    const int col = j0 + l16;
+    const uint64_t valid = col < p.R ? ~0ull : 0ull;  // columns past R get key 0
+    float ph[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) ph[ii] = part[4 * g + ii][col];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) keys[4 * g + ii][col] = affinity_key(acc[ii] + ph[ii], col) & valid;
+  }
+  __syncthreads();
+
+  // wave w ranks rows 2w and 2w + 1 of the block; lane j is candidate j
+#pragma unroll
+  for (int q = 0; q < MR / MW; ++q) {
+    const int row = (MR / MW) * wave + q;
+    if (i0 + row >= p.R) break;  // uniform
+    int32_t* out = p.idx + ((int64_t)b * p.R + i0 + row) * p.topk;
+    const uint64_t kj = lane < ncol ? keys[row][lane] : 0ull;
+    if (p.topk == 1) {
+      const uint64_t best = wave_max_key(kj);
+      if (lane == 0) out[0] = 63 - (int)(uint32_t)best;
+    } else {
+      // 16 keys per block (ncol is a multiple of 16), all 8 broadcast reads
+      // of a block issued before its compares
+      int rank = 0;
+      for (int m0 = 0; m0 < ncol; m0 += 16) {
+        ulonglong2 km[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) km[e] = *reinterpret_cast<const ulonglong2*>(&keys[row][m0 + 2 * e]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          rank += km[e].x > kj;
+          rank += km[e].y > kj;
+        }
+      }
+      if (lane < p.R && rank < p.topk) out[rank] = lane;
+    }
+  }
+}
+
 }  // namespace
 
+// dynamic LDS of the vector form
 size_t route_lds_bytes(const Shape& s) {
   const int ldr = (s.R + 3) / 4 * 4;
   const int ldc = s.R <= 64 ? RouteCfg<1>::LDC : RouteCfg<4>::LDC;
@@ -155,12 +308,23 @@ size_t route_lds_bytes(const Shape& s) {
 
 hipError_t launch_route(const float* Qr, const float* Kr, int32_t* idx,
                         const Shape& s, hipStream_t stream) {
-  RouteParams p{Qr, Kr, idx, s.R, s.C, s.topk, (s.R + RB - 1) / RB, (s.R + 3) / 4 * 4};
-  dim3 grid((unsigned)(s.B * p.row_blocks));
-  void* args[] = {&p};
+  void* args[1];
+  if (s.R <= 64 && s.C % 32 == 0) {
+    RouteParams p{Qr, Kr, idx, s.B, s.R, s.C, s.topk, (s.R + MR - 1) / MR, 0};
+    args[0] = &p;
+    const unsigned grid = (unsigned)(((s.B + 7) / 8) * 8 * p.row_blocks);
+    const int nh = s.C / 32;
+    const void* fn = nh % 8 == 0   ? reinterpret_cast<const void*>(&route_mfma_kernel<8>)
+                     : nh % 4 == 0 ? reinterpret_cast<const void*>(&route_mfma_kernel<4>)
+                     : nh % 2 == 0 ? reinterpret_cast<const void*>(&route_mfma_kernel<2>)
+                                   : reinterpret_cast<const void*>(&route_mfma_kernel<1>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(MW * 64), args, 0, stream);
+  }
+  RouteParams p{Qr, Kr, idx, s.B, s.R, s.C, s.topk, (s.R + RB - 1) / RB, (s.R + 3) / 4 * 4};
+  args[0] = &p;
   const void* fn = s.R <= 64 ? reinterpret_cast<const void*>(&route_kernel<1>)
                              : reinterpret_cast<const void*>(&route_kernel<4>);
-  return hipLaunchKernel(fn, grid, dim3(NT), args, route_lds_bytes(s), stream);
+  return hipLaunchKernel(fn, dim3((unsigned)(s.B * p.row_blocks)), dim3(NT), args, route_lds_bytes(s), stream);
 }
 
 }  // namespace bra

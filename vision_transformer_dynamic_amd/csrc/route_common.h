@@ -1,7 +1,7 @@
-// Routing arithmetic: region affinity A[i][j] = Q^r[i,:] . K^r[j,:] in one
-// fixed order, and the top-k tie rule (explainer "BiFormer Reshapes Visual
-// Attention with 'Bi-Level Routing'", Part 2.2 pseudocode steps 4-5). Any
-// kernel that routes uses these, so all routing tables agree bit for bit.
+// Routing arithmetic of the vector form of the route kernel: region affinity
+// A[i][j] = Q^r[i,:] . K^r[j,:] in one fixed order, and the top-k tie rule
+// (explainer "BiFormer Reshapes Visual Attention with 'Bi-Level Routing'",
+// Part 2.2 pseudocode steps 4-5).
 #pragma once
 
 #include <hip/hip_runtime.h>
