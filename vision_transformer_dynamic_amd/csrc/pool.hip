@@ -55,7 +55,9 @@ __device__ inline void accum16<4>(float* acc, const uint4 v) {
 template <int ESIZE>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   constexpr int VEC = 16 / ESIZE;  // elements per 16-byte vector
-  __shared__ float red[2][256 * VEC];
+  // per-thread partial sums of Q and K, sized to the launched block (dynamic
+  // LDS), so the LDS does not cap how many workgroups a CU holds
+  extern __shared__ float red[];  // [2][blockDim.x * VEC]
 
   const int R = p.S * p.S;
   const int b = blockIdx.x / R;
@@ -98,10 +100,12 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
       }
     }
   }
+  float* redq = red;
+  float* redk = red + blockDim.x * VEC;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    red[0][t * VEC + e] = acc[0][e];
-    red[1][t * VEC + e] = acc[1][e];
+    redq[t * VEC + e] = acc[0][e];
+    redk[t * VEC + e] = acc[1][e];
   }
   __syncthreads();
 
@@ -114,7 +118,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     const int g = cc / VEC;
     const int e = cc - g * VEC;
     float s = 0.f;
-    for (int u = g; u < nthr; u += G) s += red[which][u * VEC + e];
+    const float* part = which ? redk : redq;
+    for (int u = g; u < nthr; u += G) s += part[u * VEC + e];
     float* out = which ? p.Kr : p.Qr;
     out[((int64_t)b * R + r) * p.C + cc] = s * inv_n;
   }
@@ -135,9 +140,10 @@ hipError_t launch_pool(const void* Q, const void* K, float* Qr, float* Kr,
   while (bs < G) bs *= 2;
   dim3 grid((unsigned)(s.B * s.R));
   void* args[] = {&p};
+  const size_t lds = 2 * sizeof(float) * (size_t)bs * vec;
   if (dtype == kBF16)
-    return hipLaunchKernel(reinterpret_cast<const void*>(&pool_kernel<2>), grid, dim3(bs), args, 0, stream);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&pool_kernel<4>), grid, dim3(bs), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&pool_kernel<2>), grid, dim3(bs), args, lds, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&pool_kernel<4>), grid, dim3(bs), args, lds, stream);
 }
 
 }  // namespace bra
