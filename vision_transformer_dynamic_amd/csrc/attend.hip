@@ -344,7 +344,7 @@ __device__ __forceinline__ void store_outputs(const AttnParams& p, const Item& i
         o[4 + e] = us.acc[uu][1][e] * inv;
       }
     }
-    TT::store8(Og + us.qoff[uu], o);
+    TT::store8_nt(Og + us.qoff[uu], o);
   }
 }
 
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
         o[0] += lo.x; o[1] += lo.y; o[2] += lo.z; o[3] += lo.w;
         o[4] += hi.x; o[5] += hi.y; o[6] += hi.z; o[7] += hi.w;
       }
-      TT::store8(Og + qoff[t], o);
+      TT::store8_nt(Og + qoff[t], o);
     }
   }
 }

@@ -66,6 +66,11 @@ struct Tr<__bf16> {
   __device__ static inline void store8(__bf16* p, const float* v) {
     *reinterpret_cast<op8*>(p) = from_f32(v);
   }
+  // non-temporal: the attention output is not read again by the kernel, and
+  // the hint keeps it from piling up as dirty lines in L2
+  __device__ static inline void store8_nt(__bf16* p, const float* v) {
+    __builtin_nontemporal_store(from_f32(v), reinterpret_cast<op8*>(p));
+  }
   // 16-deep contraction: 4 slots per lane
   typedef shortx4 op4;
   __device__ static inline floatx4 mma16(op4 a, op4 b, floatx4 c) {
@@ -124,6 +129,10 @@ struct Tr<float> {
   __device__ static inline void store8(float* p, const float* v) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __device__ static inline void store8_nt(float* p, const float* v) {
+    __builtin_nontemporal_store(floatx4{v[0], v[1], v[2], v[3]}, reinterpret_cast<floatx4*>(p));
+    __builtin_nontemporal_store(floatx4{v[4], v[5], v[6], v[7]}, reinterpret_cast<floatx4*>(p + 4));
   }
   typedef floatx4 op4;
   __device__ static inline floatx4 mma16(op4 a, op4 b, floatx4 c) {
