@@ -344,7 +344,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
       o[e] = dq[0][e] * p.scale;
       o[4 + e] = dq[1][e] * p.scale;
     }
-    TT::store8(dQg + qtok * p.C + ch0 + 8 * g, o);
+    TT::store8_nt(dQg + qtok * p.C + ch0 + 8 * g, o);
     if (g == 0) {
       const int64_t at = ((int64_t)b * p.H * p.W + qtok) * p.heads + head;
       p.lse[at] = lse;
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
         o[e] = dq[0][e] * p.scale;
         o[4 + e] = dq[1][e] * p.scale;
       }
-      TT::store8(dQg + qtok[t] * p.C + ch0 + 8 * g, o);
+      TT::store8_nt(dQg + qtok[t] * p.C + ch0 + 8 * g, o);
       if (g == 0) {
         const int64_t at = ((int64_t)b * p.H * p.W + qtok[t]) * p.heads + head;
         p.lse[at] = lse;
@@ -777,8 +777,8 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
       ok[4 + e] = dk[1][kt2][e] * p.scale;
     }
     const int off = ktok[kt2] * p.C + ch0 + 8 * g;
-    TT::store8(dVg + off, ov);
-    TT::store8(dKg + off, ok);
+    TT::store8_nt(dVg + off, ov);
+    TT::store8_nt(dKg + off, ok);
   }
 }
 
