@@ -164,48 +164,6 @@ __global__ __launch_bounds__(NT) void route_kernel(RouteParams p) {
 constexpr int MR = 16;    // affinity rows per workgroup
 constexpr int MW = 8;     // waves: 4 candidate tiles x 2 channel halves
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-// Order-preserving key of candidate j with affinity a: a larger key beats a
-// smaller one exactly when the affinity is larger, or equal with a lower
-// index. -0 is folded into +0 first, so zeros tie as they compare.
-__device__ inline uint64_t affinity_key(float a, int j) {
-  uint32_t u = __float_as_uint(a == 0.f ? 0.f : a);
-  u = (u >> 31) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(63 - j);
-}
-
-// the larger of a and the key with halves (lo, hi)
-__device__ inline uint64_t key_max(uint64_t a, uint32_t lo, uint32_t hi) {
-  const uint64_t b = ((uint64_t)hi << 32) | lo;
-  return b > a ? b : a;
-}
-
-// Largest key over the 64 lanes, in every lane: DPP within rows of 16 (swap
-// neighbours, swap pairs, rotate by 4, rotate by 8), then the permlane swaps
-// across rows. max is exact, so the order of combination does not matter.
-__device__ inline uint64_t wave_max_key(uint64_t v) {
-#define BRA_KEY_DPP(ctrl)                                                                         \
-  v = key_max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, ctrl, 0xF, 0xF, false),      \
-              (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), ctrl, 0xF, 0xF, false))
-  BRA_KEY_DPP(0xB1);   // quad_perm 1,0,3,2
-  BRA_KEY_DPP(0x4E);   // quad_perm 2,3,0,1
-  BRA_KEY_DPP(0x124);  // row_ror:4
-  BRA_KEY_DPP(0x128);  // row_ror:8
-#undef BRA_KEY_DPP
-  {
-    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-    v = key_max(key_max(v, lo[0], hi[0]), lo[1], hi[1]);
-  }
-  {
-    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-    v = key_max(key_max(v, lo[0], hi[0]), lo[1], hi[1]);
-  }
-  return v;
-}
-
 // NS: 16-channel steps per wave loaded at once (a divisor of C / 32; all of a
 // chunk's loads are issued before its products)
 template <int NS>
@@ -243,12 +201,7 @@ __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk ahead of the products
 #pragma unroll
-      for (int m = 0; m < NS; ++m) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].x, k[m].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].y, k[m].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].z, k[m].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m].w, k[m].w, acc, 0, 0, 0);
-      }
+      for (int m = 0; m < NS; ++m) acc = affinity_mfma_step(acc, a[m], k[m]);
     }
     // lane holds rows 4 g .. 4 g + 3 of candidate column j0 + l16
     if (half == 1) {
@@ -257,9 +210,11 @@ __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
     }
   }
   __syncthreads();
-  if (active && half == 0) {
+  if (half == 0) {
+    // every one of the 64 key columns is written: columns past R (including
+    // whole tiles past ncol, whose waves computed nothing) get key 0
     const int col = j0 + l16;
-    const uint64_t valid = col < p.R ? ~0ull : 0ull;  // columns past R get key 0
+    const uint64_t valid = active && col < p.R ? ~0ull : 0ull;
     float ph[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) ph[ii] = part[4 * g + ii][col];
@@ -274,24 +229,12 @@ __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
     const int row = (MR / MW) * wave + q;
     if (i0 + row >= p.R) break;  // uniform
     int32_t* out = p.idx + ((int64_t)b * p.R + i0 + row) * p.topk;
-    const uint64_t kj = lane < ncol ? keys[row][lane] : 0ull;
+    const uint64_t kj = keys[row][lane];
     if (p.topk == 1) {
       const uint64_t best = wave_max_key(kj);
       if (lane == 0) out[0] = 63 - (int)(uint32_t)best;
     } else {
-      // 16 keys per block (ncol is a multiple of 16), all 8 broadcast reads
-      // of a block issued before its compares
-      int rank = 0;
-      for (int m0 = 0; m0 < ncol; m0 += 16) {
-        ulonglong2 km[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) km[e] = *reinterpret_cast<const ulonglong2*>(&keys[row][m0 + 2 * e]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          rank += km[e].x > kj;
-          rank += km[e].y > kj;
-        }
-      }
+      const int rank = key_rank64(&keys[row][0], kj);
       if (lane < p.R && rank < p.topk) out[rank] = lane;
     }
   }
