@@ -12,10 +12,13 @@
 //
 // with dK, dV of a token summed over every query region routed to its region.
 //
-// Three kernels, all deterministic (no atomics on gradients):
-//  1. bwd_routes_kernel: per image, the inverse routing table - for every key
+// Three steps, all deterministic (no atomics on gradients):
+//  1. inverse_table: per image, the inverse routing table - for every key
 //     region, the ascending list of query regions whose rows hold it. A row
-//     with an entry outside [0, S*S) is marked bad and left out.
+//     with an entry outside [0, S*S) is marked bad and left out. With at most
+//     64 keys per query and 64 regions it runs as B leading workgroups of the
+//     dQ launch (only step 3 needs it); otherwise bwd_routes_kernel, a launch
+//     of its own.
 //  2. dQ: the forward's transposed products (S^T = K Q^T, dP^T = V dO^T,
 //     dQ^T = K^T dZ^T with K^T through LDS), D from O and dO, and the base-2
 //     log-sum-exp of every query, written for kernel 3. With at most 64 keys
@@ -32,6 +35,8 @@
 #include "attn_common.h"
 
 #include <math.h>
+
+#include <algorithm>
 
 namespace bra {
 namespace {
@@ -54,6 +59,7 @@ struct BwdParams {
   int H, W, C, S, topk;
   int sh, sw, n, R, kv, heads;
   int HG, nhg, nqb, ntq, nitems_q;    // dq kernel
+  int ntab;                           // dq head kernel: leading workgroups that build the inverse table (0 or B)
   int HGk, nhgk, nkb, nitems_kv;      // dkv kernel
   float c;      // scale * log2(e)
   float scale;  // 1 / sqrt(d)
@@ -66,51 +72,62 @@ __device__ inline int corner_of(const BwdParams& p, int r) {
   return ry * p.sh * p.W + rx * p.sw;
 }
 
-__device__ inline int xcd_remap() {
-  const int nwg = gridDim.x, bid = blockIdx.x;
+// workgroup id -> work item, for the grid past its first `skip` workgroups
+__device__ inline int xcd_remap(int skip = 0) {
+  const int nwg = gridDim.x - skip, bid = blockIdx.x - skip;
   const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
   return x * q8 + min(x, r8) + loc;  // consecutive work items to one XCD
 }
 
 // ---------------------------------------------------------------------------
-// 1. Inverse routing table, one workgroup per image. Each routing row becomes
-// a bit mask of its regions in LDS (bitwise OR is order-free); then one wave
-// per key region tests 64 rows at a time and places the good rows that hold
-// it with a ballot prefix count, so each list comes out ascending.
-__global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
-  __shared__ uint32_t mask[kMaxRegions][kMaxRegions / 32];
-  __shared__ int rowbad[kMaxRegions];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int R = p.R, k = p.topk;
+// 1. Inverse routing table of image b, by one workgroup (a multiple of 64
+// threads) in lds: R rows of (R + 31) / 32 mask words, then R row flags. Each
+// routing row becomes a bit mask of its regions (bitwise OR is order-free);
+// then one wave per key region tests 64 rows at a time and places the good
+// rows that hold it with a ballot prefix count, so each list comes out
+// ascending.
+__device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int R = p.R, k = p.topk, nw = (R + 31) >> 5;
+  uint32_t* mask = lds;                                  // [R][nw]
+  int* rowbad = reinterpret_cast<int*>(lds + R * nw);    // [R]
   const int32_t* idx = p.idx + (int64_t)b * R * k;
-  for (int e = tid; e < R * (kMaxRegions / 32); e += 256) mask[e / (kMaxRegions / 32)][e % (kMaxRegions / 32)] = 0u;
-  for (int i = tid; i < R; i += 256) rowbad[i] = 0;
+  for (int e = tid; e < R * nw; e += nt) mask[e] = 0u;
+  for (int i = tid; i < R; i += nt) rowbad[i] = 0;
   __syncthreads();
-  for (int e = tid; e < R * k; e += 256) {
+  for (int e = tid; e < R * k; e += nt) {
     const int i = e / k, r = idx[e];
     if (r < 0 || r >= R)
       rowbad[i] = 1;
     else
-      atomicOr(&mask[i][r >> 5], 1u << (r & 31));
+      atomicOr(&mask[i * nw + (r >> 5)], 1u << (r & 31));
   }
   __syncthreads();
-  // wave w compacts the lists of key regions w, w + 4, ...: 64 rows per step,
-  // hits placed by a ballot prefix count, so each list is ascending
-  const int wave = tid >> 6, lane = tid & 63;
+  // wave w compacts the lists of key regions w, w + nwaves, ...
+  const int wave = tid >> 6, lane = tid & 63, nwaves = nt >> 6;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int r = wave; r < R; r += 4) {
+  for (int r = wave; r < R; r += nwaves) {
     int* L = p.inv_list + ((int64_t)b * R + r) * R;
     int m = 0;
     for (int i0 = 0; i0 < R; i0 += 64) {
       const int i = i0 + lane;
-      const bool hit = i < R && !rowbad[i] && ((mask[i][r >> 5] >> (r & 31)) & 1u);
+      const bool hit = i < R && !rowbad[i] && ((mask[i * nw + (r >> 5)] >> (r & 31)) & 1u);
       const uint64_t bal = __ballot(hit);
       if (hit) L[m + __popcll(bal & below)] = i;
       m += __popcll(bal);
     }
     if (lane == 0) p.inv_cnt[b * R + r] = m;
   }
-  for (int r = tid; r < R; r += 256) p.bad[b * R + r] = rowbad[r];
+  for (int r = tid; r < R; r += nt) p.bad[b * R + r] = rowbad[r];
+}
+
+// LDS bytes of inverse_table
+constexpr size_t inverse_table_lds(int R) { return sizeof(uint32_t) * ((size_t)R * ((R + 31) / 32) + R); }
+
+// For more than 64 regions: a launch of its own, one workgroup per image.
+__global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
+  __shared__ uint32_t lds[kMaxRegions * (kMaxRegions / 32) + kMaxRegions];
+  inverse_table(p, blockIdx.x, lds);
 }
 
 // Chunk token table: tok[kappa - c0] = token (inside the image) of routed key
@@ -376,7 +393,14 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
   const int g = lane >> 4, col = lane & 15;
   const int ldk = KC + TT::PADV;
 
-  int w = xcd_remap();
+  if ((int)blockIdx.x < p.ntab) {
+    // one of the first B workgroups (when the launch builds the inverse
+    // routing table): the table of image blockIdx.x, in this kernel's dynamic
+    // LDS. They come first in dispatch order, so their slots free up at once.
+    inverse_table(p, blockIdx.x, reinterpret_cast<uint32_t*>(smem_raw));
+    return;
+  }
+  int w = xcd_remap(p.ntab);
   const int hg = w % p.nhg;
   w /= p.nhg;
   const int qb = w % p.nqb;
@@ -838,10 +862,21 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
 
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel((const void*)&bwd_routes_kernel, dim3(s.B), dim3(256), args, 0, stream);
-  if (e != hipSuccess) return e;
-
+  hipError_t e = hipSuccess;
+  // The inverse routing table: for the single-chunk dQ kernel (many short
+  // workgroups) with at most 64 regions, its LDS fits in the dQ kernel's and B
+  // workgroups put ahead of the dQ grid build it there, one launch fewer.
+  // Otherwise a launch of its own: the several-chunk dQ kernel's few long
+  // workgroups can fill the machine in one round, and extra ones would push
+  // some of them into a second.
   const bool multi = s.kv > KC, ragged = s.kv % KC != 0;
+  const bool fold = !multi && s.R <= 64;
+  const int extra = fold ? s.B : 0;
+  if (!fold) {
+    e = hipLaunchKernel((const void*)&bwd_routes_kernel, dim3(s.B), dim3(256), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+
   const void* fq;
   size_t ldsq;
   if (!multi) {
@@ -852,8 +887,9 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
     ph.HG = H8;
     ph.nhg = (s.heads + H8 - 1) / H8;
     const int64_t nqh = (int64_t)s.B * s.R * p.nqb * ph.nhg;
-    if (nqh >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (nqh + extra >= (int64_t(1) << 31)) return hipErrorInvalidValue;
     ph.nitems_q = (int)nqh;
+    ph.ntab = extra;
     const bool one = s.n <= 16;
     if (dtype == kBF16)
       fq = ragged ? (one ? (const void*)&bwd_dq_head_kernel<__bf16, true, 1> : (const void*)&bwd_dq_head_kernel<__bf16, true, 4>)
@@ -861,9 +897,9 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
     else
       fq = ragged ? (one ? (const void*)&bwd_dq_head_kernel<float, true, 1> : (const void*)&bwd_dq_head_kernel<float, true, 4>)
                   : (one ? (const void*)&bwd_dq_head_kernel<float, false, 1> : (const void*)&bwd_dq_head_kernel<float, false, 4>);
-    ldsq = esz * (size_t)H8 * D * (KC + padv);
+    ldsq = std::max(esz * (size_t)H8 * D * (KC + padv), fold ? inverse_table_lds(s.R) : 0);
     void* hargs[] = {&ph};
-    e = hipLaunchKernel(fq, dim3((unsigned)ph.nitems_q), dim3(H8 * 64), hargs, ldsq, stream);
+    e = hipLaunchKernel(fq, dim3((unsigned)(ph.nitems_q + extra)), dim3(H8 * 64), hargs, ldsq, stream);
   } else {
     if (dtype == kBF16)
       fq = ragged ? (const void*)&bwd_dq_kernel<__bf16, true> : (const void*)&bwd_dq_kernel<__bf16, false>;
