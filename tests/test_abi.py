@@ -210,7 +210,7 @@ def test_backward_workspace_bytes(lib):
     B, H, W, C, heads, S, k = 2, 16, 16, 64, 2, 4, 2
     tok = B * H * W * heads
     up = lambda x: -(-x // 256) * 256
-    assert lib.bra_backward_workspace_bytes(B, H, W, C, heads, S, k) == 2 * up(4 * tok) + 2 * up(4 * B * 16) + up(4 * B * 16 * 16)
+    assert lib.bra_backward_workspace_bytes(B, H, W, C, heads, S, k) == 2 * up(4 * tok) + 3 * up(4 * B * 16) + up(4 * B * 16 * 16)
     assert lib.bra_backward_workspace_bytes(B, H, W, C, 0, S, k) == 0
     assert lib.bra_backward_workspace_bytes(B, H, W, C, 3, S, k) == 0
 

@@ -56,7 +56,8 @@ struct BwdParams {
   int* inv_cnt;   // [B*R]
   int* inv_list;  // [B*R*R]
   int* bad;       // [B*R]
-  int H, W, C, S, topk;
+  int* order;     // [B*R]: per image, the key regions by descending in-degree (ties: lower index first)
+  int B, H, W, C, S, topk;
   int sh, sw, n, R, kv, heads;
   int HG, nhg, nqb, ntq, nitems_q;    // dq kernel
   int ntab;                           // dq head kernel: leading workgroups that build the inverse table (0 or B)
@@ -91,6 +92,7 @@ __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds) {
   const int R = p.R, k = p.topk, nw = (R + 31) >> 5;
   uint32_t* mask = lds;                                  // [R][nw]
   int* rowbad = reinterpret_cast<int*>(lds + R * nw);    // [R]
+  int* deg = rowbad + R;                                 // [R]: in-degree of each key region
   const int32_t* idx = p.idx + (int64_t)b * R * k;
   for (int e = tid; e < R * nw; e += nt) mask[e] = 0u;
   for (int i = tid; i < R; i += nt) rowbad[i] = 0;
@@ -116,17 +118,29 @@ __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds) {
       if (hit) L[m + __popcll(bal & below)] = i;
       m += __popcll(bal);
     }
-    if (lane == 0) p.inv_cnt[b * R + r] = m;
+    if (lane == 0) {
+      p.inv_cnt[b * R + r] = m;
+      deg[r] = m;
+    }
   }
-  for (int r = tid; r < R; r += nt) p.bad[b * R + r] = rowbad[r];
+  __syncthreads();
+  // the dK/dV kernel's order: key region r goes to place #{heavier, or as
+  // heavy with a lower index}
+  for (int r = tid; r < R; r += nt) {
+    p.bad[b * R + r] = rowbad[r];
+    const int dr = deg[r];
+    int place = 0;
+    for (int q = 0; q < R; ++q) place += deg[q] > dr || (deg[q] == dr && q < r);
+    p.order[b * R + place] = r;
+  }
 }
 
 // LDS bytes of inverse_table
-constexpr size_t inverse_table_lds(int R) { return sizeof(uint32_t) * ((size_t)R * ((R + 31) / 32) + R); }
+constexpr size_t inverse_table_lds(int R) { return sizeof(uint32_t) * ((size_t)R * ((R + 31) / 32) + 2 * R); }
 
 // For more than 64 regions: a launch of its own, one workgroup per image.
 __global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
-  __shared__ uint32_t lds[kMaxRegions * (kMaxRegions / 32) + kMaxRegions];
+  __shared__ uint32_t lds[kMaxRegions * (kMaxRegions / 32) + 2 * kMaxRegions];
   inverse_table(p, blockIdx.x, lds);
 }
 
@@ -682,13 +696,16 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int g = lane >> 4, col = lane & 15;
 
-  int w = xcd_remap();
+  // workgroup -> (place t, image b, key block, head group), images fastest
+  // after the key blocks and head groups: the heaviest key regions of every
+  // image start first, and image b stays on XCD (b * nkb * nhgk + ...) % 8
+  int w = blockIdx.x;
   const int hg = w % p.nhgk;
   w /= p.nhgk;
   const int kb = w % p.nkb;
   w /= p.nkb;
-  const int r = w % p.R;
-  const int b = w / p.R;
+  const int b = w % p.B;
+  const int r = p.order[b * p.R + w / p.B];
   const int hl = wave >> 1, kh = wave & 1;
   const int lt = kh * 64 + lane;  // lane within the head's two waves
   const int head = hg * p.HGk + hl;
@@ -813,7 +830,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 size_t backward_workspace_bytes(const Shape& s) {
   const size_t tok = (size_t)s.B * s.H * s.W * s.heads;
   const size_t reg = (size_t)s.B * s.R;
-  return 2 * align256(4 * tok) + 2 * align256(4 * reg) + align256(4 * reg * s.R);
+  return 2 * align256(4 * tok) + 3 * align256(4 * reg) + align256(4 * reg * s.R);
 }
 
 hipError_t launch_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -833,7 +850,10 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   w += align256(4 * reg);
   p.bad = reinterpret_cast<int*>(w);
   w += align256(4 * reg);
+  p.order = reinterpret_cast<int*>(w);
+  w += align256(4 * reg);
   p.inv_list = reinterpret_cast<int*>(w);
+  p.B = s.B;
   p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S; p.topk = s.topk;
   p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R; p.kv = s.kv; p.heads = s.heads;
   p.scale = 1.0f / sqrtf((float)s.d);
