@@ -370,14 +370,8 @@ __global__ __launch_bounds__(NV == 2 ? kMaxUnits * 64 : 512) void attend_kernel(
   const int col = lane & 15;    // query column of the 16-query tile
   const op8 ones = TT::ones();
 
-  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
-  // each XCD a contiguous range of work items (same image -> same L2).
-  int wg;
-  {
-    const int nwg = gridDim.x, bid = blockIdx.x;
-    const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
-    wg = x * q8 + min(x, r8) + loc;
-  }
+  // XCD-aware order, each XCD's range walked from its end (xcd_item)
+  const int wg = xcd_item(blockIdx.x, gridDim.x, true);
   const int ldk = p.HG * D + TT::PADK;   // LDS row stride of K (elements)
   const int ldv = KC + TT::PADV;         // LDS row stride of V^T (elements)
   const int bufsz = KC * ldk + p.HG * D * ldv;
@@ -479,12 +473,7 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   const op8 ones = TT::ones();
   const int ldv = KC + TT::PADV;
 
-  int wg;
-  {
-    const int nwg = gridDim.x, bid = blockIdx.x;
-    const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
-    wg = x * q8 + min(x, r8) + loc;
-  }
+  const int wg = xcd_item(blockIdx.x, gridDim.x, true);  // XCD-aware order, each range walked from its end
   const Item it = item_at(p, wg);
   // role: attention wave for head `head`, or (LCE) convolution wave for it
   const bool att = !LCE || wave < p.HG;

@@ -73,12 +73,9 @@ __device__ inline int corner_of(const BwdParams& p, int r) {
   return ry * p.sh * p.W + rx * p.sw;
 }
 
-// workgroup id -> work item, for the grid past its first `skip` workgroups
-__device__ inline int xcd_remap(int skip = 0) {
-  const int nwg = gridDim.x - skip, bid = blockIdx.x - skip;
-  const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
-  return x * q8 + min(x, r8) + loc;  // consecutive work items to one XCD
-}
+// workgroup id -> work item (consecutive items to one XCD), for the grid past
+// its first `skip` workgroups
+__device__ inline int xcd_remap(int skip = 0) { return xcd_item(blockIdx.x - skip, gridDim.x - skip); }
 
 // ---------------------------------------------------------------------------
 // 1. Inverse routing table of image b, by one workgroup (a multiple of 64

@@ -51,6 +51,19 @@ __device__ inline int fdiv(int a, FastDiv f, int* rem) {
 }
 
 // dtype codes match bra_dtype in include/bra.h
+// Work item of workgroup bid among n. Workgroups are dealt round-robin to the
+// 8 XCDs, so XCD x = bid % 8 is given the contiguous items
+// [x * (n / 8) + min(x, n % 8), ...): consecutive items (regions of one image)
+// share an L2. The pool, route and attention kernels split images over the
+// XCDs this same way. reverse: the XCD walks its range from the end, so the
+// attention kernel starts on the images the pool kernel read last, which are
+// the likeliest to be still cached.
+__device__ inline int xcd_item(int bid, int n, bool reverse = false) {
+  const int x = bid & 7, loc = bid >> 3, q8 = n >> 3, r8 = n & 7;
+  const int cnt = q8 + (x < r8 ? 1 : 0);
+  return x * q8 + (x < r8 ? x : r8) + (reverse ? cnt - 1 - loc : loc);
+}
+
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 

@@ -5,9 +5,11 @@
 // regional representations by average pooling).
 //
 // HBM-bound: every input byte is read once, 2*B*R*C fp32 values are written.
-// One workgroup per (image, region) pools both Q and K. (One wave per region
-// with a lane-shuffle reduction measured slower at the stage-1 shape.) A region is sh rows of
-// one contiguous segment of sw*C elements, read as 16-byte vectors; every
+// One workgroup per (image, region) pools both Q and K; an image's regions
+// go to one XCD (xcd_item), as in the route and attention kernels. (One wave
+// per region with a lane-shuffle reduction measured slower at the stage-1
+// shape.) A region is sh rows of one contiguous segment of sw*C elements,
+// read as 16-byte vectors; every
 // thread issues all of its loads (up to NL per tensor) before it adds any, so
 // a workgroup has its whole region in flight at once. The block size is a
 // multiple of the number of 16-byte channel groups per token, so a thread
@@ -60,8 +62,9 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   extern __shared__ float red[];  // [2][blockDim.x * VEC]
 
   const int R = p.S * p.S;
-  const int b = blockIdx.x / R;
-  const int r = blockIdx.x - b * R;
+  const int w = xcd_item(blockIdx.x, gridDim.x);
+  const int b = w / R;
+  const int r = w - b * R;
 
   const int G = p.C / VEC;                // 16-byte channel groups per token
   const int nthr = (blockDim.x / G) * G;  // active threads, multiple of G

@@ -23,8 +23,8 @@
 // two halves are added in a fixed order through LDS. Each affinity becomes a
 // 64-bit key (order-preserving bits of the value, then 63 - j), so "beats" is
 // one unsigned compare; k = 1 is a wave-wide maximum of the keys. The row
-// blocks of one image are given workgroup ids that are equal mod 8, so they
-// run on one XCD and share its L2 copy of K^r[b].
+// blocks of one image run on one XCD (xcd_item) and share its L2 copy of
+// K^r[b]; images are split over the XCDs as in the pool and attention kernels.
 //
 // Other shapes (vector form). One workgroup per (image b, block of 4 affinity rows);
 // each of its 4 waves owns one row, and lane j owns the candidates j, j+64,
@@ -173,12 +173,9 @@ __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tile = wave & 3, half = wave >> 2;
   const int g = lane >> 4, l16 = lane & 15;
-  // workgroup x -> image (x % 8) + 8 * (x / 8 / row_blocks), row block (x / 8) % row_blocks
-  const int slot = blockIdx.x >> 3;
-  const int bq = slot / p.row_blocks;
-  const int b = (blockIdx.x & 7) + 8 * bq;
-  if (b >= p.B) return;  // whole workgroup
-  const int i0 = (slot - bq * p.row_blocks) * MR;
+  const int w = xcd_item(blockIdx.x, gridDim.x);  // (image, row block), an image's blocks on one XCD
+  const int b = w / p.row_blocks;
+  const int i0 = (w - b * p.row_blocks) * MR;
   const int ncol = (p.R + 15) & ~15;
   const int j0 = tile * 16;
   const bool active = j0 < ncol;
@@ -255,7 +252,7 @@ hipError_t launch_route(const float* Qr, const float* Kr, int32_t* idx,
   if (s.R <= 64 && s.C % 32 == 0) {
     RouteParams p{Qr, Kr, idx, s.B, s.R, s.C, s.topk, (s.R + MR - 1) / MR, 0};
     args[0] = &p;
-    const unsigned grid = (unsigned)(((s.B + 7) / 8) * 8 * p.row_blocks);
+    const unsigned grid = (unsigned)(s.B * p.row_blocks);
     const int nh = s.C / 32;
     const void* fn = nh % 8 == 0   ? reinterpret_cast<const void*>(&route_mfma_kernel<8>)
                      : nh % 4 == 0 ? reinterpret_cast<const void*>(&route_mfma_kernel<4>)
