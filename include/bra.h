@@ -41,7 +41,8 @@
  *
  * Workspace
  *   bra_forward and bra_route need bra_workspace_bytes(...) bytes of device
- *   scratch (region descriptors and, for bra_forward, the routing table).
+ *   scratch (the fp32 region means Q^r, K^r and, for bra_forward, the routing
+ *   table, which bra_forward leaves there).
  *   Pass a caller-owned buffer (256-byte aligned), or NULL/0 to let the call
  *   allocate and free it stream-ordered (hipMallocAsync / hipFreeAsync) on
  *   `stream`.

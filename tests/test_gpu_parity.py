@@ -253,8 +253,7 @@ def test_deterministic_and_stream_ordered():
                          ids=lambda w: w.name)
 def test_forward_routing_table_equals_bra_route(w):
     """bra_forward leaves its routing table in the workspace: it must equal the
-    one bra_route computes, bit for bit (whether the forward pass routes in the
-    attention kernel or in the route kernel)."""
+    one bra_route computes, bit for bit."""
     q, k, v = _gpu(*wl.make_inputs(w))
     nbytes = bra.workspace_bytes(w.B, w.H, w.W, w.C, w.S, w.topk)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
