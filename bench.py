@@ -379,6 +379,7 @@ def main(argv=None):
     attn_flop = 4.0 * tokens * w.kv * w.C
     aff_flop = 2.0 * w.B * w.R * w.R * w.C
     attn_bytes = 4.0 * tokens * w.C * esz  # read Q, K, V once, write O
+    pr_bytes = 2.0 * tokens * w.C * esz + 4.0 * w.B * w.R * w.C * 4 + 4.0 * w.B * w.R * w.topk
     peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
     ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
     if attn_flop / attn_bytes < ridge:
@@ -418,6 +419,12 @@ def main(argv=None):
         "tflops": round((attn_flop + aff_flop) / (ms_per_step * 1e-3) / 1e12, 3),
         "phases_us": {"pool_route": round(route_us, 2), "attend": round(attend_us, 2),
                       "step_wall": round(wall_ms * 1e3, 2), "step_events": round(ev_ms * 1e3, 2)},
+        # the pool + route phase against the HBM peak: its algorithmic bytes
+        # (read Q and K once, the region means written and read back, the
+        # table written) over its measured time, both launches and the gap
+        # between them included
+        "phase_hbm": {"pool_route": {"algorithmic_bytes": pr_bytes, "GB/s": round(pr_bytes / (route_us * 1e-6) / 1e9, 1),
+                                     "frac_of_peak": round(pr_bytes / (route_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}},
         "roofline": roof,
     }
     if from_input is not None:
