@@ -695,7 +695,8 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
 
   // workgroup -> (place t, image b, key block, head group), images fastest
   // after the key blocks and head groups: the heaviest key regions of every
-  // image start first, and image b stays on XCD (b * nkb * nhgk + ...) % 8
+  // image start first. (When B * nkb * nhgk is a multiple of 8, an image's
+  // workgroups all land on one XCD, since workgroups are dealt round-robin.)
   int w = blockIdx.x;
   const int hg = w % p.nhgk;
   w /= p.nhgk;

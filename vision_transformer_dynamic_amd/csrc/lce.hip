@@ -35,12 +35,7 @@ __global__ __launch_bounds__(64) void lce_kernel(LceParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int lane = threadIdx.x;
 
-  int wg;
-  {
-    const int nwg = gridDim.x, bid = blockIdx.x;
-    const int x = bid & 7, loc = bid >> 3, q8 = nwg >> 3, r8 = nwg & 7;
-    wg = x * q8 + min(x, r8) + loc;  // consecutive work to one XCD
-  }
+  const int wg = xcd_item(blockIdx.x, gridDim.x);  // consecutive work to one XCD
   const int cg = wg % p.ncg;
   int rest = wg / p.ncg;
   const int tx = rest % p.tiles_x;
