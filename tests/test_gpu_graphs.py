@@ -22,6 +22,7 @@ SHAPES = [
     wl.custom(2, 28, 28, 64, 2, 7, 2, "bf16", seed=60),   # single-chunk attention, n = 16
     wl.custom(2, 16, 16, 64, 2, 2, 2, "bf16", seed=61),   # chunked attention: n = 64, 128 keys per query
     wl.custom(1, 16, 16, 32, 1, 4, 2, "f32", seed=62),    # fp32
+    wl.custom(32, 14, 14, 128, 4, 7, 8, "bf16", seed=63), # image-resident attention
 ]
 
 REPLAYS = 3

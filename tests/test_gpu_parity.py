@@ -141,6 +141,46 @@ def test_edge_shapes(w):
     _check_case(w, q, k, v, images=list(range(w.B)))
 
 
+# Image-resident attention (bf16, at most 64 keys per query, n a multiple of
+# 4, at least 128 (image, head) pairs): one workgroup stages a head's whole
+# image in LDS. Region sizes 16, 4, 12 (two runs of 4 keys per block of 8), 8
+# and 64 (four query tiles per region), full and ragged key counts, H != W.
+IMAGE_RESIDENT = [
+    wl.custom(32, 28, 28, 128, 4, 7, 4, "bf16", seed=70),   # n=16, kv=64
+    wl.custom(16, 14, 14, 256, 8, 7, 16, "bf16", seed=71),  # n=4, kv=64
+    wl.custom(64, 14, 14, 64, 2, 7, 8, "bf16", seed=72),    # n=4, kv=32
+    wl.custom(64, 21, 28, 64, 2, 7, 5, "bf16", seed=73),    # n=12 (3 x 4), kv=60
+    wl.custom(128, 8, 16, 32, 1, 4, 3, "bf16", seed=74),    # n=8 (2 x 4), kv=24
+    wl.custom(128, 24, 24, 32, 1, 3, 1, "bf16", seed=75),   # n=64: four query tiles per region
+]
+
+
+@pytest.mark.parametrize("w", IMAGE_RESIDENT, ids=[w.name for w in IMAGE_RESIDENT])
+def test_image_resident_shapes(w):
+    q, k, v = wl.make_inputs(w)
+    mism, _, _ = _check_case(w, q, k, v)
+    assert mism == 0
+
+
+def test_image_resident_out_of_range_entries_give_nan_rows_only():
+    w = wl.custom(64, 14, 14, 64, 2, 7, 2, "bf16", seed=76)
+    q, k, v = _gpu(*wl.make_inputs(w))
+    idx = bra.route(q, k, w.S, w.topk)
+    good = bra.attend(q, k, v, idx, w.heads, w.S).float().cpu()
+    bad_idx = idx.clone()
+    bad_idx[5, 3, 1] = 49
+    bad_idx[63, 10, 0] = -1
+    out = bra.attend(q, k, v, bad_idx, w.heads, w.S).float().cpu()
+    o = out.reshape(64, 7, 2, 7, 2, 64).permute(0, 1, 3, 2, 4, 5).reshape(64, 49, 4, 64)
+    gd = good.reshape(64, 7, 2, 7, 2, 64).permute(0, 1, 3, 2, 4, 5).reshape(64, 49, 4, 64)
+    assert torch.isnan(o[5, 3]).all() and torch.isnan(o[63, 10]).all()
+    o[5, 3] = 0
+    o[63, 10] = 0
+    gd[5, 3] = 0
+    gd[63, 10] = 0
+    assert torch.equal(o, gd)
+
+
 # The (S, k) schedules of the explainer's Part 6.3 table over the four stage
 # maps of a 224 x 224 input (56, 28, 14, 7; C = 64 * 2^stage, head dim 32):
 # S = 7 with k = [1, 4, 16, 49], S = 7 with k = [1, 2, 8, 32], and

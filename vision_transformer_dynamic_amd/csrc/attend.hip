@@ -701,6 +701,258 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Image-resident kernel (bf16, kv <= 64 routed keys, n a multiple of 4, no
+// fused local context term). With small regions the routed sets of an
+// image's query regions overlap heavily: at 28x28 with 16-token regions and 4
+// routed regions each head's key is gathered about 4 times per image, at
+// 14x14 with 4-token regions and 16 routed regions about 16 times, and the
+// per-region kernels above fetch it through the caches every time. Here one
+// workgroup = one (image, head): it stages that head's K (a row per token)
+// and V^T (a column per token) for the whole image in LDS once, in
+// region-major order (position = region * n + token inside the region, so a
+// routed region's keys are n consecutive positions), together with the
+// image's routing table; then each wave takes (query region, 16-query tile)
+// units and reads the routed keys' operands from LDS. The products and the
+// softmax are those of the single-chunk kernel. Every query operand is
+// loaded before the staging, so no unit waits on HBM.
+constexpr int kImgWaves = 16;  // waves per workgroup
+constexpr int kImgUnits = 4;   // (region, 16-query tile) units per wave at most
+constexpr int kImgLdk = D + 8; // LDS row stride of K (elements)
+
+struct ImgParams {
+  const __bf16* Q;
+  const __bf16* K;
+  const __bf16* V;
+  const int32_t* idx;
+  __bf16* O;
+  int H, W, C, S, topk, sh, sw, n, R, kv, heads;
+  int HW;      // tokens per image
+  int nunits;  // R * 16-query tiles per region
+  int ldv;     // LDS row stride of V^T (elements, a multiple of 8)
+  float c;     // softmax scale * log2(e)
+  FastDiv div_n, div_sw, div_S, div_nt;
+};
+
+// Region-major position -> token offset inside the image.
+__device__ inline int img_token(const ImgParams& p, int pos) {
+  int t, rx, tx;
+  const int r = fdiv(pos, p.div_n, &t);
+  const int ry = fdiv(r, p.div_S, &rx);
+  const int ty = fdiv(t, p.div_sw, &tx);
+  return (ry * p.sh + ty) * p.W + rx * p.sw + tx;
+}
+
+// Value v of lane src (src in [0, 64)).
+__device__ inline int lane_value(int v, int src) { return __builtin_amdgcn_ds_bpermute(src << 2, v); }
+
+// One (query region, 16-query tile) unit u of the image-resident kernel: the
+// routed keys' operands from the staged K and V^T, both products, the
+// softmax and the output stores (qoff < 0: the lane's query is past n).
+template <bool RAGGED, bool N8>
+__device__ __forceinline__ void image_unit(const ImgParams& p, int u, int lane, int g, int col,
+                                           const __bf16* Ks, const __bf16* Vt, const int* rpos,
+                                           Tr<__bf16>::op8 qop, int qoff, __bf16* Og) {
+  typedef Tr<__bf16> TT;
+  typedef TT::op8 op8;
+  const op8 ones = TT::ones();
+  const int vrow = 8 * (col >> 2) + (col & 3);  // channel row of V^T tile 0; tile 1 is +4
+  int t;
+  const int r = fdiv(u, p.div_nt, &t);
+  // position of routed key kappa = lane
+  int kpos = 0;
+  bool kbad = false;
+  if (lane < p.kv) {
+    int tk;
+    const int jr = fdiv(lane, p.div_n, &tk);
+    const int base = rpos[r * p.topk + jr];
+    kbad = base < 0;
+    kpos = kbad ? 0 : base + tk;
+  }
+  if (__builtin_amdgcn_ballot_w64(kbad) != 0) {  // uniform
+    // a routing entry outside [0, S*S): never dereferenced; output NaN
+    float nanv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nanv[e] = __builtin_nanf("");
+    if (qoff >= 0) TT::store8(Og + qoff, nanv);
+    return;
+  }
+  // K operands: row col of tile (st, tb) is key st*32 + 8*(col/4) + col%4 + 4*tb
+  op8 kop[2][2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
+      const int pos = lane_value(kpos, key);
+      kop[st][tb] = (!RAGGED || key < p.kv) ? TT::load8(Ks + pos * kImgLdk + 8 * g) : TT::zero();
+    }
+  // V operands: row col of tile (st, ct) is channel vrow + 4*ct; slots are
+  // keys st*32 + 8g .. +7
+  op8 vop[2][2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int key0 = st * 32 + 8 * g;
+    const int pos0 = lane_value(kpos, key0);
+    const int pos1 = N8 ? 0 : lane_value(kpos, key0 + 4);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int row = vrow + 4 * ct;
+      const __bf16* vr = Vt + row * p.ldv;
+      if (N8) {
+        vop[st][ct] = (!RAGGED || key0 < p.kv) ? TT::load8(vr + vt_col(row, pos0)) : TT::zero();
+      } else {
+        bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + vt_col(row, pos0));
+        bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + vt_col(row, pos1));
+        if (RAGGED && key0 >= p.kv) lo = bf16x4{};
+        if (RAGGED && key0 + 4 >= p.kv) hi = bf16x4{};
+        vop[st][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+  }
+  float s[2][8];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const floatx4 sa = TT::mma(kop[st][0], qop, floatx4{0.f, 0.f, 0.f, 0.f});
+    const floatx4 sb = TT::mma(kop[st][1], qop, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[st][e] = sa[e];
+      s[st][4 + e] = sb[e];
+    }
+  }
+  if (RAGGED) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (st * 32 + 8 * g + e >= p.kv) s[st][e] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
+  mx = wave_max_groups(mx);
+  const float mc = mx * p.c;
+  floatx4 acc[3] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    float pe[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
+    const op8 pop = TT::from_f32(pe);
+    acc[0] = TT::mma(vop[st][0], pop, acc[0]);
+    acc[1] = TT::mma(vop[st][1], pop, acc[1]);
+    acc[2] = TT::mma(ones, pop, acc[2]);
+  }
+  if (qoff >= 0) {
+    const float inv = 1.0f / acc[2][0];
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[e] = acc[0][e] * inv;
+      o[4 + e] = acc[1][e] * inv;
+    }
+    TT::store8_nt(Og + qoff, o);
+  }
+}
+
+// N8: n is a multiple of 8, so each block of 8 keys 8g..8g+7 is 8 consecutive
+// positions (one 16-byte V^T read); otherwise (n a multiple of 4) it is two
+// runs of 4. RAGGED: kv < 64 (whole runs of 4 or 8 keys are past kv).
+template <bool RAGGED, bool N8>
+__global__ __launch_bounds__(kImgWaves * 64) void attend_image_kernel(ImgParams p) {
+  typedef Tr<__bf16> TT;
+  typedef TT::op8 op8;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __bf16* Ks = reinterpret_cast<__bf16*>(smem_raw);            // [HW][kImgLdk]
+  __bf16* Vt = Ks + p.HW * kImgLdk;                              // [D][ldv]
+  int* rpos = reinterpret_cast<int*>(Vt + D * p.ldv);           // [R][topk]: first position of the routed region, -1 if out of range
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int col = lane & 15;
+
+  // items (image, head), heads of one image adjacent: they share the image's
+  // cache lines on one XCD (xcd_item)
+  const int w = xcd_item(blockIdx.x, gridDim.x, true);
+  const int head = w % p.heads, b = w / p.heads;
+  const int64_t img = (int64_t)b * p.HW * p.C;
+  const int ch0 = head * D;
+
+  // ---- query operands of the wave's units
+  op8 qop[kImgUnits];
+  int qoff[kImgUnits];
+#pragma unroll
+  for (int uu = 0; uu < kImgUnits; ++uu) {
+    const int u = wave + kImgWaves * uu;
+    qoff[uu] = -1;
+    qop[uu] = TT::zero();
+    if (u < p.nunits) {
+      int t, rx, qx;
+      const int r = fdiv(u, p.div_nt, &t);
+      const int qi = t * 16 + col;
+      if (qi < p.n) {
+        const int ry = fdiv(r, p.div_S, &rx);
+        const int qy = fdiv(qi, p.div_sw, &qx);
+        qoff[uu] = ((ry * p.sh + qy) * p.W + rx * p.sw + qx) * p.C + ch0 + 8 * g;
+        qop[uu] = TT::load8(p.Q + img + qoff[uu]);
+      }
+    }
+  }
+
+  // ---- the image's routing table
+  const int nroute = p.R * p.topk;
+  for (int e = tid; e < nroute; e += kImgWaves * 64) {
+    const int r = p.idx[(int64_t)b * nroute + e];
+    rpos[e] = (r >= 0 && r < p.R) ? r * p.n : -1;
+  }
+
+  // ---- K rows and V^T columns of the head: item f = (position pair pp,
+  // 16-byte channel vector cv); four lanes read a token's 64 bytes
+  const int nitems = p.HW * 2;  // HW / 2 pairs x 4 vectors
+  const __bf16* Kg = p.K + img + ch0;
+  const __bf16* Vg = p.V + img + ch0;
+  for (int base = 0; base < nitems; base += 2 * kImgWaves * 64) {
+    uint4 kr[2][2], vr[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int f = base + tid + kImgWaves * 64 * j;
+      kr[j][0] = kr[j][1] = vr[j][0] = vr[j][1] = make_uint4(0u, 0u, 0u, 0u);
+      if (f < nitems) {
+        const int cv = f & 3, pp = f >> 2;
+        const int t0 = img_token(p, 2 * pp), t1 = img_token(p, 2 * pp + 1);
+        kr[j][0] = *reinterpret_cast<const uint4*>(Kg + t0 * p.C + 8 * cv);
+        kr[j][1] = *reinterpret_cast<const uint4*>(Kg + t1 * p.C + 8 * cv);
+        vr[j][0] = *reinterpret_cast<const uint4*>(Vg + t0 * p.C + 8 * cv);
+        vr[j][1] = *reinterpret_cast<const uint4*>(Vg + t1 * p.C + 8 * cv);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int f = base + tid + kImgWaves * 64 * j;
+      if (f < nitems) {
+        const int cv = f & 3, pp = f >> 2;
+        *reinterpret_cast<uint4*>(Ks + (2 * pp) * kImgLdk + 8 * cv) = kr[j][0];
+        *reinterpret_cast<uint4*>(Ks + (2 * pp + 1) * kImgLdk + 8 * cv) = kr[j][1];
+        store_vt_pair(Vt, p.ldv, 8 * cv, vt_col(8 * cv, 2 * pp), vr[j][0], vr[j][1]);
+      }
+    }
+  }
+  __syncthreads();
+
+  __bf16* Og = p.O + img;
+#pragma unroll
+  for (int uu = 0; uu < kImgUnits; ++uu) {
+    const int u = wave + kImgWaves * uu;
+    if (u < p.nunits)  // uniform
+      image_unit<RAGGED, N8>(p, u, lane, g, col, Ks, Vt, rpos, qop[uu], qoff[uu], Og);
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -772,12 +1024,99 @@ const void* pick_attend(int dtype, const AttnLaunch& L) {
   return ragged ? pick_attend_r<float, true>(L.nv, L.multi) : pick_attend_r<float, false>(L.nv, L.multi);
 }
 
+// Image-resident kernel: the shape conditions, the V^T row stride and the LDS
+// size. False when the per-region kernels take the shape.
+constexpr size_t kImgMaxLds = 160 * 1024;
+
+// V^T row stride: the image's positions rounded up to 32 plus the pad (a
+// multiple of 8 elements) whose operand reads spread best over the LDS banks
+// (a 16-byte read is served 16 lanes per pass over 64 four-byte banks; the 16
+// lanes of a pass read the same key block from 16 channel rows).
+int image_ldv(int HW) {
+  const int base = (HW + 31) / 32 * 32;
+  int best = base, bestc = 1 << 30;
+  for (int pad = 0; pad < 64; pad += 8) {
+    const int L = (base + pad) / 2;  // dwords per row
+    int cost = 0;
+    for (int P = 0; P < 16; P += 4)  // key block offset (dwords); higher bits shift every lane alike
+      for (int ct = 0; ct < 2; ++ct) {
+        int cnt[64] = {0}, m = 0;
+        for (int c = 0; c < 16; ++c) {
+          const int row = 8 * (c >> 2) + (c & 3) + 4 * ct;
+          const int w0 = row * L + (P ^ (((row >> 3) & 7) << 2));
+          for (int x = 0; x < 4; ++x) m = std::max(m, ++cnt[(w0 + x) & 63]);
+        }
+        cost += m;
+      }
+    if (cost < bestc) {
+      bestc = cost;
+      best = base + pad;
+    }
+  }
+  return best;
+}
+
+bool plan_image(const Shape& s, ImgParams* p, size_t* lds) {
+  if (s.kv > KC || s.n % 4 != 0) return false;
+  const int ntiles = (s.n + 15) / 16;
+  if (s.R * ntiles > kImgWaves * kImgUnits) return false;
+  // one workgroup per (image, head): fewer than half the compute units busy
+  // is slower than the per-region split
+  if ((int64_t)s.B * s.heads < 128) return false;
+  const int HW = s.H * s.W;
+  const int ldv = image_ldv(HW);
+  const size_t bytes = 2 * (size_t)HW * kImgLdk + 2 * (size_t)D * ldv + 4 * (size_t)s.R * s.topk;
+  if (bytes > kImgMaxLds) return false;
+  *p = ImgParams{};
+  p->H = s.H; p->W = s.W; p->C = s.C; p->S = s.S; p->topk = s.topk;
+  p->sh = s.sh; p->sw = s.sw; p->n = s.n; p->R = s.R; p->kv = s.kv; p->heads = s.heads;
+  p->HW = HW;
+  p->nunits = s.R * ntiles;
+  p->ldv = ldv;
+  p->c = 1.4426950408889634f / sqrtf((float)s.d);
+  p->div_n = make_fastdiv(s.n);
+  p->div_sw = make_fastdiv(s.sw);
+  p->div_S = make_fastdiv(s.S);
+  p->div_nt = make_fastdiv(ntiles);
+  *lds = bytes;
+  return true;
+}
+
+hipError_t launch_image(const ImgParams& p0, size_t lds, int B, hipStream_t stream) {
+  ImgParams p = p0;
+  const bool ragged = p.kv % KC != 0, n8 = p.n % 8 == 0;
+  const int which = (ragged ? 2 : 0) + (n8 ? 1 : 0);
+  const void* fns[4] = {(const void*)&attend_image_kernel<false, false>, (const void*)&attend_image_kernel<false, true>,
+                        (const void*)&attend_image_kernel<true, false>, (const void*)&attend_image_kernel<true, true>};
+  // more than the default 64 KiB of dynamic LDS: raise the kernel's limit once
+  static bool raised[4] = {false, false, false, false};
+  if (!raised[which]) {
+    const hipError_t e = hipFuncSetAttribute(fns[which], hipFuncAttributeMaxDynamicSharedMemorySize, (int)kImgMaxLds);
+    if (e != hipSuccess) return e;
+    raised[which] = true;
+  }
+  void* args[] = {&p};
+  return hipLaunchKernel(fns[which], dim3((unsigned)(B * p.heads)), dim3(kImgWaves * 64), args, lds, stream);
+}
+
 }  // namespace
 
 hipError_t launch_attend(const void* Q, const void* K, const void* V,
                          const int32_t* idx, const void* lce_w, const void* lce_b, void* O,
                          const Shape& s, int dtype, hipStream_t stream) {
   const bool lce = lce_w != nullptr;
+  if (!lce && dtype == kBF16) {
+    ImgParams ip;
+    size_t lds;
+    if (plan_image(s, &ip, &lds)) {
+      ip.Q = static_cast<const __bf16*>(Q);
+      ip.K = static_cast<const __bf16*>(K);
+      ip.V = static_cast<const __bf16*>(V);
+      ip.idx = idx;
+      ip.O = static_cast<__bf16*>(O);
+      return launch_image(ip, lds, s.B, stream);
+    }
+  }
   if (s.kv <= KC) {
     // single chunk: one wave per head, up to 8 heads per workgroup
     AttnParams p = plan_attend(s, dtype).p;
