@@ -143,14 +143,18 @@ def test_edge_shapes(w):
 
 # Image-resident attention (bf16, at most 64 keys per query, n a multiple of
 # 4, at least 128 (image, head) pairs): one workgroup stages a head's whole
-# image in LDS. Region sizes 16, 4, 12 (two runs of 4 keys per block of 8), 8
-# and 64 (four query tiles per region), full and ragged key counts, H != W.
+# image in LDS. Region sizes 16, 4 (four regions per 16-query unit), 12 (two
+# runs of 4 keys per block of 8), 8 (two regions per unit, also with an odd
+# region count) and 64 (four query tiles per region), full and ragged key
+# counts, H != W.
 IMAGE_RESIDENT = [
     wl.custom(32, 28, 28, 128, 4, 7, 4, "bf16", seed=70),   # n=16, kv=64
     wl.custom(16, 14, 14, 256, 8, 7, 16, "bf16", seed=71),  # n=4, kv=64
     wl.custom(64, 14, 14, 64, 2, 7, 8, "bf16", seed=72),    # n=4, kv=32
     wl.custom(64, 21, 28, 64, 2, 7, 5, "bf16", seed=73),    # n=12 (3 x 4), kv=60
     wl.custom(128, 8, 16, 32, 1, 4, 3, "bf16", seed=74),    # n=8 (2 x 4), kv=24
+    wl.custom(128, 8, 16, 32, 1, 4, 8, "bf16", seed=77),    # n=8, kv=64
+    wl.custom(128, 6, 12, 32, 1, 3, 5, "bf16", seed=78),    # n=8, 9 regions: a unit with one region
     wl.custom(128, 24, 24, 32, 1, 3, 1, "bf16", seed=75),   # n=64: four query tiles per region
 ]
 

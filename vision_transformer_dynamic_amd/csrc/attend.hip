@@ -712,12 +712,22 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
 // and V^T (a column per token) for the whole image in LDS once, in
 // region-major order (position = region * n + token inside the region, so a
 // routed region's keys are n consecutive positions), together with the
-// image's routing table; then each wave takes (query region, 16-query tile)
-// units and reads the routed keys' operands from LDS. The products and the
-// softmax are those of the single-chunk kernel. Every query operand is
-// loaded before the staging, so no unit waits on HBM.
-constexpr int kImgWaves = 16;  // waves per workgroup
-constexpr int kImgUnits = 4;   // (region, 16-query tile) units per wave at most
+// image's routing table; then each wave takes units of 16 query columns and
+// reads the routed keys' operands from LDS. Every query operand is loaded
+// before the staging, so no unit waits on HBM.
+//
+// A unit is one 16-query tile of one region (n >= 12), or QR = 16 / n whole
+// regions side by side (n = 4 or 8: 4 or 2 regions), so that no query column
+// of the products is idle and the softmax work per query is not repeated for
+// empty columns. With several regions in a tile, region j's products use the
+// query operand and the probabilities with every column outside region j set
+// to zero:
+//   S^T  = sum_j K_j Q_j^T       (each column only meets its own region's keys)
+//   O^T  = sum_j V_j^T P_j^T     (each column only gathers its own region's values)
+// and the denominator tile uses the unmasked P^T (each column holds only its
+// own region's probabilities). The matrix-core work equals that of QR
+// separate units; the softmax and the stores are done once.
+constexpr int kImgUnits = 4;   // units per wave at most
 constexpr int kImgLdk = D + 8; // LDS row stride of K (elements)
 
 struct ImgParams {
@@ -728,10 +738,10 @@ struct ImgParams {
   __bf16* O;
   int H, W, C, S, topk, sh, sw, n, R, kv, heads;
   int HW;      // tokens per image
-  int nunits;  // R * 16-query tiles per region
+  int nunits;  // units per image
   int ldv;     // LDS row stride of V^T (elements, a multiple of 8)
   float c;     // softmax scale * log2(e)
-  FastDiv div_n, div_sw, div_S, div_nt;
+  FastDiv div_n, div_sw, div_S, div_nt;  // div_nt: 16-query tiles per region (one region per unit)
 };
 
 // Region-major position -> token offset inside the image.
@@ -746,81 +756,88 @@ __device__ inline int img_token(const ImgParams& p, int pos) {
 // Value v of lane src (src in [0, 64)).
 __device__ inline int lane_value(int v, int src) { return __builtin_amdgcn_ds_bpermute(src << 2, v); }
 
-// One (query region, 16-query tile) unit u of the image-resident kernel: the
-// routed keys' operands from the staged K and V^T, both products, the
-// softmax and the output stores (qoff < 0: the lane's query is past n).
-template <bool RAGGED, bool N8>
+// Region and query (inside the region) of query column col of unit u; false
+// when the column holds no query.
+template <int QR>
+__device__ inline bool image_query(const ImgParams& p, int u, int col, int* r, int* qi) {
+  if (QR == 1) {
+    int t;
+    *r = fdiv(u, p.div_nt, &t);
+    *qi = t * 16 + col;
+    return *qi < p.n;
+  }
+  constexpr int NQ = 16 / QR;  // = n
+  *r = u * QR + col / NQ;
+  *qi = col % NQ;
+  return *r < p.R;
+}
+
+// One unit u: the routed keys' operands from the staged K and V^T, both
+// products, the softmax and the output stores (qoff < 0: the lane's column
+// holds no query).
+template <bool RAGGED, bool N8, int QR>
 __device__ __forceinline__ void image_unit(const ImgParams& p, int u, int lane, int g, int col,
                                            const __bf16* Ks, const __bf16* Vt, const int* rpos,
                                            Tr<__bf16>::op8 qop, int qoff, __bf16* Og) {
   typedef Tr<__bf16> TT;
   typedef TT::op8 op8;
   const op8 ones = TT::ones();
+  const op8 zero = TT::zero();
   const int vrow = 8 * (col >> 2) + (col & 3);  // channel row of V^T tile 0; tile 1 is +4
-  int t;
-  const int r = fdiv(u, p.div_nt, &t);
-  // position of routed key kappa = lane
-  int kpos = 0;
-  bool kbad = false;
-  if (lane < p.kv) {
-    int tk;
-    const int jr = fdiv(lane, p.div_n, &tk);
-    const int base = rpos[r * p.topk + jr];
-    kbad = base < 0;
-    kpos = kbad ? 0 : base + tk;
-  }
-  if (__builtin_amdgcn_ballot_w64(kbad) != 0) {  // uniform
-    // a routing entry outside [0, S*S): never dereferenced; output NaN
-    float nanv[8];
+  int r0, t;
+  if (QR == 1) r0 = fdiv(u, p.div_nt, &t);
+  else r0 = u * QR;
+  const int jl = QR == 1 ? 0 : col / (16 / QR);  // the lane's region in the unit
+
+  // position of routed key kappa = lane of each region j; a region with an
+  // entry outside [0, S*S) reads position 0 and its queries are set to NaN
+  int kpos[QR];
+  bool bad = false;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) nanv[e] = __builtin_nanf("");
-    if (qoff >= 0) TT::store8(Og + qoff, nanv);
-    return;
+  for (int j = 0; j < QR; ++j) {
+    const int r = r0 + j;
+    kpos[j] = 0;
+    bool kbad = false;
+    if (lane < p.kv && r < p.R) {
+      int tk;
+      const int jr = fdiv(lane, p.div_n, &tk);
+      const int base = rpos[r * p.topk + jr];
+      kbad = base < 0;
+      kpos[j] = kbad ? 0 : base + tk;
+    }
+    const bool rbad = __builtin_amdgcn_ballot_w64(kbad) != 0;
+    if (jl == j) bad = rbad;
   }
-  // K operands: row col of tile (st, tb) is key st*32 + 8*(col/4) + col%4 + 4*tb
-  op8 kop[2][2];
+
+  // ---- S^T = sum_j K_j Q_j^T. K operand row col of tile (st, tb) is key
+  // st*32 + 8*(col/4) + col%4 + 4*tb; slots are channels 8g..8g+7
+  floatx4 sacc[2][2];
 #pragma unroll
   for (int st = 0; st < 2; ++st)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
-      const int pos = lane_value(kpos, key);
-      kop[st][tb] = (!RAGGED || key < p.kv) ? TT::load8(Ks + pos * kImgLdk + 8 * g) : TT::zero();
-    }
-  // V operands: row col of tile (st, ct) is channel vrow + 4*ct; slots are
-  // keys st*32 + 8g .. +7
-  op8 vop[2][2];
+    for (int tb = 0; tb < 2; ++tb) sacc[st][tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const int key0 = st * 32 + 8 * g;
-    const int pos0 = lane_value(kpos, key0);
-    const int pos1 = N8 ? 0 : lane_value(kpos, key0 + 4);
+  for (int j = 0; j < QR; ++j) {
+    const op8 qj = (QR == 1 || jl == j) ? qop : zero;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const int row = vrow + 4 * ct;
-      const __bf16* vr = Vt + row * p.ldv;
-      if (N8) {
-        vop[st][ct] = (!RAGGED || key0 < p.kv) ? TT::load8(vr + vt_col(row, pos0)) : TT::zero();
-      } else {
-        bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + vt_col(row, pos0));
-        bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + vt_col(row, pos1));
-        if (RAGGED && key0 >= p.kv) lo = bf16x4{};
-        if (RAGGED && key0 + 4 >= p.kv) hi = bf16x4{};
-        vop[st][ct] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
+        const int pos = lane_value(kpos[j], key);
+        const op8 k = (!RAGGED || key < p.kv) ? TT::load8(Ks + pos * kImgLdk + 8 * g) : zero;
+        sacc[st][tb] = TT::mma(k, qj, sacc[st][tb]);
       }
-    }
   }
+  // lane group g holds keys st*32 + 8g + e, e = 0..7, of its column
   float s[2][8];
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const floatx4 sa = TT::mma(kop[st][0], qop, floatx4{0.f, 0.f, 0.f, 0.f});
-    const floatx4 sb = TT::mma(kop[st][1], qop, floatx4{0.f, 0.f, 0.f, 0.f});
+  for (int st = 0; st < 2; ++st)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      s[st][e] = sa[e];
-      s[st][4 + e] = sb[e];
+      s[st][e] = sacc[st][0][e];
+      s[st][4 + e] = sacc[st][1][e];
     }
-  }
   if (RAGGED) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -835,24 +852,54 @@ __device__ __forceinline__ void image_unit(const ImgParams& p, int u, int lane, 
     for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
   mx = wave_max_groups(mx);
   const float mc = mx * p.c;
-  floatx4 acc[3] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  op8 pop[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     float pe[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
-    const op8 pop = TT::from_f32(pe);
-    acc[0] = TT::mma(vop[st][0], pop, acc[0]);
-    acc[1] = TT::mma(vop[st][1], pop, acc[1]);
-    acc[2] = TT::mma(ones, pop, acc[2]);
+    pop[st] = TT::from_f32(pe);
   }
+
+  // ---- O^T = sum_j V_j^T P_j^T. V operand row col of tile (st, ct) is
+  // channel vrow + 4*ct; slots are keys st*32 + 8g .. +7
+  floatx4 acc[3] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int j = 0; j < QR; ++j) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const op8 pj = (QR == 1 || jl == j) ? pop[st] : zero;
+      const int key0 = st * 32 + 8 * g;
+      const int pos0 = lane_value(kpos[j], key0);
+      const int pos1 = N8 ? 0 : lane_value(kpos[j], key0 + 4);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int row = vrow + 4 * ct;
+        const __bf16* vr = Vt + row * p.ldv;
+        op8 v;
+        if (N8) {
+          v = (!RAGGED || key0 < p.kv) ? TT::load8(vr + vt_col(row, pos0)) : zero;
+        } else {
+          bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr + vt_col(row, pos0));
+          bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + vt_col(row, pos1));
+          if (RAGGED && key0 >= p.kv) lo = bf16x4{};
+          if (RAGGED && key0 + 4 >= p.kv) hi = bf16x4{};
+          v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        acc[ct] = TT::mma(v, pj, acc[ct]);
+      }
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st) acc[2] = TT::mma(ones, pop[st], acc[2]);
+
   if (qoff >= 0) {
     const float inv = 1.0f / acc[2][0];
     float o[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      o[e] = acc[0][e] * inv;
-      o[4 + e] = acc[1][e] * inv;
+      o[e] = bad ? __builtin_nanf("") : acc[0][e] * inv;
+      o[4 + e] = bad ? __builtin_nanf("") : acc[1][e] * inv;
     }
     TT::store8_nt(Og + qoff, o);
   }
@@ -860,9 +907,11 @@ __device__ __forceinline__ void image_unit(const ImgParams& p, int u, int lane, 
 
 // N8: n is a multiple of 8, so each block of 8 keys 8g..8g+7 is 8 consecutive
 // positions (one 16-byte V^T read); otherwise (n a multiple of 4) it is two
-// runs of 4. RAGGED: kv < 64 (whole runs of 4 or 8 keys are past kv).
-template <bool RAGGED, bool N8>
-__global__ __launch_bounds__(kImgWaves * 64) void attend_image_kernel(ImgParams p) {
+// runs of 4. RAGGED: kv < 64 (whole runs of 4 or 8 keys are past kv). QR:
+// regions per unit. The workgroup has between 1 and 16 waves; wave w takes
+// units w, w + waves, ... (at most kImgUnits).
+template <bool RAGGED, bool N8, int QR>
+__global__ __launch_bounds__(1024) void attend_image_kernel(ImgParams p) {
   typedef Tr<__bf16> TT;
   typedef TT::op8 op8;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -871,6 +920,8 @@ __global__ __launch_bounds__(kImgWaves * 64) void attend_image_kernel(ImgParams 
   int* rpos = reinterpret_cast<int*>(Vt + D * p.ldv);           // [R][topk]: first position of the routed region, -1 if out of range
 
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int nwaves = nthr >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
@@ -888,25 +939,22 @@ __global__ __launch_bounds__(kImgWaves * 64) void attend_image_kernel(ImgParams 
   int qoff[kImgUnits];
 #pragma unroll
   for (int uu = 0; uu < kImgUnits; ++uu) {
-    const int u = wave + kImgWaves * uu;
+    const int u = wave + nwaves * uu;
     qoff[uu] = -1;
     qop[uu] = TT::zero();
-    if (u < p.nunits) {
-      int t, rx, qx;
-      const int r = fdiv(u, p.div_nt, &t);
-      const int qi = t * 16 + col;
-      if (qi < p.n) {
-        const int ry = fdiv(r, p.div_S, &rx);
-        const int qy = fdiv(qi, p.div_sw, &qx);
-        qoff[uu] = ((ry * p.sh + qy) * p.W + rx * p.sw + qx) * p.C + ch0 + 8 * g;
-        qop[uu] = TT::load8(p.Q + img + qoff[uu]);
-      }
+    int r, qi;
+    if (u < p.nunits && image_query<QR>(p, u, col, &r, &qi)) {
+      int rx, qx;
+      const int ry = fdiv(r, p.div_S, &rx);
+      const int qy = fdiv(qi, p.div_sw, &qx);
+      qoff[uu] = ((ry * p.sh + qy) * p.W + rx * p.sw + qx) * p.C + ch0 + 8 * g;
+      qop[uu] = TT::load8(p.Q + img + qoff[uu]);
     }
   }
 
   // ---- the image's routing table
   const int nroute = p.R * p.topk;
-  for (int e = tid; e < nroute; e += kImgWaves * 64) {
+  for (int e = tid; e < nroute; e += nthr) {
     const int r = p.idx[(int64_t)b * nroute + e];
     rpos[e] = (r >= 0 && r < p.R) ? r * p.n : -1;
   }
@@ -916,11 +964,11 @@ __global__ __launch_bounds__(kImgWaves * 64) void attend_image_kernel(ImgParams 
   const int nitems = p.HW * 2;  // HW / 2 pairs x 4 vectors
   const __bf16* Kg = p.K + img + ch0;
   const __bf16* Vg = p.V + img + ch0;
-  for (int base = 0; base < nitems; base += 2 * kImgWaves * 64) {
+  for (int base = 0; base < nitems; base += 2 * nthr) {
     uint4 kr[2][2], vr[2][2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int f = base + tid + kImgWaves * 64 * j;
+      const int f = base + tid + nthr * j;
       kr[j][0] = kr[j][1] = vr[j][0] = vr[j][1] = make_uint4(0u, 0u, 0u, 0u);
       if (f < nitems) {
         const int cv = f & 3, pp = f >> 2;
@@ -933,7 +981,7 @@ __global__ __launch_bounds__(kImgWaves * 64) void attend_image_kernel(ImgParams 
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int f = base + tid + kImgWaves * 64 * j;
+      const int f = base + tid + nthr * j;
       if (f < nitems) {
         const int cv = f & 3, pp = f >> 2;
         *reinterpret_cast<uint4*>(Ks + (2 * pp) * kImgLdk + 8 * cv) = kr[j][0];
@@ -947,9 +995,9 @@ __global__ __launch_bounds__(kImgWaves * 64) void attend_image_kernel(ImgParams 
   __bf16* Og = p.O + img;
 #pragma unroll
   for (int uu = 0; uu < kImgUnits; ++uu) {
-    const int u = wave + kImgWaves * uu;
+    const int u = wave + nwaves * uu;
     if (u < p.nunits)  // uniform
-      image_unit<RAGGED, N8>(p, u, lane, g, col, Ks, Vt, rpos, qop[uu], qoff[uu], Og);
+      image_unit<RAGGED, N8, QR>(p, u, lane, g, col, Ks, Vt, rpos, qop[uu], qoff[uu], Og);
   }
 }
 
@@ -1056,10 +1104,19 @@ int image_ldv(int HW) {
   return best;
 }
 
-bool plan_image(const Shape& s, ImgParams* p, size_t* lds) {
+struct ImgLaunch {
+  ImgParams p;
+  size_t lds;
+  int waves;  // per workgroup
+  int qr;     // regions per unit
+};
+
+bool plan_image(const Shape& s, ImgLaunch* L) {
   if (s.kv > KC || s.n % 4 != 0) return false;
+  const int qr = s.n == 4 ? 4 : s.n == 8 ? 2 : 1;
   const int ntiles = (s.n + 15) / 16;
-  if (s.R * ntiles > kImgWaves * kImgUnits) return false;
+  const int nunits = qr > 1 ? (s.R + qr - 1) / qr : s.R * ntiles;
+  if (nunits > 16 * kImgUnits) return false;
   // one workgroup per (image, head): fewer than half the compute units busy
   // is slower than the per-region split
   if ((int64_t)s.B * s.heads < 128) return false;
@@ -1067,36 +1124,49 @@ bool plan_image(const Shape& s, ImgParams* p, size_t* lds) {
   const int ldv = image_ldv(HW);
   const size_t bytes = 2 * (size_t)HW * kImgLdk + 2 * (size_t)D * ldv + 4 * (size_t)s.R * s.topk;
   if (bytes > kImgMaxLds) return false;
-  *p = ImgParams{};
-  p->H = s.H; p->W = s.W; p->C = s.C; p->S = s.S; p->topk = s.topk;
-  p->sh = s.sh; p->sw = s.sw; p->n = s.n; p->R = s.R; p->kv = s.kv; p->heads = s.heads;
-  p->HW = HW;
-  p->nunits = s.R * ntiles;
-  p->ldv = ldv;
-  p->c = 1.4426950408889634f / sqrtf((float)s.d);
-  p->div_n = make_fastdiv(s.n);
-  p->div_sw = make_fastdiv(s.sw);
-  p->div_S = make_fastdiv(s.S);
-  p->div_nt = make_fastdiv(ntiles);
-  *lds = bytes;
+  ImgParams& p = L->p;
+  p = ImgParams{};
+  p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S; p.topk = s.topk;
+  p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R; p.kv = s.kv; p.heads = s.heads;
+  p.HW = HW;
+  p.nunits = nunits;
+  p.ldv = ldv;
+  p.c = 1.4426950408889634f / sqrtf((float)s.d);
+  p.div_n = make_fastdiv(s.n);
+  p.div_sw = make_fastdiv(s.sw);
+  p.div_S = make_fastdiv(s.S);
+  p.div_nt = make_fastdiv(ntiles);
+  L->lds = bytes;
+  L->qr = qr;
+  // about two units per wave, at most 16 waves (a wave takes up to kImgUnits)
+  L->waves = std::min(16, (nunits + 1) / 2);
   return true;
 }
 
-hipError_t launch_image(const ImgParams& p0, size_t lds, int B, hipStream_t stream) {
-  ImgParams p = p0;
+hipError_t launch_image(const ImgLaunch& L, int B, hipStream_t stream) {
+  ImgParams p = L.p;
   const bool ragged = p.kv % KC != 0, n8 = p.n % 8 == 0;
-  const int which = (ragged ? 2 : 0) + (n8 ? 1 : 0);
-  const void* fns[4] = {(const void*)&attend_image_kernel<false, false>, (const void*)&attend_image_kernel<false, true>,
-                        (const void*)&attend_image_kernel<true, false>, (const void*)&attend_image_kernel<true, true>};
+  // (RAGGED, N8, QR): n = 8 has two regions per unit, n = 4 four
+  int which;
+  const void* fn;
+  if (n8) {
+    which = (ragged ? 4 : 0) + (L.qr == 2 ? 1 : 0);
+    fn = ragged ? (L.qr == 2 ? (const void*)&attend_image_kernel<true, true, 2> : (const void*)&attend_image_kernel<true, true, 1>)
+                : (L.qr == 2 ? (const void*)&attend_image_kernel<false, true, 2> : (const void*)&attend_image_kernel<false, true, 1>);
+  } else {
+    which = (ragged ? 4 : 0) + (L.qr == 4 ? 3 : 2);
+    fn = ragged ? (L.qr == 4 ? (const void*)&attend_image_kernel<true, false, 4> : (const void*)&attend_image_kernel<true, false, 1>)
+                : (L.qr == 4 ? (const void*)&attend_image_kernel<false, false, 4> : (const void*)&attend_image_kernel<false, false, 1>);
+  }
   // more than the default 64 KiB of dynamic LDS: raise the kernel's limit once
-  static bool raised[4] = {false, false, false, false};
+  static bool raised[8] = {false, false, false, false, false, false, false, false};
   if (!raised[which]) {
-    const hipError_t e = hipFuncSetAttribute(fns[which], hipFuncAttributeMaxDynamicSharedMemorySize, (int)kImgMaxLds);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kImgMaxLds);
     if (e != hipSuccess) return e;
     raised[which] = true;
   }
   void* args[] = {&p};
-  return hipLaunchKernel(fns[which], dim3((unsigned)(B * p.heads)), dim3(kImgWaves * 64), args, lds, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)(B * p.heads)), dim3(L.waves * 64), args, L.lds, stream);
 }
 
 }  // namespace
@@ -1105,16 +1175,23 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
                          const int32_t* idx, const void* lce_w, const void* lce_b, void* O,
                          const Shape& s, int dtype, hipStream_t stream) {
   const bool lce = lce_w != nullptr;
-  if (!lce && dtype == kBF16) {
-    ImgParams ip;
-    size_t lds;
-    if (plan_image(s, &ip, &lds)) {
-      ip.Q = static_cast<const __bf16*>(Q);
-      ip.K = static_cast<const __bf16*>(K);
-      ip.V = static_cast<const __bf16*>(V);
-      ip.idx = idx;
-      ip.O = static_cast<__bf16*>(O);
-      return launch_image(ip, lds, s.B, stream);
+  // The local context term is fused into the single-chunk kernel for bf16
+  // regions of 16 to 64 tokens (at most 8 x 8). For smaller regions the halo
+  // is several times the region (6 x 6 positions around 2 x 2) and the
+  // separate pass after the attention kernel measured faster (14x14 map,
+  // 2 x 2 regions: 38 us for attention + pass vs 47 us fused).
+  const bool fuse = lce && dtype == kBF16 && s.kv <= KC && s.sh <= 8 && s.sw <= 8 && s.n >= 16;
+  if (!fuse && dtype == kBF16) {
+    ImgLaunch L;
+    if (plan_image(s, &L)) {
+      L.p.Q = static_cast<const __bf16*>(Q);
+      L.p.K = static_cast<const __bf16*>(K);
+      L.p.V = static_cast<const __bf16*>(V);
+      L.p.idx = idx;
+      L.p.O = static_cast<__bf16*>(O);
+      const hipError_t e = launch_image(L, s.B, stream);
+      if (e != hipSuccess || !lce) return e;
+      return launch_lce(V, lce_w, lce_b, O, s, dtype, stream);
     }
   }
   if (s.kv <= KC) {
@@ -1130,12 +1207,6 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
     const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
     const bool ragged = s.kv % KC != 0;
     const bool one = s.n <= 16;  // one query tile per item
-    // The local context term is fused for bf16 regions of 16 to 64 tokens
-    // (at most 8 x 8). For smaller regions the halo is several times the
-    // region (6 x 6 positions around 2 x 2) and the separate pass after the
-    // attention kernel measured faster (14x14 map, 2 x 2 regions: 38 us for
-    // attention + pass vs 47 us fused).
-    const bool fuse = lce && dtype == kBF16 && s.sh <= 8 && s.sw <= 8 && s.n >= 16;
     const bool small = s.sh <= 4 && s.sw <= 4;
     size_t lds = esz * (size_t)HG * D * (KC + padv);  // V^T tiles
     int waves = HG;
