@@ -1145,25 +1145,21 @@ bool plan_image(const Shape& s, ImgLaunch* L) {
 
 hipError_t launch_image(const ImgLaunch& L, int B, hipStream_t stream) {
   ImgParams p = L.p;
-  const bool ragged = p.kv % KC != 0, n8 = p.n % 8 == 0;
-  // (RAGGED, N8, QR): n = 8 has two regions per unit, n = 4 four
-  int which;
-  const void* fn;
-  if (n8) {
-    which = (ragged ? 4 : 0) + (L.qr == 2 ? 1 : 0);
-    fn = ragged ? (L.qr == 2 ? (const void*)&attend_image_kernel<true, true, 2> : (const void*)&attend_image_kernel<true, true, 1>)
-                : (L.qr == 2 ? (const void*)&attend_image_kernel<false, true, 2> : (const void*)&attend_image_kernel<false, true, 1>);
-  } else {
-    which = (ragged ? 4 : 0) + (L.qr == 4 ? 3 : 2);
-    fn = ragged ? (L.qr == 4 ? (const void*)&attend_image_kernel<true, false, 4> : (const void*)&attend_image_kernel<true, false, 1>)
-                : (L.qr == 4 ? (const void*)&attend_image_kernel<false, false, 4> : (const void*)&attend_image_kernel<false, false, 1>);
-  }
-  // more than the default 64 KiB of dynamic LDS: raise the kernel's limit once
-  static bool raised[8] = {false, false, false, false, false, false, false, false};
-  if (!raised[which]) {
+  const bool ragged = p.kv % KC != 0;
+  // (RAGGED, N8, QR): n = 8 has two regions per unit, n = 4 four, other
+  // multiples of 4 one (N8 when a multiple of 8)
+  const void* fns[2][4] = {
+      {(const void*)&attend_image_kernel<false, true, 1>, (const void*)&attend_image_kernel<false, false, 1>,
+       (const void*)&attend_image_kernel<false, true, 2>, (const void*)&attend_image_kernel<false, false, 4>},
+      {(const void*)&attend_image_kernel<true, true, 1>, (const void*)&attend_image_kernel<true, false, 1>,
+       (const void*)&attend_image_kernel<true, true, 2>, (const void*)&attend_image_kernel<true, false, 4>}};
+  const int form = L.qr == 2 ? 2 : L.qr == 4 ? 3 : (p.n % 8 == 0 ? 0 : 1);
+  const void* fn = fns[ragged][form];
+  // more than the default 64 KiB of dynamic LDS: raise the kernel's limit
+  // (an attribute of the kernel, set on every launch: no state is kept)
+  if (L.lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kImgMaxLds);
     if (e != hipSuccess) return e;
-    raised[which] = true;
   }
   void* args[] = {&p};
   return hipLaunchKernel(fn, dim3((unsigned)(B * p.heads)), dim3(L.waves * 64), args, L.lds, stream);
