@@ -156,6 +156,7 @@ IMAGE_RESIDENT = [
     wl.custom(128, 8, 16, 32, 1, 4, 8, "bf16", seed=77),    # n=8, kv=64
     wl.custom(128, 6, 12, 32, 1, 3, 5, "bf16", seed=78),    # n=8, 9 regions: a unit with one region
     wl.custom(128, 24, 24, 32, 1, 3, 1, "bf16", seed=75),   # n=64: four query tiles per region
+    wl.custom(128, 32, 32, 32, 1, 8, 4, "bf16", seed=79),   # 64 units (16 waves x 4), about 149 KB of LDS
 ]
 
 

@@ -893,16 +893,20 @@ __device__ __forceinline__ void image_unit(const ImgParams& p, int u, int lane, 
 #pragma unroll
   for (int st = 0; st < 2; ++st) acc[2] = TT::mma(ones, pop[st], acc[2]);
 
-  if (qoff >= 0) {
-    const float inv = 1.0f / acc[2][0];
-    float o[8];
+  // v_rcp_f32 (within 1 ulp) for the denominator: the output is rounded to
+  // bf16 after the multiply
+  const float inv = __builtin_amdgcn_rcpf(acc[2][0]);
+  float o[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[e] = bad ? __builtin_nanf("") : acc[0][e] * inv;
-      o[4 + e] = bad ? __builtin_nanf("") : acc[1][e] * inv;
-    }
-    TT::store8_nt(Og + qoff, o);
+  for (int e = 0; e < 4; ++e) {
+    o[e] = acc[0][e] * inv;
+    o[4 + e] = acc[1][e] * inv;
   }
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {  // uniform; rare
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = bad ? __builtin_nanf("") : o[e];
+  }
+  if (qoff >= 0) TT::store8_nt(Og + qoff, o);
 }
 
 // N8: n is a multiple of 8, so each block of 8 keys 8g..8g+7 is 8 consecutive
