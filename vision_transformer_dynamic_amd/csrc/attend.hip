@@ -297,7 +297,9 @@ __device__ __forceinline__ void compute_chunk(const AttnParams& p, const Item& i
     // the accumulators at 0, so there is nothing to rescale
     const float mnew = MULTI ? fmaxf(us.m[uu], mx) : mx;
     const float mc = mnew * p.c;
-    if (MULTI) {
+    // rescale only when some lane's running max grew: otherwise every alpha
+    // is exp2(0) = 1 and the product would leave the accumulators unchanged
+    if (MULTI && __builtin_amdgcn_ballot_w64(mnew > us.m[uu]) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(us.m[uu] * p.c - mc);
 #pragma unroll
       for (int ct = 0; ct < 3; ++ct) us.acc[uu][ct] *= alpha;

@@ -36,16 +36,17 @@ struct FastDiv {
 
 inline FastDiv make_fastdiv(int d) { return FastDiv{1.0f / (float)d, d}; }
 
+// The repair is written as selects, not branches, so that it never splits a
+// wave's control flow (at most one of the two applies).
 __device__ inline int fdiv(int a, FastDiv f, int* rem) {
   int q = (int)((float)a * f.inv);
   int r = a - q * f.d;
-  if (r < 0) {
-    --q;
-    r += f.d;
-  } else if (r >= f.d) {
-    ++q;
-    r -= f.d;
-  }
+  const bool lo = r < 0;
+  q = lo ? q - 1 : q;
+  r = lo ? r + f.d : r;
+  const bool hi = r >= f.d;
+  q = hi ? q + 1 : q;
+  r = hi ? r - f.d : r;
   *rem = r;
   return q;
 }
