@@ -53,6 +53,7 @@ constexpr int kMaxUnits = 16; // chunked kernel: units (= waves) per workgroup
 constexpr int kMinWaves = 4;  // chunked kernel: waves per workgroup at least (they share the chunk loads)
 constexpr int QB = 64;        // single-chunk kernel: queries per work item (<= 4 tiles of 16)
 constexpr int QBM = 128;      // chunked kernel: queries per work item (<= 8 tiles of 16)
+constexpr size_t kChunkMaxLds = 156 * 1024;  // chunked kernel: LDS of its four chunk buffers at most (static LDS on top)
 
 struct AttnParams {
   const void* Q;
@@ -68,7 +69,7 @@ struct AttnParams {
   int nhg;     // head groups
   int nitems;  // B * R * nqb * nhg
   int lg_oct;  // log2(8 * HG * D / VEC): pair items per 8-pair octet of a chunk
-  int nbuf;    // LDS chunk buffers (2: double-buffered, when kv spans several chunks)
+  int nbuf;    // LDS chunk buffers (2: double-buffered; 4: two chunks per barrier)
   int own_tab; // single-chunk kernel: every attention wave builds its own key table
   int qblk;    // queries per work item
   float c;     // softmax scale * log2(e)
@@ -353,7 +354,8 @@ __device__ __forceinline__ void store_outputs(const AttnParams& p, const Item& i
 // NV: 16-byte vectors per tensor per thread per chunk (2 or 4, even).
 // MULTI: kv spans more than one chunk (prefetch the next chunk during compute).
 // RAGGED: kv is not a multiple of 64 (the last chunk masks its missing keys).
-template <typename T, int NV, bool MULTI, bool RAGGED>
+// PAIR: four LDS chunk buffers, two chunks staged per barrier (p.nbuf == 4).
+template <typename T, int NV, bool MULTI, bool RAGGED, bool PAIR>
 __global__ __launch_bounds__(NV == 2 ? kMaxUnits * 64 : 512) void attend_kernel(AttnParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
@@ -402,6 +404,31 @@ __global__ __launch_bounds__(NV == 2 ? kMaxUnits * 64 : 512) void attend_kernel(
       load_kv<T, NV, TOK>(p, it, tid, rtab, 0, kA, vA);
       if (MULTI && nchunks > 1) load_kv<T, NV, TOK>(p, it, tid, rtab, KC, kB, vB);
     }
+    if constexpr (MULTI && PAIR) {
+      // four LDS buffers: both chunks of a pair are staged behind one
+      // barrier. Pair s uses buffers 2s, 2s + 1 (mod 4); pair s + 2 reuses
+      // them only after the barrier of pair s + 1, which every wave reaches
+      // after computing pair s.
+      for (int ch = 0; ch < nchunks; ch += 2) {
+        T* K0 = reinterpret_cast<T*>(smem_raw) + (ch & 3) * bufsz;
+        T* K1 = reinterpret_cast<T*>(smem_raw) + ((ch + 1) & 3) * bufsz;
+        const bool two = ch + 1 < nchunks;  // uniform
+        if (loader) {
+          store_kv<T, NV>(p, tid, K0, K0 + KC * ldk, ldk, ldv, kA, vA);
+          if (two) store_kv<T, NV>(p, tid, K1, K1 + KC * ldk, ldk, ldv, kB, vB);
+        }
+        __syncthreads();
+        // the next pair's loads: set A now, set B after the first chunk's
+        // products (set B is free from its store until then)
+        if (loader && ch + 2 < nchunks) load_kv<T, NV, TOK>(p, it, tid, rtab, (ch + 2) * KC, kA, vA);
+        compute_chunk<T, MULTI, RAGGED>(p, it, wave, g, col, K0, K0 + KC * ldk, ldk, ldv, min(KC, p.kv - ch * KC),
+                                        ones, us);
+        if (loader && ch + 3 < nchunks) load_kv<T, NV, TOK>(p, it, tid, rtab, (ch + 3) * KC, kB, vB);
+        if (two)
+          compute_chunk<T, MULTI, RAGGED>(p, it, wave, g, col, K1, K1 + KC * ldk, ldk, ldv,
+                                          min(KC, p.kv - (ch + 1) * KC), ones, us);
+      }
+    } else {
     for (int ch = 0; ch < nchunks; ch += 2) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -426,6 +453,7 @@ __global__ __launch_bounds__(NV == 2 ? kMaxUnits * 64 : 512) void attend_kernel(
         }
         compute_chunk<T, MULTI, RAGGED>(p, it, wave, g, col, Ks, Vt, ldk, ldv, min(KC, p.kv - c0), ones, us);
       }
+    }
     }
   }
   store_outputs<T>(p, it, us, bad);
@@ -1053,7 +1081,10 @@ AttnLaunch plan_attend(const Shape& s, int dtype) {
   const int padk = dtype == kBF16 ? Tr<__bf16>::PADK : Tr<float>::PADK;
   const int padv = dtype == kBF16 ? Tr<__bf16>::PADV : Tr<float>::PADV;
   const size_t buf = esz * ((size_t)KC * (HG * D + padk) + (size_t)HG * D * (KC + padv));
-  p.nbuf = (s.kv > KC && 2 * buf <= 65536) ? 2 : 1;
+  // four buffers (two chunks per barrier) from four chunks on, when they
+  // fit; else two (double-buffered) within the default 64 KiB; else one
+  const int nch = (s.kv + KC - 1) / KC;
+  p.nbuf = s.kv <= KC ? 1 : (nch >= 4 && 4 * buf <= kChunkMaxLds) ? 4 : (2 * buf <= 65536 ? 2 : 1);
   L.lds = p.nbuf * buf;
   L.waves = std::max(kMinWaves, std::min(kMaxUnits, HG * qtiles));
   L.nv = (KC * (HG * D / vec) + L.waves * 64 - 1) / (L.waves * 64);  // <= 4: at least 4 waves
@@ -1067,15 +1098,19 @@ AttnLaunch plan_attend(const Shape& s, int dtype) {
 }
 
 template <typename T, bool RAGGED>
-const void* pick_attend_r(int nv, bool multi) {
-  if (multi) return nv <= 2 ? (const void*)&attend_kernel<T, 2, true, RAGGED> : (const void*)&attend_kernel<T, 4, true, RAGGED>;
-  return nv <= 2 ? (const void*)&attend_kernel<T, 2, false, RAGGED> : (const void*)&attend_kernel<T, 4, false, RAGGED>;
+const void* pick_attend_r(int nv, bool multi, bool pair) {
+  if (multi && pair)
+    return nv <= 2 ? (const void*)&attend_kernel<T, 2, true, RAGGED, true> : (const void*)&attend_kernel<T, 4, true, RAGGED, true>;
+  if (multi)
+    return nv <= 2 ? (const void*)&attend_kernel<T, 2, true, RAGGED, false> : (const void*)&attend_kernel<T, 4, true, RAGGED, false>;
+  return nv <= 2 ? (const void*)&attend_kernel<T, 2, false, RAGGED, false> : (const void*)&attend_kernel<T, 4, false, RAGGED, false>;
 }
 
 const void* pick_attend(int dtype, const AttnLaunch& L) {
-  const bool ragged = L.p.kv % KC != 0;
-  if (dtype == kBF16) return ragged ? pick_attend_r<__bf16, true>(L.nv, L.multi) : pick_attend_r<__bf16, false>(L.nv, L.multi);
-  return ragged ? pick_attend_r<float, true>(L.nv, L.multi) : pick_attend_r<float, false>(L.nv, L.multi);
+  const bool ragged = L.p.kv % KC != 0, pair = L.p.nbuf == 4;
+  if (dtype == kBF16)
+    return ragged ? pick_attend_r<__bf16, true>(L.nv, L.multi, pair) : pick_attend_r<__bf16, false>(L.nv, L.multi, pair);
+  return ragged ? pick_attend_r<float, true>(L.nv, L.multi, pair) : pick_attend_r<float, false>(L.nv, L.multi, pair);
 }
 
 // Image-resident kernel: the shape conditions, the V^T row stride and the LDS
@@ -1164,7 +1199,7 @@ hipError_t launch_image(const ImgLaunch& L, int B, hipStream_t stream) {
   // more than the default 64 KiB of dynamic LDS: raise the kernel's limit
   // (an attribute of the kernel, set on every launch: no state is kept)
   if (L.lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kImgMaxLds);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
     if (e != hipSuccess) return e;
   }
   void* args[] = {&p};
@@ -1255,7 +1290,15 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
   L.p.Q = Q; L.p.K = K; L.p.V = V; L.p.idx = idx; L.p.O = O;
   void* args[] = {&L.p};
   if (L.nv > 4 || (L.nv > 2 && L.waves > 8)) return hipErrorInvalidValue;  // the kernels' launch bounds
-  hipError_t e = hipLaunchKernel(pick_attend(dtype, L), dim3((unsigned)L.nwg), dim3(L.waves * 64), args, L.lds, stream);
+  const void* fn = pick_attend(dtype, L);
+  hipError_t e;
+  if (L.lds > 64 * 1024) {
+    // more than the default 64 KiB of dynamic LDS: raise the kernel's limit to
+    // this launch's size (its static LDS comes on top)
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
+    if (e != hipSuccess) return e;
+  }
+  e = hipLaunchKernel(fn, dim3((unsigned)L.nwg), dim3(L.waves * 64), args, L.lds, stream);
   if (e != hipSuccess || !lce) return e;
   return launch_lce(V, lce_w, lce_b, O, s, dtype, stream);
 }
