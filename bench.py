@@ -71,6 +71,26 @@ def attend_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def attention_kernel_name(w):
+    """The attention kernel the library launches for workload w (its dispatch
+    rule: more than 64 keys per query take the chunked kernel; bf16 regions of
+    a multiple of 4 tokens with at least 128 (image, head) pairs, at most 64
+    units of 16 query columns and an image's head slice within 160 KB of LDS
+    take the image-resident kernel; the rest the per-region kernel). The LDS
+    bound here takes the largest row pad the library may choose."""
+    n = (w.H // w.S) * (w.W // w.S)
+    R, HW = w.S * w.S, w.H * w.W
+    if n * w.topk > 64:
+        return "attend_kernel"
+    if w.dtype == "bf16" and n % 4 == 0 and w.B * w.heads >= 128:
+        qr = 4 if n == 4 else 2 if n == 8 else 1
+        units = -(-R // qr) if qr > 1 else R * -(-n // 16)
+        lds = 2 * HW * 40 + 2 * 32 * (-(-HW // 32) * 32 + 56) + 4 * R * w.topk
+        if units <= 64 and lds <= 160 * 1024:
+            return "attend_image_kernel"
+    return "attend_head_kernel"
+
+
 def profiled_traffic():
     """HBM bytes per attention launch from the committed counter summary, if it
     was taken on the current attention kernel source; else None."""
@@ -392,7 +412,7 @@ def main(argv=None):
                 "frac": round(achieved / peak_tf, 4)}
     traffic = profiled_traffic() if w is wl.HEADLINE else None
     roof["traffic"] = traffic
-    roof["kernel"] = "attend_head_kernel" if w.kv <= 64 else "attend_kernel"
+    roof["kernel"] = attention_kernel_name(w)
     roof["algorithmic_bytes_per_launch"] = attn_bytes
     roof["launch_us"] = round(attend_us, 2)
     # the same bytes moved by a plain streaming kernel on this GPU, and the
