@@ -14,8 +14,8 @@
 // workgroup = one work item (image b, query region i, block of <= 128 of the
 // region's queries, group of HG heads); each of its waves owns one "unit" =
 // (head, tile of 16 queries) and keeps its accumulators in registers, and the
-// waves share every staged 64-key chunk. The single-chunk kernel below has
-// its own split.
+// waves share every staged 64-key chunk. The single-chunk kernel and the
+// image-resident kernel below have their own splits.
 //
 // Transposed products. With d = 32 the score tile is computed as
 //   S^T[16 keys x 16 queries] = K[16 x 32] . Q^T[32 x 16]
