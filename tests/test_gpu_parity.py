@@ -123,7 +123,7 @@ EDGE = [
     wl.custom(2, 9, 9, 64, 2, 1, 1, "bf16", seed=16),      # one region: global attention
     wl.custom(1, 14, 14, 256, 8, 7, 16, "f32", seed=17),   # fp32, stage-3 shape
     wl.custom(2, 24, 24, 64, 2, 3, 2, "f32", seed=18),     # fp32, n=64, two head group of 1
-    wl.custom(1, 32, 32, 64, 2, 2, 2, "f32", seed=19),     # fp32, n=256, two 128-query blocks
+    wl.custom(1, 32, 32, 64, 2, 2, 2, "f32", seed=19),     # fp32, n=256: one 256-query block per head
     wl.custom(3, 10, 15, 96, 3, 5, 4, "bf16", seed=20, content="clustered"),
     # chunked kernel (more than 64 keys per query) launch shapes: 4 heads of
     # one 16-query tile each in 4 waves (each thread stages four 16-byte

@@ -52,7 +52,7 @@ constexpr int MAXU = 1;       // chunked kernel: (head, 16-query tile) units per
 constexpr int kMaxUnits = 16; // chunked kernel: units (= waves) per workgroup
 constexpr int kMinWaves = 4;  // chunked kernel: waves per workgroup at least (they share the chunk loads)
 constexpr int QB = 64;        // single-chunk kernel: queries per work item (<= 4 tiles of 16)
-constexpr int QBM = 128;      // chunked kernel: queries per work item (<= 8 tiles of 16)
+constexpr int QBM = 128;      // chunked kernel: queries per work item (<= 8 tiles of 16; 2 * QBM for large regions)
 constexpr size_t kChunkMaxLds = 156 * 1024;  // chunked kernel: LDS of its four chunk buffers at most (static LDS on top)
 
 struct AttnParams {
@@ -1059,8 +1059,10 @@ AttnLaunch plan_attend(const Shape& s, int dtype) {
   // chunked kernel: 128-query items, one wave per (head, 16-query tile) unit
   // (more queries per staged chunk measured faster at the dense 128x128
   // shape: 30.1 us with 128, 39.4 with 64 queries and two units per wave,
-  // 43.3 with 32)
-  p.qblk = s.kv > KC ? QBM : QB;
+  // 43.3 with 32); regions of 256 tokens or more take 256-query items of one
+  // head (16 waves, each chunk staged for twice the queries: 28.0 -> 26.9 us
+  // at the dense shape)
+  p.qblk = s.kv > KC ? (s.n >= 2 * QBM ? 2 * QBM : QBM) : QB;
   p.nqb = (s.n + p.qblk - 1) / p.qblk;
   const int qtiles = (min(s.n, p.qblk) + 15) / 16;
   const int cap = dtype == kBF16 ? 4 : 2;  // keeps LDS at or below 64 KiB
