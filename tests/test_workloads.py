@@ -36,3 +36,17 @@ def test_clustered_tokens_share_their_region_mean():
     # V is iid, not clustered
     gv = v.reshape(1, 4, 4, 4, 4, 32).permute(0, 1, 3, 2, 4, 5).reshape(1, 16, 16, 32)
     assert gv.std(dim=2).mean().item() > 0.85
+
+
+def test_bench_names_the_dispatched_attention_kernel():
+    """bench.py labels its roofline with the attention kernel the library
+    dispatches: the per-region kernel at stage 1 and for fp32, the
+    image-resident kernel at the 28x28 and 14x14 stage shapes, the chunked
+    kernel at the dense shape (more than 64 keys per query)."""
+    import bench
+    names = [bench.attention_kernel_name(w) for w in wl.WORKLOADS]
+    assert names == ["attend_head_kernel", "attend_head_kernel", "attend_image_kernel",
+                     "attend_image_kernel", "attend_kernel"]
+    # too few (image, head) pairs, or regions not a multiple of 4 tokens
+    assert bench.attention_kernel_name(wl.custom(2, 28, 28, 128, 4, 7, 4)) == "attend_head_kernel"
+    assert bench.attention_kernel_name(wl.custom(64, 21, 21, 64, 2, 7, 4)) == "attend_head_kernel"
