@@ -308,3 +308,42 @@ def test_forward_routing_table_equals_bra_route(w):
     ref = bra.route(q, k, w.S, w.topk)
     torch.cuda.synchronize()
     assert torch.equal(table, ref)
+
+
+def test_concurrent_calls_from_threads():
+    """Calls from several host threads on their own streams, with shapes whose
+    attention kernels need different amounts of LDS (the image-resident kernel
+    at 28x28 and 14x14, the chunked kernel at a 256-token region in fp32),
+    give the bits of the same calls made one after another."""
+    import threading
+
+    shapes = [wl.custom(32, 28, 28, 128, 4, 7, 4, "bf16", seed=90),
+              wl.custom(16, 14, 14, 256, 8, 7, 16, "bf16", seed=91),
+              wl.custom(1, 32, 32, 64, 2, 2, 2, "f32", seed=92)]
+    inputs = [_gpu(*wl.make_inputs(w)) for w in shapes]
+    ref = [bra.forward(*x, w.heads, w.S, w.topk) for w, x in zip(shapes, inputs)]
+    torch.cuda.synchronize()
+    got = [[None] * 8 for _ in shapes]
+    errors = []
+
+    def work(i):
+        try:
+            w, x = shapes[i], inputs[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for r in range(8):
+                    got[i][r] = bra.forward(*x, w.heads, w.S, w.topk)
+            s.synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(shapes)):
+        for r in range(8):
+            assert torch.equal(got[i][r], ref[i]), (shapes[i].name, r)

@@ -1199,9 +1199,10 @@ hipError_t launch_image(const ImgLaunch& L, int B, hipStream_t stream) {
   const int form = L.qr == 2 ? 2 : L.qr == 4 ? 3 : (p.n % 8 == 0 ? 0 : 1);
   const void* fn = fns[ragged][form];
   // more than the default 64 KiB of dynamic LDS: raise the kernel's limit
-  // (an attribute of the kernel, set on every launch: no state is kept)
+  // (an attribute of the kernel, set on every launch: no state is kept) to
+  // the most any launch of it uses, one value for every caller
   if (L.lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kImgMaxLds);
     if (e != hipSuccess) return e;
   }
   void* args[] = {&p};
@@ -1295,9 +1296,11 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
   const void* fn = pick_attend(dtype, L);
   hipError_t e;
   if (L.lds > 64 * 1024) {
-    // more than the default 64 KiB of dynamic LDS: raise the kernel's limit to
-    // this launch's size (its static LDS comes on top)
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.lds);
+    // more than the default 64 KiB of dynamic LDS: raise the kernel's limit
+    // to the most any launch of it uses (one value for every caller, so
+    // concurrent calls cannot lower it under each other; the kernel's static
+    // LDS comes on top)
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kChunkMaxLds);
     if (e != hipSuccess) return e;
   }
   e = hipLaunchKernel(fn, dim3((unsigned)L.nwg), dim3(L.waves * 64), args, L.lds, stream);
