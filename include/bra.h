@@ -14,8 +14,9 @@
  * Tensors
  *   Q, K, V, O : [B, H, W, C] row-major, channels fastest, all of one dtype,
  *                caller-owned device memory, 16-byte aligned. O must not
- *                alias Q, K or V.
- *   idx        : [B, S*S, topk] int32 device memory, 4-byte aligned.
+ *                overlap Q, K, V or idx (BRA_EINVAL).
+ *   idx        : [B, S*S, topk] int32 device memory, 4-byte aligned; as the
+ *                output of bra_route it must not overlap Q or K.
  * Regions      : S must divide H and W (no padding). Region r covers rows
  *                [(r/S)*H/S, (r/S+1)*H/S) and columns [(r%S)*W/S, (r%S+1)*W/S);
  *                n = (H/S)*(W/S) tokens per region.
@@ -40,12 +41,13 @@
  *   thread-safe; calls that share a workspace must be ordered by the caller.
  *
  * Workspace
- *   bra_forward and bra_route need bra_workspace_bytes(...) bytes of device
- *   scratch (the fp32 region means Q^r, K^r and, for bra_forward, the routing
- *   table, which bra_forward leaves there).
- *   Pass a caller-owned buffer (256-byte aligned), or NULL/0 to let the call
- *   allocate and free it stream-ordered (hipMallocAsync / hipFreeAsync) on
- *   `stream`.
+ *   The routing step keeps the fp32 region means Q^r, K^r (and, in
+ *   bra_forward, the routing table) in device scratch of
+ *   bra_workspace_bytes(...) bytes. bra_route and bra_forward allocate it
+ *   and free it stream-ordered (hipMallocAsync / hipFreeAsync) on `stream`;
+ *   bra_route_ws and bra_forward_ws take a caller-owned buffer (256-byte
+ *   aligned, not overlapping any tensor argument) instead and allocate
+ *   nothing.
  */
 #ifndef BRA_H_
 #define BRA_H_
@@ -76,8 +78,15 @@ typedef enum bra_status {
 /* Static, NUL-terminated description of a status code. Never NULL. */
 const char* bra_status_string(bra_status status);
 
-/* Bytes of device workspace that bra_forward and bra_route need for these
- * sizes (0 if the sizes are invalid). */
+/* Diagnostics: the name of the attention kernel that bra_attend (with_lce
+ * = 0) or bra_attend_lce (with_lce != 0) launches for these sizes, as
+ * profilers list it; NULL if the sizes are invalid or unsupported. A static
+ * string; no device work. */
+const char* bra_attend_kernel(int B, int H, int W, int C, int heads, int S, int topk,
+                              bra_dtype dtype, int with_lce);
+
+/* Bytes of device workspace that bra_route_ws and bra_forward_ws need for
+ * these sizes (0 if the sizes are invalid). */
 size_t bra_workspace_bytes(int B, int H, int W, int C, int S, int topk);
 
 /*
@@ -93,8 +102,42 @@ size_t bra_workspace_bytes(int B, int H, int W, int C, int S, int topk);
  */
 bra_status bra_route(const void* Q, const void* K, int32_t* idx,
                      int B, int H, int W, int C, int S, int topk,
-                     bra_dtype dtype, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream);
+                     bra_dtype dtype, hipStream_t stream);
+
+/* bra_route_ws - bra_route with the caller's workspace (at least
+ * bra_workspace_bytes(B, H, W, C, S, topk) bytes, 256-byte aligned; a null
+ * or too small buffer gives BRA_EINVAL). Same table, bit for bit. */
+bra_status bra_route_ws(const void* Q, const void* K, int32_t* idx,
+                        int B, int H, int W, int C, int S, int topk,
+                        bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * bra_pool - the region means alone (explainer Part 2.2 step 3 and
+ * pseudocode step 3; paper summary Section 6, regional representations by
+ * averaging): Qr[b][r][:] and Kr[b][r][:] are the means of Q and K over the
+ * n tokens of region r, accumulated in fp32 in a fixed order: exactly the
+ * means bra_route computes before it routes.
+ *   Qr, Kr : [B, S*S, C] fp32 device memory, 16-byte aligned, not
+ *            overlapping each other, Q or K (BRA_EINVAL).
+ */
+bra_status bra_pool(const void* Q, const void* K, float* Qr, float* Kr,
+                    int B, int H, int W, int C, int S,
+                    bra_dtype dtype, hipStream_t stream);
+
+/*
+ * bra_route_pooled - the routing step from given region means (explainer
+ * Part 2.2 pseudocode steps 4-5): the affinity A = Qr Kr^T of every image
+ * over all C channels in fp32 and the topk largest entries of each row, in
+ * the order and with the tie rule of bra_route. bra_route is bra_pool
+ * followed by this call, bit for bit.
+ *   Qr, Kr : [B, S*S, C] fp32 device memory, 16-byte aligned.
+ *   idx    : [B, S*S, topk] int32 output, 4-byte aligned, not overlapping
+ *            Qr or Kr (BRA_EINVAL).
+ * Same limits on S, C and topk as bra_route.
+ */
+bra_status bra_route_pooled(const float* Qr, const float* Kr, int32_t* idx,
+                            int B, int S, int C, int topk, hipStream_t stream);
 
 /*
  * bra_attend - token-level attention over routed regions (explainer Part 2.2,
@@ -120,8 +163,18 @@ bra_status bra_attend(const void* Q, const void* K, const void* V,
  */
 bra_status bra_forward(const void* Q, const void* K, const void* V, void* O,
                        int B, int H, int W, int C, int heads, int S, int topk,
-                       bra_dtype dtype, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream);
+                       bra_dtype dtype, hipStream_t stream);
+
+/* bra_forward_ws - bra_forward with the caller's workspace (at least
+ * bra_workspace_bytes(B, H, W, C, S, topk) bytes, 256-byte aligned; a null
+ * or too small buffer gives BRA_EINVAL). The routing table is left in the
+ * workspace at byte offset 2 * align256(4 * B * S*S * C), [B, S*S, topk]
+ * int32, after the region means Q^r and K^r ([B, S*S, C] fp32 each, at
+ * offsets 0 and align256(4 * B * S*S * C)). Same output, bit for bit. */
+bra_status bra_forward_ws(const void* Q, const void* K, const void* V, void* O,
+                          int B, int H, int W, int C, int heads, int S, int topk,
+                          bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * Local context enhancement (LCE): the "+ dwconv(value)" term of the module
@@ -157,8 +210,10 @@ bra_status bra_attend_lce(const void* Q, const void* K, const void* V,
 
 /* bra_forward_lce - the whole module output of explainer pseudocode steps
  * 1 and 3-7: bra_forward plus the local context term. Same arguments,
- * checks, workspace and streams as bra_forward, plus weight and bias; its
- * routing table is bra_route's, bit for bit. */
+ * checks and streams as bra_forward, plus weight and bias, and a workspace
+ * as in bra_forward_ws, except that NULL/0 asks for a stream-ordered
+ * allocation as bra_forward makes; its routing table is bra_route's, bit
+ * for bit. */
 bra_status bra_forward_lce(const void* Q, const void* K, const void* V,
                            const void* weight, const void* bias, void* O,
                            int B, int H, int W, int C, int heads, int S, int topk,
@@ -183,14 +238,16 @@ bra_status bra_forward_lce(const void* Q, const void* K, const void* V,
  *              in `dtype`, 16-byte aligned, read only.
  *   idx      : the routing table of the forward, [B, S*S, topk] int32, with
  *              distinct entries per row (as bra_route writes them). A row
- *              with an entry outside [0, S*S) makes that region's dQ NaN and
- *              its queries contribute nothing to dK, dV.
- *   dQ, dK, dV : outputs [B, H, W, C] in `dtype`, 16-byte aligned, pairwise
- *              distinct and distinct from the inputs (BRA_EINVAL). Every
+ *              with an entry outside [0, S*S), or with a repeated entry,
+ *              makes that region's dQ NaN and its queries contribute
+ *              nothing to dK, dV.
+ *   dQ, dK, dV : outputs [B, H, W, C] in `dtype`, 16-byte aligned, not
+ *              overlapping each other, the inputs or idx (BRA_EINVAL). Every
  *              element is written (tokens no region routes to get 0 in dK
  *              and dV).
  *   workspace  : bra_backward_workspace_bytes(...) bytes, 256-byte aligned,
- *              or NULL/0 for a stream-ordered allocation as in bra_forward.
+ *              not overlapping any tensor argument, or NULL/0 for a
+ *              stream-ordered allocation as in bra_forward.
  *
  * Deterministic: no atomics touch the gradients; fp32 accumulation.
  */
@@ -229,8 +286,9 @@ bra_status bra_qkv_pool(const void* X, const void* Wqkv, const void* bqkv, void*
 
 /* bra_forward_qkv - the module from its input: bra_qkv_pool into Q, K, V
  * (kept for the caller, e.g. for the backward) and the workspace's region
- * means, routing from those means, then attention into O. Workspace and
- * streams as bra_forward (bra_workspace_bytes bytes). */
+ * means, routing from those means, then attention into O. Workspace as in
+ * bra_forward_lce (bra_workspace_bytes bytes, or NULL/0 for a stream-ordered
+ * allocation); streams as bra_forward. */
 bra_status bra_forward_qkv(const void* X, const void* Wqkv, const void* bqkv, void* Q, void* K, void* V, void* O,
                            int B, int H, int W, int C, int heads, int S, int topk,
                            bra_dtype dtype, void* workspace, size_t workspace_bytes,

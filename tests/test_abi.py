@@ -22,6 +22,11 @@ EINVAL, EUNSUP = bra.BRA_EINVAL, bra.BRA_EUNSUPPORTED
 P = 0x10000  # aligned fake device pointers (never dereferenced)
 P2, P3, P4, PW = 0x20000, 0x30000, 0x40000, 0x50000
 PF, PB = 0x60000, 0x70000  # local-context filter weight and bias
+WS = 0x1000000  # workspace (1 MiB by default), clear of every tensor above
+# Maps of the default shape (1 x 16 x 16 x 32 fp32) are 32 KiB; the fake
+# pointers are 64 KiB apart, so offsets below place one tensor partly inside
+# another.
+MAP = 16 * 16 * 32 * 4
 
 
 @pytest.fixture(scope="module")
@@ -69,19 +74,29 @@ def test_workspace_bytes(lib):
     assert lib.bra_workspace_bytes(1, 16, 16, 32, 4, 17) == 0  # topk > S*S
 
 
-def _fwd(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4, ws=PW, wsb=1 << 20):
-    return lib.bra_forward(q, kk, v, o, B, H, W, C, heads, S, k, dt, ws, wsb, None)
+def _fwd(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4, ws=WS, wsb=1 << 20):
+    return lib.bra_forward_ws(q, kk, v, o, B, H, W, C, heads, S, k, dt, ws, wsb, None)
 
 
-def _route(lib, B=1, H=16, W=16, C=32, S=4, k=2, dt=0, q=P, kk=P2, idx=P3, ws=PW, wsb=1 << 20):
-    return lib.bra_route(q, kk, idx, B, H, W, C, S, k, dt, ws, wsb, None)
+def _route(lib, B=1, H=16, W=16, C=32, S=4, k=2, dt=0, q=P, kk=P2, idx=P3, ws=WS, wsb=1 << 20):
+    return lib.bra_route_ws(q, kk, idx, B, H, W, C, S, k, dt, ws, wsb, None)
+
+
+# the forms without a workspace argument (they would allocate one: only calls
+# that fail validation, before any HIP call, are made here)
+def _fwd_alloc(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4):
+    return lib.bra_forward(q, kk, v, o, B, H, W, C, heads, S, k, dt, None)
+
+
+def _route_alloc(lib, B=1, H=16, W=16, C=32, S=4, k=2, dt=0, q=P, kk=P2, idx=P3):
+    return lib.bra_route(q, kk, idx, B, H, W, C, S, k, dt, None)
 
 
 def _attend(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, idx=P4, o=PW):
     return lib.bra_attend(q, kk, v, idx, o, B, H, W, C, heads, S, k, dt, None)
 
 
-def _fwd_lce(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4, ws=PW, wsb=1 << 20,
+def _fwd_lce(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4, ws=WS, wsb=1 << 20,
              wt=PF, bias=PB):
     return lib.bra_forward_lce(q, kk, v, wt, bias, o, B, H, W, C, heads, S, k, dt, ws, wsb, None)
 
@@ -92,11 +107,11 @@ def _attend_lce(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2,
 
 
 def _bwd(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4, do=PF, idx=PB,
-         dq=0x80000, dk=0x90000, dv=0xA0000, ws=PW, wsb=1 << 20):
+         dq=0x80000, dk=0x90000, dv=0xA0000, ws=WS, wsb=1 << 20):
     return lib.bra_attend_backward(q, kk, v, o, do, idx, dq, dk, dv, B, H, W, C, heads, S, k, dt, ws, wsb, None)
 
 
-@pytest.mark.parametrize("call", [_fwd, _route, _attend, _fwd_lce, _attend_lce, _bwd])
+@pytest.mark.parametrize("call", [_fwd, _route, _fwd_alloc, _route_alloc, _attend, _fwd_lce, _attend_lce, _bwd])
 @pytest.mark.parametrize(
     "kwargs,status",
     [
@@ -119,7 +134,7 @@ def test_host_validation(lib, call, kwargs, status):
     assert call(lib, **kwargs) == status
 
 
-@pytest.mark.parametrize("call", [_fwd, _attend, _fwd_lce, _attend_lce, _bwd])
+@pytest.mark.parametrize("call", [_fwd, _fwd_alloc, _attend, _fwd_lce, _attend_lce, _bwd])
 @pytest.mark.parametrize(
     "kwargs,status",
     [
@@ -165,7 +180,7 @@ def _qkv(lib, B=1, H=16, W=16, C=32, S=4, dt=0, x=P, w=P2, b=0, q=P3, k=P4, v=PW
 
 
 def _fqkv(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, x=P, w=P2, b=0, q=P3, kk=P4, v=PW, o=PF,
-          ws=0xC0000, wsb=1 << 20):
+          ws=WS, wsb=1 << 20):
     return lib.bra_forward_qkv(x, w, b, q, kk, v, o, B, H, W, C, heads, S, k, dt, ws, wsb, None)
 
 
@@ -201,7 +216,8 @@ def test_projection_pooled_outputs_validation(lib):
 
 
 @pytest.mark.parametrize("kwargs", [dict(dq=P), dict(dk=P3), dict(dv=PF), dict(dq=0x90000), dict(dk=0xA0000),
-                                    dict(do=0), dict(idx=0), dict(idx=PB + 2), dict(dv=0xA0000 + 8)])
+                                    dict(do=0), dict(idx=0), dict(idx=PB + 2), dict(dv=0xA0000 + 8),
+                                    dict(dq=P + 256), dict(dk=0x80000 + MAP - 16), dict(dv=PF + 16)])
 def test_backward_validation(lib, kwargs):
     assert _bwd(lib, **kwargs) == EINVAL
 
@@ -218,8 +234,30 @@ def test_backward_workspace_bytes(lib):
 @pytest.mark.parametrize("call", [_fwd, _route, _fwd_lce, _bwd])
 def test_workspace_validation(lib, call):
     assert call(lib, wsb=16) == EINVAL           # too small
-    assert call(lib, ws=PW + 64) == EINVAL       # not 256-byte aligned
+    assert call(lib, ws=WS + 64) == EINVAL       # not 256-byte aligned
     assert call(lib, ws=0, wsb=16) == EINVAL     # size without a buffer
+    assert call(lib, ws=P2 - 256) == EINVAL      # workspace runs into K (1 MiB from 0x1ff00)
+
+
+@pytest.mark.parametrize("call", [_fwd, _route])
+def test_workspace_forms_need_a_workspace(lib, call):
+    # the *_ws entry points never allocate: no buffer is an error
+    assert call(lib, ws=0, wsb=0) == EINVAL
+
+
+
+@pytest.mark.parametrize("call", [_fwd, _fwd_alloc, _attend, _fwd_lce, _attend_lce])
+@pytest.mark.parametrize("o", [P + 16, P2 + MAP - 16, P3 - MAP + 16])
+def test_output_may_not_partly_overlap_inputs(lib, call, o):
+    assert call(lib, o=o) == EINVAL
+
+
+def test_index_table_may_not_overlap_output_or_inputs(lib):
+    assert _attend(lib, idx=PW + 64) == EINVAL          # idx inside O
+    assert _attend_lce(lib, idx=PW + 64) == EINVAL
+    assert _route(lib, idx=P + 64) == EINVAL            # idx inside Q
+    assert _route_alloc(lib, idx=P2 + 1024) == EINVAL   # idx inside K
+    assert _bwd(lib, idx=0x80000 + 64) == EINVAL        # idx inside dQ
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -98,23 +98,31 @@ def test_unrouted_tokens_get_zero_key_and_value_gradients():
         parity.assert_grad_close(_f64(out.cpu()), r, "bf16", name)
 
 
-def test_bad_route_entry_gives_nan_dq_of_its_region_only():
-    w = wl.custom(1, 14, 14, 64, 2, 7, 2, "bf16", seed=82)
+BAD_ROWS = [wl.custom(1, 14, 14, 64, 2, 7, 2, "bf16", seed=82),   # at most 64 keys per query
+            wl.custom(1, 28, 28, 64, 2, 7, 6, "bf16", seed=83)]   # several 64-key chunks
+
+
+@pytest.mark.parametrize("w", BAD_ROWS, ids=[w.name for w in BAD_ROWS])
+@pytest.mark.parametrize("kind", ["out_of_range", "repeated"])
+def test_bad_route_row_gives_nan_dq_of_its_region_only(w, kind):
+    """A routing row with an entry outside [0, S*S), or with a repeated entry
+    (which bra_route never writes), gives NaN dQ for its region's queries and
+    leaves them out of dK and dV."""
     q, k, v = (t.to(DEV) for t in wl.make_inputs(w))
     g = wl.make_grad_output(w).to(DEV)
     idx = bra.route(q, k, w.S, w.topk)
     o = bra.attend(q, k, v, idx, w.heads, w.S)
     bad = idx.clone()
-    bad[0, 5, 1] = 49
+    bad[0, 5, 1] = w.R if kind == "out_of_range" else bad[0, 5, 0]
     dq, dk, dv = bra.attend_backward(q, k, v, o, g, bad, w.heads, w.S)
     torch.cuda.synchronize()
-    rq = dq.float().cpu().reshape(1, 7, 2, 7, 2, 64).permute(0, 1, 3, 2, 4, 5).reshape(1, 49, 4, 64)
-    assert torch.isnan(rq[0, 5]).all()
-    keep = [r for r in range(49) if r != 5]
-    assert not torch.isnan(rq[0, keep]).any()
+    ys, xs = (torch.as_tensor(a) for a in O.region_token_coords(w.H, w.W, w.S, 5))
+    dqf = dq.float().cpu()
+    assert torch.isnan(dqf[0, ys, xs]).all()
+    dqf[0, ys, xs] = 0
+    assert not torch.isnan(dqf).any()
     assert not torch.isnan(dk).any() and not torch.isnan(dv).any()
     # the bad region's queries are left out of dK, dV: the oracle without them
-    routes = bad.cpu().numpy().copy()
     ref = O.attend_backward(_f64(q.cpu()), _f64(k.cpu()), _f64(v.cpu()), idx.cpu().numpy(),
                             _f64(g.cpu()) * _region_mask(w, 5), w.heads, w.S)
     for name, out, r in zip(("dK", "dV"), (dk, dv), ref[1:]):

@@ -347,3 +347,82 @@ def test_concurrent_calls_from_threads():
     for i in range(len(shapes)):
         for r in range(8):
             assert torch.equal(got[i][r], ref[i]), (shapes[i].name, r)
+
+
+@pytest.mark.parametrize("w", [wl.WORKLOADS[0], wl.WORKLOADS[2], wl.WORKLOADS[4],
+                               wl.custom(2, 16, 16, 48, 1, 16, 9, "bf16", seed=28)],
+                         ids=lambda w: w.name)
+def test_workspace_forms_are_bit_identical(w):
+    """bra_route / bra_forward (stream-ordered scratch of their own) against
+    bra_route_ws / bra_forward_ws (the caller's workspace): the same bits."""
+    q, k, v = _gpu(*wl.make_inputs(w))
+    nbytes = bra.workspace_bytes(w.B, w.H, w.W, w.C, w.S, w.topk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    idx_a = bra.route(q, k, w.S, w.topk)
+    idx_b = bra.route_ws(q, k, w.S, w.topk, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_b)
+    if w.C % w.heads == 0 and w.C // w.heads == 32:
+        o_a = bra.forward(q, k, v, w.heads, w.S, w.topk)
+        o_b = bra.forward_ws(q, k, v, w.heads, w.S, w.topk, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b)
+
+
+@pytest.mark.parametrize("w", wl.WORKLOADS, ids=[w.name for w in wl.WORKLOADS])
+def test_pooled_means_match_oracle(w):
+    """The region means Q^r, K^r that the pool kernel leaves in the workspace
+    (offsets 0 and align256(4 B S^2 C)) against the oracle's fp64 means of the
+    exact inputs: the summary's region-average identity rests on them, and
+    routing alone cannot see a common scale error of both. Bound: the fp32
+    summation error of n terms, n 2^-24 mean|x|, plus 2e-6."""
+    q, k, v = wl.make_inputs(w)
+    qd, kd, vd = _gpu(q, k, v)
+    nbytes = bra.workspace_bytes(w.B, w.H, w.W, w.C, w.S, w.topk)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    bra.forward_ws(qd, kd, vd, w.heads, w.S, w.topk, ws)
+    torch.cuda.synchronize()
+    pooled = -(-4 * w.B * w.R * w.C // 256) * 256
+    for name, t, off in (("Q^r", q, 0), ("K^r", k, pooled)):
+        got = ws[off: off + 4 * w.B * w.R * w.C].view(torch.float32).reshape(w.B, w.R, w.C).cpu().double().numpy()
+        x = _f64(t)
+        ref = O.region_mean(x, w.S)
+        mabs = O.region_mean(np.abs(x), w.S)
+        bound = 2e-6 + w.n * 2.0 ** -24 * mabs
+        err = np.abs(got - ref)
+        assert np.all(err <= bound), f"{w.name} {name}: worst excess {float((err - bound).max()):.3e}"
+        print(f"[means] {w.name} {name}: max-abs {float(err.max()):.2e}", flush=True)
+
+
+# Non-finite inputs are outside the method's definition, but the table must
+# still be well formed: every slot written with a distinct region index, and
+# the same bits on every call. The vector route form (C not a multiple of 32,
+# or more than 64 regions) orders NaN affinities with the same keys as the
+# matrix-core form.
+NAN_ROUTE = [
+    wl.custom(1, 16, 16, 48, 1, 16, 9, "bf16", seed=29),   # 256 regions
+    wl.custom(2, 14, 14, 40, 1, 7, 4, "f32", seed=30),     # C = 40
+    wl.custom(2, 14, 14, 64, 2, 7, 4, "bf16", seed=31),    # matrix-core form
+]
+
+
+@pytest.mark.parametrize("w", NAN_ROUTE, ids=[w.name for w in NAN_ROUTE])
+def test_nan_token_still_writes_every_routing_slot(w):
+    q, k, _ = wl.make_inputs(w)
+    q[0, 1, 1, :] = float("nan")   # a token of region 0: Q^r[0, 0] is NaN, so is row 0
+    k[0, 5, 3, :] = float("nan")   # every row has one NaN candidate
+    qd, kd = _gpu(q, k)
+    a = torch.full((w.B, w.R, w.topk), -7, dtype=torch.int32, device=DEV)
+    b = torch.full((w.B, w.R, w.topk), -9, dtype=torch.int32, device=DEV)
+    bra.route(qd, kd, w.S, w.topk, out=a)
+    bra.route(qd, kd, w.S, w.topk, out=b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    t = a.cpu().numpy()
+    assert t.min() >= 0 and t.max() < w.R
+    for row in t.reshape(-1, w.topk):
+        assert len(set(row.tolist())) == w.topk
+    # image 1 has no NaN: it routes as the oracle does
+    if w.B > 1:
+        A = _oracle_affinity(_f64(q[1:]), _f64(k[1:]), w.S)
+        assert parity.exact_route_mismatches(O.topk_route(A, w.topk), t[1:]) == 0

@@ -1,5 +1,7 @@
 """Seeded input generators: determinism, shapes, dtypes and the clustered recipe."""
 
+import re
+
 import torch
 
 from vision_transformer_dynamic_amd import workloads as wl
@@ -40,9 +42,10 @@ def test_clustered_tokens_share_their_region_mean():
 
 def test_bench_names_the_dispatched_attention_kernel():
     """bench.py labels its roofline with the attention kernel the library
-    dispatches: the per-region kernel at stage 1 and for fp32, the
-    image-resident kernel at the 28x28 and 14x14 stage shapes, the chunked
-    kernel at the dense shape (more than 64 keys per query)."""
+    dispatches (bra_attend_kernel, the dispatch decision itself): the
+    per-region kernel at stage 1 and for fp32, the image-resident kernel at
+    the 28x28 and 14x14 stage shapes, the chunked kernel at the dense shape
+    (more than 64 keys per query)."""
     import bench
     names = [bench.attention_kernel_name(w) for w in wl.WORKLOADS]
     assert names == ["attend_head_kernel", "attend_head_kernel", "attend_image_kernel",
@@ -50,3 +53,37 @@ def test_bench_names_the_dispatched_attention_kernel():
     # too few (image, head) pairs, or regions not a multiple of 4 tokens
     assert bench.attention_kernel_name(wl.custom(2, 28, 28, 128, 4, 7, 4)) == "attend_head_kernel"
     assert bench.attention_kernel_name(wl.custom(64, 21, 21, 64, 2, 7, 4)) == "attend_head_kernel"
+
+
+def _profile_traces():
+    """Committed kernel-trace summaries: {workload name: text}."""
+    import os
+    import re
+    root = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+    out = {}
+    for name in sorted(os.listdir(root)):
+        if name.endswith("_kernel_trace.md"):
+            text = open(os.path.join(root, name)).read()
+            m = re.search(r"^workload: (\S+)$", text, flags=re.M)
+            if m:
+                out[m.group(1)] = text
+    return out
+
+
+def test_profiled_kernels_are_the_dispatched_ones():
+    """Each committed kernel trace of a workload lists the attention kernel
+    that the library's dispatch names for it, and no other attention kernel."""
+    import bench
+    traces = _profile_traces()
+    assert traces, "no kernel trace under profiles/ names its workload"
+    kinds = ("attend_head_kernel", "attend_image_kernel", "attend_kernel")
+    for w in wl.WORKLOADS:
+        if w.name not in traces:
+            continue
+        text = traces[w.name]
+        want = bench.attention_kernel_name(w)
+        assert want in text, (w.name, want)
+        for other in kinds:
+            if other != want:
+                # attend_kernel is a prefix-free match only as a whole word
+                assert not re.search(r"\b" + other + r"I", text), (w.name, other)

@@ -6,9 +6,14 @@ computation runs in the library's HIP kernels. PyTorch supplies device memory
 and the current stream. If the library has not been built, every call raises
 ``RuntimeError``; there is no fallback.
 
+    pool(q, k, S)                                      -> (q_r, k_r) region means [B, S*S, C] float32
+    route_pooled(q_r, k_r, S, topk)                    -> idx from given region means
+    attend_kernel(B, H, W, C, heads, S, topk, dtype)   -> name of the attention kernel launched
     route(q, k, S, topk)                               -> idx [B, S*S, topk] int32
+    route_ws(q, k, S, topk, workspace)                 -> the same, in a caller workspace
     attend(q, k, v, idx, heads, S)                     -> o   [B, H, W, C]
     forward(q, k, v, heads, S, topk)                   -> o   [B, H, W, C]
+    forward_ws(q, k, v, heads, S, topk, workspace)     -> the same, in a caller workspace
     attend_lce(q, k, v, idx, weight, bias, heads, S)   -> o + 5x5 depthwise conv of v
     forward_lce(q, k, v, weight, bias, heads, S, topk) -> o + 5x5 depthwise conv of v
     attend_backward(q, k, v, o, do, idx, heads, S)     -> (dq, dk, dv), routing held fixed
@@ -32,9 +37,14 @@ __all__ = [
     "library_path",
     "load_library",
     "workspace_bytes",
+    "attend_kernel",
+    "pool",
+    "route_pooled",
     "route",
+    "route_ws",
     "attend",
     "forward",
+    "forward_ws",
     "attend_lce",
     "forward_lce",
     "attend_backward",
@@ -51,8 +61,8 @@ BRA_BF16 = 1
 BRA_OK, BRA_EINVAL, BRA_EUNSUPPORTED, BRA_EHIP, BRA_ENOMEM = range(5)
 
 # Every symbol include/bra.h declares.
-EXPORTS = ("bra_status_string", "bra_workspace_bytes", "bra_route", "bra_attend", "bra_forward",
-           "bra_attend_lce", "bra_forward_lce", "bra_backward_workspace_bytes", "bra_attend_backward",
+EXPORTS = ("bra_status_string", "bra_attend_kernel", "bra_workspace_bytes", "bra_pool", "bra_route_pooled",
+           "bra_route", "bra_route_ws", "bra_attend", "bra_forward", "bra_forward_ws", "bra_attend_lce", "bra_forward_lce", "bra_backward_workspace_bytes", "bra_attend_backward",
            "bra_qkv_pool", "bra_forward_qkv")
 
 _lib = None
@@ -87,12 +97,22 @@ def load_library():
     lib.bra_status_string.argtypes = [i32]
     lib.bra_workspace_bytes.restype = sz
     lib.bra_workspace_bytes.argtypes = [i32] * 6
+    lib.bra_attend_kernel.restype = ctypes.c_char_p
+    lib.bra_attend_kernel.argtypes = [i32] * 7 + [i32, i32]
+    lib.bra_pool.restype = i32
+    lib.bra_pool.argtypes = [vp] * 4 + [i32] * 5 + [i32, vp]
+    lib.bra_route_pooled.restype = i32
+    lib.bra_route_pooled.argtypes = [vp] * 3 + [i32] * 4 + [vp]
     lib.bra_route.restype = i32
-    lib.bra_route.argtypes = [vp, vp, vp] + [i32] * 6 + [i32, vp, sz, vp]
+    lib.bra_route.argtypes = [vp, vp, vp] + [i32] * 6 + [i32, vp]
+    lib.bra_route_ws.restype = i32
+    lib.bra_route_ws.argtypes = [vp, vp, vp] + [i32] * 6 + [i32, vp, sz, vp]
     lib.bra_attend.restype = i32
     lib.bra_attend.argtypes = [vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
     lib.bra_forward.restype = i32
-    lib.bra_forward.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [i32, vp, sz, vp]
+    lib.bra_forward.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
+    lib.bra_forward_ws.restype = i32
+    lib.bra_forward_ws.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [i32, vp, sz, vp]
     lib.bra_attend_lce.restype = i32
     lib.bra_attend_lce.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
     lib.bra_forward_lce.restype = i32
@@ -157,23 +177,89 @@ def _workspace(q: torch.Tensor, S: int, topk: int, workspace):
     need = workspace_bytes(B, H, W, C, S, topk)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
-        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes")
+    if (workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous()
+            or workspace.device != q.device):
+        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on q's device")
     return workspace, need
 
 
-def route(q: torch.Tensor, k: torch.Tensor, S: int, topk: int, out=None, workspace=None) -> torch.Tensor:
-    """Routing table [B, S*S, topk] int32 (descending affinity, lower index on ties)."""
+def attend_kernel(B: int, H: int, W: int, C: int, heads: int, S: int, topk: int, dtype: torch.dtype,
+                  with_lce: bool = False) -> str:
+    """Name of the attention kernel bra_attend (or bra_attend_lce) launches
+    for these sizes, as a profiler lists it."""
+    code = BRA_F32 if dtype == torch.float32 else BRA_BF16 if dtype == torch.bfloat16 else -1
+    name = load_library().bra_attend_kernel(B, H, W, C, heads, S, topk, code, int(bool(with_lce)))
+    if name is None:
+        raise ValueError("invalid or unsupported sizes for BRA")
+    return name.decode()
+
+
+def _means_check(t: torch.Tensor, B: int, R: int, C: int, dev):
+    if t.dtype != torch.float32 or t.shape != (B, R, C) or not t.is_contiguous() or t.device != dev:
+        raise ValueError("region means must be contiguous float32 [B, S*S, C] tensors on the maps' device")
+
+
+def pool(q: torch.Tensor, k: torch.Tensor, S: int, out=None):
+    """Region means (q_r, k_r), float32 [B, S*S, C] (bra_pool)."""
     lib = load_library()
     _check_maps(q, k)
     B, H, W, C = q.shape
     if out is None:
+        out = tuple(torch.empty((B, S * S, C), dtype=torch.float32, device=q.device) for _ in range(2))
+    qr, kr = out
+    for t in (qr, kr):
+        _means_check(t, B, S * S, C, q.device)
+    _check(lib.bra_pool(q.data_ptr(), k.data_ptr(), qr.data_ptr(), kr.data_ptr(), B, H, W, C, S,
+                        _dtype_code(q), _stream(q.device)))
+    return qr, kr
+
+
+def route_pooled(qr: torch.Tensor, kr: torch.Tensor, S: int, topk: int, out=None) -> torch.Tensor:
+    """Routing table from given region means (bra_route_pooled)."""
+    lib = load_library()
+    if qr.dim() != 3:
+        raise ValueError("region means must be [B, S*S, C]")
+    B, R, C = qr.shape
+    for t in (qr, kr):
+        _means_check(t, B, S * S, C, qr.device)
+    out = _route_out(qr, S, topk, out)
+    _check(lib.bra_route_pooled(qr.data_ptr(), kr.data_ptr(), out.data_ptr(), B, S, C, topk, _stream(qr.device)))
+    return out
+
+
+def _route_out(q, S, topk, out):
+    B = q.shape[0]
+    if out is None:
         out = torch.empty((B, S * S, topk), dtype=torch.int32, device=q.device)
-    if out.dtype != torch.int32 or not out.is_contiguous() or out.shape != (B, S * S, topk):
-        raise ValueError("out must be a contiguous int32 [B, S*S, topk] tensor")
-    ws, nbytes = _workspace(q, S, topk, workspace)
+    if out.dtype != torch.int32 or not out.is_contiguous() or out.shape != (B, S * S, topk) or out.device != q.device:
+        raise ValueError("out must be a contiguous int32 [B, S*S, topk] tensor on q's device")
+    return out
+
+
+def route(q: torch.Tensor, k: torch.Tensor, S: int, topk: int, out=None, workspace=None) -> torch.Tensor:
+    """Routing table [B, S*S, topk] int32 (descending affinity, lower index on
+    ties). With a workspace this is bra_route_ws; without, bra_route, which
+    allocates its scratch stream-ordered."""
+    if workspace is not None:
+        return route_ws(q, k, S, topk, workspace, out=out)
+    lib = load_library()
+    _check_maps(q, k)
+    B, H, W, C = q.shape
+    out = _route_out(q, S, topk, out)
     _check(lib.bra_route(q.data_ptr(), k.data_ptr(), out.data_ptr(), B, H, W, C, S, topk,
-                         _dtype_code(q), ws.data_ptr(), nbytes, _stream(q.device)))
+                         _dtype_code(q), _stream(q.device)))
+    return out
+
+
+def route_ws(q: torch.Tensor, k: torch.Tensor, S: int, topk: int, workspace: torch.Tensor, out=None) -> torch.Tensor:
+    """route() in a caller workspace of workspace_bytes(...) bytes (bra_route_ws)."""
+    lib = load_library()
+    _check_maps(q, k)
+    B, H, W, C = q.shape
+    out = _route_out(q, S, topk, out)
+    ws, nbytes = _workspace(q, S, topk, workspace)
+    _check(lib.bra_route_ws(q.data_ptr(), k.data_ptr(), out.data_ptr(), B, H, W, C, S, topk,
+                            _dtype_code(q), ws.data_ptr(), nbytes, _stream(q.device)))
     return out
 
 
@@ -196,7 +282,25 @@ def attend(q, k, v, idx: torch.Tensor, heads: int, S: int, out=None) -> torch.Te
 
 
 def forward(q, k, v, heads: int, S: int, topk: int, out=None, workspace=None) -> torch.Tensor:
-    """Full BRA forward (without the local-context dwconv term)."""
+    """Full BRA forward (without the local-context dwconv term). With a
+    workspace this is bra_forward_ws; without, bra_forward, which allocates
+    its scratch stream-ordered."""
+    if workspace is not None:
+        return forward_ws(q, k, v, heads, S, topk, workspace, out=out)
+    lib = load_library()
+    _check_maps(q, k, v)
+    B, H, W, C = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_maps(q, out)
+    _check(lib.bra_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           B, H, W, C, heads, S, topk, _dtype_code(q), _stream(q.device)))
+    return out
+
+
+def forward_ws(q, k, v, heads: int, S: int, topk: int, workspace: torch.Tensor, out=None) -> torch.Tensor:
+    """forward() in a caller workspace of workspace_bytes(...) bytes
+    (bra_forward_ws); the routing table is left in it."""
     lib = load_library()
     _check_maps(q, k, v)
     B, H, W, C = q.shape
@@ -204,9 +308,9 @@ def forward(q, k, v, heads: int, S: int, topk: int, out=None, workspace=None) ->
         out = torch.empty_like(q)
     _check_maps(q, out)
     ws, nbytes = _workspace(q, S, topk, workspace)
-    _check(lib.bra_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                           B, H, W, C, heads, S, topk, _dtype_code(q),
-                           ws.data_ptr(), nbytes, _stream(q.device)))
+    _check(lib.bra_forward_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              B, H, W, C, heads, S, topk, _dtype_code(q),
+                              ws.data_ptr(), nbytes, _stream(q.device)))
     return out
 
 

@@ -22,6 +22,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libbra.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["pool.hip", "route.hip", "attend.hip", "lce.hip", "backward.hip", "qkv.hip", "bra_api.hip"]
+# achievable-peak probes of the benchmark: a library of their own
+PEAK_LIB_NAME = "libbra_peak.so"
+PEAK_LIB_PATH = os.path.join(PKG, PEAK_LIB_NAME)
+PEAK_SOURCES = ["peak.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -64,29 +68,36 @@ def _check_resources(report: str, src: str):
             raise RuntimeError(f"{src}: kernel {current} has {m.group(1)} = {m.group(2)}")
 
 
+def _link(objs, tmp, name, dest):
+    tmp_lib = os.path.join(tmp, name)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp_lib, *objs])
+    staged = dest + ".tmp"
+    shutil.copyfile(tmp_lib, staged)
+    os.replace(staged, dest)
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every HIP source and link the shared library; return its path."""
+    """Compile every HIP source and link the shared libraries (the operator's
+    and the benchmark's peak probes); return the operator library's path."""
     tmp = tempfile.mkdtemp(prefix="bra_build_")
     try:
-        objs = []
+        srcs = SOURCES + PEAK_SOURCES
+        objs = {}
         cmds = []
-        for src in SOURCES:
+        for src in srcs:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            objs.append(obj)
+            objs[src] = obj
             cmds.append([HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage",
                          "-c", os.path.join(CSRC, src), "-o", obj])
         with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-            for src, out in zip(SOURCES, ex.map(_run, cmds)):
+            for src, out in zip(srcs, ex.map(_run, cmds)):
                 _check_resources(out, src)
                 if verbose:
                     for line in out.splitlines():
                         if "remark" in line and ("Name" in line or "VGPRs:" in line or "Occupancy" in line):
                             print(line.split("remark: ")[-1], file=sys.stderr)
-        tmp_lib = os.path.join(tmp, LIB_NAME)
-        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp_lib, *objs])
-        staged = LIB_PATH + ".tmp"
-        shutil.copyfile(tmp_lib, staged)
-        os.replace(staged, LIB_PATH)
+        _link([objs[s_] for s_ in SOURCES], tmp, LIB_NAME, LIB_PATH)
+        _link([objs[s_] for s_ in PEAK_SOURCES], tmp, PEAK_LIB_NAME, PEAK_LIB_PATH)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
     return LIB_PATH

@@ -1211,16 +1211,32 @@ hipError_t launch_image(const ImgLaunch& L, int B, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+
+// The local context term is fused into the single-chunk kernel for bf16
+// regions of 16 to 64 tokens (at most 8 x 8). For smaller regions the halo
+// is several times the region (6 x 6 positions around 2 x 2) and the
+// separate pass after the attention kernel measured faster (14x14 map,
+// 2 x 2 regions: 38 us for attention + pass vs 47 us fused).
+bool fuse_lce(const Shape& s, int dtype, bool lce) {
+  return lce && dtype == kBF16 && s.kv <= KC && s.sh <= 8 && s.sw <= 8 && s.n >= 16;
+}
+
+}  // namespace
+
+const char* attend_kernel_name(const Shape& s, int dtype, bool lce) {
+  if (!fuse_lce(s, dtype, lce) && dtype == kBF16) {
+    ImgLaunch L;
+    if (plan_image(s, &L)) return "attend_image_kernel";
+  }
+  return s.kv <= KC ? "attend_head_kernel" : "attend_kernel";
+}
+
 hipError_t launch_attend(const void* Q, const void* K, const void* V,
                          const int32_t* idx, const void* lce_w, const void* lce_b, void* O,
                          const Shape& s, int dtype, hipStream_t stream) {
   const bool lce = lce_w != nullptr;
-  // The local context term is fused into the single-chunk kernel for bf16
-  // regions of 16 to 64 tokens (at most 8 x 8). For smaller regions the halo
-  // is several times the region (6 x 6 positions around 2 x 2) and the
-  // separate pass after the attention kernel measured faster (14x14 map,
-  // 2 x 2 regions: 38 us for attention + pass vs 47 us fused).
-  const bool fuse = lce && dtype == kBF16 && s.kv <= KC && s.sh <= 8 && s.sw <= 8 && s.n >= 16;
+  const bool fuse = fuse_lce(s, dtype, lce);
   if (!fuse && dtype == kBF16) {
     ImgLaunch L;
     if (plan_image(s, &L)) {

@@ -15,10 +15,11 @@
 // Three steps, all deterministic (no atomics on gradients):
 //  1. inverse_table: per image, the inverse routing table - for every key
 //     region, the ascending list of query regions whose rows hold it. A row
-//     with an entry outside [0, S*S) is marked bad and left out. With at most
-//     64 keys per query and 64 regions it runs as B leading workgroups of the
-//     dQ launch (only step 3 needs it); otherwise bwd_routes_kernel, a launch
-//     of its own.
+//     with an entry outside [0, S*S), or a repeated entry, is marked bad and
+//     left out (the dQ kernels give its queries NaN). With at most 64 keys
+//     per query and 64 regions it runs as B leading workgroups of the dQ
+//     launch (only step 3 needs it); otherwise bwd_routes_kernel, a launch of
+//     its own.
 //  2. dQ: the forward's transposed products (S^T = K Q^T, dP^T = V dO^T,
 //     dQ^T = K^T dZ^T with K^T through LDS), D from O and dO, and the base-2
 //     log-sum-exp of every query, written for kernel 3. With at most 64 keys
@@ -102,6 +103,13 @@ __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds) {
       atomicOr(&mask[i * nw + (r >> 5)], 1u << (r & 31));
   }
   __syncthreads();
+  // a row with a repeated entry holds fewer than k distinct regions: bad too
+  for (int i = tid; i < R; i += nt) {
+    int cnt = 0;
+    for (int e = 0; e < nw; ++e) cnt += __popc(mask[i * nw + e]);
+    if (cnt != k) rowbad[i] = 1;
+  }
+  __syncthreads();
   // wave w compacts the lists of key regions w, w + nwaves, ...
   const int wave = tid >> 6, lane = tid & 63, nwaves = nt >> 6;
   const uint64_t below = (uint64_t(1) << lane) - 1;
@@ -179,6 +187,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int tok[KC];
   __shared__ int rb[kMaxRegions];
+  __shared__ uint32_t rmask[kMaxRegions / 32];  // the row's regions, for the repeated-entry check
   __shared__ int sbad;
 
   const int tid = threadIdx.x;
@@ -205,12 +214,14 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
 
   // the routed regions' corners
   if (tid == 0) sbad = 0;
+  if (tid < kMaxRegions / 32) rmask[tid] = 0u;
   __syncthreads();
   for (int j = tid; j < p.topk; j += blockDim.x) {
     const int r = p.idx[((int64_t)b * p.R + i) * p.topk + j];
     const bool ok = r >= 0 && r < p.R;
     rb[j] = corner_of(p, ok ? r : 0);
     if (!ok) sbad = 1;
+    else atomicOr(&rmask[r >> 5], 1u << (r & 31));
   }
 
   // the wave's queries: B operands of q and dO, and D = dO . O per query
@@ -237,7 +248,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
   }
   const float Dq = wave_sum_groups(dpart);
   __syncthreads();
-  const bool bad = sbad;
+  // an entry outside [0, S*S), or a repeated one (fewer distinct regions than topk)
+  int distinct = 0;
+#pragma unroll
+  for (int e = 0; e < kMaxRegions / 32; ++e) distinct += __popc(rmask[e]);
+  const bool bad = sbad || distinct != p.topk;
   T* dQg = static_cast<T*>(p.dQ) + img;
   if (bad) {
     // a routing entry outside [0, S*S): gradient NaN for the region's queries
@@ -478,7 +493,18 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
 
   // the wave's key table
   const bool ok = rid >= 0 && rid < p.R;
-  const bool bad = __builtin_amdgcn_ballot_w64(lane < p.kv && !ok) != 0;  // uniform
+  bool bad = __builtin_amdgcn_ballot_w64(lane < p.kv && !ok) != 0;  // uniform
+  // a repeated entry: slot j's region (held by lane j * n, the slot's first
+  // key) is held by more than one slot's first key
+  if (p.topk > 1) {
+    int tk;
+    (void)fdiv(lane, p.div_n, &tk);
+    const bool first = lane < p.kv && tk == 0;
+    for (int j = 0; j < p.topk; ++j) {  // uniform; topk * n <= 64
+      const int rj = __builtin_amdgcn_readlane(rid, j * p.n);
+      bad |= __popcll(__builtin_amdgcn_ballot_w64(first && rid == rj)) > 1;
+    }
+  }
   int* wt = wtok + wave * KC;
   wt[lane] = lane < p.kv ? corner_of(p, ok ? rid : 0) + ktok : -1;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

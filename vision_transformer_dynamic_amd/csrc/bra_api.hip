@@ -49,19 +49,20 @@ size_t index_bytes(const Shape& s) { return align_up(sizeof(int32_t) * (size_t)s
 // Workspace: [Qr | Kr | idx], each 256-byte aligned.
 size_t workspace_for(const Shape& s) { return 2 * pooled_bytes(s) + index_bytes(s); }
 
-// Holds the workspace for one call: the caller's, or a stream-ordered one.
+// Holds the workspace for one call: the caller's, or a stream-ordered one
+// (only where `may_alloc`; the *_ws entry points never allocate).
 struct Workspace {
   char* ptr = nullptr;
   bool owned = false;
   hipStream_t stream = nullptr;
-  bra_status acquire(void* user, size_t user_bytes, size_t need, hipStream_t s) {
+  bra_status acquire(void* user, size_t user_bytes, size_t need, hipStream_t s, bool may_alloc = true) {
     stream = s;
     if (user != nullptr) {
       if (user_bytes < need || !aligned(user, kAlign)) return BRA_EINVAL;
       ptr = static_cast<char*>(user);
       return BRA_OK;
     }
-    if (user_bytes != 0) return BRA_EINVAL;
+    if (user_bytes != 0 || !may_alloc) return BRA_EINVAL;
     void* p = nullptr;
     if (hipMallocAsync(&p, need, s) != hipSuccess || p == nullptr) return BRA_ENOMEM;
     ptr = static_cast<char*>(p);
@@ -78,6 +79,19 @@ bool bad_tensor(const void* p) { return p == nullptr || !aligned(p, 16); }
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
+}
+
+// Bytes of one [B, H, W, C] map and of the routing table.
+size_t map_bytes(const Shape& s, int dtype) { return (dtype == bra::kBF16 ? 2 : 4) * (size_t)s.B * s.H * s.W * s.C; }
+size_t table_bytes(const Shape& s) { return sizeof(int32_t) * (size_t)s.B * s.R * s.topk; }
+
+// A caller workspace (ws, nbytes) must not overlap any of the tensors
+// (p[i], n[i]); a null workspace is the library's own.
+bool workspace_overlaps(const void* ws, size_t nbytes, const void* const* p, const size_t* n, int count) {
+  if (ws == nullptr) return false;
+  for (int i = 0; i < count; ++i)
+    if (p[i] != nullptr && overlaps(ws, nbytes, p[i], n[i])) return true;
+  return false;
 }
 
 // Local-context filter arguments: weight [C][5][5] (4-byte aligned), bias [C]
@@ -116,25 +130,84 @@ const char* bra_status_string(bra_status status) {
   return "unknown status";
 }
 
+const char* bra_attend_kernel(int B, int H, int W, int C, int heads, int S, int topk, bra_dtype dtype,
+                              int with_lce) {
+  Shape s;
+  if (check_shape(B, H, W, C, heads, S, topk, (int)dtype, &s) != BRA_OK) return nullptr;
+  return bra::attend_kernel_name(s, (int)dtype, with_lce != 0);
+}
+
+bra_status bra_pool(const void* Q, const void* K, float* Qr, float* Kr, int B, int H, int W, int C, int S,
+                    bra_dtype dtype, hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, -1, S, 1, (int)dtype, &s);
+  if (st != BRA_OK) return st;
+  if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(Qr) || bad_tensor(Kr)) return BRA_EINVAL;
+  const size_t mb = map_bytes(s, (int)dtype), pb = sizeof(float) * (size_t)s.B * s.R * s.C;
+  if (overlaps(Qr, pb, Kr, pb)) return BRA_EINVAL;
+  for (const void* o : {(const void*)Qr, (const void*)Kr})
+    if (overlaps(o, pb, Q, mb) || overlaps(o, pb, K, mb)) return BRA_EINVAL;
+  if (bra::launch_pool(Q, K, Qr, Kr, s, (int)dtype, stream) != hipSuccess) return BRA_EHIP;
+  return BRA_OK;
+}
+
+bra_status bra_route_pooled(const float* Qr, const float* Kr, int32_t* idx, int B, int S, int C, int topk,
+                            hipStream_t stream) {
+  Shape s;
+  // the map size does not enter the routing: a map of one token per region
+  bra_status st = check_shape(B, S, S, C, -1, S, topk, bra::kBF16, &s);  // the limits of bra_route's C
+  if (st != BRA_OK) return st;
+  if (bad_tensor(Qr) || bad_tensor(Kr)) return BRA_EINVAL;
+  if (idx == nullptr || !aligned(idx, 4)) return BRA_EINVAL;
+  const size_t pb = sizeof(float) * (size_t)s.B * s.R * s.C, tb = table_bytes(s);
+  if (overlaps(idx, tb, Qr, pb) || overlaps(idx, tb, Kr, pb)) return BRA_EINVAL;
+  if (bra::launch_route(Qr, Kr, idx, s, stream) != hipSuccess) return BRA_EHIP;
+  return BRA_OK;
+}
+
 size_t bra_workspace_bytes(int B, int H, int W, int C, int S, int topk) {
   Shape s;
   if (check_shape(B, H, W, C, -1, S, topk, bra::kBF16, &s) != BRA_OK) return 0;
   return workspace_for(s);
 }
 
-bra_status bra_route(const void* Q, const void* K, int32_t* idx,
-                     int B, int H, int W, int C, int S, int topk,
-                     bra_dtype dtype, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+bra_status route_impl(const void* Q, const void* K, int32_t* idx, int B, int H, int W, int C, int S, int topk,
+                      int dtype, void* workspace, size_t workspace_bytes, bool may_alloc, hipStream_t stream) {
   Shape s;
-  bra_status st = check_shape(B, H, W, C, -1, S, topk, (int)dtype, &s);
+  bra_status st = check_shape(B, H, W, C, -1, S, topk, dtype, &s);
   if (st != BRA_OK) return st;
   if (bad_tensor(Q) || bad_tensor(K)) return BRA_EINVAL;
   if (idx == nullptr || !aligned(idx, 4)) return BRA_EINVAL;
+  const size_t mb = map_bytes(s, dtype), tb = table_bytes(s);
+  if (overlaps(idx, tb, Q, mb) || overlaps(idx, tb, K, mb)) return BRA_EINVAL;
+  const void* ts[] = {Q, K, idx};
+  const size_t ns[] = {mb, mb, tb};
+  if (workspace_overlaps(workspace, workspace_bytes, ts, ns, 3)) return BRA_EINVAL;
   Workspace ws;
-  st = ws.acquire(workspace, workspace_bytes, 2 * pooled_bytes(s), stream);
+  st = ws.acquire(workspace, workspace_bytes, 2 * pooled_bytes(s), stream, may_alloc);
   if (st != BRA_OK) return st;
-  return enqueue_route(Q, K, idx, s, (int)dtype, ws.ptr, stream);
+  return enqueue_route(Q, K, idx, s, dtype, ws.ptr, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+bra_status bra_route(const void* Q, const void* K, int32_t* idx,
+                     int B, int H, int W, int C, int S, int topk,
+                     bra_dtype dtype, hipStream_t stream) {
+  return route_impl(Q, K, idx, B, H, W, C, S, topk, (int)dtype, nullptr, 0, true, stream);
+}
+
+bra_status bra_route_ws(const void* Q, const void* K, int32_t* idx,
+                        int B, int H, int W, int C, int S, int topk,
+                        bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return route_impl(Q, K, idx, B, H, W, C, S, topk, (int)dtype, workspace, workspace_bytes, false, stream);
 }
 
 }  // extern "C"
@@ -150,7 +223,10 @@ bra_status attend_impl(const void* Q, const void* K, const void* V, const int32_
   if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(V) || bad_tensor(O))
     return BRA_EINVAL;
   if (idx == nullptr || !aligned(idx, 4)) return BRA_EINVAL;
-  if (O == Q || O == K || O == V) return BRA_EINVAL;
+  const size_t mb = map_bytes(s, dtype);
+  if (overlaps(O, mb, Q, mb) || overlaps(O, mb, K, mb) || overlaps(O, mb, V, mb) ||
+      overlaps(O, mb, idx, table_bytes(s)))
+    return BRA_EINVAL;
   if (weight != nullptr && (st = check_lce(weight, bias, O, s, dtype)) != BRA_OK) return st;
   if (bra::launch_attend(Q, K, V, idx, weight, bias, O, s, dtype, stream) != hipSuccess) return BRA_EHIP;
   return BRA_OK;
@@ -158,16 +234,23 @@ bra_status attend_impl(const void* Q, const void* K, const void* V, const int32_
 
 bra_status forward_impl(const void* Q, const void* K, const void* V, const void* weight, const void* bias, void* O,
                         int B, int H, int W, int C, int heads, int S, int topk, int dtype, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        size_t workspace_bytes, bool may_alloc, hipStream_t stream) {
   Shape s;
   bra_status st = check_shape(B, H, W, C, heads, S, topk, dtype, &s);
   if (st != BRA_OK) return st;
   if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(V) || bad_tensor(O))
     return BRA_EINVAL;
-  if (O == Q || O == K || O == V) return BRA_EINVAL;
+  const size_t mb = map_bytes(s, dtype);
+  if (overlaps(O, mb, Q, mb) || overlaps(O, mb, K, mb) || overlaps(O, mb, V, mb)) return BRA_EINVAL;
   if (weight != nullptr && (st = check_lce(weight, bias, O, s, dtype)) != BRA_OK) return st;
+  {
+    const size_t esz = dtype == bra::kBF16 ? 2 : 4;
+    const void* ts[] = {Q, K, V, O, weight, bias};
+    const size_t ns[] = {mb, mb, mb, mb, esz * 25 * (size_t)s.C, esz * (size_t)s.C};
+    if (workspace_overlaps(workspace, workspace_bytes, ts, ns, 6)) return BRA_EINVAL;
+  }
   Workspace ws;
-  st = ws.acquire(workspace, workspace_bytes, workspace_for(s), stream);
+  st = ws.acquire(workspace, workspace_bytes, workspace_for(s), stream, may_alloc);
   if (st != BRA_OK) return st;
   int32_t* idx = reinterpret_cast<int32_t*>(ws.ptr + 2 * pooled_bytes(s));
   st = enqueue_route(Q, K, idx, s, dtype, ws.ptr, stream);
@@ -189,10 +272,17 @@ bra_status bra_attend(const void* Q, const void* K, const void* V,
 
 bra_status bra_forward(const void* Q, const void* K, const void* V, void* O,
                        int B, int H, int W, int C, int heads, int S, int topk,
-                       bra_dtype dtype, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+                       bra_dtype dtype, hipStream_t stream) {
+  return forward_impl(Q, K, V, nullptr, nullptr, O, B, H, W, C, heads, S, topk, (int)dtype, nullptr, 0, true,
+                      stream);
+}
+
+bra_status bra_forward_ws(const void* Q, const void* K, const void* V, void* O,
+                          int B, int H, int W, int C, int heads, int S, int topk,
+                          bra_dtype dtype, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   return forward_impl(Q, K, V, nullptr, nullptr, O, B, H, W, C, heads, S, topk, (int)dtype, workspace,
-                      workspace_bytes, stream);
+                      workspace_bytes, false, stream);
 }
 
 bra_status bra_attend_lce(const void* Q, const void* K, const void* V,
@@ -210,7 +300,7 @@ bra_status bra_forward_lce(const void* Q, const void* K, const void* V,
                            hipStream_t stream) {
   if (weight == nullptr) return BRA_EINVAL;
   return forward_impl(Q, K, V, weight, bias, O, B, H, W, C, heads, S, topk, (int)dtype, workspace,
-                      workspace_bytes, stream);
+                      workspace_bytes, true, stream);
 }
 
 }  // extern "C"
@@ -233,15 +323,23 @@ bra_status bra_attend_backward(const void* Q, const void* K, const void* V, cons
   if (st != BRA_OK) return st;
   const void* ins[] = {Q, K, V, O, dO};
   void* outs[] = {dQ, dK, dV};
+  const size_t mb = map_bytes(s, (int)dtype), tb = table_bytes(s);
   for (const void* t : ins)
     if (bad_tensor(t)) return BRA_EINVAL;
-  for (void* t : outs) {
-    if (bad_tensor(t)) return BRA_EINVAL;
-    for (const void* u : ins)
-      if (t == u) return BRA_EINVAL;
-  }
-  if (dQ == dK || dQ == dV || dK == dV) return BRA_EINVAL;
   if (idx == nullptr || !aligned(idx, 4)) return BRA_EINVAL;
+  for (int i = 0; i < 3; ++i) {
+    if (bad_tensor(outs[i])) return BRA_EINVAL;
+    for (const void* u : ins)
+      if (overlaps(outs[i], mb, u, mb)) return BRA_EINVAL;
+    if (overlaps(outs[i], mb, idx, tb)) return BRA_EINVAL;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], mb, outs[j], mb)) return BRA_EINVAL;
+  }
+  {
+    const void* ts[] = {Q, K, V, O, dO, dQ, dK, dV, idx};
+    const size_t ns[] = {mb, mb, mb, mb, mb, mb, mb, mb, tb};
+    if (workspace_overlaps(workspace, workspace_bytes, ts, ns, 9)) return BRA_EINVAL;
+  }
   Workspace ws;
   st = ws.acquire(workspace, workspace_bytes, bra::backward_workspace_bytes(s), stream);
   if (st != BRA_OK) return st;
@@ -305,6 +403,12 @@ bra_status bra_forward_qkv(const void* X, const void* Wqkv, const void* bqkv, vo
   if (st != BRA_OK) return st;
   void* outs[] = {Q, K, V, O};
   if ((st = check_proj(X, Wqkv, bqkv, outs, 4, s, (int)dtype)) != BRA_OK) return st;
+  {
+    const size_t mb = map_bytes(s, (int)dtype), esz = dtype == BRA_BF16 ? 2 : 4;
+    const void* ts[] = {X, Wqkv, bqkv, Q, K, V, O};
+    const size_t ns[] = {mb, esz * 3 * (size_t)s.C * s.C, esz * 3 * (size_t)s.C, mb, mb, mb, mb};
+    if (workspace_overlaps(workspace, workspace_bytes, ts, ns, 7)) return BRA_EINVAL;
+  }
   Workspace ws;
   st = ws.acquire(workspace, workspace_bytes, workspace_for(s), stream);
   if (st != BRA_OK) return st;

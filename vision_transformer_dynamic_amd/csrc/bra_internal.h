@@ -83,6 +83,10 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
                          const int32_t* idx, const void* lce_w, const void* lce_b, void* O,
                          const Shape& s, int dtype, hipStream_t stream);
 
+// Name of the attention kernel launch_attend runs for this shape (the same
+// dispatch decision; the convolution pass, where there is one, follows it).
+const char* attend_kernel_name(const Shape& s, int dtype, bool lce);
+
 // O += lce(V): 5x5 depthwise convolution of V over the whole map, zero
 // padding, per-channel bias (lce_b may be null). C must be a multiple of 32.
 hipError_t launch_lce(const void* V, const void* lce_w, const void* lce_b, void* O,

@@ -21,8 +21,9 @@
 // candidates 16 (w % 4) .. +15 over channel half w / 4, its operands loaded
 // straight from memory as 16-byte vectors (one round trip for C <= 256); the
 // two halves are added in a fixed order through LDS. Each affinity becomes a
-// 64-bit key (order-preserving bits of the value, then 63 - j), so "beats" is
-// one unsigned compare; k = 1 is a wave-wide maximum of the keys. The row
+// 64-bit key (order-preserving bits of the value, then a decreasing function
+// of j), so "beats" is one unsigned compare; k = 1 is a wave-wide maximum of
+// the keys. The row
 // blocks of one image run on one XCD (xcd_item) and share its L2 copy of
 // K^r[b]; images are split over the XCDs as in the pool and attention kernels.
 //
@@ -34,8 +35,10 @@
 // the current one is used. A[i][j] is accumulated as four fused multiply-add
 // chains, one per channel residue mod 4, in increasing channel order, and
 // combined as (s0 + s1) + (s2 + s3). The query row is read as a broadcast,
-// K^r row j by lane j. Each lane counts its rank against the whole row
-// (broadcast LDS reads): R compares per candidate, independent of k.
+// K^r row j by lane j. The row's affinities become the same 64-bit keys as
+// in the matrix-core form (so both forms order NaN alike and every slot is
+// written), and each lane counts its rank against the whole row (broadcast
+// LDS reads): R compares per candidate, independent of k.
 #include "bra_internal.h"
 #include "route_common.h"
 
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(NT) void route_kernel(RouteParams p) {
   extern __shared__ __align__(16) float sm[];
   float* Ks = sm;                 // R x LDC
   float* Qs = Ks + p.R * LDC;     // RB x LDC
-  float* As = Qs + RB * LDC;      // RB x ldr
+  uint64_t* As = reinterpret_cast<uint64_t*>(Qs + RB * LDC);  // RB x ldr keys
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -138,25 +141,25 @@ __global__ __launch_bounds__(NT) void route_kernel(RouteParams p) {
     }
   }
 
-  // affinity row to LDS (the wave's own row); columns R..ldr-1 hold -inf
+  // the wave's affinity row as keys in LDS; columns R..ldr-1 hold key 0
   const int row = wave;
-  float* a = As + row * p.ldr;
+  uint64_t* a = As + row * p.ldr;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const int j = lane + 64 * u;
-    if (j < p.ldr) a[j] = j < p.R ? affinity_finish(acc[u]) : -INFINITY;
+    if (j < p.ldr) a[j] = j < p.R ? affinity_key(affinity_finish(acc[u]), j) : 0ull;
   }
   __syncthreads();
   if (row >= nrows) return;  // wave-uniform; no barrier follows
 
-  // ranks
+  // ranks (the keys are a strict total order, so every slot is written once)
   int32_t* out = p.idx + ((int64_t)b * p.R + i0 + row) * p.topk;
 #pragma unroll 1
   for (int u = 0; u < NU; ++u) {
     const int j = lane + 64 * u;
-    const float aj = j < p.R ? a[j] : -INFINITY;
-    const int rank = affinity_rank(a, p.ldr, aj, j);
-    if (j < p.R && rank < p.topk) out[rank] = j;
+    if (j >= p.R) break;
+    const int rank = key_rank(a, p.ldr, a[j]);
+    if (rank < p.topk) out[rank] = j;
   }
 }
 
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
     const uint64_t kj = keys[row][lane];
     if (p.topk == 1) {
       const uint64_t best = wave_max_key(kj);
-      if (lane == 0) out[0] = 63 - (int)(uint32_t)best;
+      if (lane == 0) out[0] = key_index(best);
     } else {
       const int rank = key_rank64(&keys[row][0], kj);
       if (lane < p.R && rank < p.topk) out[rank] = lane;
@@ -239,11 +242,12 @@ __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
 
 }  // namespace
 
-// dynamic LDS of the vector form
+// dynamic LDS of the vector form: the staged slices (floats), then the key
+// rows (16-byte aligned: R * ldc + RB * ldc floats is a multiple of 4)
 size_t route_lds_bytes(const Shape& s) {
   const int ldr = (s.R + 3) / 4 * 4;
   const int ldc = s.R <= 64 ? RouteCfg<1>::LDC : RouteCfg<4>::LDC;
-  return sizeof(float) * ((size_t)s.R * ldc + (size_t)RB * ldc + (size_t)RB * ldr);
+  return sizeof(float) * ((size_t)s.R * ldc + (size_t)RB * ldc) + sizeof(uint64_t) * (size_t)RB * ldr;
 }
 
 hipError_t launch_route(const float* Qr, const float* Kr, int32_t* idx,

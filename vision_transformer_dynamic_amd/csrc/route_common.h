@@ -29,14 +29,21 @@ __device__ inline floatx4 affinity_mfma_step(floatx4 acc, const float4 a, const 
   return acc;
 }
 
-// Order-preserving key of candidate j (< 64) with affinity a: a larger key
-// beats a smaller one exactly when the affinity is larger, or equal with a
-// lower index. -0 is folded into +0 first, so zeros tie as they compare.
+// Order-preserving key of candidate j (0 <= j < 2^16) with affinity a: a
+// larger key beats a smaller one exactly when the affinity is larger, or
+// equal with a lower index. -0 is folded into +0 first, so zeros tie as they
+// compare. Every bit pattern, NaN included, maps to a distinct key per j, so
+// the keys of a row are a strict total order and every rank is unique (a NaN
+// with the sign bit clear ranks above +inf, one with it set below -inf).
+// A key is never 0, which marks candidates past the last region.
 __device__ inline uint64_t affinity_key(float a, int j) {
   uint32_t u = __float_as_uint(a == 0.f ? 0.f : a);
   u = (u >> 31) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(63 - j);
+  return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
 }
+
+// Candidate index of a key made by affinity_key.
+__device__ inline int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 
 // the larger of a and the key with halves (lo, hi)
 __device__ inline uint64_t key_max(uint64_t a, uint32_t lo, uint32_t hi) {
@@ -104,18 +111,15 @@ __device__ inline float affinity_finish(const float4 acc) {
   return (acc.x + acc.y) + (acc.z + acc.w);
 }
 
-// Number of candidates among a[0..ldr) that rank above candidate j with
-// affinity aj: m ranks above j when a[m] > aj, or a[m] == aj and m < j (a
-// strict total order, so ranks are unique). Entries past the last region must
-// hold -inf; a is 16-byte aligned and ldr a multiple of 4.
-__device__ inline int affinity_rank(const float* a, int ldr, float aj, int j) {
+// Rank of key kj among the keys keys[0..ldr) of a row in LDS (16-byte
+// aligned, ldr a multiple of 2, entries past the last region 0): how many
+// beat it.
+__device__ inline int key_rank(const uint64_t* keys, int ldr, uint64_t kj) {
   int rank = 0;
-  for (int m = 0; m < ldr; m += 4) {
-    const float4 am = *reinterpret_cast<const float4*>(a + m);
-    rank += (am.x > aj) || (am.x == aj && m + 0 < j);
-    rank += (am.y > aj) || (am.y == aj && m + 1 < j);
-    rank += (am.z > aj) || (am.z == aj && m + 2 < j);
-    rank += (am.w > aj) || (am.w == aj && m + 3 < j);
+  for (int m = 0; m < ldr; m += 2) {
+    const ulonglong2 km = *reinterpret_cast<const ulonglong2*>(keys + m);
+    rank += km.x > kj;
+    rank += km.y > kj;
   }
   return rank;
 }
