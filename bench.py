@@ -17,7 +17,9 @@ TFLOP/s, the fraction of the binding roofline (HBM for the stage shapes, the
 bf16 matrix cores for the dense map), the pool + route phase against HBM, and
 the oracle on one host thread and on all the host cores the run may use. The
 ``peaks`` object holds what a plain bf16 matrix-core loop and a plain
-streaming copy reach on this part, beside the published peaks.
+streaming copy reach on this part, beside the published peaks; the
+``detection`` list measures two detection-shaped maps at S = 16 (256
+regions) the same way.
 
 Side measurements of the headline workload (not its value): ``with_lce``
 (the module output with the local context term, a seeded synthetic 5x5
@@ -68,6 +70,7 @@ def parse_args(argv=None):
                     help="oracle sample per thread setting for the other workloads and the all-core run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the matrix-core loop and copy probes")
+    ap.add_argument("--peaks-only", action="store_true", help="only run the matrix-core loop and copy probes")
     ap.add_argument("--no-lce", action="store_true", help="skip the side measurement with the local context term")
     ap.add_argument("--no-train", action="store_true", help="skip the side measurement of the training step")
     ap.add_argument("--no-proj", action="store_true", help="skip the side measurement from the block input")
@@ -273,21 +276,15 @@ def capture(fns):
     return g
 
 
-def run_graphs(cycle, singles, nsets, count):
-    """Replay exactly `count` steps: whole cycles, then single-set graphs."""
-    full, rem = divmod(count, nsets)
-    for _ in range(full):
-        cycle.replay()
-    for s in range(rem):
-        singles[s].replay()
-
-
 class Timer:
-    """Graphs of one phase over every input copy, timed with HIP events on
-    the stream they run on."""
+    """A phase (one call per input copy, `fns[i]` for copy i) captured as HIP
+    graphs of exactly `warmup` and exactly `steps` calls, the copies taken in
+    rotation, and timed with HIP events on the stream the graphs run on: one
+    graph launch for the whole timed run, so no host launch gap sits between
+    its calls."""
 
-    def __init__(self, stream, nsets, steps, warmup):
-        self.stream, self.nsets, self.steps, self.warmup = stream, nsets, steps, warmup
+    def __init__(self, stream, steps, warmup):
+        self.stream, self.steps, self.warmup = stream, steps, warmup
 
     def graphs(self, fns):
         import torch
@@ -296,26 +293,32 @@ class Timer:
             f()
         torch.cuda.synchronize()
         with torch.cuda.stream(self.stream):
-            cyc = capture(fns)
-            sing = [capture([f]) for f in fns]
+            gw = capture([fns[i % len(fns)] for i in range(max(1, self.warmup))])
+            gk = capture([fns[i % len(fns)] for i in range(self.steps)])
         torch.cuda.synchronize()
-        return cyc, sing
+        return gw, gk
 
-    def us(self, fns):
-        """Average microseconds of one call of the phase."""
+    def run(self, fns):
+        """(events us per call, wall-clock us per call) of `steps` calls."""
         import torch
 
-        cyc, sing = self.graphs(fns)
+        gw, gk = self.graphs(fns)
         with torch.cuda.stream(self.stream):
-            run_graphs(cyc, sing, self.nsets, max(self.nsets, self.warmup))
+            gw.replay()
             torch.cuda.synchronize()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
             a.record(self.stream)
-            run_graphs(cyc, sing, self.nsets, self.steps)
+            gk.replay()
             b.record(self.stream)
             torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / self.steps
+            t1 = time.perf_counter()
+        return a.elapsed_time(b) * 1e3 / self.steps, (t1 - t0) * 1e6 / self.steps
+
+    def us(self, fns):
+        """Average microseconds of one call of the phase (HIP events)."""
+        return self.run(fns)[0]
 
 
 def hbm(nbytes, us):
@@ -376,25 +379,12 @@ def measure(w, args, dev, stream, side=False):
     for s in steps:  # eager warm-up of every copy (also the first-launch code loading)
         s()
     torch.cuda.synchronize()
-    tm = Timer(stream, nsets, args.steps, args.warmup)
+    tm = Timer(stream, args.steps, args.warmup)
 
-    # ---- timed region: K whole steps
-    cycle, singles = tm.graphs(steps)
-    with torch.cuda.stream(stream):
-        run_graphs(cycle, singles, nsets, args.warmup)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        run_graphs(cycle, singles, nsets, args.steps)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    wall_us = (t1 - t0) * 1e6 / args.steps
-    ev_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # ---- timed region: exactly K whole steps (one graph of K steps, the
+    # input copies in rotation), bracketed by synchronisations
+    ev_us, wall_us = tm.run(steps)
     step_us = max(wall_us, ev_us)
-    del cycle, singles
 
     # ---- the same launches one phase at a time
     attend_us = tm.us([s.attend for s in steps])
@@ -577,11 +567,11 @@ def main(argv=None):
 
     bra.load_library()
     head = wl.BY_NAME[args.workload] if args.workload else wl.HEADLINE
-    todo = [head] if args.only else [head] + [w for w in wl.WORKLOADS if w is not head]
+    todo = [head] if args.only else [head] + [w for w in wl.WORKLOADS + wl.DETECTION if w is not head]
 
     # ---- CPU oracle first, before anything touches the GPU
     cpu = {}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.peaks_only:
         for w in todo:
             q, k, v = wl.make_inputs(w)
             single = args.cpu_seconds if w is head else args.cpu_seconds_other
@@ -593,6 +583,9 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream()
+    if args.peaks_only:
+        print(json.dumps({"peaks": measure_peaks(dev, stream)}))
+        return 0
     peaks = None if (args.no_peaks or args.only) else measure_peaks(dev, stream)
 
     entries = {}
@@ -647,6 +640,8 @@ def main(argv=None):
         result["peaks"] = peaks
     if not args.only:
         result["configs"] = [entries[w.name] for w in wl.WORKLOADS if w.name in entries]
+        # detection-shaped maps at S = 16 (256 regions), beside the five
+        result["detection"] = [entries[w.name] for w in wl.DETECTION if w.name in entries]
     print(json.dumps(result))
     return 0
 

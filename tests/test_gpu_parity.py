@@ -426,3 +426,20 @@ def test_nan_token_still_writes_every_routing_slot(w):
     if w.B > 1:
         A = _oracle_affinity(_f64(q[1:]), _f64(k[1:]), w.S)
         assert parity.exact_route_mismatches(O.topk_route(A, w.topk), t[1:]) == 0
+
+
+# Detection-shaped maps at S = 16 (256 regions; explainer Part 4.3, S = 16
+# for object detection): the two measured detection workloads, and 96 x 96
+# maps whose 36-token regions make every 64-key chunk ragged, k = 4 and 8.
+DETECTION_SHAPES = wl.DETECTION + [
+    wl.custom(2, 96, 96, 64, 2, 16, 4, "bf16", seed=96),
+    wl.custom(2, 96, 96, 64, 2, 16, 8, "bf16", seed=97, content="clustered"),
+    wl.custom(2, 64, 64, 64, 2, 16, 4, "bf16", seed=98),
+]
+
+
+@pytest.mark.parametrize("w", DETECTION_SHAPES, ids=[w.name for w in DETECTION_SHAPES])
+def test_detection_shapes_s16(w):
+    q, k, v = wl.make_inputs(w)
+    mism, _, _ = _check_case(w, q, k, v, images=list(range(w.B)))
+    assert mism == 0

@@ -90,7 +90,16 @@ WORKLOADS = [
     Workload("dense-b2-128x128-c64-h2-s8-k4-bf16-clustered", 2, 128, 128, 64, 2, 8, 4, "bf16", 4, "clustered"),
 ]
 
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Detection-shaped maps at S = 16 (explainer Part 4.3: S = 16 for object
+# detection; paper summary Appendix C: larger S for dense prediction): 256
+# regions per image, the routing over 256 candidates. Measured beside the
+# five workloads above; not part of them.
+DETECTION = [
+    Workload("det-b2-128x128-c64-h2-s16-k4-bf16", 2, 128, 128, 64, 2, 16, 4, "bf16", 5),
+    Workload("det-b2-64x64-c64-h2-s16-k8-bf16-clustered", 2, 64, 64, 64, 2, 16, 8, "bf16", 6, "clustered"),
+]
+
+BY_NAME = {w.name: w for w in WORKLOADS + DETECTION}
 
 # The headline workload: stage-1 shape, 56x56 map, S = 7.
 HEADLINE = WORKLOADS[1]
