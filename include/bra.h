@@ -37,8 +37,10 @@
  *   build does not implement gives BRA_EUNSUPPORTED. A HIP error reported while enqueueing gives BRA_EHIP;
  *   a failed workspace allocation gives BRA_ENOMEM. On any error nothing has
  *   been enqueued, except for BRA_EHIP, where earlier launches of the same
- *   call may already be queued. The library keeps no global state and is
- *   thread-safe; calls that share a workspace must be ordered by the caller.
+ *   call may already be queued. The library is thread-safe; its only state
+ *   is the static scratch of bra_forward_static (one buffer per GPU and the
+ *   cached device address of each). Calls that share a workspace must be
+ *   ordered by the caller.
  *
  * Workspace
  *   The routing step keeps the fp32 region means Q^r, K^r (and, in
@@ -72,7 +74,8 @@ typedef enum bra_status {
   BRA_EINVAL = 1,
   BRA_EUNSUPPORTED = 2,
   BRA_EHIP = 3,
-  BRA_ENOMEM = 4
+  BRA_ENOMEM = 4,
+  BRA_ESCRATCH = 5  /* bra_forward_static: more scratch than its static buffer holds */
 } bra_status;
 
 /* Static, NUL-terminated description of a status code. Never NULL. */
@@ -175,6 +178,28 @@ bra_status bra_forward_ws(const void* Q, const void* K, const void* V, void* O,
                           int B, int H, int W, int C, int heads, int S, int topk,
                           bra_dtype dtype, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * bra_forward_static - bra_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The same kernels and the same output, bit for bit; the
+ * region means and the routing table go to a library-owned static device
+ * buffer of BRA_STATIC_SCRATCH_BYTES instead of a workspace. The call
+ * allocates nothing.
+ *
+ * The buffer is one file-scope device array: each GPU the library runs on
+ * holds its own copy until the process ends, and every call on that GPU
+ * shares it (its contents are the last call's; nothing in it needs to start
+ * at zero). Calls that overlap in time on one GPU (unordered streams, host
+ * threads) race on it and give undefined results: order them. `stream` must
+ * belong to the current device (BRA_EINVAL otherwise). Sizes whose
+ * bra_workspace_bytes(...) exceeds BRA_STATIC_SCRATCH_BYTES give
+ * BRA_ESCRATCH; every other check is bra_forward's.
+ */
+#define BRA_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+bra_status bra_forward_static(const void* Q, const void* K, const void* V, void* O,
+                              int B, int H, int W, int C, int heads, int S, int topk,
+                              bra_dtype dtype, hipStream_t stream);
 
 /*
  * Local context enhancement (LCE): the "+ dwconv(value)" term of the module

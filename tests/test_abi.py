@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(5):
+    for code in range(6):
         s = lib.bra_status_string(code)
         assert isinstance(s, bytes) and len(s) > 3
     assert lib.bra_status_string(0) == b"success"
@@ -265,3 +265,22 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setenv("BRA_LIBRARY", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         bra.load_library()
+
+
+def _fwd_static(lib, B=1, H=16, W=16, C=32, heads=1, S=4, k=2, dt=0, q=P, kk=P2, v=P3, o=P4):
+    return lib.bra_forward_static(q, kk, v, o, B, H, W, C, heads, S, k, dt, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(H=18), EINVAL), (dict(k=0), EINVAL), (dict(q=0), EINVAL), (dict(o=P + 2), EINVAL),
+    (dict(heads=3), EINVAL), (dict(C=64, heads=1), EUNSUP), (dict(dt=7), EUNSUP),
+])
+def test_static_entry_point_validation(lib, kwargs, status):
+    assert _fwd_static(lib, **kwargs) == status
+
+
+def test_static_entry_point_rejects_sizes_beyond_its_buffer(lib):
+    # 1024 images of 56 x 56 x 64 at S = 7: 25.7 MB of region means
+    assert lib.bra_workspace_bytes(1024, 56, 56, 64, 7, 1) > bra.STATIC_SCRATCH_BYTES
+    assert _fwd_static(lib, B=1024, H=56, W=56, C=64, heads=2, S=7, k=1, dt=1) == bra.BRA_ESCRATCH
+    assert lib.bra_workspace_bytes(512, 56, 56, 64, 7, 1) <= bra.STATIC_SCRATCH_BYTES

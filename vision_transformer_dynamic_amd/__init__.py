@@ -14,6 +14,7 @@ and the current stream. If the library has not been built, every call raises
     attend(q, k, v, idx, heads, S)                     -> o   [B, H, W, C]
     forward(q, k, v, heads, S, topk)                   -> o   [B, H, W, C]
     forward_ws(q, k, v, heads, S, topk, workspace)     -> the same, in a caller workspace
+    forward_static(q, k, v, heads, S, topk)            -> the same, in the library's static scratch
     attend_lce(q, k, v, idx, weight, bias, heads, S)   -> o + 5x5 depthwise conv of v
     forward_lce(q, k, v, weight, bias, heads, S, topk) -> o + 5x5 depthwise conv of v
     attend_backward(q, k, v, o, do, idx, heads, S)     -> (dq, dk, dv), routing held fixed
@@ -45,6 +46,7 @@ __all__ = [
     "attend",
     "forward",
     "forward_ws",
+    "forward_static",
     "attend_lce",
     "forward_lce",
     "attend_backward",
@@ -58,11 +60,12 @@ _LIB_ENV = "BRA_LIBRARY"
 
 BRA_F32 = 0
 BRA_BF16 = 1
-BRA_OK, BRA_EINVAL, BRA_EUNSUPPORTED, BRA_EHIP, BRA_ENOMEM = range(5)
+BRA_OK, BRA_EINVAL, BRA_EUNSUPPORTED, BRA_EHIP, BRA_ENOMEM, BRA_ESCRATCH = range(6)
+STATIC_SCRATCH_BYTES = 16 << 20  # BRA_STATIC_SCRATCH_BYTES
 
 # Every symbol include/bra.h declares.
 EXPORTS = ("bra_status_string", "bra_attend_kernel", "bra_workspace_bytes", "bra_pool", "bra_route_pooled",
-           "bra_route", "bra_route_ws", "bra_attend", "bra_forward", "bra_forward_ws", "bra_attend_lce", "bra_forward_lce", "bra_backward_workspace_bytes", "bra_attend_backward",
+           "bra_route", "bra_route_ws", "bra_attend", "bra_forward", "bra_forward_ws", "bra_forward_static", "bra_attend_lce", "bra_forward_lce", "bra_backward_workspace_bytes", "bra_attend_backward",
            "bra_qkv_pool", "bra_forward_qkv")
 
 _lib = None
@@ -113,6 +116,8 @@ def load_library():
     lib.bra_forward.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
     lib.bra_forward_ws.restype = i32
     lib.bra_forward_ws.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [i32, vp, sz, vp]
+    lib.bra_forward_static.restype = i32
+    lib.bra_forward_static.argtypes = [vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
     lib.bra_attend_lce.restype = i32
     lib.bra_attend_lce.argtypes = [vp, vp, vp, vp, vp, vp, vp] + [i32] * 7 + [i32, vp]
     lib.bra_forward_lce.restype = i32
@@ -311,6 +316,20 @@ def forward_ws(q, k, v, heads: int, S: int, topk: int, workspace: torch.Tensor, 
     _check(lib.bra_forward_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                               B, H, W, C, heads, S, topk, _dtype_code(q),
                               ws.data_ptr(), nbytes, _stream(q.device)))
+    return out
+
+
+def forward_static(q, k, v, heads: int, S: int, topk: int, out=None) -> torch.Tensor:
+    """forward() with the library's static device scratch (bra_forward_static):
+    no allocation in the call; calls on one GPU must be ordered."""
+    lib = load_library()
+    _check_maps(q, k, v)
+    B, H, W, C = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check_maps(q, out)
+    _check(lib.bra_forward_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  B, H, W, C, heads, S, topk, _dtype_code(q), _stream(q.device)))
     return out
 
 

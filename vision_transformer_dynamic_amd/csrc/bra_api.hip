@@ -5,6 +5,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 namespace {
 
 using bra::Shape;
@@ -106,6 +108,38 @@ bra_status check_lce(const void* weight, const void* bias, const void* O, const 
   return BRA_OK;
 }
 
+// ---- scratch of the entry point that allocates nothing (bra_forward_static)
+// A file-scope device array: each GPU the library runs on holds its own copy
+// until the process ends. Its device address is looked up once per device,
+// with that device current; host code never uses the array's name itself
+// (on the host it only stands for the symbol).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;  // BRA_STATIC_SCRATCH_BYTES
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of the current device's copy of `scratch`; `stream`
+// must belong to the current device (NULL: the current device's default).
+bra_status static_scratch(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return BRA_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return BRA_EUNSUPPORTED;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return BRA_EHIP;
+    if (sdev != dev) return BRA_EINVAL;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BRA_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<char*>(g_scratch_ptr[dev]);
+  return BRA_OK;
+}
+
 bra_status enqueue_route(const void* Q, const void* K, int32_t* idx, const Shape& s, int dtype,
                          char* ws, hipStream_t stream) {
   float* Qr = reinterpret_cast<float*>(ws);
@@ -126,6 +160,7 @@ const char* bra_status_string(bra_status status) {
     case BRA_EUNSUPPORTED: return "unsupported configuration (head dim other than 32, more than 256 regions, C not a multiple of 8 or too large, or unknown dtype)";
     case BRA_EHIP: return "HIP runtime error while enqueueing a kernel";
     case BRA_ENOMEM: return "device workspace allocation failed";
+    case BRA_ESCRATCH: return "the problem needs more scratch than the static buffer of bra_forward_static holds (BRA_STATIC_SCRATCH_BYTES = 16 MiB)";
   }
   return "unknown status";
 }
@@ -283,6 +318,22 @@ bra_status bra_forward_ws(const void* Q, const void* K, const void* V, void* O,
                           hipStream_t stream) {
   return forward_impl(Q, K, V, nullptr, nullptr, O, B, H, W, C, heads, S, topk, (int)dtype, workspace,
                       workspace_bytes, false, stream);
+}
+
+bra_status bra_forward_static(const void* Q, const void* K, const void* V, void* O,
+                              int B, int H, int W, int C, int heads, int S, int topk,
+                              bra_dtype dtype, hipStream_t stream) {
+  Shape s;
+  bra_status st = check_shape(B, H, W, C, heads, S, topk, (int)dtype, &s);
+  if (st != BRA_OK) return st;
+  if (bad_tensor(Q) || bad_tensor(K) || bad_tensor(V) || bad_tensor(O)) return BRA_EINVAL;
+  if (workspace_for(s) > kStaticScratchBytes) return BRA_ESCRATCH;
+  // every other argument check happens in forward_impl, before any launch;
+  // the pointer lookup below makes no allocation
+  char* ws = nullptr;
+  if ((st = static_scratch(stream, &ws)) != BRA_OK) return st;
+  return forward_impl(Q, K, V, nullptr, nullptr, O, B, H, W, C, heads, S, topk, (int)dtype, ws, kStaticScratchBytes,
+                      false, stream);
 }
 
 bra_status bra_attend_lce(const void* Q, const void* K, const void* V,
