@@ -44,12 +44,15 @@ def test_bench_names_the_dispatched_attention_kernel():
     """bench.py labels its roofline with the attention kernel the library
     dispatches (bra_attend_kernel, the dispatch decision itself): the
     per-region kernel at stage 1 and for fp32, the image-resident kernel at
-    the 28x28 and 14x14 stage shapes, the chunked kernel at the dense shape
-    (more than 64 keys per query)."""
+    the 28x28 and 14x14 stage shapes, the kernel that stages every routed key
+    in LDS at the dense shape (more than 64 keys per query, bf16)."""
     import bench
     names = [bench.attention_kernel_name(w) for w in wl.WORKLOADS]
     assert names == ["attend_head_kernel", "attend_head_kernel", "attend_image_kernel",
-                     "attend_image_kernel", "attend_kernel"]
+                     "attend_image_kernel", "attend_dense_kernel"]
+    # more than 64 keys per query in fp32, or more than 1024 in bf16: the chunked kernel
+    assert bench.attention_kernel_name(wl.custom(1, 16, 16, 64, 2, 4, 6, "f32")) == "attend_kernel"
+    assert bench.attention_kernel_name(wl.custom(1, 48, 48, 64, 2, 2, 2, "bf16")) == "attend_kernel"
     # too few (image, head) pairs, or regions not a multiple of 4 tokens
     assert bench.attention_kernel_name(wl.custom(2, 28, 28, 128, 4, 7, 4)) == "attend_head_kernel"
     assert bench.attention_kernel_name(wl.custom(64, 21, 21, 64, 2, 7, 4)) == "attend_head_kernel"
@@ -76,7 +79,7 @@ def test_profiled_kernels_are_the_dispatched_ones():
     import bench
     traces = _profile_traces()
     assert traces, "no kernel trace under profiles/ names its workload"
-    kinds = ("attend_head_kernel", "attend_image_kernel", "attend_kernel")
+    kinds = ("attend_head_kernel", "attend_image_kernel", "attend_dense_kernel", "attend_kernel")
     for w in wl.WORKLOADS:
         if w.name not in traces:
             continue
@@ -85,5 +88,6 @@ def test_profiled_kernels_are_the_dispatched_ones():
         assert want in text, (w.name, want)
         for other in kinds:
             if other != want:
-                # attend_kernel is a prefix-free match only as a whole word
-                assert not re.search(r"\b" + other + r"I", text), (w.name, other)
+                # the name as a whole identifier, mangled (...13attend_kernelI...)
+                # or demangled (...::attend_kernel<...)
+                assert not re.search(r"(?<![A-Za-z_])" + other + r"[I<]", text), (w.name, other)

@@ -1229,7 +1229,8 @@ const char* attend_kernel_name(const Shape& s, int dtype, bool lce) {
     ImgLaunch L;
     if (plan_image(s, &L)) return "attend_image_kernel";
   }
-  return s.kv <= KC ? "attend_head_kernel" : "attend_kernel";
+  if (s.kv <= KC) return "attend_head_kernel";
+  return dense_attend_fits(s, dtype) ? "attend_dense_kernel" : "attend_kernel";
 }
 
 hipError_t launch_attend(const void* Q, const void* K, const void* V,
@@ -1303,6 +1304,11 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(waves * 64), args, lds, stream);
     if (e != hipSuccess || !lce || fuse) return e;
+    return launch_lce(V, lce_w, lce_b, O, s, dtype, stream);
+  }
+  if (dense_attend_fits(s, dtype)) {
+    const hipError_t e = launch_attend_dense(Q, K, V, idx, O, s, stream);
+    if (e != hipSuccess || !lce) return e;
     return launch_lce(V, lce_w, lce_b, O, s, dtype, stream);
   }
   AttnLaunch L = plan_attend(s, dtype);

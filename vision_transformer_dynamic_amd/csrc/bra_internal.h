@@ -83,6 +83,13 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
                          const int32_t* idx, const void* lce_w, const void* lce_b, void* O,
                          const Shape& s, int dtype, hipStream_t stream);
 
+// bf16 attention with more than 64 and at most 1024 keys per query: every
+// routed key of a head staged in LDS by direct-to-LDS loads, V read with the
+// transposing LDS reads (attend_dense.hip).
+bool dense_attend_fits(const Shape& s, int dtype);
+hipError_t launch_attend_dense(const void* Q, const void* K, const void* V, const int32_t* idx, void* O,
+                               const Shape& s, hipStream_t stream);
+
 // Name of the attention kernel launch_attend runs for this shape (the same
 // dispatch decision; the convolution pass, where there is one, follows it).
 const char* attend_kernel_name(const Shape& s, int dtype, bool lce);

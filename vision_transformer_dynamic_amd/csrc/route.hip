@@ -11,8 +11,8 @@
 // regions in descending affinity with the lower index first on exact ties.
 // The affinity rows never reach HBM.
 //
-// Two forms; each shape always takes the same one, so every routing table of
-// a shape is the same bits.
+// Three forms; each shape always takes the same one, so every routing table
+// of a shape is the same bits.
 //
 // R <= 64 and C a multiple of 32 (matrix-core form; every shape with heads of
 // 32 channels). The affinity of one image is a 64 x 64 (padded)
@@ -26,6 +26,10 @@
 // the keys. The row
 // blocks of one image run on one XCD (xcd_item) and share its L2 copy of
 // K^r[b]; images are split over the XCDs as in the pool and attention kernels.
+//
+// 64 < R <= 256 and C a multiple of 32 (matrix-core form for many regions,
+// route_mfma256_kernel below): one 16-candidate tile per wave over all
+// channels, and the k best taken one at a time for k <= 32.
 //
 // Other shapes (vector form). One workgroup per (image b, block of 4 affinity rows);
 // each of its 4 waves owns one row, and lane j owns the candidates j, j+64,
@@ -240,6 +244,89 @@ __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
   }
 }
 
+// ---- matrix-core form for 64 < R <= 256 (C a multiple of 32) ----
+// One workgroup per (image, block of 16 rows), 16 waves: wave t computes the
+// 16 x 16 tile of candidates 16 t .. 16 t + 15 over all C channels (the
+// 16-channel steps in increasing order from a zero accumulator, with the
+// same 16x16x4 fp32 products), so each affinity is one fixed sequence. The
+// tile's keys go to LDS ([16 rows][256]: key 0 past R), then wave t ranks row
+// t of the block: lane l holds candidates l, l + 64, l + 128, l + 192. For k
+// up to 32 the k best are taken one at a time (a wave-wide maximum of the
+// keys, then the winner's key cleared), k rounds of a few dozen
+// instructions; for larger k every candidate counts the keys that beat it
+// (256 compares each), as in the other forms. Keys are unique, so both give
+// the same table: descending affinity, the lower index first on ties.
+constexpr int BR = 16;     // affinity rows per workgroup
+constexpr int BW = 16;     // waves: one 16-candidate tile each
+constexpr int BMAX = 256;  // candidates
+
+template <int NS>
+__global__ __launch_bounds__(BW * 64) void route_mfma256_kernel(RouteParams p) {
+  __shared__ __align__(16) uint64_t keys[BR][BMAX];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int w = xcd_item(blockIdx.x, gridDim.x);  // (image, row block), an image's blocks on one XCD
+  const int b = w / p.row_blocks;
+  const int i0 = (w - b * p.row_blocks) * BR;
+  const int j0 = wave * 16;
+  const int64_t img = (int64_t)b * p.R;
+
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (j0 < p.R) {  // uniform
+    // A operand: query row i0 + l16; B operand: candidate row j0 + l16;
+    // channels 16 t + 4 g .. + 3 at step t (rows past R read row R - 1;
+    // their results are never used)
+    const float* qrow = p.Qr + (img + min(i0 + l16, p.R - 1)) * p.C + 4 * g;
+    const float* krow = p.Kr + (img + min(j0 + l16, p.R - 1)) * p.C + 4 * g;
+    const int nsteps = p.C >> 4;
+    for (int t0 = 0; t0 < nsteps; t0 += NS) {
+      float4 a[NS], k[NS];
+#pragma unroll
+      for (int m = 0; m < NS; ++m) {
+        a[m] = *reinterpret_cast<const float4*>(qrow + 16 * (t0 + m));
+        k[m] = *reinterpret_cast<const float4*>(krow + 16 * (t0 + m));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk ahead of the products
+#pragma unroll
+      for (int m = 0; m < NS; ++m) acc = affinity_mfma_step(acc, a[m], k[m]);
+    }
+  }
+  {
+    // every one of the 256 key columns is written: columns past R get key 0
+    const int col = j0 + l16;
+    const uint64_t valid = col < p.R ? ~0ull : 0ull;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) keys[4 * g + ii][col] = affinity_key(acc[ii], col) & valid;
+  }
+  __syncthreads();
+
+  const int row = wave;
+  if (i0 + row >= p.R) return;  // uniform; no barrier follows
+  int32_t* out = p.idx + (img + i0 + row) * p.topk;
+  uint64_t kc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) kc[u] = keys[row][lane + 64 * u];
+  if (p.topk <= 32) {
+    for (int r = 0; r < p.topk; ++r) {  // uniform
+      uint64_t best = kc[0];
+#pragma unroll
+      for (int u = 1; u < 4; ++u) best = kc[u] > best ? kc[u] : best;
+      best = wave_max_key(best);
+      if (lane == 0) out[r] = key_index(best);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kc[u] = kc[u] == best ? 0ull : kc[u];
+    }
+  } else {
+#pragma unroll 1
+    for (int u = 0; u < 4; ++u) {
+      const int j = lane + 64 * u;
+      if (j >= p.R) break;
+      const int rank = key_rank(&keys[row][0], BMAX, kc[u]);
+      if (rank < p.topk) out[rank] = j;
+    }
+  }
+}
+
 }  // namespace
 
 // dynamic LDS of the vector form: the staged slices (floats), then the key
@@ -263,6 +350,15 @@ hipError_t launch_route(const float* Qr, const float* Kr, int32_t* idx,
                      : nh % 2 == 0 ? reinterpret_cast<const void*>(&route_mfma_kernel<2>)
                                    : reinterpret_cast<const void*>(&route_mfma_kernel<1>);
     return hipLaunchKernel(fn, dim3(grid), dim3(MW * 64), args, 0, stream);
+  }
+  if (s.R <= BMAX && s.C % 32 == 0) {
+    RouteParams p{Qr, Kr, idx, s.B, s.R, s.C, s.topk, (s.R + BR - 1) / BR, 0};
+    args[0] = &p;
+    const int nsteps = s.C / 16;  // even
+    const void* fn = nsteps % 8 == 0   ? reinterpret_cast<const void*>(&route_mfma256_kernel<8>)
+                     : nsteps % 4 == 0 ? reinterpret_cast<const void*>(&route_mfma256_kernel<4>)
+                                       : reinterpret_cast<const void*>(&route_mfma256_kernel<2>);
+    return hipLaunchKernel(fn, dim3((unsigned)(s.B * p.row_blocks)), dim3(BW * 64), args, 0, stream);
   }
   RouteParams p{Qr, Kr, idx, s.B, s.R, s.C, s.topk, (s.R + RB - 1) / RB, (s.R + 3) / 4 * 4};
   args[0] = &p;
