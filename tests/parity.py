@@ -102,7 +102,7 @@ def assert_lce_output_close(out: np.ndarray, ref: np.ndarray, dtype: str, what: 
 
 GRAD_F32_REL = 1e-4
 GRAD_BF16_REL = 2e-2
-GRAD_BF16_MEAN_REL = 1e-2
+GRAD_BF16_MEAN_REL = 5e-3
 
 
 def assert_grad_close(out: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
@@ -110,7 +110,8 @@ def assert_grad_close(out: np.ndarray, ref: np.ndarray, dtype: str, what: str = 
     elementwise bound scales with the tensor's largest reference value: fp32
     1e-4 * max(1, max|ref|); bf16 2e-2 * max(1, max|ref|) (bf16 rounding of
     the probabilities and of dZ inside the products, 2^-8 relative each, and
-    of the stored gradient) plus mean-rel <= 1e-2."""
+    of the stored gradient) plus mean-rel <= 5e-3, the forward's bar (the
+    measured bf16 mean-rel is 2.1e-3 to 3.4e-3 over every tested shape)."""
     assert np.all(np.isfinite(out)), f"{what}: non-finite gradients"
     max_abs, mean_rel = output_errors(out, ref)
     scale = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
