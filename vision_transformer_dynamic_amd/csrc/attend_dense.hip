@@ -28,9 +28,9 @@
 //  * Scores, softmax and P are as in the other attention kernels: S^T tiles
 //    put a query's 8 keys of each 32-key step in one lane, whose
 //    probabilities are exactly the P^T slots the lane supplies next, so P
-//    never leaves registers; online softmax over 64-key chunks, rescaling
-//    only when some lane's running maximum grew; the denominator is a matrix
-//    product against an all-ones operand, from the same bf16 P.
+//    never leaves registers; online softmax over 64-key chunks with a lazy
+//    running maximum (below); the denominator is a matrix product against an
+//    all-ones operand, from the same bf16 P.
 //  * Output tile ct of O^T holds channels 16 ct .. 16 ct + 15; a lane holds 4
 //    consecutive channels of its query per tile (two 8-byte stores).
 #include "bra_internal.h"
@@ -59,6 +59,7 @@ struct DenseParams {
   int nqb;     // query blocks per region
   int qblk;    // queries per block (a multiple of 16, <= 256)
   float c;     // softmax scale * log2(e)
+  float lazy;  // kLazy / c: how far a score may exceed the running maximum
   FastDiv div_n, div_sw, div_S;
 };
 
@@ -138,12 +139,23 @@ __device__ __forceinline__ int issue_phase(const DenseParams& p, const int* rtab
   return cnt;
 }
 
-// Scores, softmax and P.V for one 64-key chunk at rows r0 .. r0 + 63 of a
-// phase buffer. nvalid: keys of the chunk below kv (RAGGED only).
+// Scores, softmax and P.V for one 64-key chunk. kl: this lane's K operand
+// row of the chunk (key 8 (col / 4) + col % 4, chunk g swizzled), vl[ct]:
+// this lane's transposing-read address of tile ct (key row 8g + col / 4,
+// channels 16 ct + 4 (col % 4)); the rest of each address is a constant.
+// nvalid: keys of the chunk below kv (RAGGED only).
+//
+// Online softmax with a lazy maximum: a lane's running maximum m moves only
+// when a score exceeds it by more than kLazy / c (2^8 in the exponent), so
+// the probabilities exp2(c (s - m)) stay below 2^8 (exact enough in fp32 and
+// in bf16, whose relative rounding does not depend on the magnitude) and the
+// accumulators are rescaled far less often than the maximum grows.
+constexpr float kLazy = 8.0f;
+
 template <bool RAGGED>
-__device__ __forceinline__ void dense_chunk(const DenseParams& p, const unsigned char* kbuf, const unsigned char* vbuf,
-                                            int r0, int nvalid, int g, int col, const bf16x8& qop, const bf16x8& ones,
-                                            floatx4 (&acc)[3], float& m_run) {
+__device__ __forceinline__ void dense_chunk(const DenseParams& p, const unsigned char* kl, const unsigned char* vl0,
+                                            const unsigned char* vl1, int nvalid, int g, const bf16x8& qop,
+                                            const bf16x8& ones, floatx4 (&acc)[3], float& m_run) {
   typedef Tr<__bf16> TT;
   // ---- S^T: rows of tile (st, tb) are keys st*32 + 8*(col/4) + col%4 + 4*tb
   float s[2][8];
@@ -152,8 +164,7 @@ __device__ __forceinline__ void dense_chunk(const DenseParams& p, const unsigned
     floatx4 sab[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int r = r0 + st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
-      const bf16x8 k = *reinterpret_cast<const bf16x8*>(kbuf + k_off(r, g));
+      const bf16x8 k = *reinterpret_cast<const bf16x8*>(kl + (st * 32 + 4 * tb) * kRowBytes);
       sab[tb] = TT::mma(k, qop, floatx4{0.f, 0.f, 0.f, 0.f});
     }
 #pragma unroll
@@ -174,21 +185,21 @@ __device__ __forceinline__ void dense_chunk(const DenseParams& p, const unsigned
 #pragma unroll
   for (int e = 2; e < 16; ++e) mx = fmaxf(mx, s[e >> 3][e & 7]);
   mx = wave_max_groups(mx);
-  const float mnew = fmaxf(m_run, mx);
-  const float mc = mnew * p.c;
-  if (__builtin_amdgcn_ballot_w64(mnew > m_run) != 0) {  // some lane's maximum grew (uniform)
-    const float alpha = __builtin_amdgcn_exp2f(m_run * p.c - mc);
+  const bool grow = mx > m_run + p.lazy;  // always at the first chunk (m_run = -inf)
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform
+    const float mnew = grow ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) * p.c);  // 1 where m stays, 0 at the start
 #pragma unroll
     for (int ct = 0; ct < 3; ++ct) acc[ct] *= alpha;
     m_run = mnew;
   }
+  const float mc = m_run * p.c;
   // ---- O^T += V^T P^T over the chunk's two 32-key steps. The V^T operand
   // of tile ct, lane group g: row = channel 16 ct + lane % 16, slots = keys
   // st*32 + 8g .. +7, from two transposing reads (keys +0..3, +4..7). In a
   // read, lane col = 4 s + q of the group reads key row 8g + s at channels
-  // 16 ct + 4 q .. +3 (chunk 2 ct + q / 2, half q % 2), so that lane j of the
-  // group receives channel 16 ct + j of the four keys.
-  const int srow = col >> 2, q = col & 3;
+  // 16 ct + 4 q .. +3, so that lane j of the group receives channel
+  // 16 ct + j of the four keys.
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     float pe[8];
@@ -197,11 +208,9 @@ __device__ __forceinline__ void dense_chunk(const DenseParams& p, const unsigned
     const bf16x8 pop = TT::from_f32(pe);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const int rowa = r0 + st * 32 + 8 * g + srow;
-      const int ch = 2 * ct + (q >> 1);
-      const int rb = (q & 1) * 8;
-      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vbuf + v_off(rowa, ch) + rb));
-      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(vbuf + v_off(rowa + 4, ch) + rb));
+      const unsigned char* va_p = (ct == 0 ? vl0 : vl1) + st * 32 * kRowBytes;
+      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va_p));
+      const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(va_p + 4 * kRowBytes));
       const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       acc[ct] = TT::mma(va, pop, acc[ct]);
     }
@@ -300,12 +309,20 @@ __global__ __launch_bounds__(kDenseTiles * 64) void attend_dense_kernel(DensePar
     const int rows = min(kPhaseRows, p.kvpad - p0);
     const unsigned char* kbuf = ph == 0 ? k0 : ph == 1 ? k1 : ph == 2 ? k2 : k3;
     const unsigned char* vbuf = ph == 0 ? v0 : ph == 1 ? v1 : ph == 2 ? v2 : v3;
+    // this lane's operand addresses in the phase's first chunk (k_off and
+    // v_off with the chunk-independent part of the row: bits 3-4 of the key
+    // rows a lane reads do not change from chunk to chunk)
+    const unsigned char* kl = kbuf + k_off(8 * (col >> 2) + (col & 3), g);
+    const int srow = col >> 2, q = col & 3;
+    const unsigned char* vl0 = vbuf + v_off(8 * g + srow, q >> 1) + (q & 1) * 8;
+    const unsigned char* vl1 = vbuf + v_off(8 * g + srow, 2 + (q >> 1)) + (q & 1) * 8;
     for (int r0 = 0; r0 < rows; r0 += KC) {  // uniform
       const int nvalid = p.kv - (p0 + r0);
+      const int db = r0 * kRowBytes;
       if (RAGGED && nvalid < KC)
-        dense_chunk<true>(p, kbuf, vbuf, r0, nvalid, g, col, qop, ones, acc, m_run);
+        dense_chunk<true>(p, kl + db, vl0 + db, vl1 + db, nvalid, g, qop, ones, acc, m_run);
       else
-        dense_chunk<false>(p, kbuf, vbuf, r0, KC, g, col, qop, ones, acc, m_run);
+        dense_chunk<false>(p, kl + db, vl0 + db, vl1 + db, KC, g, qop, ones, acc, m_run);
     }
   }
 
@@ -346,6 +363,7 @@ hipError_t launch_attend_dense(const void* Q, const void* K, const void* V, cons
   p.qblk = std::min(16 * kDenseTiles, (s.n + 15) / 16 * 16);
   p.nqb = (s.n + p.qblk - 1) / p.qblk;
   p.c = 1.4426950408889634f / sqrtf((float)s.d);
+  p.lazy = kLazy / p.c;
   p.div_n = make_fastdiv(s.n);
   p.div_sw = make_fastdiv(s.sw);
   p.div_S = make_fastdiv(s.S);
