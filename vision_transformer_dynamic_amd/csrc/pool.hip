@@ -5,7 +5,8 @@
 // regional representations by average pooling).
 //
 // HBM-bound: every input byte is read once, 2*B*R*C fp32 values are written.
-// One workgroup per (image, region) pools both Q and K; an image's regions
+// Small bf16 regions take one wave per region (pool_wave_kernel below).
+// Otherwise one workgroup per (image, region) pools both Q and K; an image's regions
 // go to one XCD (xcd_item), as in the route and attention kernels. (One wave
 // per region with a lane-shuffle reduction measured slower at the stage-1
 // shape.) A region is sh rows of one contiguous segment of sw*C elements,
@@ -29,6 +30,7 @@ struct PoolParams {
   float* Qr;
   float* Kr;
   int H, W, C, S, sh, sw;
+  int nregions;  // B * S * S
 };
 
 template <int VEC>
@@ -128,11 +130,94 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   }
 }
 
+// ---- small regions: one wave per region, four regions per workgroup ----
+// For bf16 regions of at most 256 / G tokens (G = C / 8 channel groups of
+// 16 bytes: the 28 x 28 and 14 x 14 stage maps), the per-region workgroups
+// above are mostly launch and reduction overhead. Here lane l owns channel
+// group g = l % G and the region's tokens l / G, l / G + 64 / G, ... (at most
+// NB per tensor, all loaded before any is added), and the 64 / G lanes of a
+// group are combined by exchanges across lane bits log2(G) .. 5 (DPP row
+// rotation by 8 for bit 3, the permlane swaps for bits 4 and 5), in the same
+// order every time. No LDS, no barrier.
+__device__ inline float xsum8(float v) {  // v + v[lane ^ 8]
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+__device__ inline float xsum16(float v) {  // v + v[lane ^ 16]
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float xsum32(float v) {  // v + v[lane ^ 32]
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int G, int NB>
+__global__ __launch_bounds__(256) void pool_wave_kernel(PoolParams p) {
+  constexpr int TS = 64 / G;  // token stride between a lane's tokens
+  const int R = p.S * p.S;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = xcd_item(blockIdx.x, gridDim.x) * 4 + wave;  // region; an image's regions on one XCD
+  if (w >= p.nregions) return;  // uniform; no barrier in this kernel
+  const int b = w / R, r = w - b * R;
+  const int y0 = (r / p.S) * p.sh, x0 = (r - (r / p.S) * p.S) * p.sw;
+  const int g = lane % G, t0 = lane / G;
+  const int n = p.sh * p.sw;
+  const int64_t img = (int64_t)b * p.H * p.W * p.C;
+  const __bf16* Qb = static_cast<const __bf16*>(p.Q) + img + 8 * g;
+  const __bf16* Kb = static_cast<const __bf16*>(p.K) + img + 8 * g;
+  uint4 vq[NB], vk[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int t = t0 + j * TS;
+    vq[j] = vk[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (t < n) {
+      const int ty = t / p.sw, tx = t - ty * p.sw;
+      const int off = ((y0 + ty) * p.W + x0 + tx) * p.C;
+      vq[j] = *reinterpret_cast<const uint4*>(Qb + off);
+      vk[j] = *reinterpret_cast<const uint4*>(Kb + off);
+    }
+  }
+  float aq[8] = {}, ak[8] = {};
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    accum16<8>(aq, vq[j]);
+    accum16<8>(ak, vk[j]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (G <= 8) { aq[e] = xsum8(aq[e]); ak[e] = xsum8(ak[e]); }
+    if (G <= 16) { aq[e] = xsum16(aq[e]); ak[e] = xsum16(ak[e]); }
+    if (G <= 32) { aq[e] = xsum32(aq[e]); ak[e] = xsum32(ak[e]); }
+  }
+  if (lane < G) {
+    const float inv = 1.0f / (float)n;
+    float* oq = p.Qr + ((int64_t)b * R + r) * p.C + 8 * g;
+    float* ok = p.Kr + ((int64_t)b * R + r) * p.C + 8 * g;
+    *reinterpret_cast<float4*>(oq) = make_float4(aq[0] * inv, aq[1] * inv, aq[2] * inv, aq[3] * inv);
+    *reinterpret_cast<float4*>(oq + 4) = make_float4(aq[4] * inv, aq[5] * inv, aq[6] * inv, aq[7] * inv);
+    *reinterpret_cast<float4*>(ok) = make_float4(ak[0] * inv, ak[1] * inv, ak[2] * inv, ak[3] * inv);
+    *reinterpret_cast<float4*>(ok + 4) = make_float4(ak[4] * inv, ak[5] * inv, ak[6] * inv, ak[7] * inv);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pool(const void* Q, const void* K, float* Qr, float* Kr,
                        const Shape& s, int dtype, hipStream_t stream) {
-  PoolParams p{Q, K, Qr, Kr, s.H, s.W, s.C, s.S, s.sh, s.sw};
+  PoolParams p{Q, K, Qr, Kr, s.H, s.W, s.C, s.S, s.sh, s.sw, s.B * s.R};
+  // small bf16 regions (at most four 16-byte vectors per tensor per lane):
+  // one wave per region (measured at 28 x 28, C = 128: 8.5 vs 9.2 us; at
+  // 14 x 14, C = 256: 6.5 vs 8.1 us; the same at the 56 x 56 stage map, and
+  // slower for 16 x 16 regions, whose tokens would take several rounds)
+  const int G8 = s.C / 8;
+  if (dtype == kBF16 && (G8 == 8 || G8 == 16 || G8 == 32) && s.n * G8 <= 256) {
+    void* a[] = {&p};
+    const unsigned grid = (unsigned)((s.B * s.R + 3) / 4);
+    const void* fn = G8 == 8 ? (const void*)&pool_wave_kernel<8, 4> : G8 == 16 ? (const void*)&pool_wave_kernel<16, 4>
+                                                                             : (const void*)&pool_wave_kernel<32, 4>;
+    return hipLaunchKernel(fn, dim3(grid), dim3(256), a, 0, stream);
+  }
   const int vec = dtype == kBF16 ? 8 : 4;
   const int G = s.C / vec;
 
