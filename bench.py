@@ -396,6 +396,9 @@ def measure(w, args, dev, stream, side=False):
     ref_outs = [torch.empty_like(s_.q) for s_ in steps]
     stream_us = tm.us([lambda s_=s_, o_=o_: torch.addcmul(s_.q, s_.k, s_.v, out=o_) for s_, o_ in zip(steps, ref_outs)])
     del ref_outs
+    # the backward of the attention (routing held fixed) from the timed
+    # steps' outputs: dQ, dK, dV
+    backward_us = None if args.no_train else tm.us([s_.backward for s_ in steps])
 
     # the timed steps computed the real thing: spot-check one copy, and the
     # phase-by-phase routing against the fused one
@@ -428,6 +431,8 @@ def measure(w, args, dev, stream, side=False):
         "phase_hbm": {"pool": hbm(f["pool_bytes"], pool_us), "route": hbm(f["route_bytes"], route_us),
                       "pool_route": hbm(f["pool_bytes"] + f["route_bytes"], pool_route_us)},
     }
+    if backward_us is not None:
+        entry["us"]["backward"] = round(backward_us, 2)
     extras = {"step_us": step_us, "wall_us": wall_us, "ev_us": ev_us, "nsets": nsets}
 
     if side and not args.no_lce:

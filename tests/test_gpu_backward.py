@@ -134,3 +134,78 @@ def _region_mask(w, region):
     ys, xs = O.region_token_coords(w.H, w.W, w.S, region)
     m[0, ys, xs, 0] = 0.0
     return m
+
+
+# Shapes the one-launch image-resident backward takes (bf16, regions of 4, 8
+# or 16 tokens, at most 64 regions, at least 128 (image, head) pairs): every
+# region size, full and ragged key sets (kv < 64), H != W.
+IMAGE_BWD = [
+    wl.custom(64, 8, 8, 64, 2, 4, 16, "bf16", seed=90),     # n = 4, kv = 64
+    wl.custom(32, 14, 14, 128, 4, 7, 8, "bf16", seed=91),   # n = 4, kv = 32
+    wl.custom(32, 8, 16, 128, 4, 4, 8, "bf16", seed=92),    # n = 8 (2 x 4), kv = 64, H != W
+    wl.custom(32, 14, 28, 128, 4, 7, 3, "bf16", seed=93),   # n = 8 (2 x 4), kv = 24, H != W
+    wl.custom(32, 16, 16, 128, 4, 4, 4, "bf16", seed=94),   # n = 16, kv = 64
+    wl.custom(32, 16, 16, 128, 4, 4, 2, "bf16", seed=95, content="clustered"),  # n = 16, kv = 32
+]
+
+
+@pytest.mark.parametrize("w", IMAGE_BWD, ids=[w.name for w in IMAGE_BWD])
+def test_image_resident_backward(w):
+    _check_backward(w)
+
+
+def test_image_resident_backward_is_deterministic():
+    w = IMAGE_BWD[1]
+    q, k, v = wl.make_inputs(w)
+    g = wl.make_grad_output(w)
+    _, _, dq, dk, dv = _run(w, q, k, v, g)
+    _, _, dq2, dk2, dv2 = _run(w, q, k, v, g)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+def test_image_resident_unrouted_tokens_get_zero_key_and_value_gradients():
+    """As above on 64 images (the image-resident backward): every region
+    routes to itself except region 0, which routes to region 1."""
+    w = wl.custom(64, 16, 16, 64, 2, 4, 1, "bf16", seed=96)
+    q, k, v = (t.to(DEV) for t in wl.make_inputs(w))
+    g = wl.make_grad_output(w).to(DEV)
+    idx = torch.arange(16, dtype=torch.int32, device=DEV).reshape(1, 16, 1).repeat(w.B, 1, 1).contiguous()
+    idx[:, 0, 0] = 1
+    o = bra.attend(q, k, v, idx, w.heads, w.S)
+    dq, dk, dv = bra.attend_backward(q, k, v, o, g, idx, w.heads, w.S)
+    torch.cuda.synchronize()
+    assert torch.all(dk[:, :4, :4] == 0) and torch.all(dv[:, :4, :4] == 0)
+    sel = [0, w.B - 1]
+    ref = O.attend_backward(_f64(q.cpu()[sel]), _f64(k.cpu()[sel]), _f64(v.cpu()[sel]), idx.cpu().numpy()[sel],
+                            _f64(g.cpu()[sel]), w.heads, w.S)
+    for name, out, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        parity.assert_grad_close(_f64(out.cpu()[sel]), r, "bf16", name)
+
+
+@pytest.mark.parametrize("kind", ["out_of_range", "repeated"])
+def test_image_resident_bad_route_row(kind):
+    """The bad-row rule on the image-resident backward (64 images, 2 x 2
+    regions, kv = 16): NaN dQ for the bad region's queries only, which are left
+    out of dK and dV; the other images are untouched."""
+    w = wl.custom(64, 14, 14, 64, 2, 7, 4, "bf16", seed=97)
+    q, k, v = (t.to(DEV) for t in wl.make_inputs(w))
+    g = wl.make_grad_output(w).to(DEV)
+    idx = bra.route(q, k, w.S, w.topk)
+    o = bra.attend(q, k, v, idx, w.heads, w.S)
+    bad = idx.clone()
+    bad[0, 5, 1] = w.R if kind == "out_of_range" else bad[0, 5, 0]
+    dq, dk, dv = bra.attend_backward(q, k, v, o, g, bad, w.heads, w.S)
+    dq0, dk0, dv0 = bra.attend_backward(q, k, v, o, g, idx, w.heads, w.S)
+    torch.cuda.synchronize()
+    ys, xs = (torch.as_tensor(a) for a in O.region_token_coords(w.H, w.W, w.S, 5))
+    dqf = dq.float().cpu()
+    assert torch.isnan(dqf[0, ys, xs]).all()
+    dqf[0, ys, xs] = 0
+    assert not torch.isnan(dqf).any()
+    assert not torch.isnan(dk).any() and not torch.isnan(dv).any()
+    # images other than 0 are those of the good table, bit for bit
+    assert torch.equal(dq[1:], dq0[1:]) and torch.equal(dk[1:], dk0[1:]) and torch.equal(dv[1:], dv0[1:])
+    ref = O.attend_backward(_f64(q.cpu()[:1]), _f64(k.cpu()[:1]), _f64(v.cpu()[:1]), idx.cpu().numpy()[:1],
+                            _f64(g.cpu()[:1]) * _region_mask(w, 5), w.heads, w.S)
+    for name, out, r in zip(("dK", "dV"), (dk, dv), ref[1:]):
+        parity.assert_grad_close(_f64(out.cpu()[:1]), r, "bf16", name)

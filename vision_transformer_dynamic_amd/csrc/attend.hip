@@ -943,8 +943,9 @@ __device__ __forceinline__ void image_unit(const ImgParams& p, int u, int lane, 
 // positions (one 16-byte V^T read); otherwise (n a multiple of 4) it is two
 // runs of 4. RAGGED: kv < 64 (whole runs of 4 or 8 keys are past kv). QR:
 // regions per unit. The workgroup has between 1 and 16 waves; wave w takes
-// units w, w + waves, ... (at most kImgUnits).
-template <bool RAGGED, bool N8, int QR>
+// units w, w + waves, ... (at most MAXU: 1 when an image has at most 16
+// units, each in a wave of its own; else kImgUnits).
+template <bool RAGGED, bool N8, int QR, int MAXU>
 __global__ __launch_bounds__(1024) void attend_image_kernel(ImgParams p) {
   typedef Tr<__bf16> TT;
   typedef TT::op8 op8;
@@ -969,10 +970,10 @@ __global__ __launch_bounds__(1024) void attend_image_kernel(ImgParams p) {
   const int ch0 = head * D;
 
   // ---- query operands of the wave's units
-  op8 qop[kImgUnits];
-  int qoff[kImgUnits];
+  op8 qop[MAXU];
+  int qoff[MAXU];
 #pragma unroll
-  for (int uu = 0; uu < kImgUnits; ++uu) {
+  for (int uu = 0; uu < MAXU; ++uu) {
     const int u = wave + nwaves * uu;
     qoff[uu] = -1;
     qop[uu] = TT::zero();
@@ -1028,7 +1029,7 @@ __global__ __launch_bounds__(1024) void attend_image_kernel(ImgParams p) {
 
   __bf16* Og = p.O + img;
 #pragma unroll
-  for (int uu = 0; uu < kImgUnits; ++uu) {
+  for (int uu = 0; uu < MAXU; ++uu) {
     const int u = wave + nwaves * uu;
     if (u < p.nunits)  // uniform
       image_unit<RAGGED, N8, QR>(p, u, lane, g, col, Ks, Vt, rpos, qop[uu], qoff[uu], Og);
@@ -1181,23 +1182,30 @@ bool plan_image(const Shape& s, ImgLaunch* L) {
   p.div_nt = make_fastdiv(ntiles);
   L->lds = bytes;
   L->qr = qr;
+  // one unit per wave when an image has at most 16 (14x14 map, 2 x 2
+  // regions: 13 waves, 12.5 vs 14.0 us with about two units per wave); else
   // about two units per wave, at most 16 waves (a wave takes up to kImgUnits)
-  L->waves = std::min(16, (nunits + 1) / 2);
+  L->waves = nunits <= 16 ? nunits : std::min(16, (nunits + 1) / 2);
   return true;
 }
 
 hipError_t launch_image(const ImgLaunch& L, int B, hipStream_t stream) {
   ImgParams p = L.p;
   const bool ragged = p.kv % KC != 0;
-  // (RAGGED, N8, QR): n = 8 has two regions per unit, n = 4 four, other
-  // multiples of 4 one (N8 when a multiple of 8)
-  const void* fns[2][4] = {
-      {(const void*)&attend_image_kernel<false, true, 1>, (const void*)&attend_image_kernel<false, false, 1>,
-       (const void*)&attend_image_kernel<false, true, 2>, (const void*)&attend_image_kernel<false, false, 4>},
-      {(const void*)&attend_image_kernel<true, true, 1>, (const void*)&attend_image_kernel<true, false, 1>,
-       (const void*)&attend_image_kernel<true, true, 2>, (const void*)&attend_image_kernel<true, false, 4>}};
+  // [one unit per wave][RAGGED][form]; form (N8, QR): n = 8 has two
+  // regions per unit, n = 4 four, other multiples of 4 one (N8 when a
+  // multiple of 8)
+  const void* fns[2][2][4] = {
+      {{(const void*)&attend_image_kernel<false, true, 1, kImgUnits>, (const void*)&attend_image_kernel<false, false, 1, kImgUnits>,
+        (const void*)&attend_image_kernel<false, true, 2, kImgUnits>, (const void*)&attend_image_kernel<false, false, 4, kImgUnits>},
+       {(const void*)&attend_image_kernel<true, true, 1, kImgUnits>, (const void*)&attend_image_kernel<true, false, 1, kImgUnits>,
+        (const void*)&attend_image_kernel<true, true, 2, kImgUnits>, (const void*)&attend_image_kernel<true, false, 4, kImgUnits>}},
+      {{(const void*)&attend_image_kernel<false, true, 1, 1>, (const void*)&attend_image_kernel<false, false, 1, 1>,
+        (const void*)&attend_image_kernel<false, true, 2, 1>, (const void*)&attend_image_kernel<false, false, 4, 1>},
+       {(const void*)&attend_image_kernel<true, true, 1, 1>, (const void*)&attend_image_kernel<true, false, 1, 1>,
+        (const void*)&attend_image_kernel<true, true, 2, 1>, (const void*)&attend_image_kernel<true, false, 4, 1>}}};
   const int form = L.qr == 2 ? 2 : L.qr == 4 ? 3 : (p.n % 8 == 0 ? 0 : 1);
-  const void* fn = fns[ragged][form];
+  const void* fn = fns[p.nunits <= 16][ragged][form];
   // more than the default 64 KiB of dynamic LDS: raise the kernel's limit
   // (an attribute of the kernel, set on every launch: no state is kept) to
   // the most any launch of it uses, one value for every caller

@@ -860,6 +860,7 @@ size_t backward_workspace_bytes(const Shape& s) {
 hipError_t launch_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                            const int32_t* idx, void* dQ, void* dK, void* dV, void* ws, const Shape& s, int dtype,
                            hipStream_t stream) {
+  if (backward_image_fits(s, dtype)) return launch_backward_image(Q, K, V, O, dO, idx, dQ, dK, dV, s, stream);
   BwdParams p{};
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.dO = dO; p.idx = idx;
   p.dQ = dQ; p.dK = dK; p.dV = dV;

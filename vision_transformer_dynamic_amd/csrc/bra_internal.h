@@ -114,4 +114,12 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
                            const int32_t* idx, void* dQ, void* dK, void* dV, void* ws, const Shape& s, int dtype,
                            hipStream_t stream);
 
+// The same backward in one launch for small bf16 maps (regions of 4, 8 or 16
+// tokens, at most 64 regions, the image's K, V, Q and dO rows of one head in
+// LDS): backward_image.hip. launch_backward takes it when it fits.
+bool backward_image_fits(const Shape& s, int dtype);
+hipError_t launch_backward_image(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                 const int32_t* idx, void* dQ, void* dK, void* dV, const Shape& s,
+                                 hipStream_t stream);
+
 }  // namespace bra
