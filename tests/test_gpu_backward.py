@@ -146,6 +146,9 @@ IMAGE_BWD = [
     wl.custom(32, 14, 28, 128, 4, 7, 3, "bf16", seed=93),   # n = 8 (2 x 4), kv = 24, H != W
     wl.custom(32, 16, 16, 128, 4, 4, 4, "bf16", seed=94),   # n = 16, kv = 64
     wl.custom(32, 16, 16, 128, 4, 4, 2, "bf16", seed=95, content="clustered"),  # n = 16, kv = 32
+    # K, V and then Q, dO in the same LDS (the four row arrays do not fit together)
+    wl.custom(32, 28, 28, 128, 4, 7, 2, "bf16", seed=98),   # n = 16, kv = 32
+    wl.custom(32, 16, 32, 128, 4, 8, 8, "bf16", seed=99),   # n = 8 (2 x 4), kv = 64, 64 regions
 ]
 
 

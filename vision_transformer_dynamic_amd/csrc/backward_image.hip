@@ -109,8 +109,12 @@ __device__ inline int tile_region(uint32_t packed, int j) {
 }
 
 // QR = 16 / n regions per unit (n = 4, 8, 16). RAGGED: kv < 64. MAXU: units
-// per wave at most (wave w takes units w, w + waves, ...).
-template <int QR, bool RAGGED, int MAXU>
+// per wave at most (wave w takes units w, w + waves, ...). SPLIT: the four
+// row arrays do not fit in LDS together (28 x 28 map): K and V are staged
+// for phase 1, whose query operands come from memory, and Q and dO take
+// their place for phase 2, whose key operands are read from LDS into
+// registers before the swap.
+template <int QR, bool RAGGED, int MAXU, bool SPLIT>
 __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
   typedef Tr<__bf16> TT;
   typedef TT::op8 op8;
@@ -119,8 +123,8 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __bf16* Ks = reinterpret_cast<__bf16*>(smem_raw);  // [HW][kRowE] each
   __bf16* Vs = Ks + p.HW * kRowE;
-  __bf16* Qs = Vs + p.HW * kRowE;
-  __bf16* Ds = Qs + p.HW * kRowE;
+  __bf16* Qs = SPLIT ? Ks : Vs + p.HW * kRowE;
+  __bf16* Ds = SPLIT ? Vs : Qs + p.HW * kRowE;
   float* lse_s = reinterpret_cast<float*>(Ds + p.HW * kRowE);  // [HW4]: base-2 log-sum-exp of every query
   float* dd_s = lse_s + p.HW4;                                  // [HW4]: D of every query
   uint64_t* rmask = reinterpret_cast<uint64_t*>(dd_s + p.HW4);  // [R]: routed regions of query region i
@@ -148,29 +152,44 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
     rout[e] = 0;
   }
 
-  // ---- O of the query columns of the wave's phase-1 units (for D)
-  op8 oop[MAXU];
+  // ---- O (for D) of the query columns of the wave's phase-1 units, and
+  // with SPLIT their Q and dO
+  op8 oop[MAXU], qg[SPLIT ? MAXU : 1], dg[SPLIT ? MAXU : 1];
 #pragma unroll
   for (int uu = 0; uu < MAXU; ++uu) {
     const int qpos = 16 * (wave + nw * uu) + col;
     oop[uu] = TT::zero();
-    if (qpos < p.HW) oop[uu] = TT::load8(p.O + img + pos_token(p, qpos) * p.C + ch0 + 8 * g);
+    if (SPLIT) qg[uu] = dg[uu] = TT::zero();
+    if (qpos < p.HW) {
+      const int64_t off = img + pos_token(p, qpos) * p.C + ch0 + 8 * g;
+      oop[uu] = TT::load8(p.O + off);
+      if (SPLIT) {
+        qg[uu] = TT::load8(p.Q + off);
+        dg[uu] = TT::load8(p.dO + off);
+      }
+    }
   }
 
-  // ---- K, V, Q and dO rows of the head: item f = (position, 16-byte chunk)
+  // ---- K and V rows of the head (and Q and dO without SPLIT): item f =
+  // (position, 16-byte chunk)
   const int nitems = p.HW * 4;
   for (int f = tid; f < nitems; f += nthr) {
     const int pos = f >> 2, cv = f & 3;
     const int64_t off = img + pos_token(p, pos) * p.C + ch0 + 8 * cv;
+    const int at = pos * kRowE + 8 * cv;
     const uint4 vk = *reinterpret_cast<const uint4*>(p.K + off);
     const uint4 vv = *reinterpret_cast<const uint4*>(p.V + off);
-    const uint4 vq = *reinterpret_cast<const uint4*>(p.Q + off);
-    const uint4 vd = *reinterpret_cast<const uint4*>(p.dO + off);
-    const int at = pos * kRowE + 8 * cv;
-    *reinterpret_cast<uint4*>(Ks + at) = vk;
-    *reinterpret_cast<uint4*>(Vs + at) = vv;
-    *reinterpret_cast<uint4*>(Qs + at) = vq;
-    *reinterpret_cast<uint4*>(Ds + at) = vd;
+    if (SPLIT) {
+      *reinterpret_cast<uint4*>(Ks + at) = vk;
+      *reinterpret_cast<uint4*>(Vs + at) = vv;
+    } else {
+      const uint4 vq = *reinterpret_cast<const uint4*>(p.Q + off);
+      const uint4 vd = *reinterpret_cast<const uint4*>(p.dO + off);
+      *reinterpret_cast<uint4*>(Ks + at) = vk;
+      *reinterpret_cast<uint4*>(Vs + at) = vv;
+      *reinterpret_cast<uint4*>(Qs + at) = vq;
+      *reinterpret_cast<uint4*>(Ds + at) = vd;
+    }
   }
   __syncthreads();  // masks cleared
 
@@ -205,8 +224,14 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
     if (u >= p.nunits) break;  // uniform
     const int qpos = 16 * u + col;
     const bool qv = qpos < p.HW;
-    const op8 qop = qv ? TT::load8(Qs + qpos * kRowE + 8 * g) : TT::zero();
-    const op8 dop = qv ? TT::load8(Ds + qpos * kRowE + 8 * g) : TT::zero();
+    op8 qop, dop;
+    if (SPLIT) {
+      qop = qg[uu];
+      dop = dg[uu];
+    } else {
+      qop = qv ? TT::load8(Qs + qpos * kRowE + 8 * g) : TT::zero();
+      dop = qv ? TT::load8(Ds + qpos * kRowE + 8 * g) : TT::zero();
+    }
     float dpart = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dpart += (float)dop[e] * (float)oop[uu][e];
@@ -334,7 +359,29 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
       }
     }
   }
-  __syncthreads();  // log-sum-exp, D and the inverse masks complete
+  // with SPLIT: the key operands of the wave's phase-2 units (B operands of
+  // S = Q K^T and dP = dO V^T: column = key col, slots = channels 8g ..)
+  // from the K and V rows, then Q and dO in their place
+  op8 kBs[SPLIT ? MAXU : 1], vBs[SPLIT ? MAXU : 1];
+  if (SPLIT) {
+#pragma unroll
+    for (int uu = 0; uu < MAXU; ++uu) {
+      const int kp = 16 * (wave + nw * uu) + col;
+      kBs[uu] = kp < p.HW ? TT::load8(Ks + kp * kRowE + 8 * g) : TT::zero();
+      vBs[uu] = kp < p.HW ? TT::load8(Vs + kp * kRowE + 8 * g) : TT::zero();
+    }
+    __syncthreads();  // every read of K and V done
+    for (int f = tid; f < nitems; f += nthr) {
+      const int pos = f >> 2, cv = f & 3;
+      const int64_t off = img + pos_token(p, pos) * p.C + ch0 + 8 * cv;
+      const int at = pos * kRowE + 8 * cv;
+      const uint4 vq = *reinterpret_cast<const uint4*>(p.Q + off);
+      const uint4 vd = *reinterpret_cast<const uint4*>(p.dO + off);
+      *reinterpret_cast<uint4*>(Qs + at) = vq;
+      *reinterpret_cast<uint4*>(Ds + at) = vd;
+    }
+  }
+  __syncthreads();  // log-sum-exp, D, the inverse masks (and Q, dO) complete
 
   // ---- phase 2: dK, dV per key unit
 #pragma unroll
@@ -344,8 +391,8 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
     const int kp = 16 * u + col;  // the lane's key column
     const bool kvld = kp < p.HW;
     // B operands of S = Q K^T and dP = dO V^T: column = key col, slots = channels 8g ..
-    const op8 kB = kvld ? TT::load8(Ks + kp * kRowE + 8 * g) : TT::zero();
-    const op8 vB = kvld ? TT::load8(Vs + kp * kRowE + 8 * g) : TT::zero();
+    const op8 kB = SPLIT ? kBs[uu] : kvld ? TT::load8(Ks + kp * kRowE + 8 * g) : TT::zero();
+    const op8 vB = SPLIT ? vBs[uu] : kvld ? TT::load8(Vs + kp * kRowE + 8 * g) : TT::zero();
     const uint64_t mine = kvld ? imask[kp / N] : 0ull;
     uint64_t U = 0;  // incoming query regions of the unit's key regions (uniform)
 #pragma unroll
@@ -415,9 +462,10 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
   }
 }
 
-size_t bwd_image_lds(const Shape& s) {
+size_t bwd_image_lds(const Shape& s, bool split) {
   const size_t HW = (size_t)s.H * s.W, HW4 = (HW + 3) / 4 * 4;
-  return 2 * 4 * HW * kRowE + 2 * 4 * HW4 + 2 * 8 * (size_t)s.R + 4 * (size_t)s.R * s.topk + 4 * (size_t)s.R;
+  return (split ? 2 : 4) * 2 * HW * kRowE + 2 * 4 * HW4 + 2 * 8 * (size_t)s.R + 4 * (size_t)s.R * s.topk +
+         4 * (size_t)s.R;
 }
 
 }  // namespace
@@ -431,7 +479,7 @@ bool backward_image_fits(const Shape& s, int dtype) {
   if ((int64_t)s.B * s.heads < 128) return false;
   const int nunits = (s.H * s.W + 15) / 16;
   if (nunits > 64) return false;  // at most 4 units per wave
-  return bwd_image_lds(s) <= kBwdImgMaxLds;
+  return bwd_image_lds(s, true) <= kBwdImgMaxLds;
 }
 
 hipError_t launch_backward_image(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -458,27 +506,27 @@ hipError_t launch_backward_image(const void* Q, const void* K, const void* V, co
   p.div_sw = make_fastdiv(s.sw);
   p.div_S = make_fastdiv(s.S);
   p.div_topk = make_fastdiv(s.topk);
-  // about two units per wave (13 units at 14 x 14: 7 waves)
+  // about two units per wave (13 units at 14 x 14: 7 waves), at most 16 waves
   const int waves = std::min(16, (p.nunits + 1) / 2);
   const int maxu = (p.nunits + waves - 1) / waves;  // <= 4
+  const bool split = bwd_image_lds(s, false) > kBwdImgMaxLds;
   const bool ragged = s.kv < KC;
   const int form = s.n == 4 ? 0 : s.n == 8 ? 1 : 2;
-  // [ragged][form][units per wave: 1, 2, 4]
-  const void* fns[2][3][3] = {
-      {{(const void*)&bwd_image_kernel<4, false, 1>, (const void*)&bwd_image_kernel<4, false, 2>,
-        (const void*)&bwd_image_kernel<4, false, 4>},
-       {(const void*)&bwd_image_kernel<2, false, 1>, (const void*)&bwd_image_kernel<2, false, 2>,
-        (const void*)&bwd_image_kernel<2, false, 4>},
-       {(const void*)&bwd_image_kernel<1, false, 1>, (const void*)&bwd_image_kernel<1, false, 2>,
-        (const void*)&bwd_image_kernel<1, false, 4>}},
-      {{(const void*)&bwd_image_kernel<4, true, 1>, (const void*)&bwd_image_kernel<4, true, 2>,
-        (const void*)&bwd_image_kernel<4, true, 4>},
-       {(const void*)&bwd_image_kernel<2, true, 1>, (const void*)&bwd_image_kernel<2, true, 2>,
-        (const void*)&bwd_image_kernel<2, true, 4>},
-       {(const void*)&bwd_image_kernel<1, true, 1>, (const void*)&bwd_image_kernel<1, true, 2>,
-        (const void*)&bwd_image_kernel<1, true, 4>}}};
-  const void* fn = fns[ragged][form][maxu <= 1 ? 0 : maxu <= 2 ? 1 : 2];
-  const size_t lds = bwd_image_lds(s);
+  const int mu = maxu <= 1 ? 0 : maxu <= 2 ? 1 : 2;
+#define BRA_BI(QR, RG, SP)                                                                   \
+  {(const void*)&bwd_image_kernel<QR, RG, 1, SP>, (const void*)&bwd_image_kernel<QR, RG, 2, SP>, \
+   (const void*)&bwd_image_kernel<QR, RG, 4, SP>}
+  // [split][ragged][form][units per wave: 1, 2, 4]
+  const void* fns[2][2][3][3] = {
+      {{BRA_BI(4, false, false), BRA_BI(2, false, false), BRA_BI(1, false, false)},
+       {BRA_BI(4, true, false), BRA_BI(2, true, false), BRA_BI(1, true, false)}},
+      // (4-token regions never need SPLIT: at most 64 regions, 256 positions)
+      {{{nullptr, nullptr, nullptr}, BRA_BI(2, false, true), BRA_BI(1, false, true)},
+       {{nullptr, nullptr, nullptr}, BRA_BI(2, true, true), BRA_BI(1, true, true)}}};
+#undef BRA_BI
+  const void* fn = fns[split][ragged][form][mu];
+  if (fn == nullptr) return hipErrorInvalidValue;
+  const size_t lds = bwd_image_lds(s, split);
   // more than the default 64 KiB of dynamic LDS: raise the kernel's limit
   // to the most any launch of it uses (one value for every caller)
   if (lds > 64 * 1024) {
