@@ -293,8 +293,9 @@ def test_deterministic_and_stream_ordered():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("w", [wl.WORKLOADS[0], wl.WORKLOADS[1], wl.WORKLOADS[3], wl.WORKLOADS[4],
-                               wl.custom(1, 16, 16, 32, 1, 16, 7, "bf16", seed=27)],
+@pytest.mark.parametrize("w", [wl.WORKLOADS[0], wl.WORKLOADS[1], wl.WORKLOADS[2], wl.WORKLOADS[3], wl.WORKLOADS[4],
+                               wl.custom(1, 16, 16, 32, 1, 16, 7, "bf16", seed=27),
+                               wl.custom(128, 24, 24, 32, 1, 3, 1, "bf16", seed=75)],
                          ids=lambda w: w.name)
 def test_forward_routing_table_equals_bra_route(w):
     """bra_forward leaves its routing table in the workspace: it must equal the
@@ -349,7 +350,7 @@ def test_concurrent_calls_from_threads():
             assert torch.equal(got[i][r], ref[i]), (shapes[i].name, r)
 
 
-@pytest.mark.parametrize("w", [wl.WORKLOADS[0], wl.WORKLOADS[2], wl.WORKLOADS[4],
+@pytest.mark.parametrize("w", [wl.WORKLOADS[0], wl.WORKLOADS[2], wl.WORKLOADS[3], wl.WORKLOADS[4],
                                wl.custom(2, 16, 16, 48, 1, 16, 9, "bf16", seed=28)],
                          ids=lambda w: w.name)
 def test_workspace_forms_are_bit_identical(w):
