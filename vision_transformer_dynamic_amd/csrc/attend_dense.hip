@@ -316,7 +316,12 @@ __global__ __launch_bounds__(kDenseTiles * 64) void attend_dense_kernel(DensePar
     const int srow = col >> 2, q = col & 3;
     const unsigned char* vl0 = vbuf + v_off(8 * g + srow, q >> 1) + (q & 1) * 8;
     const unsigned char* vl1 = vbuf + v_off(8 * g + srow, 2 + (q >> 1)) + (q & 1) * 8;
-    for (int r0 = 0; r0 < rows; r0 += KC) {  // uniform
+    // the phase's chunks unrolled, so every operand address is the lane's
+    // base plus a constant (dense map: 24.0 -> 23.4 us)
+#pragma unroll
+    for (int c = 0; c < kPhaseRows / KC; ++c) {
+      const int r0 = c * KC;
+      if (r0 >= rows) break;  // uniform
       const int nvalid = p.kv - (p0 + r0);
       const int db = r0 * kRowBytes;
       if (RAGGED && nvalid < KC)

@@ -307,14 +307,40 @@ __global__ __launch_bounds__(BW * 64) void route_mfma256_kernel(RouteParams p) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) kc[u] = keys[row][lane + 64 * u];
   if (p.topk <= 32) {
+    // each lane's four keys in descending order (a five-step exchange
+    // network), then k rounds: the largest head key of the wave wins and
+    // its lane moves to its next key. A round compares the high halves only
+    // (the affinity's order bits: one 32-bit maximum across the wave, single
+    // instructions per step); the low halves (the index) decide only when
+    // several lanes hold the same high half. The winners are the 64-bit key
+    // maxima, so the table is the one the one-by-one extraction gives.
+#define BRA_CSWAP(a, b)                         \
+  {                                             \
+    const uint64_t hi_ = kc[a] > kc[b] ? kc[a] : kc[b]; \
+    const uint64_t lo_ = kc[a] > kc[b] ? kc[b] : kc[a]; \
+    kc[a] = hi_;                                \
+    kc[b] = lo_;                                \
+  }
+    BRA_CSWAP(0, 1) BRA_CSWAP(2, 3) BRA_CSWAP(0, 2) BRA_CSWAP(1, 3) BRA_CSWAP(1, 2)
+#undef BRA_CSWAP
     for (int r = 0; r < p.topk; ++r) {  // uniform
-      uint64_t best = kc[0];
-#pragma unroll
-      for (int u = 1; u < 4; ++u) best = kc[u] > best ? kc[u] : best;
-      best = wave_max_key(best);
-      if (lane == 0) out[r] = key_index(best);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kc[u] = kc[u] == best ? 0ull : kc[u];
+      const uint32_t hi = (uint32_t)(kc[0] >> 32);
+      const uint32_t m = wave_max_u32(hi);
+      const uint64_t tied = __builtin_amdgcn_ballot_w64(hi == m);
+      uint64_t win = tied;
+      if (__builtin_popcountll(tied) > 1) {  // uniform; equal high halves: the larger low half
+        const uint32_t lo = hi == m ? (uint32_t)kc[0] : 0u;
+        const uint32_t ml = wave_max_u32(lo);
+        win = __builtin_amdgcn_ballot_w64(hi == m && lo == ml);
+      }
+      const int wl = __builtin_ctzll(win);
+      if (lane == 0) out[r] = key_index(((uint64_t)m << 32) | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)kc[0], wl));
+      if (lane == wl) {
+        kc[0] = kc[1];
+        kc[1] = kc[2];
+        kc[2] = kc[3];
+        kc[3] = 0ull;
+      }
     }
   } else {
 #pragma unroll 1

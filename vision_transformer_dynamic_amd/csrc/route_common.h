@@ -76,6 +76,26 @@ __device__ inline uint64_t wave_max_key(uint64_t v) {
   return v;
 }
 
+// Largest 32-bit value over the 64 lanes, in every lane (the same steps as
+// wave_max_key on one word).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#define BRA_U32_DPP(ctrl) v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false))
+  BRA_U32_DPP(0xB1);   // quad_perm 1,0,3,2
+  BRA_U32_DPP(0x4E);   // quad_perm 2,3,0,1
+  BRA_U32_DPP(0x124);  // row_ror:4
+  BRA_U32_DPP(0x128);  // row_ror:8
+#undef BRA_U32_DPP
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(max(v, (uint32_t)r[0]), (uint32_t)r[1]);
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = max(max(v, (uint32_t)r[0]), (uint32_t)r[1]);
+  }
+  return v;
+}
+
 // Rank of key kj among the 64 keys of a row held in LDS (16-byte aligned):
 // how many beat it. All 8 broadcast reads of a 16-key block are issued before
 // its compares.
