@@ -494,6 +494,9 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int rtab[8 * KC];  // token offset of every routed key (per attention wave, or one shared)
   __shared__ int sbad;
+  // two heads' output halves of a tile's query rows, per tile parity (bf16
+  // without the convolution term: 16 queries x 8 chunks of 16 bytes)
+  __shared__ __align__(16) uint4 xrow[(!LCE && sizeof(T) == 2) ? 2 * 16 * 8 : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -645,6 +648,12 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   }
   if (!att || !head_ok) return;
 
+  // bf16, two heads per workgroup, no convolution term: the two head waves
+  // exchange their 64-byte halves of every query row through LDS and each
+  // stores whole 128-byte rows, so every line is written once, by one
+  // instruction (with halves, 1.22x O's bytes reached memory at the stage-1
+  // shape; whole rows: 1.00x, and 23.6 -> 23.2 us)
+  const bool rows = !LCE && sizeof(T) == 2 && p.HG == 2 && it.nh == 2;  // uniform per workgroup
   T* Og = static_cast<T*>(p.O) + it.img;
   if (bad) {
     // a routing entry outside [0, S*S): never dereferenced; output NaN
@@ -726,7 +735,33 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
         o[0] += lo.x; o[1] += lo.y; o[2] += lo.z; o[3] += lo.w;
         o[4] += hi.x; o[5] += hi.y; o[6] += hi.z; o[7] += hi.w;
       }
-      TT::store8_nt(Og + qoff[t], o);
+      if constexpr (sizeof(T) == 2) {
+        if (rows) xrow[(t & 1) * 128 + col * 8 + head * 4 + g] = __builtin_bit_cast(uint4, TT::from_f32(o));
+        else TT::store8_nt(Og + qoff[t], o);
+      } else {
+        TT::store8_nt(Og + qoff[t], o);
+      }
+    }
+    if constexpr (sizeof(T) == 2) {
+      if (rows) {
+        // head wave h stores queries 8h .. 8h + 7 of the tile: lane = (query,
+        // 16-byte chunk of the 128-byte row). Tile parities alternate, so
+        // one barrier per tile suffices: a wave writes parity t & 1 again
+        // only after the next barrier, which the other wave reaches after
+        // its reads of it.
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads and writes done
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const int q = 8 * head + (lane >> 3), c = lane & 7;
+        const int qi = it.q0 + t * 16 + q;
+        if (qi < it.q0 + it.nq) {
+          int qx;
+          const int qy = fdiv(qi, p.div_sw, &qx);
+          const uint4 v = xrow[(t & 1) * 128 + q * 8 + c];
+          __builtin_nontemporal_store(__builtin_bit_cast(op8, v),
+                                      reinterpret_cast<op8*>(Og + (it.qcorner + qy * p.W + qx) * p.C + it.cb + 8 * c));
+        }
+      }
     }
   }
 }
