@@ -31,8 +31,10 @@
 //    never leaves registers; online softmax over 64-key chunks with a lazy
 //    running maximum (below); the denominator is a matrix product against an
 //    all-ones operand, from the same bf16 P.
-//  * Output tile ct of O^T holds channels 16 ct .. 16 ct + 15; a lane holds 4
-//    consecutive channels of its query per tile (two 8-byte stores).
+//  * Row r of output tile ct of O^T is channel 8 (r / 4) + 4 ct + r % 4, so
+//    a lane holds 8 consecutive channels of its query over the two tiles
+//    (one 16-byte store; with 4 channels per tile and two 8-byte stores, 1.8
+//    times O's bytes reached memory).
 #include "bra_internal.h"
 #include "attn_common.h"
 
@@ -142,7 +144,7 @@ __device__ __forceinline__ int issue_phase(const DenseParams& p, const int* rtab
 // Scores, softmax and P.V for one 64-key chunk. kl: this lane's K operand
 // row of the chunk (key 8 (col / 4) + col % 4, chunk g swizzled), vl[ct]:
 // this lane's transposing-read address of tile ct (key row 8g + col / 4,
-// channels 16 ct + 4 (col % 4)); the rest of each address is a constant.
+// channels 8 (col % 4) + 4 ct); the rest of each address is a constant.
 // nvalid: keys of the chunk below kv (RAGGED only).
 //
 // Online softmax with a lazy maximum: a lane's running maximum m moves only
@@ -195,11 +197,10 @@ __device__ __forceinline__ void dense_chunk(const DenseParams& p, const unsigned
   }
   const float mc = m_run * p.c;
   // ---- O^T += V^T P^T over the chunk's two 32-key steps. The V^T operand
-  // of tile ct, lane group g: row = channel 16 ct + lane % 16, slots = keys
-  // st*32 + 8g .. +7, from two transposing reads (keys +0..3, +4..7). In a
-  // read, lane col = 4 s + q of the group reads key row 8g + s at channels
-  // 16 ct + 4 q .. +3, so that lane j of the group receives channel
-  // 16 ct + j of the four keys.
+  // of tile ct, lane group g: slots = keys st*32 + 8g .. +7, from two
+  // transposing reads (keys +0..3, +4..7). In a read, lane col = 4 s + q of
+  // the group reads key row 8g + s at channels 8 q + 4 ct .. +3, so that lane
+  // j of the group receives channel 8 (j / 4) + 4 ct + j % 4 of the four keys.
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     float pe[8];
@@ -314,8 +315,8 @@ __global__ __launch_bounds__(kDenseTiles * 64) void attend_dense_kernel(DensePar
     // rows a lane reads do not change from chunk to chunk)
     const unsigned char* kl = kbuf + k_off(8 * (col >> 2) + (col & 3), g);
     const int srow = col >> 2, q = col & 3;
-    const unsigned char* vl0 = vbuf + v_off(8 * g + srow, q >> 1) + (q & 1) * 8;
-    const unsigned char* vl1 = vbuf + v_off(8 * g + srow, 2 + (q >> 1)) + (q & 1) * 8;
+    const unsigned char* vl0 = vbuf + v_off(8 * g + srow, q);      // channels 8 q .. +3
+    const unsigned char* vl1 = vbuf + v_off(8 * g + srow, q) + 8;  // channels 8 q + 4 .. +7
     // the phase's chunks unrolled, so every operand address is the lane's
     // base plus a constant (dense map: 24.0 -> 23.4 us)
 #pragma unroll
@@ -331,21 +332,17 @@ __global__ __launch_bounds__(kDenseTiles * 64) void attend_dense_kernel(DensePar
     }
   }
 
-  // ---- normalise and store: tile ct holds channels 16 ct + 4 g .. + 3
+  // ---- normalise and store: tile ct holds channels 8 g + 4 ct .. + 3, so
+  // the lane's 8 channels are one 16-byte store
   if (!qvalid) return;
-  __bf16* Og = p.O + img + qoff;
   const float inv = bad ? __builtin_nanf("") : 1.0f / acc[2][0];
+  float o[8];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    bf16x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      const bf16x2 t = __builtin_convertvector(floatx2{acc[ct][e] * inv, acc[ct][e + 1] * inv}, bf16x2);
-      o[e] = t[0];
-      o[e + 1] = t[1];
-    }
-    __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(Og + 16 * ct + 4 * g));
+  for (int e = 0; e < 4; ++e) {
+    o[e] = acc[0][e] * inv;
+    o[4 + e] = acc[1][e] * inv;
   }
+  TT::store8_nt(p.O + img + qoff + 8 * g, o);
 }
 
 }  // namespace

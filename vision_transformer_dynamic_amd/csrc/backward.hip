@@ -79,13 +79,14 @@ __device__ inline int corner_of(const BwdParams& p, int r) {
 __device__ inline int xcd_remap(int skip = 0) { return xcd_item(blockIdx.x - skip, gridDim.x - skip); }
 
 // ---------------------------------------------------------------------------
-// 1. Inverse routing table of image b, by one workgroup (a multiple of 64
-// threads) in lds: R rows of (R + 31) / 32 mask words, then R row flags. Each
-// routing row becomes a bit mask of its regions (bitwise OR is order-free);
-// then one wave per key region tests 64 rows at a time and places the good
-// rows that hold it with a ballot prefix count, so each list comes out
-// ascending.
-__device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds) {
+// 1. Inverse routing table of image b, key regions [r0, r1), by one
+// workgroup (a multiple of 64 threads) in lds: R rows of (R + 31) / 32 mask
+// words, then R row flags and R in-degrees. Each routing row becomes a bit
+// mask of its regions (bitwise OR is order-free); the in-degree of every key
+// region is a count over the good rows; then one wave per key region of the
+// range tests 64 rows at a time and places the good rows that hold it with a
+// ballot prefix count, so each list comes out ascending.
+__device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds, int r0, int r1) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int R = p.R, k = p.topk, nw = (R + 31) >> 5;
   uint32_t* mask = lds;                                  // [R][nw]
@@ -110,10 +111,16 @@ __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds) {
     if (cnt != k) rowbad[i] = 1;
   }
   __syncthreads();
-  // wave w compacts the lists of key regions w, w + nwaves, ...
+  for (int r = tid; r < R; r += nt) {
+    int m = 0;
+    for (int i = 0; i < R; ++i) m += !rowbad[i] && ((mask[i * nw + (r >> 5)] >> (r & 31)) & 1u);
+    deg[r] = m;
+  }
+  __syncthreads();
+  // wave w compacts the lists of key regions r0 + w, r0 + w + nwaves, ...
   const int wave = tid >> 6, lane = tid & 63, nwaves = nt >> 6;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int r = wave; r < R; r += nwaves) {
+  for (int r = r0 + wave; r < r1; r += nwaves) {
     int* L = p.inv_list + ((int64_t)b * R + r) * R;
     int m = 0;
     for (int i0 = 0; i0 < R; i0 += 64) {
@@ -123,15 +130,11 @@ __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds) {
       if (hit) L[m + __popcll(bal & below)] = i;
       m += __popcll(bal);
     }
-    if (lane == 0) {
-      p.inv_cnt[b * R + r] = m;
-      deg[r] = m;
-    }
+    if (lane == 0) p.inv_cnt[b * R + r] = m;
   }
-  __syncthreads();
   // the dK/dV kernel's order: key region r goes to place #{heavier, or as
   // heavy with a lower index}
-  for (int r = tid; r < R; r += nt) {
+  for (int r = r0 + tid; r < r1; r += nt) {
     p.bad[b * R + r] = rowbad[r];
     const int dr = deg[r];
     int place = 0;
@@ -143,10 +146,14 @@ __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds) {
 // LDS bytes of inverse_table
 constexpr size_t inverse_table_lds(int R) { return sizeof(uint32_t) * ((size_t)R * ((R + 31) / 32) + 2 * R); }
 
-// For more than 64 regions: a launch of its own, one workgroup per image.
+// For more than 64 regions: a launch of its own, one workgroup per (image,
+// block of kRoutesBlock key regions); each rebuilds the image's masks.
+constexpr int kRoutesBlock = 16;
 __global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
   __shared__ uint32_t lds[kMaxRegions * (kMaxRegions / 32) + 2 * kMaxRegions];
-  inverse_table(p, blockIdx.x, lds);
+  const int nblk = (p.R + kRoutesBlock - 1) / kRoutesBlock;
+  const int b = blockIdx.x / nblk, r0 = (blockIdx.x - b * nblk) * kRoutesBlock;
+  inverse_table(p, b, lds, r0, min(p.R, r0 + kRoutesBlock));
 }
 
 // Chunk token table: tok[kappa - c0] = token (inside the image) of routed key
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
     // one of the first B workgroups (when the launch builds the inverse
     // routing table): the table of image blockIdx.x, in this kernel's dynamic
     // LDS. They come first in dispatch order, so their slots free up at once.
-    inverse_table(p, blockIdx.x, reinterpret_cast<uint32_t*>(smem_raw));
+    inverse_table(p, blockIdx.x, reinterpret_cast<uint32_t*>(smem_raw), 0, p.R);
     return;
   }
   int w = xcd_remap(p.ntab);
@@ -918,7 +925,8 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   const bool fold = !multi && s.R <= 64;
   const int extra = fold ? s.B : 0;
   if (!fold) {
-    e = hipLaunchKernel((const void*)&bwd_routes_kernel, dim3(s.B), dim3(256), args, 0, stream);
+    const unsigned nblk = (unsigned)((s.R + kRoutesBlock - 1) / kRoutesBlock);
+    e = hipLaunchKernel((const void*)&bwd_routes_kernel, dim3(s.B * nblk), dim3(256), args, 0, stream);
     if (e != hipSuccess) return e;
   }
 

@@ -91,15 +91,6 @@ __device__ inline shortx4 read_tr(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
 }
 
-// Four fp32 values as 4 bf16 (8 bytes), non-temporal: the gradients are not
-// read again by this kernel.
-__device__ inline void store4_nt(__bf16* dst, float a, float b, float c, float d) {
-  const bf16x2 lo = __builtin_convertvector(floatx2{a, b}, bf16x2);
-  const bf16x2 hi = __builtin_convertvector(floatx2{c, d}, bf16x2);
-  const bf16x4 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
-  __builtin_nontemporal_store(v, reinterpret_cast<bf16x4*>(dst));
-}
-
 // Region j of a tile packed as byte j of one word (0xFF: none), so that a
 // lane-varying j is a shift and not an index into a private array (which
 // would go to scratch memory).
@@ -318,10 +309,11 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
       for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f((s[st][e] - mx) * p.c);
     const float lse = mx * p.c + __builtin_log2f(wave_sum_groups(sum));
 
-    // dQ^T = sum_j K_j^T dZ_j^T: the K^T operand of tile ct (rows = channels
-    // 16 ct + lane % 16, slots = keys st*32 + 8g .. +7) from two transposing
-    // reads, in which lane col = 4 s + q reads key row st*32 + 8g + s (+4) at
-    // channels 16 ct + 4 q .. +3
+    // dQ^T = sum_j K_j^T dZ_j^T: the K^T operand of tile ct (slots = keys
+    // st*32 + 8g .. +7) from two transposing reads, in which lane col = 4 s + q
+    // reads key row st*32 + 8g + s (+4) at channels 8 q + 4 ct .. +3, so that
+    // row r of the tile is channel 8 (r / 4) + 4 ct + r % 4 and each lane ends
+    // with 8 consecutive channels of its query (one 16-byte store)
     floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -339,20 +331,23 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
         const int p1 = lane_value(kpos[j], st * 32 + 8 * g + 4 + srow);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const shortx4 lo = read_tr(Ks + p0 * kRowE + 16 * ct + 4 * q4);
-          const shortx4 hi = read_tr(Ks + p1 * kRowE + 16 * ct + 4 * q4);
+          const shortx4 lo = read_tr(Ks + p0 * kRowE + 8 * q4 + 4 * ct);
+          const shortx4 hi = read_tr(Ks + p1 * kRowE + 8 * q4 + 4 * ct);
           const op8 kt = __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           dq[ct] = TT::mma(kt, zj, dq[ct]);
         }
       }
     }
     if (qv) {
-      // tile ct: this lane holds channels 16 ct + 4g .. +3 of its query
-      __bf16* dst_q = p.dQ + img + pos_token(p, qpos) * p.C + ch0 + 4 * g;
+      // tile ct: this lane holds channels 8g + 4 ct .. +3 of its query
       const float f = bad ? __builtin_nanf("") : p.scale;
+      float o[8];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        store4_nt(dst_q + 16 * ct, dq[ct][0] * f, dq[ct][1] * f, dq[ct][2] * f, dq[ct][3] * f);
+      for (int e = 0; e < 4; ++e) {
+        o[e] = dq[0][e] * f;
+        o[4 + e] = dq[1][e] * f;
+      }
+      TT::store8_nt(p.dQ + img + pos_token(p, qpos) * p.C + ch0 + 8 * g, o);
       if (g == 0) {
         lse_s[qpos] = lse;
         dd_s[qpos] = Dq;
@@ -434,30 +429,34 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
       }
       const op4 pB = TT::from_f32_4(pr);
       const op4 zB = TT::from_f32_4(dz);
-      // dV^T += dO^T P and dK^T += Q^T dZ: A operand of tile ct (rows =
-      // channels 16 ct + lane % 16, slots = slots 4g .. +3) by a transposing
-      // read in which lane col = 4 s + q reads slot row 4g + s at channels
-      // 16 ct + 4 q .. +3
+      // dV^T += dO^T P and dK^T += Q^T dZ: A operand of tile ct (slots =
+      // slots 4g .. +3) by a transposing read in which lane col = 4 s + q reads
+      // slot row 4g + s at channels 8 q + 4 ct .. +3 (row r of the tile is
+      // channel 8 (r / 4) + 4 ct + r % 4, as in phase 1)
       const int ts = 4 * g + srow;
       const int tr = tile_region(qpk, ts / N);
       const int tpos = tr >= 0 ? tr * N + ts % N : 0;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const op4 dOA = read_tr(Ds + tpos * kRowE + 16 * ct + 4 * q4);
-        const op4 QA = read_tr(Qs + tpos * kRowE + 16 * ct + 4 * q4);
+        const op4 dOA = read_tr(Ds + tpos * kRowE + 8 * q4 + 4 * ct);
+        const op4 QA = read_tr(Qs + tpos * kRowE + 8 * q4 + 4 * ct);
         dv[ct] = TT::mma16(dOA, pB, dv[ct]);
         dk[ct] = TT::mma16(QA, zB, dk[ct]);
       }
     }
     if (kvld) {
-      // tile ct: this lane holds channels 16 ct + 4g .. +3 of its key
-      const int off = pos_token(p, kp) * p.C + ch0 + 4 * g;
+      // tile ct: this lane holds channels 8g + 4 ct .. +3 of its key
+      const int off = pos_token(p, kp) * p.C + ch0 + 8 * g;
+      float ov[8], ok[8];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        store4_nt(p.dV + img + off + 16 * ct, dv[ct][0], dv[ct][1], dv[ct][2], dv[ct][3]);
-        store4_nt(p.dK + img + off + 16 * ct, dk[ct][0] * p.scale, dk[ct][1] * p.scale, dk[ct][2] * p.scale,
-                  dk[ct][3] * p.scale);
+      for (int e = 0; e < 4; ++e) {
+        ov[e] = dv[0][e];
+        ov[4 + e] = dv[1][e];
+        ok[e] = dk[0][e] * p.scale;
+        ok[4 + e] = dk[1][e] * p.scale;
       }
+      TT::store8_nt(p.dV + img + off, ov);
+      TT::store8_nt(p.dK + img + off, ok);
     }
   }
 }
