@@ -55,6 +55,11 @@ def test_workload_backward(w):
     _check_backward(w)
 
 
+@pytest.mark.parametrize("w", wl.DETECTION, ids=[w.name for w in wl.DETECTION])
+def test_detection_backward(w):
+    _check_backward(w, images=list(range(w.B)))
+
+
 @pytest.mark.parametrize("w", EDGE, ids=[w.name for w in EDGE])
 def test_edge_shapes_backward(w):
     _check_backward(w, images=list(range(w.B)))
