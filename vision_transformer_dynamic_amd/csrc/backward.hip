@@ -420,6 +420,9 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
   constexpr int PAIRS = KC / 2 * CVH / 64;  // (key pair, vector) items of the K^T tile per lane
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int wtok[8 * KC];  // per wave: token of every routed key, -1 past kv
+  // two heads' dQ halves of a tile's query rows, per tile parity (bf16: 16
+  // queries x 8 chunks of 16 bytes)
+  __shared__ __align__(16) uint4 xrow[sizeof(T) == 2 ? 2 * 16 * 8 : 1];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -441,7 +444,11 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
   const int i = w % p.R;
   const int b = w / p.R;
   const int head = hg * p.HG + wave;
-  if (head >= p.heads) return;  // wave-uniform; no barrier in this kernel
+  if (head >= p.heads) return;  // wave-uniform; the only barrier below needs both heads present
+  // bf16 with two heads per workgroup: the head waves exchange their halves
+  // of every dQ row through LDS and store whole 128-byte rows (uniform per
+  // workgroup: both waves are present and share the routing row)
+  const bool rows = sizeof(T) == 2 && p.HG == 2 && hg * 2 + 1 < p.heads;
   const int ch0 = head * D;
   const int64_t img = (int64_t)b * p.H * p.W * p.C;
   const T* Kg = static_cast<const T*>(p.K) + img;
@@ -619,11 +626,32 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
         o[e] = dq[0][e] * p.scale;
         o[4 + e] = dq[1][e] * p.scale;
       }
-      TT::store8_nt(dQg + qtok[t] * p.C + ch0 + 8 * g, o);
+      if constexpr (sizeof(T) == 2) {
+        if (rows) xrow[(t & 1) * 128 + col * 8 + wave * 4 + g] = __builtin_bit_cast(uint4, TT::from_f32(o));
+        else TT::store8_nt(dQg + qtok[t] * p.C + ch0 + 8 * g, o);
+      } else {
+        TT::store8_nt(dQg + qtok[t] * p.C + ch0 + 8 * g, o);
+      }
       if (g == 0) {
         const int64_t at = ((int64_t)b * p.H * p.W + qtok[t]) * p.heads + head;
         p.lse[at] = lse;
         p.dd[at] = Dq[t];
+      }
+    }
+    if constexpr (sizeof(T) == 2) {
+      if (rows) {
+        // whole 128-byte rows of the two heads: wave h stores queries 8h ..
+        // 8h + 7 of the tile (tile parities alternate: one barrier per tile)
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        const int q = 8 * wave + (lane >> 3), c = lane & 7;
+        const int tq = __builtin_amdgcn_ds_bpermute(q << 2, qtok[t]);  // lane q holds query q's token
+        if (tq >= 0) {
+          const uint4 v = xrow[(t & 1) * 128 + q * 8 + c];
+          __builtin_nontemporal_store(__builtin_bit_cast(op8, v),
+                                      reinterpret_cast<op8*>(dQg + tq * p.C + hg * p.HG * D + 8 * c));
+        }
       }
     }
   }
@@ -837,9 +865,13 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
 
   T* dKg = static_cast<T*>(p.dK) + img;
   T* dVg = static_cast<T*>(p.dV) + img;
+  // bf16 with two heads: the head waves of one key half exchange their
+  // 64-byte halves of every dK and dV row through the (now free) stage LDS,
+  // and wave (head h, key half kh) stores whole 128-byte rows of key tile h
+  // of that half (uniform per workgroup)
+  const bool rows = sizeof(T) == 2 && p.HGk == 2 && hg * 2 + 1 < p.heads;
 #pragma unroll
   for (int kt2 = 0; kt2 < 2; ++kt2) {
-    if (!kval[kt2]) continue;
     float ov[8], ok[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -848,9 +880,40 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
       ok[e] = dk[0][kt2][e] * p.scale;
       ok[4 + e] = dk[1][kt2][e] * p.scale;
     }
+    if constexpr (sizeof(T) == 2) {
+      if (rows) {
+        // [tensor][key half][key tile][key][head][chunk]
+        uint4* xr = reinterpret_cast<uint4*>(smem_raw);
+        const int at = ((kh * 2 + kt2) * 16 + col) * 8 + hl * 4 + g;
+        xr[at] = __builtin_bit_cast(uint4, TT::from_f32(ov));
+        xr[512 + at] = __builtin_bit_cast(uint4, TT::from_f32(ok));
+        continue;
+      }
+    }
+    if (!kval[kt2]) continue;
     const int off = ktok[kt2] * p.C + ch0 + 8 * g;
     TT::store8_nt(dVg + off, ov);
     TT::store8_nt(dKg + off, ok);
+  }
+  if constexpr (sizeof(T) == 2) {
+    if (rows) {
+      __syncthreads();
+      const uint4* xr = reinterpret_cast<const uint4*>(smem_raw);
+      const int kt2 = hl;  // this wave stores key tile hl of its key half
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int kc = 8 * h8 + (lane >> 3), c = lane & 7;  // key of the tile, 16-byte chunk of the row
+        const int key = kb * 64 + kh * 32 + kt2 * 16 + kc;
+        if (key < p.n) {
+          int tx;
+          const int ty = fdiv(key, p.div_sw, &tx);
+          const int off = (rcorner + ty * p.W + tx) * p.C + hg * 2 * D + 8 * c;
+          const int at = ((kh * 2 + kt2) * 16 + kc) * 8 + c;
+          __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[at]), reinterpret_cast<op8*>(dVg + off));
+          __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[512 + at]), reinterpret_cast<op8*>(dKg + off));
+        }
+      }
+    }
   }
 }
 
