@@ -217,3 +217,81 @@ def test_image_resident_bad_route_row(kind):
                             _f64(g.cpu()[:1]) * _region_mask(w, 5), w.heads, w.S)
     for name, out, r in zip(("dK", "dV"), (dk, dv), ref[1:]):
         parity.assert_grad_close(_f64(out.cpu()[:1]), r, "bf16", name)
+
+
+# Shapes the one-launch top-1 backward takes (bf16, top-k = 1, regions of 16
+# to 64 tokens): full and ragged regions, one to four 16-row tiles, an odd
+# head count (the last pair has one head), more than 64 regions (several
+# ballot steps of the routing column), H != W.
+TOP1_BWD = [
+    wl.custom(2, 56, 56, 64, 2, 7, 1, "bf16", seed=110),    # n = 64, 49 regions (the first stage's shape)
+    wl.custom(2, 56, 56, 96, 3, 8, 1, "bf16", seed=111),    # n = 49, three heads
+    wl.custom(1, 72, 72, 64, 2, 9, 1, "bf16", seed=112),    # n = 64, 81 regions
+    wl.custom(2, 24, 24, 128, 4, 4, 1, "bf16", seed=113),   # n = 36, two pairs of heads
+    wl.custom(1, 64, 64, 32, 1, 16, 1, "bf16", seed=114),   # n = 16, one head, 256 regions
+    wl.custom(2, 40, 60, 64, 2, 5, 1, "bf16", seed=115, content="clustered"),  # n = 8 x 12 = 96: not taken
+    wl.custom(2, 35, 42, 64, 2, 7, 1, "bf16", seed=116),    # n = 5 x 6 = 30, H != W
+]
+
+
+@pytest.mark.parametrize("w", TOP1_BWD, ids=[w.name for w in TOP1_BWD])
+def test_top1_backward(w):
+    _check_backward(w, images=list(range(w.B)))
+
+
+def test_top1_backward_is_deterministic():
+    w = TOP1_BWD[1]
+    q, k, v = wl.make_inputs(w)
+    g = wl.make_grad_output(w)
+    _, _, dq, dk, dv = _run(w, q, k, v, g)
+    _, _, dq2, dk2, dv2 = _run(w, q, k, v, g)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+def test_top1_backward_one_popular_region():
+    """Planted routing: every query region of image 0 routes to region 3 (a
+    list of all 49 regions for one workgroup, every other key region
+    unrouted); image 1 keeps its own routing."""
+    w = TOP1_BWD[0]
+    q, k, v = (t.to(DEV) for t in wl.make_inputs(w))
+    g = wl.make_grad_output(w).to(DEV)
+    idx = bra.route(q, k, w.S, w.topk)
+    idx[0] = 3
+    o = bra.attend(q, k, v, idx, w.heads, w.S)
+    dq, dk, dv = bra.attend_backward(q, k, v, o, g, idx, w.heads, w.S)
+    torch.cuda.synchronize()
+    ys, xs = (torch.as_tensor(a) for a in O.region_token_coords(w.H, w.W, w.S, 3))
+    keep = torch.zeros(w.H, w.W, dtype=torch.bool)
+    keep[ys, xs] = True
+    assert torch.all(dk[0].cpu()[~keep] == 0) and torch.all(dv[0].cpu()[~keep] == 0)
+    ref = O.attend_backward(_f64(q.cpu()), _f64(k.cpu()), _f64(v.cpu()), idx.cpu().numpy(), _f64(g.cpu()),
+                            w.heads, w.S)
+    for name, out, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        parity.assert_grad_close(_f64(out.cpu()), r, "bf16", name)
+
+
+def test_top1_bad_route_row():
+    """The bad-row rule on the top-1 backward: an entry outside [0, S*S) in
+    row 5 gives NaN dQ for region 5's queries only, which are left out of dK
+    and dV; image 1 is that of the good table, bit for bit."""
+    w = TOP1_BWD[0]
+    q, k, v = (t.to(DEV) for t in wl.make_inputs(w))
+    g = wl.make_grad_output(w).to(DEV)
+    idx = bra.route(q, k, w.S, w.topk)
+    o = bra.attend(q, k, v, idx, w.heads, w.S)
+    bad = idx.clone()
+    bad[0, 5, 0] = w.R
+    dq, dk, dv = bra.attend_backward(q, k, v, o, g, bad, w.heads, w.S)
+    dq0, dk0, dv0 = bra.attend_backward(q, k, v, o, g, idx, w.heads, w.S)
+    torch.cuda.synchronize()
+    ys, xs = (torch.as_tensor(a) for a in O.region_token_coords(w.H, w.W, w.S, 5))
+    dqf = dq.float().cpu()
+    assert torch.isnan(dqf[0, ys, xs]).all()
+    dqf[0, ys, xs] = 0
+    assert not torch.isnan(dqf).any()
+    assert not torch.isnan(dk).any() and not torch.isnan(dv).any()
+    assert torch.equal(dq[1:], dq0[1:]) and torch.equal(dk[1:], dk0[1:]) and torch.equal(dv[1:], dv0[1:])
+    ref = O.attend_backward(_f64(q.cpu()[:1]), _f64(k.cpu()[:1]), _f64(v.cpu()[:1]), idx.cpu().numpy()[:1],
+                            _f64(g.cpu()[:1]) * _region_mask(w, 5), w.heads, w.S)
+    for name, out, r in zip(("dK", "dV"), (dk, dv), ref[1:]):
+        parity.assert_grad_close(_f64(out.cpu()[:1]), r, "bf16", name)

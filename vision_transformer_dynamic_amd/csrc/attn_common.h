@@ -51,6 +51,16 @@ struct Tr<__bf16> {
     }
     return r;
   }
+  // The rounding error of hi = from_f32(v), itself rounded: hi + lo carries
+  // about 16 bits of v. The dQ products take dZ this way: dQ = sum_j dZ_j k_j
+  // cancels the keys' common part (a query's dZ sum to zero), which would
+  // amplify an 8-bit rounding of dZ by |k| / |k - mean k|.
+  __device__ static inline op8 residual(const float* v, op8 hi) {
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = v[e] - (float)hi[e];
+    return from_f32(r);
+  }
   __device__ static inline op8 zero() {
     op8 r;
 #pragma unroll

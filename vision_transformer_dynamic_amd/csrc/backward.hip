@@ -382,6 +382,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdParams p) {
         const int row = vrow + 4 * ct;
         const op8 kt = TT::load8(Kt + row * ldk + vt_col(row, st * 32 + 8 * g));
         dq[ct] = TT::mma(kt, zop, dq[ct]);
+        if constexpr (sizeof(T) == 2) dq[ct] = TT::mma(kt, TT::residual(dz, zop), dq[ct]);  // dZ's low bits
       }
     }
     __syncthreads();  // tok and K^T reused by the next chunk
@@ -617,6 +618,7 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
         const int row = vrow + 4 * ct;
         const op8 kt = TT::load8(Kt + row * ldk + vt_col(row, st * 32 + 8 * g));
         dq[ct] = TT::mma(kt, zop, dq[ct]);
+        if constexpr (sizeof(T) == 2) dq[ct] = TT::mma(kt, TT::residual(dz, zop), dq[ct]);  // dZ's low bits
       }
     }
     if (qtok[t] >= 0) {
@@ -931,6 +933,7 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
                            const int32_t* idx, void* dQ, void* dK, void* dV, void* ws, const Shape& s, int dtype,
                            hipStream_t stream) {
   if (backward_image_fits(s, dtype)) return launch_backward_image(Q, K, V, O, dO, idx, dQ, dK, dV, s, stream);
+  if (backward_top1_fits(s, dtype)) return launch_backward_top1(Q, K, V, dO, idx, dQ, dK, dV, s, stream);
   BwdParams p{};
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.dO = dO; p.idx = idx;
   p.dQ = dQ; p.dK = dK; p.dV = dV;

@@ -324,9 +324,11 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
         dz[e] = pr * (dp[st][e] - Dq);
       }
       const op8 zop = TT::from_f32(dz);
+      const op8 zlo = TT::residual(dz, zop);  // dZ's low bits
 #pragma unroll
       for (int j = 0; j < QR; ++j) {
         const op8 zj = (QR == 1 || jl == j) ? zop : TT::zero();
+        const op8 zjl = (QR == 1 || jl == j) ? zlo : TT::zero();
         const int p0 = lane_value(kpos[j], st * 32 + 8 * g + srow);
         const int p1 = lane_value(kpos[j], st * 32 + 8 * g + 4 + srow);
 #pragma unroll
@@ -335,6 +337,7 @@ __global__ __launch_bounds__(1024) void bwd_image_kernel(BwdImgParams p) {
           const shortx4 hi = read_tr(Ks + p1 * kRowE + 8 * q4 + 4 * ct);
           const op8 kt = __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           dq[ct] = TT::mma(kt, zj, dq[ct]);
+          dq[ct] = TT::mma(kt, zjl, dq[ct]);
         }
       }
     }

@@ -1,0 +1,399 @@
+// Backward of the token attention with top-1 routing (BiFormer's first
+// stage: every query region attends to the tokens of exactly one key region)
+// in one launch (explainer "BiFormer Reshapes Visual Attention with
+// 'Bi-Level Routing'", Part 2.2 step 4 and pseudocode steps 6-7 for the
+// forward; Part 4.3 for top-k = 1 at the first stage; Part 7 for training
+// throughput). The routing table is held fixed:
+//
+//   P = softmax(c' q k^T), dP = dO V_g^T, D = rowsum(P * dP),
+//   dZ = P * (dP - D), dQ = scale * dZ K_g, dK_g = scale * dZ^T Q, dV_g = P^T dO
+//
+// With one routed region per query region, all of a query's keys are one
+// region's tokens, so the workgroup of key region r sees every key of each
+// query region routed to r and finishes that region's dQ (no log-sum-exp or D
+// goes through memory), and it is the only one to add to dK and dV of r's
+// tokens (no atomics, no second launch). One workgroup per (image, key
+// region, pair of heads), 8 waves (head of the pair, 16-row tile):
+//
+//  * The routing column: each wave ballots idx[b, :] == r in region order, so
+//    the incoming query regions are taken in ascending order (deterministic
+//    sums). A region whose own row is outside [0, S*S) gets NaN dQ from its
+//    own key region's workgroup and is in no list.
+//  * K, V of region r and Q, dO of the incoming region go to LDS (the pair's
+//    128-byte rows, 16 bytes a thread); the next region's Q, dO are fetched
+//    into registers while the current one is processed.
+//  * Phase 1 per (head, query tile): S^T = K Q^T and dP^T = V dO^T over the
+//    region's keys, then the softmax, D = rowsum(P * dP) (equal to
+//    rowsum(dO * O) for O = P V, without reading O), dZ and
+//    dQ^T = K^T dZ^T with K^T from gfx950's transposing LDS read. Log-sum-exp
+//    and D go to LDS; the pair's dQ halves meet in LDS and leave as whole
+//    128-byte rows.
+//  * Phase 2 per (head, key tile): S = Q K^T and dP = dO V^T again with the
+//    key as the column, so P and dZ are B operands as they stand:
+//    dV^T += dO^T P and dK^T += Q^T dZ (16-deep products, dO^T and Q^T by the
+//    transposing read), summed over the incoming regions in registers.
+//  * dK and dV rows leave once at the end (zero for a region nobody routes to).
+#include "bra_internal.h"
+#include "attn_common.h"
+
+#include <math.h>
+
+namespace bra {
+namespace {
+
+constexpr int kRowT = 40;  // LDS row stride in elements: 32 channels + 16 bytes of pad
+constexpr int kHeadRows = 64 * kRowT;  // one head's rows of one tensor
+constexpr int kTop1Threads = 512;
+
+struct BwdTop1Params {
+  const __bf16* Q;
+  const __bf16* K;
+  const __bf16* V;
+  const __bf16* dO;
+  const int32_t* idx;
+  __bf16* dQ;
+  __bf16* dK;
+  __bf16* dV;
+  int H, W, C, S, sh, sw, n, R, heads;
+  int nhg;      // pairs of heads
+  float c;      // scale * log2(e)
+  float scale;  // 1 / sqrt(d)
+  FastDiv div_sw, div_S;
+};
+
+typedef __attribute__((address_space(3))) shortx4 lds_s4;
+
+// Transposing LDS read of 4 bf16 (8 bytes) at p: within each 16-lane group,
+// lane j receives element j % 4 of the reads of lanes 4 s + j / 4, s = 0..3.
+__device__ inline shortx4 read_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+}
+
+// Token offset of region i's top-left token inside the image.
+__device__ inline int region_corner(const BwdTop1Params& p, int i) {
+  int rx;
+  const int ry = fdiv(i, p.div_S, &rx);
+  return ry * p.sh * p.W + rx * p.sw;
+}
+
+// RAGGED: fewer than 64 tokens per region (the scores of the missing keys
+// are masked; their rows are zero in LDS).
+template <bool RAGGED>
+__global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p) {
+  typedef Tr<__bf16> TT;
+  typedef TT::op8 op8;
+  typedef TT::op4 op4;
+  // K, V, Q, dO rows [head][64][kRowT] (Q and dO then hold the dK, dV rows
+  // at the end), log-sum-exp and D [head][64], the dQ rows [64][8 chunks],
+  // the incoming query regions
+  __shared__ __align__(16) __bf16 rows_s[4 * 2 * kHeadRows];
+  __shared__ __align__(16) float lse_s[2 * 64];
+  __shared__ __align__(16) float dd_s[2 * 64];
+  __shared__ __align__(16) uint4 xq[64 * 8];
+  __shared__ int qlist[kMaxRegions];
+  __bf16* Ks = rows_s;
+  __bf16* Vs = Ks + 2 * kHeadRows;
+  __bf16* Qs = Vs + 2 * kHeadRows;
+  __bf16* Ds = Qs + 2 * kHeadRows;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4, col = lane & 15;
+  const int hl = wave >> 2, tq = wave & 3;  // head of the pair, tile
+  const int srow = col >> 2, q4 = col & 3;  // transposing reads: row offset, 4-channel block
+
+  int w = blockIdx.x;
+  const int hg = w % p.nhg;
+  w /= p.nhg;
+  const int r = w % p.R;
+  const int b = w / p.R;
+  const int nh = min(2, p.heads - 2 * hg);  // heads in the pair (the last pair of an odd count has one)
+  const int cb = 2 * hg * D;               // the pair's first channel
+  const int64_t img = (int64_t)b * p.H * p.W * p.C;
+  const int32_t* irow = p.idx + (int64_t)b * p.R;
+  const int ntq = (p.n + 15) >> 4;         // 16-row tiles of a region (queries and keys alike)
+  const bool busy = tq < ntq && hl < nh;   // the wave has rows in both phases (uniform)
+
+  // staging item of this thread: token tid / 8 of a region, 16-byte chunk
+  // tid % 8 of the pair's 128-byte row (chunk / 4 = head)
+  const int st_tok = tid >> 3, st_c = tid & 7;
+  const bool st_ok = st_tok < p.n && (st_c >> 2) < nh;
+  int st_tx;
+  const int st_off = fdiv(st_tok, p.div_sw, &st_tx) * p.W + st_tx;
+  const int st_at = ((st_c >> 2) * 64 + st_tok) * kRowT + 8 * (st_c & 3);
+  const int64_t st_g = img + cb + 8 * st_c;  // + token * C
+
+  // ---- K and V of key region r
+  const int rcorner = region_corner(p, r);
+  uint4 kst = make_uint4(0, 0, 0, 0), vst = kst;
+  if (st_ok) {
+    const int64_t off = st_g + (int64_t)(rcorner + st_off) * p.C;
+    kst = *reinterpret_cast<const uint4*>(p.K + off);
+    vst = *reinterpret_cast<const uint4*>(p.V + off);
+  }
+
+  // ---- the query regions routed to r, ascending (one 64-region ballot per
+  // step; at most kMaxRegions regions)
+  int cnt = 0, first = -1;
+#pragma unroll
+  for (int j = 0; j < kMaxRegions / 64; ++j) {
+    if (64 * j < p.R) {  // uniform
+      const int e = 64 * j + lane;
+      const int v = e < p.R ? irow[e] : -1;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(v == r);
+      if (first < 0 && hit != 0) first = 64 * j + __builtin_ctzll(hit);
+      if (wave == 0 && v == r) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(hit >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)hit, 0));
+        qlist[cnt + below] = e;
+      }
+      cnt += __builtin_popcountll(hit);
+    }
+  }
+  const int own = irow[r];
+  const bool own_bad = own < 0 || own >= p.R;
+
+  // ---- Q and dO of the first incoming region, into registers
+  uint4 qst = make_uint4(0, 0, 0, 0), dst = qst;
+  if (cnt > 0 && st_ok) {
+    const int64_t off = st_g + (int64_t)(region_corner(p, first) + st_off) * p.C;
+    qst = *reinterpret_cast<const uint4*>(p.Q + off);
+    dst = *reinterpret_cast<const uint4*>(p.dO + off);
+  }
+  *reinterpret_cast<uint4*>(Ks + st_at) = kst;
+  *reinterpret_cast<uint4*>(Vs + st_at) = vst;
+
+  const __bf16* Kh = Ks + hl * kHeadRows;
+  const __bf16* Vh = Vs + hl * kHeadRows;
+  const __bf16* Qh = Qs + hl * kHeadRows;
+  const __bf16* Dh = Ds + hl * kHeadRows;
+  float* lse_h = lse_s + hl * 64;
+  float* dd_h = dd_s + hl * 64;
+
+  floatx4 dv[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  floatx4 dk[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  for (int it = 0; it < cnt; ++it) {
+    *reinterpret_cast<uint4*>(Qs + st_at) = qst;
+    *reinterpret_cast<uint4*>(Ds + st_at) = dst;
+    __syncthreads();  // Q, dO rows (and K, V, the list on the first pass) in LDS
+    const int iq = qlist[it];
+    if (it + 1 < cnt && st_ok) {
+      const int64_t off = st_g + (int64_t)(region_corner(p, qlist[it + 1]) + st_off) * p.C;
+      qst = *reinterpret_cast<const uint4*>(p.Q + off);
+      dst = *reinterpret_cast<const uint4*>(p.dO + off);
+    }
+
+    // ---- phase 1: dQ, log-sum-exp and D of query tile tq
+    if (busy) {
+      const int qs = tq * 16 + col;
+      const bool qv = !RAGGED || qs < p.n;
+      const op8 qop = TT::load8(Qh + qs * kRowT + 8 * g);
+      const op8 dop = TT::load8(Dh + qs * kRowT + 8 * g);
+      // S^T = K Q^T, dP^T = V dO^T: A-operand row col of tile (st, tb) is key
+      // st*32 + 8*(col/4) + col%4 + 4*tb, so lane group g holds keys
+      // st*32 + 8g + e of its query
+      float s[2][8], dp[2][8];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
+          const op8 kk = TT::load8(Kh + key * kRowT + 8 * g);
+          const op8 vv = TT::load8(Vh + key * kRowT + 8 * g);
+          const floatx4 sa = TT::mma(kk, qop, floatx4{0.f, 0.f, 0.f, 0.f});
+          const floatx4 pa = TT::mma(vv, dop, floatx4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[st][4 * tb + e] = sa[e];
+            dp[st][4 * tb + e] = pa[e];
+          }
+        }
+      if (RAGGED) {
+        // scores of keys past n to -inf by a min against +-inf made with
+        // integer arithmetic (compare masks would be held in scalar registers)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = st * 32 + 8 * g + e;
+            const uint32_t lim = 0xff800000u ^ ((uint32_t)((key - p.n) >> 31) & 0x80000000u);
+            s[st][e] = fminf(s[st][e], __uint_as_float(lim));
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
+      mx = wave_max_groups(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f((s[st][e] - mx) * p.c);
+      const float lse = mx * p.c + __builtin_log2f(wave_sum_groups(sum));
+      // P in place of the scores, then D = rowsum(P * dP)
+      float dpart = 0.f;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s[st][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -lse));
+          dpart = __builtin_fmaf(s[st][e], dp[st][e], dpart);
+        }
+      const float Dq = wave_sum_groups(dpart);
+
+      // dQ^T = K^T dZ^T: the K^T operand of tile ct (slots = keys st*32 + 8g
+      // .. +7) from two transposing reads, in which lane col = 4 s + q reads
+      // key row st*32 + 8g + s (+4) at channels 8 q + 4 ct .. +3, so that row
+      // r of the tile is channel 8 (r / 4) + 4 ct + r % 4 and each lane ends
+      // with 8 consecutive channels of its query
+      floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float dz[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dz[e] = s[st][e] * (dp[st][e] - Dq);
+        const op8 zop = TT::from_f32(dz);
+        const op8 zlo = TT::residual(dz, zop);  // dZ's low bits
+        const int k0 = st * 32 + 8 * g + srow;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const shortx4 lo = read_tr(Kh + k0 * kRowT + 8 * q4 + 4 * ct);
+          const shortx4 hi = read_tr(Kh + (k0 + 4) * kRowT + 8 * q4 + 4 * ct);
+          const op8 kt = __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          dq[ct] = TT::mma(kt, zop, dq[ct]);
+          dq[ct] = TT::mma(kt, zlo, dq[ct]);
+        }
+      }
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = dq[0][e] * p.scale;
+        o[4 + e] = dq[1][e] * p.scale;
+      }
+      xq[qs * 8 + hl * 4 + g] = __builtin_bit_cast(uint4, TT::from_f32(o));
+      if (g == 0) {
+        // a query slot past n: P = 0 in phase 2
+        lse_h[qs] = qv ? lse : INFINITY;
+        dd_h[qs] = qv ? Dq : 0.f;
+      }
+    }
+    __syncthreads();  // dQ rows, log-sum-exp and D in LDS
+
+    if (st_ok) {
+      const int64_t off = st_g + (int64_t)(region_corner(p, iq) + st_off) * p.C;
+      __builtin_nontemporal_store(__builtin_bit_cast(op8, xq[st_tok * 8 + st_c]), reinterpret_cast<op8*>(p.dQ + off));
+    }
+
+    // ---- phase 2: dK, dV of key tile tq over the region's query tiles
+    if (busy) {
+      const int ks = tq * 16 + col;
+      // B operands of S = Q K^T and dP = dO V^T: column = key ks, slots = channels 8g ..
+      const op8 kB = TT::load8(Kh + ks * kRowT + 8 * g);
+      const op8 vB = TT::load8(Vh + ks * kRowT + 8 * g);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        if (qt >= ntq) break;  // uniform
+        const op8 qA = TT::load8(Qh + (qt * 16 + col) * kRowT + 8 * g);
+        const op8 dA = TT::load8(Dh + (qt * 16 + col) * kRowT + 8 * g);
+        const floatx4 sc = TT::mma(qA, kB, floatx4{0.f, 0.f, 0.f, 0.f});
+        const floatx4 dpv = TT::mma(dA, vB, floatx4{0.f, 0.f, 0.f, 0.f});
+        // this lane: query slots qt*16 + 4g .. +3 of key ks
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_h + qt * 16 + 4 * g);
+        const float4 d4 = *reinterpret_cast<const float4*>(dd_h + qt * 16 + 4 * g);
+        const float la[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float da[4] = {d4.x, d4.y, d4.z, d4.w};
+        float pr[4], dz[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c, -la[i]));
+          dz[i] = pr[i] * (dpv[i] - da[i]);
+        }
+        const op4 pB = TT::from_f32_4(pr);
+        const op4 zB = TT::from_f32_4(dz);
+        // dV^T += dO^T P and dK^T += Q^T dZ: A operand of tile ct (slots =
+        // query slots qt*16 + 4g .. +3) by a transposing read in which lane
+        // col = 4 s + q reads query row qt*16 + 4g + s at channels 8 q + 4 ct
+        // .. +3 (row r of the tile is channel 8 (r / 4) + 4 ct + r % 4)
+        const int ts = qt * 16 + 4 * g + srow;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const op4 dOA = read_tr(Dh + ts * kRowT + 8 * q4 + 4 * ct);
+          const op4 QA = read_tr(Qh + ts * kRowT + 8 * q4 + 4 * ct);
+          dv[ct] = TT::mma16(dOA, pB, dv[ct]);
+          dk[ct] = TT::mma16(QA, zB, dk[ct]);
+        }
+      }
+    }
+    __syncthreads();  // Q, dO, dQ rows, log-sum-exp and D consumed before the next region
+  }
+
+  // ---- dK and dV rows of key region r: the pair's 64-byte halves meet in
+  // LDS (over the Q and dO rows) and leave as whole rows. Tile ct of a lane
+  // holds channels 8g + 4 ct .. +3 of key tq*16 + col.
+  uint4* xr = reinterpret_cast<uint4*>(Qs);  // [dV, dK][key][chunk]
+  if (busy) {
+    float ov[8], ok[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ov[e] = dv[0][e];
+      ov[4 + e] = dv[1][e];
+      ok[e] = dk[0][e] * p.scale;
+      ok[4 + e] = dk[1][e] * p.scale;
+    }
+    const int at = (tq * 16 + col) * 8 + hl * 4 + g;
+    xr[at] = __builtin_bit_cast(uint4, TT::from_f32(ov));
+    xr[512 + at] = __builtin_bit_cast(uint4, TT::from_f32(ok));
+  }
+  __syncthreads();
+  if (st_ok) {
+    const int64_t off = st_g + (int64_t)(rcorner + st_off) * p.C;
+    __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[st_tok * 8 + st_c]), reinterpret_cast<op8*>(p.dV + off));
+    __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[512 + st_tok * 8 + st_c]),
+                                reinterpret_cast<op8*>(p.dK + off));
+    if (own_bad) {
+      // this region's own routing row is out of range: NaN dQ for its queries
+      float nanv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) nanv[e] = __builtin_nanf("");
+      TT::store8(p.dQ + st_g + (int64_t)(rcorner + st_off) * p.C, nanv);
+    }
+  }
+}
+
+}  // namespace
+
+bool backward_top1_fits(const Shape& s, int dtype) {
+  if (dtype != kBF16 || s.d != kHeadDim || s.topk != 1) return false;
+  // regions of 16 to 64 tokens: one to four 16-row tiles per head
+  if (s.n < 16 || s.n > 64 || s.R > kMaxRegions) return false;
+  const int64_t nwg = (int64_t)s.B * s.R * ((s.heads + 1) / 2);
+  return nwg < (int64_t(1) << 31);
+}
+
+hipError_t launch_backward_top1(const void* Q, const void* K, const void* V, const void* dO, const int32_t* idx,
+                                void* dQ, void* dK, void* dV, const Shape& s, hipStream_t stream) {
+  BwdTop1Params p{};
+  p.Q = static_cast<const __bf16*>(Q);
+  p.K = static_cast<const __bf16*>(K);
+  p.V = static_cast<const __bf16*>(V);
+  p.dO = static_cast<const __bf16*>(dO);
+  p.idx = idx;
+  p.dQ = static_cast<__bf16*>(dQ);
+  p.dK = static_cast<__bf16*>(dK);
+  p.dV = static_cast<__bf16*>(dV);
+  p.H = s.H; p.W = s.W; p.C = s.C; p.S = s.S;
+  p.sh = s.sh; p.sw = s.sw; p.n = s.n; p.R = s.R; p.heads = s.heads;
+  p.nhg = (s.heads + 1) / 2;
+  p.scale = 1.0f / sqrtf((float)s.d);
+  p.c = p.scale * 1.4426950408889634f;
+  p.div_sw = make_fastdiv(s.sw);
+  p.div_S = make_fastdiv(s.S);
+  const void* fn = s.n < 64 ? (const void*)&bwd_top1_kernel<true> : (const void*)&bwd_top1_kernel<false>;
+  void* args[] = {&p};
+  const unsigned nwg = (unsigned)((int64_t)s.B * s.R * p.nhg);
+  return hipLaunchKernel(fn, dim3(nwg), dim3(kTop1Threads), args, 0, stream);
+}
+
+}  // namespace bra

@@ -122,4 +122,13 @@ hipError_t launch_backward_image(const void* Q, const void* K, const void* V, co
                                  const int32_t* idx, void* dQ, void* dK, void* dV, const Shape& s,
                                  hipStream_t stream);
 
+// The same backward in one launch for top-1 routing (bf16, regions of 16 to
+// 64 tokens): one workgroup per (image, key region, pair of heads) takes the
+// query regions routed to its region and finishes their dQ and its dK, dV
+// (backward_top1.hip). O is not read: D = rowsum(P * dP). launch_backward
+// takes it when it fits and the image kernel does not.
+bool backward_top1_fits(const Shape& s, int dtype);
+hipError_t launch_backward_top1(const void* Q, const void* K, const void* V, const void* dO, const int32_t* idx,
+                                void* dQ, void* dK, void* dV, const Shape& s, hipStream_t stream);
+
 }  // namespace bra
