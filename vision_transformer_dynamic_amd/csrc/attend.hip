@@ -736,7 +736,7 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
         o[4] += hi.x; o[5] += hi.y; o[6] += hi.z; o[7] += hi.w;
       }
       if constexpr (sizeof(T) == 2) {
-        if (rows) xrow[(t & 1) * 128 + col * 8 + head * 4 + g] = __builtin_bit_cast(uint4, TT::from_f32(o));
+        if (rows) xrow[(t & 1) * 128 + xrow_at(col, head * 4 + g)] = __builtin_bit_cast(uint4, TT::from_f32(o));
         else TT::store8_nt(Og + qoff[t], o);
       } else {
         TT::store8_nt(Og + qoff[t], o);
@@ -757,7 +757,7 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
         if (qi < it.q0 + it.nq) {
           int qx;
           const int qy = fdiv(qi, p.div_sw, &qx);
-          const uint4 v = xrow[(t & 1) * 128 + q * 8 + c];
+          const uint4 v = xrow[(t & 1) * 128 + xrow_at(q, c)];
           __builtin_nontemporal_store(__builtin_bit_cast(op8, v),
                                       reinterpret_cast<op8*>(Og + (it.qcorner + qy * p.W + qx) * p.C + it.cb + 8 * c));
         }

@@ -211,6 +211,14 @@ __device__ inline void store_vt_pair(float* Vt, int ldv, int row0, int col, cons
     *reinterpret_cast<uint2*>(Vt + (row0 + e) * ldv + col) = make_uint2(wa[e], wb[e]);
 }
 
+// Whole-row exchange buffers ([row][8 chunks of 16 bytes], two heads' halves
+// of 128-byte output rows): chunk c of row r sits at chunk c ^ (r % 8). The
+// 16 lanes of a group writing one chunk of 16 consecutive rows then meet no
+// LDS bank conflict; unswizzled, the 128-byte row stride puts them on the
+// same banks (about 68 conflict cycles a write on gfx950, measured with
+// SQ_LDS_BANK_CONFLICT).
+__device__ inline int xrow_at(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
 // Sum over the 4 lane groups that share lane % 16, as (g0 + g1) + (g2 + g3).
 __device__ inline float wave_sum_groups(float v) { return xor32_pair_sum(xor16_pair_sum(v)); }
 

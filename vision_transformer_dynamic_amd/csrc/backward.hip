@@ -629,7 +629,7 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
         o[4 + e] = dq[1][e] * p.scale;
       }
       if constexpr (sizeof(T) == 2) {
-        if (rows) xrow[(t & 1) * 128 + col * 8 + wave * 4 + g] = __builtin_bit_cast(uint4, TT::from_f32(o));
+        if (rows) xrow[(t & 1) * 128 + xrow_at(col, wave * 4 + g)] = __builtin_bit_cast(uint4, TT::from_f32(o));
         else TT::store8_nt(dQg + qtok[t] * p.C + ch0 + 8 * g, o);
       } else {
         TT::store8_nt(dQg + qtok[t] * p.C + ch0 + 8 * g, o);
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
         const int q = 8 * wave + (lane >> 3), c = lane & 7;
         const int tq = __builtin_amdgcn_ds_bpermute(q << 2, qtok[t]);  // lane q holds query q's token
         if (tq >= 0) {
-          const uint4 v = xrow[(t & 1) * 128 + q * 8 + c];
+          const uint4 v = xrow[(t & 1) * 128 + xrow_at(q, c)];
           __builtin_nontemporal_store(__builtin_bit_cast(op8, v),
                                       reinterpret_cast<op8*>(dQg + tq * p.C + hg * p.HG * D + 8 * c));
         }
@@ -884,9 +884,9 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
     }
     if constexpr (sizeof(T) == 2) {
       if (rows) {
-        // [tensor][key half][key tile][key][head][chunk]
+        // [tensor][key half][key tile][key][head][chunk], chunks swizzled (xrow_at)
         uint4* xr = reinterpret_cast<uint4*>(smem_raw);
-        const int at = ((kh * 2 + kt2) * 16 + col) * 8 + hl * 4 + g;
+        const int at = xrow_at((kh * 2 + kt2) * 16 + col, hl * 4 + g);
         xr[at] = __builtin_bit_cast(uint4, TT::from_f32(ov));
         xr[512 + at] = __builtin_bit_cast(uint4, TT::from_f32(ok));
         continue;
@@ -910,7 +910,7 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
           int tx;
           const int ty = fdiv(key, p.div_sw, &tx);
           const int off = (rcorner + ty * p.W + tx) * p.C + hg * 2 * D + 8 * c;
-          const int at = ((kh * 2 + kt2) * 16 + kc) * 8 + c;
+          const int at = xrow_at((kh * 2 + kt2) * 16 + kc, c);
           __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[at]), reinterpret_cast<op8*>(dVg + off));
           __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[512 + at]), reinterpret_cast<op8*>(dKg + off));
         }

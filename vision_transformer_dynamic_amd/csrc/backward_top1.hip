@@ -41,8 +41,18 @@
 namespace bra {
 namespace {
 
-constexpr int kRowT = 40;  // LDS row stride in elements: 32 channels + 16 bytes of pad
+constexpr int kRowT = 32;  // LDS row of one token and head: 32 channels, 64 bytes, no pad
 constexpr int kHeadRows = 64 * kRowT;  // one head's rows of one tensor
+
+// LDS layouts, chosen by measuring gfx950's bank conflicts
+// (SQ_LDS_BANK_CONFLICT) for each access pattern of this kernel:
+//  * token rows: the 16-byte chunk c of row r sits at chunk c ^ 2 when bit 3
+//    of r is set. With that, the 16-byte operand reads (16 rows x 4 chunks,
+//    rows col or 8 (col / 4) + col % 4) and the staging writes meet no
+//    conflict, and the transposing reads 2 cycles; with 80-byte padded rows
+//    they cost 4, 4 and ~9 cycles an instruction.
+//  * whole-row exchange: xrow_at.
+__device__ inline int row_at(int row, int chunk) { return row * kRowT + 8 * (chunk ^ ((row >> 2) & 2)); }
 constexpr int kTop1Threads = 512;
 
 struct BwdTop1Params {
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
   const bool st_ok = st_tok < p.n && (st_c >> 2) < nh;
   int st_tx;
   const int st_off = fdiv(st_tok, p.div_sw, &st_tx) * p.W + st_tx;
-  const int st_at = ((st_c >> 2) * 64 + st_tok) * kRowT + 8 * (st_c & 3);
+  const int st_at = (st_c >> 2) * kHeadRows + row_at(st_tok, st_c & 3);
   const int64_t st_g = img + cb + 8 * st_c;  // + token * C
 
   // ---- K and V of key region r
@@ -187,8 +197,8 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
     if (busy) {
       const int qs = tq * 16 + col;
       const bool qv = !RAGGED || qs < p.n;
-      const op8 qop = TT::load8(Qh + qs * kRowT + 8 * g);
-      const op8 dop = TT::load8(Dh + qs * kRowT + 8 * g);
+      const op8 qop = TT::load8(Qh + row_at(qs, g));
+      const op8 dop = TT::load8(Dh + row_at(qs, g));
       // S^T = K Q^T, dP^T = V dO^T: A-operand row col of tile (st, tb) is key
       // st*32 + 8*(col/4) + col%4 + 4*tb, so lane group g holds keys
       // st*32 + 8g + e of its query
@@ -198,8 +208,8 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
-          const op8 kk = TT::load8(Kh + key * kRowT + 8 * g);
-          const op8 vv = TT::load8(Vh + key * kRowT + 8 * g);
+          const op8 kk = TT::load8(Kh + row_at(key, g));
+          const op8 vv = TT::load8(Vh + row_at(key, g));
           const floatx4 sa = TT::mma(kk, qop, floatx4{0.f, 0.f, 0.f, 0.f});
           const floatx4 pa = TT::mma(vv, dop, floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -259,8 +269,8 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
         const int k0 = st * 32 + 8 * g + srow;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const shortx4 lo = read_tr(Kh + k0 * kRowT + 8 * q4 + 4 * ct);
-          const shortx4 hi = read_tr(Kh + (k0 + 4) * kRowT + 8 * q4 + 4 * ct);
+          const shortx4 lo = read_tr(Kh + row_at(k0, q4) + 4 * ct);
+          const shortx4 hi = read_tr(Kh + row_at(k0 + 4, q4) + 4 * ct);
           const op8 kt = __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           dq[ct] = TT::mma(kt, zop, dq[ct]);
           dq[ct] = TT::mma(kt, zlo, dq[ct]);
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
         o[e] = dq[0][e] * p.scale;
         o[4 + e] = dq[1][e] * p.scale;
       }
-      xq[qs * 8 + hl * 4 + g] = __builtin_bit_cast(uint4, TT::from_f32(o));
+      xq[xrow_at(qs, hl * 4 + g)] = __builtin_bit_cast(uint4, TT::from_f32(o));
       if (g == 0) {
         // a query slot past n: P = 0 in phase 2
         lse_h[qs] = qv ? lse : INFINITY;
@@ -283,20 +293,20 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
 
     if (st_ok) {
       const int64_t off = st_g + (int64_t)(region_corner(p, iq) + st_off) * p.C;
-      __builtin_nontemporal_store(__builtin_bit_cast(op8, xq[st_tok * 8 + st_c]), reinterpret_cast<op8*>(p.dQ + off));
+      __builtin_nontemporal_store(__builtin_bit_cast(op8, xq[xrow_at(st_tok, st_c)]), reinterpret_cast<op8*>(p.dQ + off));
     }
 
     // ---- phase 2: dK, dV of key tile tq over the region's query tiles
     if (busy) {
       const int ks = tq * 16 + col;
       // B operands of S = Q K^T and dP = dO V^T: column = key ks, slots = channels 8g ..
-      const op8 kB = TT::load8(Kh + ks * kRowT + 8 * g);
-      const op8 vB = TT::load8(Vh + ks * kRowT + 8 * g);
+      const op8 kB = TT::load8(Kh + row_at(ks, g));
+      const op8 vB = TT::load8(Vh + row_at(ks, g));
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
         if (qt >= ntq) break;  // uniform
-        const op8 qA = TT::load8(Qh + (qt * 16 + col) * kRowT + 8 * g);
-        const op8 dA = TT::load8(Dh + (qt * 16 + col) * kRowT + 8 * g);
+        const op8 qA = TT::load8(Qh + row_at(qt * 16 + col, g));
+        const op8 dA = TT::load8(Dh + row_at(qt * 16 + col, g));
         const floatx4 sc = TT::mma(qA, kB, floatx4{0.f, 0.f, 0.f, 0.f});
         const floatx4 dpv = TT::mma(dA, vB, floatx4{0.f, 0.f, 0.f, 0.f});
         // this lane: query slots qt*16 + 4g .. +3 of key ks
@@ -319,8 +329,8 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
         const int ts = qt * 16 + 4 * g + srow;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const op4 dOA = read_tr(Dh + ts * kRowT + 8 * q4 + 4 * ct);
-          const op4 QA = read_tr(Qh + ts * kRowT + 8 * q4 + 4 * ct);
+          const op4 dOA = read_tr(Dh + row_at(ts, q4) + 4 * ct);
+          const op4 QA = read_tr(Qh + row_at(ts, q4) + 4 * ct);
           dv[ct] = TT::mma16(dOA, pB, dv[ct]);
           dk[ct] = TT::mma16(QA, zB, dk[ct]);
         }
@@ -342,15 +352,15 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
       ok[e] = dk[0][e] * p.scale;
       ok[4 + e] = dk[1][e] * p.scale;
     }
-    const int at = (tq * 16 + col) * 8 + hl * 4 + g;
+    const int at = xrow_at(tq * 16 + col, hl * 4 + g);
     xr[at] = __builtin_bit_cast(uint4, TT::from_f32(ov));
     xr[512 + at] = __builtin_bit_cast(uint4, TT::from_f32(ok));
   }
   __syncthreads();
   if (st_ok) {
     const int64_t off = st_g + (int64_t)(rcorner + st_off) * p.C;
-    __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[st_tok * 8 + st_c]), reinterpret_cast<op8*>(p.dV + off));
-    __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[512 + st_tok * 8 + st_c]),
+    __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[xrow_at(st_tok, st_c)]), reinterpret_cast<op8*>(p.dV + off));
+    __builtin_nontemporal_store(__builtin_bit_cast(op8, xr[512 + xrow_at(st_tok, st_c)]),
                                 reinterpret_cast<op8*>(p.dK + off));
     if (own_bad) {
       // this region's own routing row is out of range: NaN dQ for its queries
