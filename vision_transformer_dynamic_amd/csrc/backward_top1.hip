@@ -20,18 +20,18 @@
 //    sums). A region whose own row is outside [0, S*S) gets NaN dQ from its
 //    own key region's workgroup and is in no list.
 //  * K, V of region r and Q, dO of the incoming region go to LDS (the pair's
-//    128-byte rows, 16 bytes a thread); the next region's Q, dO are fetched
-//    into registers while the current one is processed.
+//    128-byte rows, 16 bytes a thread), loaded only when the list is not
+//    empty; the next region's Q, dO are fetched into registers while the
+//    current one is processed.
 //  * Phase 1 per (head, query tile): S^T = K Q^T and dP^T = V dO^T over the
 //    region's keys, then the softmax, D = rowsum(P * dP) (equal to
 //    rowsum(dO * O) for O = P V, without reading O), dZ and
-//    dQ^T = K^T dZ^T with K^T from gfx950's transposing LDS read. Log-sum-exp
-//    and D go to LDS; the pair's dQ halves meet in LDS and leave as whole
-//    128-byte rows.
-//  * Phase 2 per (head, key tile): S = Q K^T and dP = dO V^T again with the
-//    key as the column, so P and dZ are B operands as they stand:
-//    dV^T += dO^T P and dK^T += Q^T dZ (16-deep products, dO^T and Q^T by the
-//    transposing read), summed over the incoming regions in registers.
+//    dQ^T = K^T dZ^T with K^T from gfx950's transposing LDS read. P and dZ
+//    (bf16, as the products below take them) go to LDS; the pair's dQ halves
+//    meet in LDS and leave as whole 128-byte rows.
+//  * Phase 2 per (head, key tile): dV^T += dO^T P and dK^T += Q^T dZ
+//    (16-deep products; dO^T, Q^T and the P, dZ columns of the key tile by
+//    the transposing read), summed over the incoming regions in registers.
 //  * dK and dV rows leave once at the end (zero for a region nobody routes to).
 #include "bra_internal.h"
 #include "attn_common.h"
@@ -94,11 +94,11 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
   typedef TT::op8 op8;
   typedef TT::op4 op4;
   // K, V, Q, dO rows [head][64][kRowT] (Q and dO then hold the dK, dV rows
-  // at the end), log-sum-exp and D [head][64], the dQ rows [64][8 chunks],
-  // the incoming query regions
+  // at the end), P and dZ [tensor][head][64 queries][64 keys] (bf16, 16-byte
+  // chunks swizzled as in xrow_at), the dQ rows [64][8 chunks], the incoming
+  // query regions
   __shared__ __align__(16) __bf16 rows_s[4 * 2 * kHeadRows];
-  __shared__ __align__(16) float lse_s[2 * 64];
-  __shared__ __align__(16) float dd_s[2 * 64];
+  __shared__ __align__(16) __bf16 pz_s[2 * 2 * 64 * 64];
   __shared__ __align__(16) uint4 xq[64 * 8];
   __shared__ int qlist[kMaxRegions];
   __bf16* Ks = rows_s;
@@ -112,6 +112,17 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
   const int g = lane >> 4, col = lane & 15;
   const int hl = wave >> 2, tq = wave & 3;  // head of the pair, tile
   const int srow = col >> 2, q4 = col & 3;  // transposing reads: row offset, 4-channel block
+  // Lane bases of the swizzled row reads. Bit 3 of the row (the swizzle bit)
+  // is the same for every row a lane reads through one base: each base plus
+  // a constant number of whole rows (16, 32 or 4 of them) keeps it.
+  const int a_key = row_at(8 * (col >> 2) + (col & 3), g);  // A rows of S^T, dP^T (+ 32 st + 4 tb rows)
+  const int a_col = row_at(col, g);                         // rows = col (+ 16 per tile)
+  const int a_tr1 = row_at(8 * g + srow, q4);               // K^T reads (+ 32 st, + 4 rows)
+  const int a_tr2 = row_at(4 * g + srow, q4);               // dO^T, Q^T reads (+ 16 per tile)
+  // P and dZ of a query tile as B operands of the 16-deep products: lane
+  // 4 s + m of group g reads query row 4g + s (+ 16 per tile), keys
+  // 16 tq + 4m .. +3 (chunk 2 tq + m / 2, half m % 2; row % 8 is the lane's)
+  const int a_pz = (4 * g + srow) * 64 + 8 * ((2 * tq + (q4 >> 1)) ^ ((4 * g + srow) & 7)) + 4 * (q4 & 1);
 
   int w = blockIdx.x;
   const int hg = w % p.nhg;
@@ -134,15 +145,6 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
   const int st_at = (st_c >> 2) * kHeadRows + row_at(st_tok, st_c & 3);
   const int64_t st_g = img + cb + 8 * st_c;  // + token * C
 
-  // ---- K and V of key region r
-  const int rcorner = region_corner(p, r);
-  uint4 kst = make_uint4(0, 0, 0, 0), vst = kst;
-  if (st_ok) {
-    const int64_t off = st_g + (int64_t)(rcorner + st_off) * p.C;
-    kst = *reinterpret_cast<const uint4*>(p.K + off);
-    vst = *reinterpret_cast<const uint4*>(p.V + off);
-  }
-
   // ---- the query regions routed to r, ascending (one 64-region ballot per
   // step; at most kMaxRegions regions)
   int cnt = 0, first = -1;
@@ -163,22 +165,32 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
   const int own = irow[r];
   const bool own_bad = own < 0 || own >= p.R;
 
-  // ---- Q and dO of the first incoming region, into registers
+  // ---- K and V of key region r and Q and dO of the first incoming region,
+  // all issued together once the list is known (a region nobody routes to
+  // reads neither: about a third of them with top-1 routing over random
+  // features)
+  const int rcorner = region_corner(p, r);
   uint4 qst = make_uint4(0, 0, 0, 0), dst = qst;
-  if (cnt > 0 && st_ok) {
-    const int64_t off = st_g + (int64_t)(region_corner(p, first) + st_off) * p.C;
-    qst = *reinterpret_cast<const uint4*>(p.Q + off);
-    dst = *reinterpret_cast<const uint4*>(p.dO + off);
+  if (cnt > 0) {  // uniform
+    uint4 kst = make_uint4(0, 0, 0, 0), vst = kst;
+    if (st_ok) {
+      const int64_t koff = st_g + (int64_t)(rcorner + st_off) * p.C;
+      const int64_t qoff = st_g + (int64_t)(region_corner(p, first) + st_off) * p.C;
+      kst = *reinterpret_cast<const uint4*>(p.K + koff);
+      vst = *reinterpret_cast<const uint4*>(p.V + koff);
+      qst = *reinterpret_cast<const uint4*>(p.Q + qoff);
+      dst = *reinterpret_cast<const uint4*>(p.dO + qoff);
+    }
+    *reinterpret_cast<uint4*>(Ks + st_at) = kst;
+    *reinterpret_cast<uint4*>(Vs + st_at) = vst;
   }
-  *reinterpret_cast<uint4*>(Ks + st_at) = kst;
-  *reinterpret_cast<uint4*>(Vs + st_at) = vst;
 
   const __bf16* Kh = Ks + hl * kHeadRows;
   const __bf16* Vh = Vs + hl * kHeadRows;
   const __bf16* Qh = Qs + hl * kHeadRows;
   const __bf16* Dh = Ds + hl * kHeadRows;
-  float* lse_h = lse_s + hl * 64;
-  float* dd_h = dd_s + hl * 64;
+  __bf16* Ph = pz_s + hl * 64 * 64;
+  __bf16* Zh = pz_s + (2 + hl) * 64 * 64;
 
   floatx4 dv[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
   floatx4 dk[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
@@ -197,8 +209,8 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
     if (busy) {
       const int qs = tq * 16 + col;
       const bool qv = !RAGGED || qs < p.n;
-      const op8 qop = TT::load8(Qh + row_at(qs, g));
-      const op8 dop = TT::load8(Dh + row_at(qs, g));
+      const op8 qop = TT::load8(Qh + a_col + tq * 16 * kRowT);
+      const op8 dop = TT::load8(Dh + a_col + tq * 16 * kRowT);
       // S^T = K Q^T, dP^T = V dO^T: A-operand row col of tile (st, tb) is key
       // st*32 + 8*(col/4) + col%4 + 4*tb, so lane group g holds keys
       // st*32 + 8g + e of its query
@@ -207,9 +219,8 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          const int key = st * 32 + 8 * (col >> 2) + (col & 3) + 4 * tb;
-          const op8 kk = TT::load8(Kh + row_at(key, g));
-          const op8 vv = TT::load8(Vh + row_at(key, g));
+          const op8 kk = TT::load8(Kh + a_key + (st * 32 + 4 * tb) * kRowT);
+          const op8 vv = TT::load8(Vh + a_key + (st * 32 + 4 * tb) * kRowT);
           const floatx4 sa = TT::mma(kk, qop, floatx4{0.f, 0.f, 0.f, 0.f});
           const floatx4 pa = TT::mma(vv, dop, floatx4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -236,19 +247,22 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
       mx = wave_max_groups(mx);
+      // P in place of the scores (one exponential each), then D = rowsum(P * dP)
       float sum = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum += __builtin_amdgcn_exp2f((s[st][e] - mx) * p.c);
-      const float lse = mx * p.c + __builtin_log2f(wave_sum_groups(sum));
-      // P in place of the scores, then D = rowsum(P * dP)
+        for (int e = 0; e < 8; ++e) {
+          s[st][e] = __builtin_amdgcn_exp2f((s[st][e] - mx) * p.c);
+          sum += s[st][e];
+        }
+      const float inv = 1.0f / wave_sum_groups(sum);
       float dpart = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          s[st][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -lse));
+          s[st][e] *= inv;
           dpart = __builtin_fmaf(s[st][e], dp[st][e], dpart);
         }
       const float Dq = wave_sum_groups(dpart);
@@ -266,11 +280,14 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
         for (int e = 0; e < 8; ++e) dz[e] = s[st][e] * (dp[st][e] - Dq);
         const op8 zop = TT::from_f32(dz);
         const op8 zlo = TT::residual(dz, zop);  // dZ's low bits
-        const int k0 = st * 32 + 8 * g + srow;
+        // P and dZ (bf16) of keys st*32 + 8g .. +7 for phase 2; zero for a
+        // query slot past n
+        *reinterpret_cast<op8*>(Ph + qs * 64 + 8 * ((4 * st + g) ^ (qs & 7))) = qv ? TT::from_f32(s[st]) : TT::zero();
+        *reinterpret_cast<op8*>(Zh + qs * 64 + 8 * ((4 * st + g) ^ (qs & 7))) = qv ? zop : TT::zero();
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const shortx4 lo = read_tr(Kh + row_at(k0, q4) + 4 * ct);
-          const shortx4 hi = read_tr(Kh + row_at(k0 + 4, q4) + 4 * ct);
+          const shortx4 lo = read_tr(Kh + a_tr1 + st * 32 * kRowT + 4 * ct);
+          const shortx4 hi = read_tr(Kh + a_tr1 + (st * 32 + 4) * kRowT + 4 * ct);
           const op8 kt = __builtin_bit_cast(op8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           dq[ct] = TT::mma(kt, zop, dq[ct]);
           dq[ct] = TT::mma(kt, zlo, dq[ct]);
@@ -283,13 +300,8 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
         o[4 + e] = dq[1][e] * p.scale;
       }
       xq[xrow_at(qs, hl * 4 + g)] = __builtin_bit_cast(uint4, TT::from_f32(o));
-      if (g == 0) {
-        // a query slot past n: P = 0 in phase 2
-        lse_h[qs] = qv ? lse : INFINITY;
-        dd_h[qs] = qv ? Dq : 0.f;
-      }
     }
-    __syncthreads();  // dQ rows, log-sum-exp and D in LDS
+    __syncthreads();  // dQ rows, P and dZ in LDS
 
     if (st_ok) {
       const int64_t off = st_g + (int64_t)(region_corner(p, iq) + st_off) * p.C;
@@ -298,45 +310,26 @@ __global__ __launch_bounds__(kTop1Threads) void bwd_top1_kernel(BwdTop1Params p)
 
     // ---- phase 2: dK, dV of key tile tq over the region's query tiles
     if (busy) {
-      const int ks = tq * 16 + col;
-      // B operands of S = Q K^T and dP = dO V^T: column = key ks, slots = channels 8g ..
-      const op8 kB = TT::load8(Kh + row_at(ks, g));
-      const op8 vB = TT::load8(Vh + row_at(ks, g));
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
         if (qt >= ntq) break;  // uniform
-        const op8 qA = TT::load8(Qh + row_at(qt * 16 + col, g));
-        const op8 dA = TT::load8(Dh + row_at(qt * 16 + col, g));
-        const floatx4 sc = TT::mma(qA, kB, floatx4{0.f, 0.f, 0.f, 0.f});
-        const floatx4 dpv = TT::mma(dA, vB, floatx4{0.f, 0.f, 0.f, 0.f});
-        // this lane: query slots qt*16 + 4g .. +3 of key ks
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_h + qt * 16 + 4 * g);
-        const float4 d4 = *reinterpret_cast<const float4*>(dd_h + qt * 16 + 4 * g);
-        const float la[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float da[4] = {d4.x, d4.y, d4.z, d4.w};
-        float pr[4], dz[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], p.c, -la[i]));
-          dz[i] = pr[i] * (dpv[i] - da[i]);
-        }
-        const op4 pB = TT::from_f32_4(pr);
-        const op4 zB = TT::from_f32_4(dz);
+        // B operands: P and dZ of query slots qt*16 + 4g .. +3, key tq*16 + col
+        const op4 pB = read_tr(Ph + a_pz + qt * 16 * 64);
+        const op4 zB = read_tr(Zh + a_pz + qt * 16 * 64);
         // dV^T += dO^T P and dK^T += Q^T dZ: A operand of tile ct (slots =
         // query slots qt*16 + 4g .. +3) by a transposing read in which lane
         // col = 4 s + q reads query row qt*16 + 4g + s at channels 8 q + 4 ct
         // .. +3 (row r of the tile is channel 8 (r / 4) + 4 ct + r % 4)
-        const int ts = qt * 16 + 4 * g + srow;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const op4 dOA = read_tr(Dh + row_at(ts, q4) + 4 * ct);
-          const op4 QA = read_tr(Qh + row_at(ts, q4) + 4 * ct);
+          const op4 dOA = read_tr(Dh + a_tr2 + qt * 16 * kRowT + 4 * ct);
+          const op4 QA = read_tr(Qh + a_tr2 + qt * 16 * kRowT + 4 * ct);
           dv[ct] = TT::mma16(dOA, pB, dv[ct]);
           dk[ct] = TT::mma16(QA, zB, dk[ct]);
         }
       }
     }
-    __syncthreads();  // Q, dO, dQ rows, log-sum-exp and D consumed before the next region
+    __syncthreads();  // Q, dO, dQ rows, P and dZ consumed before the next region
   }
 
   // ---- dK and dV rows of key region r: the pair's 64-byte halves meet in
