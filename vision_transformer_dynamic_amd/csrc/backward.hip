@@ -671,6 +671,22 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
 // is computed. Small regions share a 16-query tile.
 constexpr int kStage = 64;  // query slots per stage
 
+// bf16 stage rows: 64-byte rows (a head's 32 channels), the 16-byte chunk c of
+// row r at c ^ 2 when bit 3 of r is set. The transposed operands come from
+// these rows by gfx950's transposing LDS read, so no transposed copy is
+// written. (Measured with SQ_LDS_BANK_CONFLICT: 16-byte reads of 16
+// consecutive rows meet no bank conflict this way, transposing reads 2 cycles;
+// the padded rows and transposed copies cost 4 and more.)
+__device__ inline int stage_row(int r, int c) { return r * D + 8 * (c ^ ((r >> 2) & 2)); }
+
+typedef __attribute__((address_space(3))) shortx4 lds_s4;
+
+// Transposing LDS read of 4 bf16 (8 bytes) at p: within each 16-lane group,
+// lane j receives element j % 4 of the reads of lanes 4 s + j / 4, s = 0..3.
+__device__ inline shortx4 read_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+}
+
 // slot s -> token of the query (inside the image), or -1 past the last slot
 __device__ __forceinline__ int slot_token(int s, int nslots, const int* corners, FastDiv div_n, FastDiv div_sw,
                                           int W) {
@@ -730,9 +746,14 @@ __device__ __forceinline__ void stage_store(T* Qn, T* dOn, T* Qt, T* dOt, float*
     const int cv = f % CVH, rest = f / CVH;
     const int qp = rest % (kStage / 2), tensor = rest / (kStage / 2);
     T* rows = tensor == 0 ? Qn : dOn;
-    *reinterpret_cast<uint4*>(rows + (2 * qp) * LDN + cv * VEC) = R.a[m];
-    *reinterpret_cast<uint4*>(rows + (2 * qp + 1) * LDN + cv * VEC) = R.b[m];
-    store_vt_pair(tensor == 0 ? Qt : dOt, LDT, cv * VEC, 2 * qp, R.a[m], R.b[m]);
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint4*>(rows + stage_row(2 * qp, cv)) = R.a[m];
+      *reinterpret_cast<uint4*>(rows + stage_row(2 * qp + 1, cv)) = R.b[m];
+    } else {
+      *reinterpret_cast<uint4*>(rows + (2 * qp) * LDN + cv * VEC) = R.a[m];
+      *reinterpret_cast<uint4*>(rows + (2 * qp + 1) * LDN + cv * VEC) = R.b[m];
+      store_vt_pair(tensor == 0 ? Qt : dOt, LDT, cv * VEC, 2 * qp, R.a[m], R.b[m]);
+    }
   }
   (lt < 64 ? lse : dd)[lt & 63] = R.v;
 }
@@ -745,9 +766,10 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   constexpr int VEC = TT::VEC;
   constexpr int CVH = D / VEC;
   constexpr int NI = 2 * (kStage / 2) * CVH / 128;  // stage items per lane (2 bf16, 4 fp32)
-  constexpr int LDN = D + 16 / (int)sizeof(T);
+  constexpr bool TRR = sizeof(T) == 2;  // bf16: swizzled rows and transposing reads, no transposed copies
+  constexpr int LDN = TRR ? D : D + 16 / (int)sizeof(T);
   constexpr int LDT = kStage + 16 / (int)sizeof(T);
-  constexpr int HEAD_ELEMS = 2 * kStage * LDN + 2 * D * LDT;  // Qn, dOn, Qt, dOt
+  constexpr int HEAD_ELEMS = 2 * kStage * LDN + (TRR ? 0 : 2 * D * LDT);  // Qn, dOn (, Qt, dOt)
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int corners[kMaxRegions];
 
@@ -817,6 +839,11 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   __syncthreads();  // corners
 
   const int vrow = 8 * (col >> 2) + (col & 3);
+  // bf16: lane bases of the row reads (row col, chunk g) and of the
+  // transposing reads (lane 4 s + q of group g: row 4g + s, chunk q); a whole
+  // number of 16-row tiles added keeps bit 3 of the row
+  const int a_row = TRR ? stage_row(col, g) : col * LDN + 8 * g;
+  const int a_tr = TRR ? stage_row(4 * g + (col >> 2), col & 3) : 0;
   StageRegs<NI> st;
   if (nstages > 0) stage_load<T, NI>(p, 0, nslots, corners, head_ok, lt, ch0, img, imgrow, head, st);
   for (int sg = 0; sg < nstages; ++sg) {
@@ -827,8 +854,8 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
     const int tiles = min(4, (nslots - sg * kStage + 15) >> 4);
     if (kt_live0) {
       for (int t = 0; t < tiles; ++t) {
-        const op8 qA = TT::load8(Qn + (t * 16 + col) * LDN + 8 * g);
-        const op8 dA = TT::load8(dOn + (t * 16 + col) * LDN + 8 * g);
+        const op8 qA = TT::load8(Qn + a_row + t * 16 * LDN);
+        const op8 dA = TT::load8(dOn + a_row + t * 16 * LDN);
         const float4 lq = *reinterpret_cast<const float4*>(lse + t * 16 + 4 * g);
         const float4 dq4 = *reinterpret_cast<const float4*>(dd + t * 16 + 4 * g);
         const float lqa[4] = {lq.x, lq.y, lq.z, lq.w};
@@ -850,9 +877,17 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          const int row = vrow + 4 * ct;  // channel of A row col
-          const op4 dOA = TT::load4(dOt + row * LDT + t * 16 + 4 * g);
-          const op4 QA = TT::load4(Qt + row * LDT + t * 16 + 4 * g);
+          // A operand row col = channel vrow + 4 ct; slots = query slots t*16 + 4g .. +3
+          op4 dOA, QA;
+          if constexpr (TRR) {
+            // lane 4 s + q reads slot row t*16 + 4g + s at channels 8 q + 4 ct .. +3
+            dOA = read_tr(dOn + a_tr + t * 16 * LDN + 4 * ct);
+            QA = read_tr(Qn + a_tr + t * 16 * LDN + 4 * ct);
+          } else {
+            const int row = vrow + 4 * ct;
+            dOA = TT::load4(dOt + row * LDT + t * 16 + 4 * g);
+            QA = TT::load4(Qt + row * LDT + t * 16 + 4 * g);
+          }
 #pragma unroll
           for (int kt2 = 0; kt2 < 2; ++kt2) {
             if (kt2 == 1 && !kt_live1) continue;
@@ -1033,7 +1068,8 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   // per head: Q and dO stage rows [64][32 + pad] and transposed [32][64 + pad],
   // then the stage's log-sum-exp and D
   const size_t pad = 16 / esz;
-  const size_t head_elems = 2 * 64 * (D + pad) + 2 * D * (64 + pad);
+  // bf16: the Q and dO rows only (64-byte rows, transposing reads); fp32: padded rows and transposed copies
+  const size_t head_elems = dtype == kBF16 ? 2 * 64 * D : 2 * 64 * (D + pad) + 2 * D * (64 + pad);
   const size_t ldsk = esz * HGk * head_elems + sizeof(float) * HGk * 2 * 64;
   return hipLaunchKernel(fk, dim3((unsigned)p.nitems_kv), dim3(HGk * 2 * 64), args, ldsk, stream);
 }
