@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libbra.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["pool.hip", "route.hip", "attend.hip", "attend_dense.hip", "lce.hip", "backward.hip", "backward_image.hip", "backward_top1.hip", "qkv.hip", "bra_api.hip"]
+SOURCES = ["pool.hip", "route.hip", "attend.hip", "attend_dense.hip", "lce.hip", "backward.hip", "backward_image.hip", "backward_top1.hip", "backward_dense.hip", "qkv.hip", "bra_api.hip"]
 # achievable-peak probes of the benchmark: a library of their own
 PEAK_LIB_NAME = "libbra_peak.so"
 PEAK_LIB_PATH = os.path.join(PKG, PEAK_LIB_NAME)

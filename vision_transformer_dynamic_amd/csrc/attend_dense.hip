@@ -37,6 +37,7 @@
 //    times O's bytes reached memory).
 #include "bra_internal.h"
 #include "attn_common.h"
+#include "lds_dma.h"
 
 #include <math.h>
 
@@ -65,24 +66,6 @@ struct DenseParams {
   FastDiv div_n, div_sw, div_S;
 };
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // vmcnt in bits [3:0] and [15:14]; expcnt and lgkmcnt left at their maximum
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Wait until at most n of the wave's vector memory loads are outstanding
-// (n clamped to 15: waiting for more of them is always safe).
-__device__ __forceinline__ void wait_vmcnt_at_most(int n) {
-  switch (n < 15 ? n : 15) {
-#define BRA_W(k) case k: wait_vmcnt<k>(); break;
-    BRA_W(0) BRA_W(1) BRA_W(2) BRA_W(3) BRA_W(4) BRA_W(5) BRA_W(6) BRA_W(7)
-    BRA_W(8) BRA_W(9) BRA_W(10) BRA_W(11) BRA_W(12) BRA_W(13) BRA_W(14)
-#undef BRA_W
-    default: wait_vmcnt<15>(); break;
-  }
-}
-
 // Byte offset of 16-byte chunk c of key row r inside a phase buffer. K: the
 // four chunks of a row rotate with bits 3-4 of the row, so that the 16 rows
 // of an operand read (rows 8 a + b + 4 t, a, b in 0..3) fall on distinct
@@ -91,25 +74,6 @@ __device__ __forceinline__ void wait_vmcnt_at_most(int n) {
 // different banks.
 __device__ __forceinline__ int k_off(int r, int c) { return r * kRowBytes + 16 * (c ^ ((r >> 3) & 3)); }
 __device__ __forceinline__ int v_off(int r, int c) { return r * kRowBytes + 16 * (c ^ (((r >> 3) & 1) << 1)); }
-
-typedef __attribute__((address_space(3))) shortx4 lds_s4;
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-
-// One direct-to-LDS load: 16 bytes per lane from gptr into the wave's 1 KB
-// block at LDS byte offset lds_off (uniform), lane l at lds_off + 16 l. The
-// instruction's address registers are read when it issues and it writes no
-// register, so nothing of it is pending in registers afterwards; its
-// completion is tracked by the wave's vector-memory counter only, which the
-// phase loop below waits on explicitly before any read of the block. (The
-// compiler cannot count these loads across the runtime-length issue loops,
-// so its own wait would be for all of them.)
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(lds_off) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_offset(const unsigned char* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>((const lds_u8*)p));
-}
 
 // Issue the direct-to-LDS loads of one phase of this wave: row blocks (16 key
 // rows, 1 KB per tensor) m = wave, wave + nw, ... of the phase. Lane l

@@ -1054,6 +1054,8 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
     ldsq = std::max(esz * (size_t)H8 * D * (KC + padv), fold ? inverse_table_lds(s.R) : 0);
     void* hargs[] = {&ph};
     e = hipLaunchKernel(fq, dim3((unsigned)(ph.nitems_q + extra)), dim3(H8 * 64), hargs, ldsq, stream);
+  } else if (backward_dq_dense_fits(s, dtype)) {
+    e = launch_backward_dq_dense(Q, K, V, O, dO, idx, dQ, p.lse, p.dd, s, stream);
   } else {
     if (dtype == kBF16)
       fq = ragged ? (const void*)&bwd_dq_kernel<__bf16, true> : (const void*)&bwd_dq_kernel<__bf16, false>;

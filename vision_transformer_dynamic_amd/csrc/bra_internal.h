@@ -122,6 +122,15 @@ hipError_t launch_backward_image(const void* Q, const void* K, const void* V, co
                                  const int32_t* idx, void* dQ, void* dK, void* dV, const Shape& s,
                                  hipStream_t stream);
 
+// dQ, log-sum-exp and D of the backward for bf16 with 65 to 1024 routed keys
+// per query: every routed key's K and V rows of a head staged in LDS by
+// direct-to-LDS loads, as in the dense forward (backward_dense.hip).
+// launch_backward takes it for the several-chunk dQ step when it fits.
+bool backward_dq_dense_fits(const Shape& s, int dtype);
+hipError_t launch_backward_dq_dense(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                                    const int32_t* idx, void* dQ, float* lse, float* dd, const Shape& s,
+                                    hipStream_t stream);
+
 // The same backward in one launch for top-1 routing (bf16, regions of 16 to
 // 64 tokens): one workgroup per (image, key region, pair of heads) takes the
 // query regions routed to its region and finishes their dQ and its dK, dV
