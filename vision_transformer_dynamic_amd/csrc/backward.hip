@@ -81,20 +81,24 @@ __device__ inline int xcd_remap(int skip = 0) { return xcd_item(blockIdx.x - ski
 // ---------------------------------------------------------------------------
 // 1. Inverse routing table of image b, key regions [r0, r1), by one
 // workgroup (a multiple of 64 threads) in lds: R rows of (R + 31) / 32 mask
-// words, then R row flags and R in-degrees. Each routing row becomes a bit
-// mask of its regions (bitwise OR is order-free); the in-degree of every key
-// region is a count over the good rows; then one wave per key region of the
-// range tests 64 rows at a time and places the good rows that hold it with a
-// ballot prefix count, so each list comes out ascending.
+// words, then R row flags, R in-degrees and R places. Each routing row becomes
+// a bit mask of its regions (bitwise OR is order-free); the in-degree of every
+// key region is an LDS count over the good rows' entries (integer adds, so the
+// order does not matter); then one wave per key region of the range tests 64
+// rows at a time and places the good rows that hold it with a ballot prefix
+// count, so each list comes out ascending. Every loop is spread over the
+// workgroup's threads: no thread walks all R rows or regions (at 256 regions
+// a thread per region doing so took about 30 us).
 __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds, int r0, int r1) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int R = p.R, k = p.topk, nw = (R + 31) >> 5;
   uint32_t* mask = lds;                                  // [R][nw]
   int* rowbad = reinterpret_cast<int*>(lds + R * nw);    // [R]
   int* deg = rowbad + R;                                 // [R]: in-degree of each key region
+  int* place = deg + R;                                  // [R]: place of key region r0 + j in the order
   const int32_t* idx = p.idx + (int64_t)b * R * k;
   for (int e = tid; e < R * nw; e += nt) mask[e] = 0u;
-  for (int i = tid; i < R; i += nt) rowbad[i] = 0;
+  for (int i = tid; i < R; i += nt) rowbad[i] = deg[i] = place[i] = 0;
   __syncthreads();
   for (int e = tid; e < R * k; e += nt) {
     const int i = e / k, r = idx[e];
@@ -111,10 +115,10 @@ __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds, int r0, 
     if (cnt != k) rowbad[i] = 1;
   }
   __syncthreads();
-  for (int r = tid; r < R; r += nt) {
-    int m = 0;
-    for (int i = 0; i < R; ++i) m += !rowbad[i] && ((mask[i * nw + (r >> 5)] >> (r & 31)) & 1u);
-    deg[r] = m;
+  // in-degrees: one count per entry of a good row (its entries are distinct)
+  for (int e = tid; e < R * k; e += nt) {
+    const int i = e / k;
+    if (!rowbad[i]) atomicAdd(&deg[idx[e]], 1);
   }
   __syncthreads();
   // wave w compacts the lists of key regions r0 + w, r0 + w + nwaves, ...
@@ -133,24 +137,30 @@ __device__ void inverse_table(const BwdParams& p, int b, uint32_t* lds, int r0, 
     if (lane == 0) p.inv_cnt[b * R + r] = m;
   }
   // the dK/dV kernel's order: key region r goes to place #{heavier, or as
-  // heavy with a lower index}
-  for (int r = r0 + tid; r < r1; r += nt) {
+  // heavy with a lower index}, counted over (r, q) pairs spread over the
+  // threads
+  const int nr = r1 - r0;
+  for (int e = tid; e < nr * R; e += nt) {
+    const int j = e / R, q = e - j * R, r = r0 + j;
+    const int dq = deg[q], dr = deg[r];
+    if (dq > dr || (dq == dr && q < r)) atomicAdd(&place[j], 1);
+  }
+  __syncthreads();
+  for (int j = tid; j < nr; j += nt) {
+    const int r = r0 + j;
     p.bad[b * R + r] = rowbad[r];
-    const int dr = deg[r];
-    int place = 0;
-    for (int q = 0; q < R; ++q) place += deg[q] > dr || (deg[q] == dr && q < r);
-    p.order[b * R + place] = r;
+    p.order[b * R + place[j]] = r;
   }
 }
 
 // LDS bytes of inverse_table
-constexpr size_t inverse_table_lds(int R) { return sizeof(uint32_t) * ((size_t)R * ((R + 31) / 32) + 2 * R); }
+constexpr size_t inverse_table_lds(int R) { return sizeof(uint32_t) * ((size_t)R * ((R + 31) / 32) + 3 * R); }
 
 // For more than 64 regions: a launch of its own, one workgroup per (image,
 // block of kRoutesBlock key regions); each rebuilds the image's masks.
 constexpr int kRoutesBlock = 16;
 __global__ __launch_bounds__(256) void bwd_routes_kernel(BwdParams p) {
-  __shared__ uint32_t lds[kMaxRegions * (kMaxRegions / 32) + 2 * kMaxRegions];
+  __shared__ uint32_t lds[kMaxRegions * (kMaxRegions / 32) + 3 * kMaxRegions];
   const int nblk = (p.R + kRoutesBlock - 1) / kRoutesBlock;
   const int b = blockIdx.x / nblk, r0 = (blockIdx.x - b * nblk) * kRoutesBlock;
   inverse_table(p, b, lds, r0, min(p.R, r0 + kRoutesBlock));
