@@ -26,13 +26,18 @@
 //     per query, bwd_dq_head_kernel: one wave per head looping over the
 //     query tiles, as in the forward. With several 64-key chunks,
 //     bwd_dq_kernel: one wave per (head, 16-query tile), two passes
-//     (log-sum-exp first).
-//  3. bwd_dkv_kernel: one wave per (head, 32 keys of one key region), looping
-//     over the queries of the inverse table's regions, staged 64 at a time
-//     in LDS (small regions share a tile): S = Q K^T and dP = dO V^T
-//     put each lane on one key with 4 queries, exactly the contraction slots
-//     of the 16-deep products dV^T += dO^T P and dK^T += Q^T dZ (dO^T, Q^T
-//     through LDS), so P and dZ never leave registers.
+//     (log-sum-exp first); in bf16 with head dim 32 and at most 1024 keys,
+//     the dense form of backward_dense.hip (every routed key staged in LDS).
+//  3. bwd_dkv_kernel: per (head, 32 keys of one key region), a loop over the
+//     queries of the inverse table's regions, staged in LDS (small regions
+//     share a tile): S = Q K^T and dP = dO V^T put each lane on one key with
+//     4 queries, exactly the contraction slots of the 16-deep products
+//     dV^T += dO^T P and dK^T += Q^T dZ (dO^T, Q^T through LDS), so P and dZ
+//     never leave registers. fp32: one wave, stages of 64 queries; bf16: two
+//     waves, stages of 128 queries, each wave taking half the 16-query tiles,
+//     the second wave's partial sums added to the first's through LDS.
+// With top-1 routing and small regions, backward_top1.hip does all three in
+// one launch.
 #include "attn_common.h"
 
 #include <math.h>
@@ -715,7 +720,9 @@ struct StageRegs {
   float v;
 };
 
-template <typename T, int NI>
+// STG: query slots per stage; the head's 2 STG threads (lane lt) share its
+// loads.
+template <typename T, int NI, int STG>
 __device__ __forceinline__ void stage_load(const BwdParams& p, int s0, int nslots, const int* corners, bool head_ok,
                                            int lt, int ch0, int64_t img, int64_t imgrow, int head,
                                            StageRegs<NI>& R) {
@@ -725,9 +732,9 @@ __device__ __forceinline__ void stage_load(const BwdParams& p, int s0, int nslot
   const T* dOg = static_cast<const T*>(p.dO) + img;
 #pragma unroll
   for (int m = 0; m < NI; ++m) {
-    const int f = lt + 128 * m;  // < 2 * (kStage / 2) * CVH
+    const int f = lt + 2 * STG * m;  // < 2 * (STG / 2) * CVH
     const int cv = f % CVH, rest = f / CVH;
-    const int qp = rest % (kStage / 2), tensor = rest / (kStage / 2);
+    const int qp = rest % (STG / 2), tensor = rest / (STG / 2);
     const T* src = tensor == 0 ? Qg : dOg;
     R.a[m] = make_uint4(0u, 0u, 0u, 0u);
     R.b[m] = R.a[m];
@@ -736,25 +743,25 @@ __device__ __forceinline__ void stage_load(const BwdParams& p, int s0, int nslot
     if (head_ok && ta >= 0) R.a[m] = *reinterpret_cast<const uint4*>(src + ta * p.C + ch0 + cv * VEC);
     if (head_ok && tb >= 0) R.b[m] = *reinterpret_cast<const uint4*>(src + tb * p.C + ch0 + cv * VEC);
   }
-  // lanes 0..63: log-sum-exp of slot s0 + lt; lanes 64..127: D of slot s0 + lt - 64
-  const int sl = lt & 63;
+  // lanes 0 .. STG-1: log-sum-exp of slot s0 + lt; the next STG: D of slot s0 + lt - STG
+  const int sl = lt % STG;
   const int tr = slot_token(s0 + sl, nslots, corners, p.div_n, p.div_sw, p.W);
-  R.v = lt < 64 ? INFINITY : 0.f;  // past the last slot: P = 0 and dZ = 0
-  if (head_ok && tr >= 0) R.v = (lt < 64 ? p.lse : p.dd)[(imgrow + tr) * p.heads + head];
+  R.v = lt < STG ? INFINITY : 0.f;  // past the last slot: P = 0 and dZ = 0
+  if (head_ok && tr >= 0) R.v = (lt < STG ? p.lse : p.dd)[(imgrow + tr) * p.heads + head];
 }
 
-template <typename T, int NI>
+template <typename T, int NI, int STG>
 __device__ __forceinline__ void stage_store(T* Qn, T* dOn, T* Qt, T* dOt, float* lse, float* dd, int lt,
                                             const StageRegs<NI>& R) {
   constexpr int VEC = Tr<T>::VEC;
   constexpr int CVH = D / VEC;
   constexpr int LDN = D + 16 / (int)sizeof(T);  // row tiles: one 16-byte pad per row
-  constexpr int LDT = kStage + 16 / (int)sizeof(T);
+  constexpr int LDT = STG + 16 / (int)sizeof(T);
 #pragma unroll
   for (int m = 0; m < NI; ++m) {
-    const int f = lt + 128 * m;
+    const int f = lt + 2 * STG * m;
     const int cv = f % CVH, rest = f / CVH;
-    const int qp = rest % (kStage / 2), tensor = rest / (kStage / 2);
+    const int qp = rest % (STG / 2), tensor = rest / (STG / 2);
     T* rows = tensor == 0 ? Qn : dOn;
     if constexpr (sizeof(T) == 2) {
       *reinterpret_cast<uint4*>(rows + stage_row(2 * qp, cv)) = R.a[m];
@@ -765,21 +772,26 @@ __device__ __forceinline__ void stage_store(T* Qn, T* dOn, T* Qt, T* dOt, float*
       store_vt_pair(tensor == 0 ? Qt : dOt, LDT, cv * VEC, 2 * qp, R.a[m], R.b[m]);
     }
   }
-  (lt < 64 ? lse : dd)[lt & 63] = R.v;
+  (lt < STG ? lse : dd)[lt % STG] = R.v;
 }
 
-template <typename T>
+// SPL: waves per (head, key half), each taking its own 4 of the stage's
+// 16-slot tiles (stages of 64 SPL slots); their partial sums meet in LDS at
+// the end in a fixed order.
+template <typename T, int SPL>
 __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   typedef Tr<T> TT;
   typedef typename TT::op8 op8;
   typedef typename TT::op4 op4;
   constexpr int VEC = TT::VEC;
   constexpr int CVH = D / VEC;
-  constexpr int NI = 2 * (kStage / 2) * CVH / 128;  // stage items per lane (2 bf16, 4 fp32)
+  constexpr int STG = kStage * SPL;  // query slots per stage
+  constexpr int NI = 2 * (STG / 2) * CVH / (128 * SPL);  // stage items per lane (2 bf16, 4 fp32)
   constexpr bool TRR = sizeof(T) == 2;  // bf16: swizzled rows and transposing reads, no transposed copies
+  static_assert(TRR || SPL == 1, "the fp32 form keeps one wave per (head, key half)");
   constexpr int LDN = TRR ? D : D + 16 / (int)sizeof(T);
-  constexpr int LDT = kStage + 16 / (int)sizeof(T);
-  constexpr int HEAD_ELEMS = 2 * kStage * LDN + (TRR ? 0 : 2 * D * LDT);  // Qn, dOn (, Qt, dOt)
+  constexpr int LDT = STG + 16 / (int)sizeof(T);
+  constexpr int HEAD_ELEMS = 2 * STG * LDN + (TRR ? 0 : 2 * D * LDT);  // Qn, dOn (, Qt, dOt)
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __shared__ int corners[kMaxRegions];
 
@@ -799,25 +811,25 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   w /= p.nkb;
   const int b = w % p.B;
   const int r = p.order[b * p.R + w / p.B];
-  const int hl = wave >> 1, kh = wave & 1;
-  const int lt = kh * 64 + lane;  // lane within the head's two waves
+  const int hl = wave / (2 * SPL), kh = (wave / SPL) & 1, sh = wave % SPL;
+  const int lt = (wave % (2 * SPL)) * 64 + lane;  // lane within the head's 2 SPL waves
   const int head = hg * p.HGk + hl;
   const bool head_ok = head < p.heads;
   const int ch0 = head * D;
   const int64_t img = (int64_t)b * p.H * p.W * p.C;
   const int64_t imgrow = (int64_t)b * p.H * p.W;
   T* Qn = reinterpret_cast<T*>(smem_raw) + hl * HEAD_ELEMS;
-  T* dOn = Qn + kStage * LDN;
-  T* Qt = dOn + kStage * LDN;
+  T* dOn = Qn + STG * LDN;
+  T* Qt = dOn + STG * LDN;
   T* dOt = Qt + D * LDT;
-  float* lse = reinterpret_cast<float*>(reinterpret_cast<T*>(smem_raw) + p.HGk * HEAD_ELEMS) + hl * 2 * kStage;
-  float* dd = lse + kStage;
+  float* lse = reinterpret_cast<float*>(reinterpret_cast<T*>(smem_raw) + p.HGk * HEAD_ELEMS) + hl * 2 * STG;
+  float* dd = lse + STG;
 
   const int cnt = p.inv_cnt[b * p.R + r];
   const int* list = p.inv_list + ((int64_t)b * p.R + r) * p.R;
   for (int e = tid; e < cnt; e += blockDim.x) corners[e] = corner_of(p, list[e]);
   const int nslots = cnt * p.n;
-  const int nstages = (nslots + kStage - 1) / kStage;
+  const int nstages = (nslots + STG - 1) / STG;
 
   // the wave's 32 keys: key tile kt2 column col is key kb*64 + kh*32 + kt2*16 + col
   const int rcorner = corner_of(p, r);
@@ -855,15 +867,16 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
   const int a_row = TRR ? stage_row(col, g) : col * LDN + 8 * g;
   const int a_tr = TRR ? stage_row(4 * g + (col >> 2), col & 3) : 0;
   StageRegs<NI> st;
-  if (nstages > 0) stage_load<T, NI>(p, 0, nslots, corners, head_ok, lt, ch0, img, imgrow, head, st);
+  if (nstages > 0) stage_load<T, NI, STG>(p, 0, nslots, corners, head_ok, lt, ch0, img, imgrow, head, st);
   for (int sg = 0; sg < nstages; ++sg) {
-    stage_store<T, NI>(Qn, dOn, Qt, dOt, lse, dd, lt, st);
+    stage_store<T, NI, STG>(Qn, dOn, Qt, dOt, lse, dd, lt, st);
     __syncthreads();  // stage in LDS
     if (sg + 1 < nstages)
-      stage_load<T, NI>(p, (sg + 1) * kStage, nslots, corners, head_ok, lt, ch0, img, imgrow, head, st);
-    const int tiles = min(4, (nslots - sg * kStage + 15) >> 4);
+      stage_load<T, NI, STG>(p, (sg + 1) * STG, nslots, corners, head_ok, lt, ch0, img, imgrow, head, st);
+    // this wave's tiles of the stage: 4 sh .. 4 sh + 3
+    const int tiles = min(4 * sh + 4, (nslots - sg * STG + 15) >> 4);
     if (kt_live0) {
-      for (int t = 0; t < tiles; ++t) {
+      for (int t = 4 * sh; t < tiles; ++t) {
         const op8 qA = TT::load8(Qn + a_row + t * 16 * LDN);
         const op8 dA = TT::load8(dOn + a_row + t * 16 * LDN);
         const float4 lq = *reinterpret_cast<const float4*>(lse + t * 16 + 4 * g);
@@ -910,6 +923,34 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
     __syncthreads();  // stage consumed before the next one is stored
   }
 
+  if constexpr (SPL == 2) {
+    // the second slot half's partial sums join the first's (the stage area is
+    // free after the loop's last barrier): [head][key half][lane][dV 16 | dK 16
+    // floats], 32 KB, inside the 2 x 16 KB of the heads' stage rows
+    float* red = reinterpret_cast<float*>(smem_raw) + ((hl * 2 + kh) * 64 + lane) * 32;
+    if (sh == 1) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) {
+          *reinterpret_cast<floatx4*>(red + (ct * 2 + kt2) * 4) = dv[ct][kt2];
+          *reinterpret_cast<floatx4*>(red + 16 + (ct * 2 + kt2) * 4) = dk[ct][kt2];
+        }
+    }
+    __syncthreads();
+    if (sh == 0) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) {
+          dv[ct][kt2] += *reinterpret_cast<const floatx4*>(red + (ct * 2 + kt2) * 4);
+          dk[ct][kt2] += *reinterpret_cast<const floatx4*>(red + 16 + (ct * 2 + kt2) * 4);
+        }
+    }
+    __syncthreads();  // the area is reused below
+  }
+  const bool holder = sh == 0;  // this wave holds the finished sums of its (head, key half)
+
   T* dKg = static_cast<T*>(p.dK) + img;
   T* dVg = static_cast<T*>(p.dV) + img;
   // bf16 with two heads: the head waves of one key half exchange their
@@ -932,12 +973,14 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
         // [tensor][key half][key tile][key][head][chunk], chunks swizzled (xrow_at)
         uint4* xr = reinterpret_cast<uint4*>(smem_raw);
         const int at = xrow_at((kh * 2 + kt2) * 16 + col, hl * 4 + g);
-        xr[at] = __builtin_bit_cast(uint4, TT::from_f32(ov));
-        xr[512 + at] = __builtin_bit_cast(uint4, TT::from_f32(ok));
+        if (holder) {
+          xr[at] = __builtin_bit_cast(uint4, TT::from_f32(ov));
+          xr[512 + at] = __builtin_bit_cast(uint4, TT::from_f32(ok));
+        }
         continue;
       }
     }
-    if (!kval[kt2]) continue;
+    if (!kval[kt2] || !holder) continue;
     const int off = ktok[kt2] * p.C + ch0 + 8 * g;
     TT::store8_nt(dVg + off, ov);
     TT::store8_nt(dKg + off, ok);
@@ -949,6 +992,7 @@ __global__ __launch_bounds__(512) void bwd_dkv_kernel(BwdParams p) {
       const int kt2 = hl;  // this wave stores key tile hl of its key half
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
+        if (!holder) break;
         const int kc = 8 * h8 + (lane >> 3), c = lane & 7;  // key of the tile, 16-byte chunk of the row
         const int key = kb * 64 + kh * 32 + kt2 * 16 + kc;
         if (key < p.n) {
@@ -1076,14 +1120,17 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   }
   if (e != hipSuccess) return e;
 
-  const void* fk = dtype == kBF16 ? (const void*)&bwd_dkv_kernel<__bf16> : (const void*)&bwd_dkv_kernel<float>;
-  // per head: Q and dO stage rows [64][32 + pad] and transposed [32][64 + pad],
-  // then the stage's log-sum-exp and D
+  // bf16: two waves per (head, key half), each on its own half of 128-slot stages
+  const int spl = dtype == kBF16 ? 2 : 1;
+  const void* fk = dtype == kBF16 ? (const void*)&bwd_dkv_kernel<__bf16, 2> : (const void*)&bwd_dkv_kernel<float, 1>;
+  // per head: Q and dO stage rows (bf16: [128][32], 64-byte rows read by the
+  // transposing read; fp32: [64][32 + pad] and transposed copies
+  // [32][64 + pad]), then the stage's log-sum-exp and D
+  const size_t stg = 64 * (size_t)spl;
   const size_t pad = 16 / esz;
-  // bf16: the Q and dO rows only (64-byte rows, transposing reads); fp32: padded rows and transposed copies
-  const size_t head_elems = dtype == kBF16 ? 2 * 64 * D : 2 * 64 * (D + pad) + 2 * D * (64 + pad);
-  const size_t ldsk = esz * HGk * head_elems + sizeof(float) * HGk * 2 * 64;
-  return hipLaunchKernel(fk, dim3((unsigned)p.nitems_kv), dim3(HGk * 2 * 64), args, ldsk, stream);
+  const size_t head_elems = dtype == kBF16 ? 2 * stg * D : 2 * stg * (D + pad) + 2 * D * (stg + pad);
+  const size_t ldsk = esz * HGk * head_elems + sizeof(float) * HGk * 2 * stg;
+  return hipLaunchKernel(fk, dim3((unsigned)p.nitems_kv), dim3(HGk * 2 * spl * 64), args, ldsk, stream);
 }
 
 }  // namespace bra
