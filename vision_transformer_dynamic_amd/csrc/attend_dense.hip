@@ -13,10 +13,10 @@
 //    instruction gathers 16 key rows (64 bytes each: the head's 32 channels)
 //    straight from K or V into a 1 KB block of LDS, no registers involved.
 //    Rows are split into phases of 256 keys, each with its own K and V
-//    buffers; every wave issues its loads phase by phase, so before computing
-//    phase p a wave waits only for its own loads of phases <= p, then one
-//    barrier. The later phases' loads stay in flight under the earlier
-//    phases' products.
+//    buffers; every wave issues its loads phase by phase. Before phase 0 a
+//    wave waits only for its own loads of phase 0, then one barrier; before
+//    phase 1 for all of its loads, then a second barrier. The later phases'
+//    loads stay in flight under phase 0's products.
 //  * K rows are the A operands of S^T = K Q^T (16-byte reads, chunks of a
 //    row swizzled so that the 16 lanes of a read pass hit distinct banks).
 //  * V stays key-major as loaded: the A operand of O^T = V^T P^T (row =
@@ -147,12 +147,16 @@ __device__ __forceinline__ void dense_chunk(const DenseParams& p, const unsigned
       for (int e = 0; e < 8; ++e)
         if (st * 32 + 8 * g + e >= nvalid) s[st][e] = -INFINITY;
   }
+  // the lane's own maximum; the 4 lane groups' maxima are combined only when
+  // some lane's exceeds the lazy bound (always at the first chunk, where
+  // m_run = -inf), so the common case has no cross-lane exchange (dense map:
+  // 23.4 -> 22.0 us)
   float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
   for (int e = 2; e < 16; ++e) mx = fmaxf(mx, s[e >> 3][e & 7]);
-  mx = wave_max_groups(mx);
-  const bool grow = mx > m_run + p.lazy;  // always at the first chunk (m_run = -inf)
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + p.lazy) != 0) {  // uniform
+    mx = wave_max_groups(mx);
+    const bool grow = mx > m_run + p.lazy;
     const float mnew = grow ? mx : m_run;
     const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) * p.c);  // 1 where m stays, 0 at the start
 #pragma unroll
@@ -268,8 +272,18 @@ __global__ __launch_bounds__(kDenseTiles * 64) void attend_dense_kernel(DensePar
 #pragma unroll
   for (int ph = 0; ph < NPH; ++ph) {
     after -= cnt[ph];
-    wait_vmcnt_at_most(after);  // this wave's loads of phases <= ph have landed
-    __builtin_amdgcn_s_barrier();  // and every other wave's
+    // Phase 0 waits for its own loads. By the end of its products the later
+    // phases have landed as well (measured per workgroup with timestamps),
+    // so phase 1 waits once for all the rest and phases 2 and 3 need no
+    // barrier, whose waits would idle the waves that finish a phase first
+    // (dense map: 22.0 -> 21.8 us).
+    if (ph == 0) {
+      wait_vmcnt_at_most(after);  // this wave's loads of phase 0 have landed
+      __builtin_amdgcn_s_barrier();  // and every other wave's
+    } else if (ph == 1) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+    }
     const int p0 = ph * kPhaseRows;
     const int rows = min(kPhaseRows, p.kvpad - p0);
     const unsigned char* kbuf = ph == 0 ? k0 : ph == 1 ? k1 : ph == 2 ? k2 : k3;
