@@ -15,7 +15,9 @@
 // loops:
 //
 //  * pass 1, phase by phase as the loads land: S^T = K Q^T per 64-key chunk
-//    and the running maximum and sum, exact (a rescale at every new maximum);
+//    and the running maximum and sum, exact (a rescale at every new maximum).
+//    Each lane keeps its own over its own keys, and the four lane groups of a
+//    query meet once at the end, not at every chunk;
 //  * pass 2 over the staged keys: S^T and dP^T = V dO^T (K and V rows as A
 //    operands), P and dZ in registers, and dQ^T += K^T dZ^T with K^T from
 //    gfx950's transposing LDS read of the same K rows. dZ enters that product
@@ -257,18 +259,21 @@ __global__ __launch_bounds__(kTiles * 64) void bwd_dq_dense_kernel(BwdDenseParam
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
-      mx = wave_max_groups(mx);
-      const float mn = fmaxf(m, mx);
+      const float mn = fmaxf(m, mx);  // finite from the first chunk on (it holds 64 keys)
+      const float mc = mn * p.c;
       float add = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) add += __builtin_amdgcn_exp2f((s[st][e] - mn) * p.c);
+        for (int e = 0; e < 8; ++e) add += __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
       l = l * __builtin_amdgcn_exp2f((m - mn) * p.c) + add;
       m = mn;
     }
   }
-  const float lse = m * p.c + __builtin_log2f(wave_sum_groups(l));
+  // the four lane groups' sums, each over its own keys with its own maximum,
+  // brought to the query's maximum
+  const float mq = wave_max_groups(m);
+  const float lse = mq * p.c + __builtin_log2f(wave_sum_groups(l * __builtin_amdgcn_exp2f((m - mq) * p.c)));
 
   // ---- pass 2: P, dP, dZ and dQ^T += K^T dZ^T over the staged keys
   floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
