@@ -96,6 +96,8 @@ ROUTE_ANY_C = [
     wl.custom(1, 16, 16, 24, 1, 8, 64, "bf16", seed=52),  # 64 regions, full routing
     wl.custom(1, 16, 16, 48, 1, 16, 9, "bf16", seed=53),  # 256 regions, C = 48
     wl.custom(3, 8, 8, 96, 3, 8, 1, "bf16", seed=54),     # 64 regions, k = 1, 3 x 32 channels
+    wl.custom(2, 14, 14, 320, 10, 7, 4, "bf16", seed=55),  # 49 regions, C = 320: query rows not staged in LDS
+    wl.custom(1, 16, 16, 288, 9, 16, 5, "f32", seed=56),   # 256 regions, C = 288: the same in the 256-candidate form
 ]
 
 

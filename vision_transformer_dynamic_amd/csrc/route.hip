@@ -171,12 +171,34 @@ __global__ __launch_bounds__(NT) void route_kernel(RouteParams p) {
 constexpr int MR = 16;    // affinity rows per workgroup
 constexpr int MW = 8;     // waves: 4 candidate tiles x 2 channel halves
 
+// The block's 16 query rows are read from memory once per workgroup into
+// LDS (rows of C + 4 floats, so the 16 rows of an operand read start on
+// different banks), instead of once per candidate-tile wave: the kernel is
+// bound by each CU's load rate, and the query rows were most of its bytes
+// (4 of the 8 waves read the same rows of each channel half). Each wave's
+// first chunk of candidate rows is issued before the staging barrier.
+constexpr int kQPad = 4;  // floats of padding per staged query row
+constexpr int kQLdsMaxC = 256;  // channels up to which the query rows are staged (LDS stays under 64 KB)
+
+// Stage query rows i0 .. i0 + 15 of image row offset img (rows past R repeat
+// row R - 1, whose results are never used) into qs[16][C + kQPad].
+__device__ inline void stage_query_rows(const RouteParams& p, int64_t img, int i0, float* qs) {
+  const int c4n = p.C >> 2;
+  for (int f = threadIdx.x; f < 16 * c4n; f += blockDim.x) {
+    const int r = f / c4n, c4 = f - r * c4n;
+    const float4 v = *reinterpret_cast<const float4*>(p.Qr + (img + min(i0 + r, p.R - 1)) * p.C + 4 * c4);
+    *reinterpret_cast<float4*>(qs + r * (p.C + kQPad) + 4 * c4) = v;
+  }
+}
+
 // NS: 16-channel steps per wave loaded at once (a divisor of C / 32; all of a
-// chunk's loads are issued before its products)
-template <int NS>
+// chunk's loads are issued before its products). QLDS: query rows staged in
+// LDS (dynamic, 16 x (C + kQPad) floats).
+template <int NS, bool QLDS>
 __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
   __shared__ float part[MR][64];                    // channel half 1 of each tile
   __shared__ __align__(16) uint64_t keys[MR][64];   // keys of the block's rows
+  extern __shared__ __align__(16) float qs[];       // QLDS: [16][C + kQPad]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tile = wave & 3, half = wave >> 2;
   const int g = lane >> 4, l16 = lane & 15;
@@ -188,21 +210,32 @@ __global__ __launch_bounds__(MW * 64) void route_mfma_kernel(RouteParams p) {
   const bool active = j0 < ncol;
 
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (active) {
-    // A operand: lane supplies query row i0 + l16, B operand candidate row
-    // j0 + l16, both the channels 16 t + 4 g .. + 3 of the half at step t
-    // (rows past R read row R - 1; their results are never used)
-    const int nh = p.C >> 5;  // 16-channel steps per half
-    const int64_t img = (int64_t)b * p.R;
-    const float* qrow = p.Qr + (img + min(i0 + l16, p.R - 1)) * p.C + half * (p.C >> 1) + 4 * g;
-    const float* krow = p.Kr + (img + min(j0 + l16, p.R - 1)) * p.C + half * (p.C >> 1) + 4 * g;
-    for (int t0 = 0; t0 < nh; t0 += NS) {
-      float4 a[NS], k[NS];
+  // A operand: lane supplies query row i0 + l16, B operand candidate row
+  // j0 + l16, both the channels 16 t + 4 g .. + 3 of the half at step t
+  // (rows past R read row R - 1; their results are never used)
+  const int nh = p.C >> 5;  // 16-channel steps per half
+  const int64_t img = (int64_t)b * p.R;
+  const float* krow = p.Kr + (img + min(j0 + l16, p.R - 1)) * p.C + half * (p.C >> 1) + 4 * g;
+  float4 k[NS];
+  if (QLDS) {
+    if (active) {
 #pragma unroll
-      for (int m = 0; m < NS; ++m) {
-        a[m] = *reinterpret_cast<const float4*>(qrow + 16 * (t0 + m));
-        k[m] = *reinterpret_cast<const float4*>(krow + 16 * (t0 + m));
+      for (int m = 0; m < NS; ++m) k[m] = *reinterpret_cast<const float4*>(krow + 16 * m);
+    }
+    stage_query_rows(p, img, i0, qs);
+    __syncthreads();
+  }
+  if (active) {
+    const float* qrow = QLDS ? qs + l16 * (p.C + kQPad) + half * (p.C >> 1) + 4 * g
+                             : p.Qr + (img + min(i0 + l16, p.R - 1)) * p.C + half * (p.C >> 1) + 4 * g;
+    for (int t0 = 0; t0 < nh; t0 += NS) {
+      float4 a[NS];
+      if (!QLDS || t0 > 0) {
+#pragma unroll
+        for (int m = 0; m < NS; ++m) k[m] = *reinterpret_cast<const float4*>(krow + 16 * (t0 + m));
       }
+#pragma unroll
+      for (int m = 0; m < NS; ++m) a[m] = *reinterpret_cast<const float4*>(qrow + 16 * (t0 + m));
       __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk ahead of the products
 #pragma unroll
       for (int m = 0; m < NS; ++m) acc = affinity_mfma_step(acc, a[m], k[m]);
@@ -260,9 +293,12 @@ constexpr int BR = 16;     // affinity rows per workgroup
 constexpr int BW = 16;     // waves: one 16-candidate tile each
 constexpr int BMAX = 256;  // candidates
 
-template <int NS>
+// QLDS: the block's query rows staged once in LDS (dynamic, 16 x (C + kQPad)
+// floats), as in route_mfma_kernel: all 16 waves read the same rows.
+template <int NS, bool QLDS>
 __global__ __launch_bounds__(BW * 64) void route_mfma256_kernel(RouteParams p) {
   __shared__ __align__(16) uint64_t keys[BR][BMAX];
+  extern __shared__ __align__(16) float qs[];  // QLDS: [16][C + kQPad]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, l16 = lane & 15;
   const int w = xcd_item(blockIdx.x, gridDim.x);  // (image, row block), an image's blocks on one XCD
@@ -272,20 +308,30 @@ __global__ __launch_bounds__(BW * 64) void route_mfma256_kernel(RouteParams p) {
   const int64_t img = (int64_t)b * p.R;
 
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (j0 < p.R) {  // uniform
-    // A operand: query row i0 + l16; B operand: candidate row j0 + l16;
-    // channels 16 t + 4 g .. + 3 at step t (rows past R read row R - 1;
-    // their results are never used)
-    const float* qrow = p.Qr + (img + min(i0 + l16, p.R - 1)) * p.C + 4 * g;
-    const float* krow = p.Kr + (img + min(j0 + l16, p.R - 1)) * p.C + 4 * g;
-    const int nsteps = p.C >> 4;
-    for (int t0 = 0; t0 < nsteps; t0 += NS) {
-      float4 a[NS], k[NS];
+  // A operand: query row i0 + l16; B operand: candidate row j0 + l16;
+  // channels 16 t + 4 g .. + 3 at step t (rows past R read row R - 1;
+  // their results are never used)
+  const float* krow = p.Kr + (img + min(j0 + l16, p.R - 1)) * p.C + 4 * g;
+  const int nsteps = p.C >> 4;
+  float4 k[NS];
+  if (QLDS) {
+    if (j0 < p.R) {  // uniform
 #pragma unroll
-      for (int m = 0; m < NS; ++m) {
-        a[m] = *reinterpret_cast<const float4*>(qrow + 16 * (t0 + m));
-        k[m] = *reinterpret_cast<const float4*>(krow + 16 * (t0 + m));
+      for (int m = 0; m < NS; ++m) k[m] = *reinterpret_cast<const float4*>(krow + 16 * m);
+    }
+    stage_query_rows(p, img, i0, qs);
+    __syncthreads();
+  }
+  if (j0 < p.R) {  // uniform
+    const float* qrow = QLDS ? qs + l16 * (p.C + kQPad) + 4 * g : p.Qr + (img + min(i0 + l16, p.R - 1)) * p.C + 4 * g;
+    for (int t0 = 0; t0 < nsteps; t0 += NS) {
+      float4 a[NS];
+      if (!QLDS || t0 > 0) {
+#pragma unroll
+        for (int m = 0; m < NS; ++m) k[m] = *reinterpret_cast<const float4*>(krow + 16 * (t0 + m));
       }
+#pragma unroll
+      for (int m = 0; m < NS; ++m) a[m] = *reinterpret_cast<const float4*>(qrow + 16 * (t0 + m));
       __builtin_amdgcn_sched_barrier(0);  // keep every load of the chunk ahead of the products
 #pragma unroll
       for (int m = 0; m < NS; ++m) acc = affinity_mfma_step(acc, a[m], k[m]);
@@ -371,20 +417,29 @@ hipError_t launch_route(const float* Qr, const float* Kr, int32_t* idx,
     args[0] = &p;
     const unsigned grid = (unsigned)(s.B * p.row_blocks);
     const int nh = s.C / 32;
-    const void* fn = nh % 8 == 0   ? reinterpret_cast<const void*>(&route_mfma_kernel<8>)
-                     : nh % 4 == 0 ? reinterpret_cast<const void*>(&route_mfma_kernel<4>)
-                     : nh % 2 == 0 ? reinterpret_cast<const void*>(&route_mfma_kernel<2>)
-                                   : reinterpret_cast<const void*>(&route_mfma_kernel<1>);
-    return hipLaunchKernel(fn, dim3(grid), dim3(MW * 64), args, 0, stream);
+    const bool ql = s.C <= kQLdsMaxC;
+    const void* fns[2][4] = {
+        {reinterpret_cast<const void*>(&route_mfma_kernel<8, false>), reinterpret_cast<const void*>(&route_mfma_kernel<4, false>),
+         reinterpret_cast<const void*>(&route_mfma_kernel<2, false>), reinterpret_cast<const void*>(&route_mfma_kernel<1, false>)},
+        {reinterpret_cast<const void*>(&route_mfma_kernel<8, true>), reinterpret_cast<const void*>(&route_mfma_kernel<4, true>),
+         reinterpret_cast<const void*>(&route_mfma_kernel<2, true>), reinterpret_cast<const void*>(&route_mfma_kernel<1, true>)}};
+    const void* fn = fns[ql][nh % 8 == 0 ? 0 : nh % 4 == 0 ? 1 : nh % 2 == 0 ? 2 : 3];
+    const size_t lds = ql ? sizeof(float) * 16 * (size_t)(s.C + kQPad) : 0;
+    return hipLaunchKernel(fn, dim3(grid), dim3(MW * 64), args, lds, stream);
   }
   if (s.R <= BMAX && s.C % 32 == 0) {
     RouteParams p{Qr, Kr, idx, s.B, s.R, s.C, s.topk, (s.R + BR - 1) / BR, 0};
     args[0] = &p;
     const int nsteps = s.C / 16;  // even
-    const void* fn = nsteps % 8 == 0   ? reinterpret_cast<const void*>(&route_mfma256_kernel<8>)
-                     : nsteps % 4 == 0 ? reinterpret_cast<const void*>(&route_mfma256_kernel<4>)
-                                       : reinterpret_cast<const void*>(&route_mfma256_kernel<2>);
-    return hipLaunchKernel(fn, dim3((unsigned)(s.B * p.row_blocks)), dim3(BW * 64), args, 0, stream);
+    const bool ql = s.C <= kQLdsMaxC;
+    const void* fns[2][3] = {
+        {reinterpret_cast<const void*>(&route_mfma256_kernel<8, false>), reinterpret_cast<const void*>(&route_mfma256_kernel<4, false>),
+         reinterpret_cast<const void*>(&route_mfma256_kernel<2, false>)},
+        {reinterpret_cast<const void*>(&route_mfma256_kernel<8, true>), reinterpret_cast<const void*>(&route_mfma256_kernel<4, true>),
+         reinterpret_cast<const void*>(&route_mfma256_kernel<2, true>)}};
+    const void* fn = fns[ql][nsteps % 8 == 0 ? 0 : nsteps % 4 == 0 ? 1 : 2];
+    const size_t lds = ql ? sizeof(float) * 16 * (size_t)(s.C + kQPad) : 0;
+    return hipLaunchKernel(fn, dim3((unsigned)(s.B * p.row_blocks)), dim3(BW * 64), args, lds, stream);
   }
   RouteParams p{Qr, Kr, idx, s.B, s.R, s.C, s.topk, (s.R + RB - 1) / RB, (s.R + 3) / 4 * 4};
   args[0] = &p;
