@@ -676,15 +676,18 @@ __global__ __launch_bounds__(512) void bwd_dq_head_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // 3. dK, dV. Workgroup = (image b, key region r, block of <= 64 of its keys,
-// group of HGk heads); wave = (head, key half of 32 keys).
+// group of HGk heads); wave = (head, key half of 32 keys, slot group).
 // The queries of the key region's incoming query regions (inverse table, in
-// order) form one flat sequence of slots, taken 64 at a time ("stages"):
-// each stage's Q and dO rows go to LDS twice, as rows (A operands of
-// S = Q K^T and dP = dO V^T) and transposed (A operands of dV^T += dO^T P and
-// dK^T += Q^T dZ), with the slots' log-sum-exp and D, all loads of a stage in
-// flight together; the next stage's loads are issued before the current one
-// is computed. Small regions share a 16-query tile.
-constexpr int kStage = 64;  // query slots per stage
+// order) form one flat sequence of slots, taken 64 SPL at a time ("stages"),
+// with SPL slot groups each taking a 1 / SPL share of a stage's 16-slot
+// tiles. Each stage's Q and dO rows go to LDS as rows (A operands of
+// S = Q K^T and dP = dO V^T); the A operands of dV^T += dO^T P and
+// dK^T += Q^T dZ are their transposes: in fp32 (SPL = 1) transposed copies
+// written beside the rows, in bf16 (SPL = 2) the transposing LDS read of the
+// rows. With the slots' log-sum-exp and D, all loads of a stage are in flight
+// together, and the next stage's loads are issued before the current one is
+// computed. Small regions share a 16-query tile.
+constexpr int kStage = 64;  // query slots per stage and slot group
 
 // bf16 stage rows: 64-byte rows (a head's 32 channels), the 16-byte chunk c of
 // row r at c ^ 2 when bit 3 of r is set. The transposed operands come from
@@ -1056,7 +1059,7 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const vo
   p.HG = HG;
   p.nhg = (s.heads + HG - 1) / HG;
   const int64_t nq = (int64_t)s.B * s.R * p.nqb * p.nhg;
-  // dkv kernel: key blocks of 64, two waves per head, up to 2 heads
+  // dkv kernel: key blocks of 64 (two 32-key halves), up to 2 heads
   p.nkb = (s.n + 63) / 64;
   const int HGk = s.heads >= 2 ? 2 : 1;
   p.HGk = HGk;
