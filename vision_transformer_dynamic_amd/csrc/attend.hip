@@ -71,6 +71,7 @@ struct AttnParams {
   int lg_oct;  // log2(8 * HG * D / VEC): pair items per 8-pair octet of a chunk
   int nbuf;    // LDS chunk buffers (2: double-buffered; 4: two chunks per barrier)
   int own_tab; // single-chunk kernel: every attention wave builds its own key table
+  int rtab_off; // single-chunk kernel: byte offset of the key tables in dynamic LDS
   int qblk;    // queries per work item
   float c;     // softmax scale * log2(e)
   FastDiv div_n, div_sw, div_S;
@@ -492,11 +493,17 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   constexpr int LNB = LCE ? ((LR + 4) * ((2 * LX + 5) / 2) * 4 + 63) / 64 : 1;  // halo items per lane
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __shared__ int rtab[8 * KC];  // token offset of every routed key (per attention wave, or one shared)
+  // token offset of every routed key: one table per attention wave, or one
+  // shared (sized by the launch, after the V^T tiles and convolution areas)
+  int* rtab = reinterpret_cast<int*>(smem_raw + p.rtab_off);
   __shared__ int sbad;
   // two heads' output halves of a tile's query rows, per tile parity (bf16
-  // without the convolution term: 16 queries x 8 chunks of 16 bytes)
-  __shared__ __align__(16) uint4 xrow[(!LCE && sizeof(T) == 2) ? 2 * 16 * 8 : 1];
+  // without the convolution term: 16 queries x 8 chunks of 16 bytes, 4 KB):
+  // the V^T tiles' area, free once both head waves hold their V operands.
+  // With 15.4 KB of LDS a workgroup (the table sized for 8 heads, the
+  // exchange rows apart) 9 fit per CU at the stage-1 shape; with 9.5 KB the
+  // registers allow 10 (attention 23.1 -> 22.8 us, forward 35.6 -> 35.5 us).
+  uint4* xrow = reinterpret_cast<uint4*>(smem_raw);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -678,6 +685,12 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
         const int row = vrow + 4 * ct;
         vop[st][ct] = TT::load8(Vt + row * ldv + vt_col(row, st * 32 + 8 * g));
       }
+  }
+  if constexpr (!LCE && sizeof(T) == 2) {
+    if (rows) {  // uniform: both head waves hold their V operands before xrow reuses the area
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+    }
   }
 
 #pragma unroll
@@ -1344,6 +1357,8 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
     // per-wave key tables pay off when many head waves would otherwise wait on
     // one: 8 heads per workgroup measured faster, 2 and 4 slower
     p.own_tab = p.HG >= 8;
+    p.rtab_off = (int)lds;
+    lds += sizeof(int) * (size_t)(p.own_tab ? p.HG : 1) * KC;
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(waves * 64), args, lds, stream);
     if (e != hipSuccess || !lce || fuse) return e;
