@@ -71,7 +71,7 @@ struct AttnParams {
   int lg_oct;  // log2(8 * HG * D / VEC): pair items per 8-pair octet of a chunk
   int nbuf;    // LDS chunk buffers (2: double-buffered; 4: two chunks per barrier)
   int own_tab; // single-chunk kernel: every attention wave builds its own key table
-  int rtab_off; // single-chunk kernel: byte offset of the key tables in dynamic LDS
+  int rtab_off; // single-chunk kernel: byte offset of the key tables in dynamic LDS (< 0: in the exchange rows)
   int qblk;    // queries per work item
   float c;     // softmax scale * log2(e)
   FastDiv div_n, div_sw, div_S;
@@ -493,17 +493,20 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
   constexpr int LNB = LCE ? ((LR + 4) * ((2 * LX + 5) / 2) * 4 + 63) / 64 : 1;  // halo items per lane
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  // token offset of every routed key: one table per attention wave, or one
-  // shared (sized by the launch, after the V^T tiles and convolution areas)
-  int* rtab = reinterpret_cast<int*>(smem_raw + p.rtab_off);
-  __shared__ int sbad;
   // two heads' output halves of a tile's query rows, per tile parity (bf16
-  // without the convolution term: 16 queries x 8 chunks of 16 bytes, 4 KB):
-  // the V^T tiles' area, free once both head waves hold their V operands.
-  // With 15.4 KB of LDS a workgroup (the table sized for 8 heads, the
-  // exchange rows apart) 9 fit per CU at the stage-1 shape; with 9.5 KB the
-  // registers allow 10 (attention 23.1 -> 22.8 us, forward 35.6 -> 35.5 us).
-  uint4* xrow = reinterpret_cast<uint4*>(smem_raw);
+  // without the convolution term: 16 queries x 8 chunks of 16 bytes, 4 KB)
+  __shared__ __align__(16) uint4 xrow[(!LCE && sizeof(T) == 2) ? 2 * 16 * 8 : 1];
+  // token offset of every routed key (one table per attention wave, or one
+  // shared), then the bad-row flag: in dynamic LDS after the V^T tiles and
+  // convolution areas, or (rtab_off < 0: bf16, two heads, no convolution
+  // term) in the exchange rows' array, which the table precedes in time. A
+  // stage-1 workgroup then takes 9216 + 4096 bytes of LDS and 74 VGPRs, so
+  // 12 fit per CU (3,072 of the 3,136 regions in the first round); with the
+  // V operands held in registers (88 VGPRs) and the table sized for 8 heads,
+  // 9 fitted (forward 35.6 -> 34.7 us over the two steps).
+  const bool tab_in_x = !LCE && sizeof(T) == 2 && p.rtab_off < 0;  // uniform
+  int* rtab = tab_in_x ? reinterpret_cast<int*>(xrow) : reinterpret_cast<int*>(smem_raw + max(p.rtab_off, 0));
+  int& sbad = rtab[(p.own_tab ? p.HG : 1) * KC];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -673,21 +676,16 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
     return;
   }
 
-  // ---- V operands: row rr = col is channel 8*(rr/4) + (rr%4) + 4*ct; slots =
-  // keys st*32 + 8g .. +7
-  op8 vop[2][2];
-  {
-    const int vrow = 8 * (col >> 2) + (col & 3);
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const int row = vrow + 4 * ct;
-        vop[st][ct] = TT::load8(Vt + row * ldv + vt_col(row, st * 32 + 8 * g));
-      }
-  }
+  // ---- V operands, read from the wave's V^T tile at each use (holding all
+  // four in registers cost 14 VGPRs, one wave per SIMD): row rr = col is
+  // channel 8*(rr/4) + (rr%4) + 4*ct; slots = keys st*32 + 8g .. +7
+  const int vrow = 8 * (col >> 2) + (col & 3);
+  auto vop_at = [&](int st, int ct) {
+    const int row = vrow + 4 * ct;
+    return TT::load8(Vt + row * ldv + vt_col(row, st * 32 + 8 * g));
+  };
   if constexpr (!LCE && sizeof(T) == 2) {
-    if (rows) {  // uniform: both head waves hold their V operands before xrow reuses the area
+    if (tab_in_x && rows) {  // uniform: both head waves are done with the key table before xrow takes its place
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
     }
@@ -728,8 +726,8 @@ __global__ __launch_bounds__(1024) void attend_head_kernel(AttnParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
       const op8 pop = TT::from_f32(pe);
-      acc[0] = TT::mma(vop[st][0], pop, acc[0]);
-      acc[1] = TT::mma(vop[st][1], pop, acc[1]);
+      acc[0] = TT::mma(vop_at(st, 0), pop, acc[0]);
+      acc[1] = TT::mma(vop_at(st, 1), pop, acc[1]);
       acc[2] = TT::mma(ones, pop, acc[2]);
     }
     if (qoff[t] >= 0) {
@@ -1357,8 +1355,12 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V,
     // per-wave key tables pay off when many head waves would otherwise wait on
     // one: 8 heads per workgroup measured faster, 2 and 4 slower
     p.own_tab = p.HG >= 8;
-    p.rtab_off = (int)lds;
-    lds += sizeof(int) * (size_t)(p.own_tab ? p.HG : 1) * KC;
+    if (dtype == kBF16 && !fuse && p.HG == 2) {
+      p.rtab_off = -1;  // the table and flag live in the exchange rows' static array
+    } else {
+      p.rtab_off = (int)lds;
+      lds += sizeof(int) * ((size_t)(p.own_tab ? p.HG : 1) * KC + 1);
+    }
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(fn, dim3((unsigned)p.nitems), dim3(waves * 64), args, lds, stream);
     if (e != hipSuccess || !lce || fuse) return e;
