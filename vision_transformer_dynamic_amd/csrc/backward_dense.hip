@@ -14,15 +14,17 @@
 // with their own buffers, so the waves never wait on the caches inside their
 // loops:
 //
-//  * pass 1, phase by phase as the loads land: S^T = K Q^T per 64-key chunk
-//    and the running maximum and sum, exact (a rescale at every new maximum).
-//    Each lane keeps its own over its own keys, and the four lane groups of a
-//    query meet once at the end, not at every chunk;
-//  * pass 2 over the staged keys: S^T and dP^T = V dO^T (K and V rows as A
-//    operands), P and dZ in registers, and dQ^T += K^T dZ^T with K^T from
-//    gfx950's transposing LDS read of the same K rows. dZ enters that product
-//    as two bf16 operands (hi and its rounding error), as in the other dQ
-//    products.
+//  * one pass, phase by phase as the loads land: S^T = K Q^T and
+//    dP^T = V dO^T per 64-key chunk (K and V rows as A operands); with D from
+//    O and dO before any key, the probabilities relative to a lazy running
+//    maximum (moved only when a score exceeds it by more than 8 / c, as in
+//    the forward; the four lane groups' maxima combined only then), their
+//    running sum, dZ = P (dP - D) in registers, and dQ^T += K^T dZ^T with
+//    K^T from gfx950's transposing LDS read of the same K rows; dQ and the
+//    log-sum-exp come from the sum at the end. dZ enters the product as two
+//    bf16 operands (hi and its rounding error), as in the other dQ products.
+//    (Two passes, an exact log-sum-exp first, measured 114.9 us against
+//    107.2 us for the dense map's backward.)
 //
 // dQ and every query's base-2 log-sum-exp and D go to memory (the dK/dV kernel
 // reads the last two). A routing row with an entry outside [0, S*S) or a
@@ -226,59 +228,28 @@ __global__ __launch_bounds__(kTiles * 64) void bwd_dq_dense_kernel(BwdDenseParam
   const int a_row = row_off(8 * (col >> 2) + (col & 3), g);
   const int a_tr = row_off(8 * g + (col >> 2), col & 3);
 
-  // ---- pass 1: running maximum and sum per query, phase by phase as the
-  // loads land
-  float m = -INFINITY, l = 0.f;
+  // ---- one pass, phase by phase as the loads land: S^T, dP^T, and with a
+  // lazy running maximum m (moved only when a score exceeds it by more than
+  // 8 / c, the four lane groups' maxima combined only then) the unnormalised
+  // P = exp2(c s - c m), its running sum, dZ = P (dP - D) and
+  // dQ^T += K^T dZ^T; at the end dQ and the log-sum-exp from the sum
+  const float lazy = 8.0f / p.c;
+  float m_run = -INFINITY, lsum = 0.f;
   float s[2][8], dp[2][8];
+  floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
   int after = 0;
 #pragma unroll
   for (int ph = 0; ph < NPH; ++ph) after += cnt[ph];
 #pragma unroll
   for (int ph = 0; ph < NPH; ++ph) {
     after -= cnt[ph];
-    wait_vmcnt_at_most(after);     // this wave's loads of phases <= ph have landed
-    __builtin_amdgcn_s_barrier();  // and every other wave's
-    const int p0 = ph * kPhaseRows;
-    const int rows = min(kPhaseRows, p.kvpad - p0);
-    const unsigned char* kl = kb[ph] + a_row;
-#pragma unroll
-    for (int c = 0; c < kPhaseRows / KC; ++c) {
-      const int r0 = c * KC;
-      if (r0 >= rows) break;  // uniform
-      chunk_products<false>(kl + r0 * kRowBytes, nullptr, qop, dop, s, dp);
-      const int nvalid = p.kv - (p0 + r0);
-      if (RAGGED && nvalid < KC) {  // uniform
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (st * 32 + 8 * g + e >= nvalid) s[st][e] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s[st][e]);
-      const float mn = fmaxf(m, mx);  // finite from the first chunk on (it holds 64 keys)
-      const float mc = mn * p.c;
-      float add = 0.f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) add += __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
-      l = l * __builtin_amdgcn_exp2f((m - mn) * p.c) + add;
-      m = mn;
+    if (ph == 0) {
+      wait_vmcnt_at_most(after);
+      __builtin_amdgcn_s_barrier();
+    } else if (ph == 1) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
     }
-  }
-  // the four lane groups' sums, each over its own keys with its own maximum,
-  // brought to the query's maximum
-  const float mq = wave_max_groups(m);
-  const float lse = mq * p.c + __builtin_log2f(wave_sum_groups(l * __builtin_amdgcn_exp2f((m - mq) * p.c)));
-
-  // ---- pass 2: P, dP, dZ and dQ^T += K^T dZ^T over the staged keys
-  floatx4 dq[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int ph = 0; ph < NPH; ++ph) {
     const int p0 = ph * kPhaseRows;
     const int rows = min(kPhaseRows, p.kvpad - p0);
     const unsigned char* kl = kb[ph] + a_row;
@@ -297,12 +268,26 @@ __global__ __launch_bounds__(kTiles * 64) void bwd_dq_dense_kernel(BwdDenseParam
           for (int e = 0; e < 8; ++e)
             if (st * 32 + 8 * g + e >= nvalid) s[st][e] = -INFINITY;
       }
+      float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+      for (int e = 2; e < 16; ++e) mx = fmaxf(mx, s[e >> 3][e & 7]);
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + lazy) != 0) {  // uniform; always at the first chunk
+        mx = wave_max_groups(mx);
+        const float mnew = mx > m_run + lazy ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) * p.c);  // 0 at the start
+        dq[0] *= alpha;
+        dq[1] *= alpha;
+        lsum *= alpha;
+        m_run = mnew;
+      }
+      const float mc = m_run * p.c;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         float dz[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -lse));
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][e], p.c, -mc));
+          lsum += pr;
           dz[e] = pr * (dp[st][e] - Dq);
         }
         const op8 zop = TT::from_f32(dz);
@@ -319,7 +304,11 @@ __global__ __launch_bounds__(kTiles * 64) void bwd_dq_dense_kernel(BwdDenseParam
       }
     }
   }
-
+  const float ltot = wave_sum_groups(lsum);
+  const float lse = m_run * p.c + __builtin_log2f(ltot);
+  const float inv_l = 1.0f / ltot;
+  dq[0] *= inv_l;
+  dq[1] *= inv_l;
   if (qvalid) {
     // tile ct: this lane holds channels 8g + 4 ct .. +3 of its query
     float o[8];
