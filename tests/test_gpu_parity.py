@@ -120,6 +120,7 @@ EDGE = [
     wl.custom(1, 20, 20, 64, 2, 2, 2, "bf16", seed=11),    # n=100: a partial query block, ragged chunks
     wl.custom(1, 8, 12, 192, 6, 4, 5, "bf16", seed=12),    # H!=W, 6 heads: partial head group
     wl.custom(2, 32, 32, 96, 3, 4, 1, "bf16", seed=19),    # 3 heads: a two-head group and a one-head group
+    wl.custom(1, 26, 40, 64, 2, 2, 2, "bf16", seed=21),    # n=260, kv=520: three staged phases, two query blocks, ragged
     wl.custom(1, 16, 16, 32, 1, 16, 7, "bf16", seed=13),   # 256 regions, n=1
     wl.custom(1, 16, 16, 32, 1, 16, 256, "bf16", seed=14), # full routing over 256 regions
     wl.custom(2, 12, 12, 64, 2, 3, 9, "bf16", seed=15),    # k = S*S
